@@ -1,0 +1,243 @@
+"""Throughput of the InternVL visual-token compression connector on one MI355X.
+
+A step is one pass of the whole hot path over one batch of the 2B-Flash
+workload (16 images x 13 tiles = 208 tiles of 1025 x 1024 bf16 ViT rows,
+D = 2048, a 53,760-token prompt): ragged tile offsets, the connector run
+(pixel_shuffle + LayerNorm, mlp1, mlp2), the router (pooling, gating,
+quantile decision) and the sequence compaction.  Inputs and weights are
+synthetic (seeded) and resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is tiles per second; ``roofline`` describes
+the dominant kernel, timed with HIP events on the launch stream inside the
+timed region; ``cpu_baseline`` times the CPU oracle on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "connector tiles/s (+visual tokens/s) at 1 GPU; % of MFMA / HBM peak"
+WORKLOAD = "internvl35_2b_flash"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def gemm_flops(cfg: dict) -> dict:
+    """Algorithmic flops per launch of each GEMM kernel name (2 M N K; per
+    launch, summed over the launches of one step when a name repeats)."""
+    T, C, D = cfg["T"], cfg["C"], cfg["D"]
+    S, S64, N = cfg["S"], cfg["S64"], cfg["N"]
+    H1, H2, L = cfg["mlp1_hidden"], cfg["mlp2_hidden"], cfg["pool_layers"]
+    return {
+        "mlp1_gemm1": 2.0 * T * S * H1 * 4 * C,
+        "mlp1_gemm2": 2.0 * T * S * D * H1,
+        "mlp2_gemm1": 2.0 * T * S64 * H2 * 16 * C,
+        "mlp2_gemm2": 2.0 * T * S64 * H2 * H2,
+        "mlp2_gemm3": 2.0 * T * S64 * D * H2,
+        "pool_kv_gemm": 2.0 * T * N * 2 * L * C * C,
+    }
+
+
+def hbm_bytes(cfg: dict, L_seq: int, Lp: int) -> dict:
+    """Algorithmic HBM bytes per launch of the bandwidth-bound kernels."""
+    T, C, D, N = cfg["T"], cfg["C"], cfg["D"], cfg["N"]
+    e = 2
+    x_read = T * N * C * e  # CLS rows are skipped
+    return {
+        "shuffle_ln": x_read + T * cfg["S"] * 4 * C * e + T * cfg["S64"] * 16 * C * e,
+        "pool_attn": T * N * 2 * C * e,  # one layer's K and V
+        "compact": 2 * Lp * D * e + L_seq * 4 * 2 + Lp * 4 * 2,
+    }
+
+
+def cpu_baseline(cfg, w, seq, n_tiles: int) -> dict:
+    """The CPU oracle as it stands, on a bounded sample: the per-tile steps
+    (connector run + router pooling and gating) on ``n_tiles`` tiles, plus
+    the batch-wide steps (quantile, decision, compaction) on the whole batch;
+    scaled to tiles/s for a whole batch."""
+    import synth
+    from oracle import connector as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    tiles = list(range(n_tiles))
+    x = synth.make_vit_tiles(cfg, tiles)
+    t0 = time.perf_counter()
+    O.connector_run(x, cfg, w)
+    gate, _, _, _ = O.connector_route(x, cfg, w)
+    t1 = time.perf_counter()
+    per_tile = (t1 - t0) / n_tiles
+    # batch-wide steps over the whole batch (gate values / features of the
+    # right shape; the work does not depend on their values)
+    T = cfg["T"]
+    g0 = np.resize(gate[:, 0], T).astype(np.float32)
+    ids, emb = seq
+    o256 = np.zeros((T, cfg["S"], cfg["D"]), np.float32)
+    o64 = np.zeros((T, cfg["S64"], cfg["D"]), np.float32)
+    t2 = time.perf_counter()
+    thr, use = O.decide(g0, cfg)
+    O.compact(ids, emb, synth.IMG_CONTEXT, use, o256, o64, cfg["S"], cfg["S64"])
+    t3 = time.perf_counter()
+    batch_s = per_tile * T + (t3 - t2)
+    return {"value": T / batch_s, "unit": "tiles/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_tiles} tiles of run+route ({per_tile:.3f} s/tile) plus quantile, "
+                      f"decision and compaction over the full {T}-tile batch "
+                      f"({t3 - t2:.2f} s); scaled to one {T}-tile batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--pool-mode", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tiles", type=int, default=32)
+    ap.add_argument("--kernel-events", choices=["timed", "separate"], default="timed")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the connector's multi-GPU sharding is described in DESIGN.md, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from vlm_visual_token_amd import Connector, ivc
+
+    with open(os.path.join(ROOT, "tests", "golden", "gate_bias.json")) as f:
+        bias = json.load(f)["gate_bias0"][WORKLOAD]
+    cfg = dict(synth.config(WORKLOAD), pool_mode=args.pool_mode)
+    T = cfg["T"]
+    w = synth.make_weights(cfg, gate_bias0=bias)
+    wd = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in w.items()}
+    ids, emb = synth.make_sequence(cfg)
+    L = len(ids)
+    con = Connector(cfg, wd, max_tiles=T, max_seq_len=L)
+    del wd
+    x = torch.empty((T, cfg["rows"], cfg["C"]), dtype=torch.bfloat16, device="cuda")
+    for t0 in range(0, T, 16):
+        x[t0:t0 + 16].copy_(torch.from_numpy(synth.make_vit_tiles(cfg, range(t0, min(T, t0 + 16)))).to(torch.bfloat16))
+    ids_d = torch.from_numpy(ids).cuda()
+    emb_d = torch.from_numpy(emb).to(torch.bfloat16).cuda()
+    tiles_d = torch.tensor(cfg["tiles"], dtype=torch.int32, device="cuda")
+    off_d = torch.empty(len(cfg["tiles"]) + 1, dtype=torch.int32, device="cuda")
+    st_d = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o256 = torch.empty((T, cfg["S"], cfg["D"]), dtype=torch.bfloat16, device="cuda")
+    o64 = torch.empty((T, cfg["S64"], cfg["D"]), dtype=torch.bfloat16, device="cuda")
+    rbuf = None
+    cbuf = None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        nonlocal rbuf, cbuf
+        ivc.ivc_tile_offsets(tiles_d, len(cfg["tiles"]), off_d, st_d, stream)
+        con.run(x, o256, o64, stream=stream)
+        rbuf = con.route(x, with_pooled=False, stream=stream, out=rbuf)
+        cbuf = con.compact(ids_d, emb_d, rbuf["use64"], o256, o64, synth.IMG_CONTEXT,
+                           stream=stream, out=cbuf)
+
+    print(f"# warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(kernel_events: bool):
+        ivc.ivc_profile_reset()
+        ivc.ivc_profile_enable(kernel_events)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ivc.ivc_profile_enable(False)
+        return ev0.elapsed_time(ev1), ivc.ivc_profile_read()
+
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    if args.kernel_events == "timed":
+        ms, prof = timed(True)
+        ms_plain = None
+    else:
+        ms, _ = timed(False)
+        ms_plain = ms
+        _, prof = timed(True)
+    ms_step = ms / args.steps
+    use64 = rbuf["use64"].cpu().numpy()
+    Lp = int(cbuf["len"].item())
+    emitted = int((use64 == 0).sum()) * cfg["S"] + int(use64.sum()) * cfg["S64"]
+    tiles_per_s = T / (ms_step / 1e3)
+
+    # roofline of the dominant kernel (largest share of the step's kernel time)
+    flops = gemm_flops(cfg)
+    hbm = hbm_bytes(cfg, L, Lp)
+    kern = {k: {"ms_avg": v[0] / v[1], "launches_per_step": v[1] / args.steps,
+                "ms_per_step": v[0] / args.steps} for k, v in prof.items()}
+    dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    d = kern[dom]
+    if dom in flops:
+        ach = flops[dom] / (d["ms_avg"] / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None}
+    else:
+        ach = hbm.get(dom, 0.0) / (d["ms_avg"] / 1e3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None}
+    for k, v in kern.items():
+        if k in flops:
+            v["tflops"] = flops[k] / (v["ms_avg"] / 1e3) / 1e12
+        if k in hbm:
+            v["gbs"] = hbm[k] / (v["ms_avg"] / 1e3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"# cpu baseline ({args.cpu_tiles} tiles)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, w, (ids, emb), args.cpu_tiles)
+
+    out = {
+        "metric": METRIC,
+        "value": tiles_per_s,
+        "unit": "tiles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded ViT rows, random-init weights, synthetic prompt ids)",
+        "config": {"workload": WORKLOAD, "tiles": T, "images": len(cfg["tiles"]),
+                   "vit_tokens_per_tile": cfg["N"], "vit_width": cfg["C"], "llm_width": cfg["D"],
+                   "seq_len": L, "pool_mode": "kv" if args.pool_mode == 0 else "folded",
+                   "parallelism": "single GPU"},
+        "visual_tokens_per_s": emitted / (ms_step / 1e3),
+        "input_vit_tokens_per_s": T * cfg["N"] / (ms_step / 1e3),
+        "routed_to_64": int(use64.sum()),
+        "compacted_len": Lp,
+        "roofline": roof,
+        "kernels": kern,
+        "cpu_baseline": cpu,
+    }
+    if ms_plain is not None:
+        out["ms_per_step_without_kernel_events"] = ms_plain / args.steps
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

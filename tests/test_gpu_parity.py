@@ -1,0 +1,318 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: permutation, routing decisions, compaction indices and positions are
+bit-exact (decisions compared on the GPU's own gate values); bf16 float
+outputs within relative L2 1e-2 and max-abs 5e-2 x RMS; fp32 outputs within
+1e-5 / 1e-4 x RMS; gate probabilities within 2e-3 absolute.  Large workloads
+are checked on 16 sampled tiles (first, last and 14 drawn), the batch-wide
+steps (quantile, decisions, compaction) on every tile.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import connector as O
+from tests.gpu_util import (TORCH_DT, assert_close, dev_vit, dev_weights, host_weights, say,
+                            to_np, workload)
+
+pytestmark = pytest.mark.gpu
+
+GATE_TOL = 2e-3
+BAND = 1e-3  # tiles whose gate[:,0] is this close to a threshold are not compared for decisions
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from vlm_visual_token_amd import ivc
+    ivc.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _connector(cfg, w_host, max_tiles, max_seq=0):
+    from vlm_visual_token_amd import Connector
+    return Connector(cfg, dev_weights(cfg, w_host), max_tiles=max_tiles, max_seq_len=max_seq)
+
+
+# ---------------------------------------------------------------------------
+# pixel shuffle: bit-exact permutation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,P,C,T,has_cls", [
+    ("f32", 8, 64, 5, 1), ("bf16", 8, 64, 3, 0), ("bf16", 32, 1024, 3, 1), ("bf16", 32, 3200, 2, 1),
+    ("f32", 4, 4, 7, 1), ("bf16", 16, 8, 9, 1)])
+@pytest.mark.parametrize("r", [2, 4])
+def test_pixel_shuffle_bit_exact(dtype, P, C, T, has_cls, r):
+    from vlm_visual_token_amd import ivc
+    say(f"pixel_shuffle dtype={dtype} P={P} C={C} T={T} cls={has_cls} r={r}")
+    g = torch.Generator().manual_seed(P * 1000 + C + r)
+    x = torch.randn((T, has_cls + P * P, C), generator=g).to(TORCH_DT[dtype])
+    xd = x.cuda()
+    Q = P // r
+    out = torch.full((T, Q * Q, r * r * C), float("nan"), dtype=xd.dtype, device="cuda")
+    ivc.ivc_pixel_shuffle(1 if dtype == "bf16" else 0, xd, T, P, C, has_cls, r, out)
+    torch.cuda.synchronize()
+    exp = O.pixel_shuffle(O.token_grid(x.float().numpy(), P, has_cls), r)
+    got = out.float().cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), exp.astype(np.float32).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# tiny Flash workload, fp32: everything, every tile
+# ---------------------------------------------------------------------------
+def _tiny_all(valid=None, poison=False):
+    cfg = workload("tiny_flash_f32")
+    w = host_weights(cfg)
+    x = synth.make_vit(cfg)
+    if poison:
+        x[:, 0, :] = np.nan
+        if valid is not None:
+            for t in range(cfg["T"]):
+                x[t, 1 + valid[t]:, :] = np.nan
+    return cfg, w, x
+
+
+def test_tiny_run_matches_oracle():
+    cfg, w, x = _tiny_all()
+    say("tiny run")
+    con = _connector(cfg, w, cfg["T"])
+    o256, o64 = con.run(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    e256, e64 = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256), e256, "f32", "out256")
+    assert_close(to_np(o64), e64, "f32", "out64")
+
+
+@pytest.mark.parametrize("padded", [False, True])
+def test_tiny_route_matches_oracle(padded):
+    cfg = workload("tiny_flash_f32")
+    valid = synth.make_valid_tokens(cfg, seed=4) if padded else None
+    cfg, w, x = _tiny_all(valid, poison=padded)
+    say(f"tiny route padded={padded}")
+    con = _connector(cfg, w, cfg["T"])
+    vd = torch.from_numpy(valid).cuda() if padded else None
+    r = con.route(torch.from_numpy(x).cuda(), valid=vd)
+    torch.cuda.synchronize()
+    assert int(r["status"].item()) == 0
+    gate = r["gate"].cpu().numpy()
+    e_gate, e_thr, e_use, e_pooled = O.connector_route(x, cfg, w, valid)
+    assert_close(to_np(r["pooled"]), e_pooled, "f32", "pooled")
+    assert np.abs(gate - e_gate).max() <= GATE_TOL
+    # decisions on the GPU's own gates: bit-exact
+    thr, use = O.decide(gate[:, 0], cfg)
+    assert float(r["thr"].item()) == thr
+    assert np.array_equal(r["use64"].cpu().numpy(), use)
+    # and on independent gates, away from the thresholds
+    far = (np.abs(e_gate[:, 0] - e_thr) > 1e-3) & (np.abs(e_gate[:, 0] - 0.5) > 1e-3)
+    assert np.array_equal(r["use64"].cpu().numpy()[far], e_use[far])
+
+
+def test_tiny_compact_matches_oracle():
+    cfg, w, x = _tiny_all()
+    say("tiny compact")
+    ids, emb = synth.make_sequence(cfg)
+    con = _connector(cfg, w, cfg["T"], len(ids))
+    xd = torch.from_numpy(x).cuda()
+    o256, o64 = con.run(xd)
+    r = con.route(xd)
+    c = con.compact(torch.from_numpy(ids).cuda(), torch.from_numpy(emb).cuda(), r["use64"], o256,
+                    o64, synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    use = r["use64"].cpu().numpy()
+    assert 0 < use.sum() < cfg["T"], "workload should route some but not all tiles"
+    _check_compact(cfg, ids, emb, use, o256, o64, c)
+
+
+def _check_compact(cfg, ids, emb, use, o256, o64, c):
+    ref = O.compact(ids, emb, synth.IMG_CONTEXT, use, to_np(o256), to_np(o64), cfg["S"], cfg["S64"])
+    assert int(c["status"].item()) == 0 and ref["status"] == 0
+    n = int(c["len"].item())
+    assert n == ref["out_len"] == len(ids) - (cfg["S"] - cfg["S64"]) * int(use.sum())
+    assert np.array_equal(c["ids"].cpu().numpy(), ref["out_ids"])
+    assert np.array_equal(c["pos"].cpu().numpy(), ref["out_pos"])
+    assert np.array_equal(c["keep_map"].cpu().numpy(), ref["keep_map"])
+    got = c["embeds"][:n].float().cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref["out_embeds"][:n].astype(np.float32).view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# bf16 tiny shapes: MFMA GEMMs with ragged row tails
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 5, 11])
+def test_bf16_small_ragged_run(T):
+    cfg = workload("tiny_flash_f32", dtype="bf16")
+    cfg = dict(cfg, T=T, tiles=[T], name="tiny_bf16")
+    w = synth.make_weights(cfg)
+    x = synth.make_vit_tiles(cfg, range(T))
+    say(f"bf16 small run T={T}")
+    con = _connector(cfg, w, T)
+    o256, o64 = con.run(torch.from_numpy(x).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    e256, e64 = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256), e256, "bf16", "out256")
+    assert_close(to_np(o64), e64, "bf16", "out64")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled tiles
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["internvl35_4b_std", "internvl3_14b_ragged", "internvl3_38b"])
+def test_standard_connector_sampled(name):
+    cfg = workload(name)
+    say(f"{name}: T={cfg['T']} C={cfg['C']} D={cfg['D']}")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, cfg["T"])
+    xd = dev_vit(cfg)
+    o256, _ = con.run(xd)
+    torch.cuda.synchronize()
+    tiles = synth.sample_tiles(cfg["T"])
+    x = synth.make_vit_tiles(cfg, tiles)
+    e256, _ = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256[tiles]), e256, "bf16", f"{name} out256")
+
+
+def test_ragged_tile_offsets():
+    from vlm_visual_token_amd import ivc
+    cfg = workload("internvl3_14b_ragged")
+    tiles = np.array(cfg["tiles"], np.int32)
+    say(f"tile offsets B={len(tiles)}")
+    td = torch.from_numpy(tiles).cuda()
+    off = torch.empty(len(tiles) + 1, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ivc.ivc_tile_offsets(td, len(tiles), off, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), O.tile_offsets(tiles))
+    assert int(st.item()) == 0
+    assert int(off[-1].item()) == cfg["T"]
+    big = torch.full((3000,), 5, dtype=torch.int32, device="cuda")
+    off = torch.empty(3001, dtype=torch.int32, device="cuda")
+    ivc.ivc_tile_offsets(big, 3000, off, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), np.arange(3001) * 5)
+    neg = torch.tensor([3, -1, 2], dtype=torch.int32, device="cuda")
+    ivc.ivc_tile_offsets(neg, 3, off, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & ivc.IVC_DEV_ERR_TILE_COUNT
+
+
+def test_flash_workload_end_to_end():
+    cfg = workload("internvl35_2b_flash")
+    say(f"2B-Flash: T={cfg['T']}")
+    w = host_weights(cfg)
+    ids, emb = synth.make_sequence(cfg)
+    con = _connector(cfg, w, cfg["T"], len(ids))
+    xd = dev_vit(cfg)
+    o256, o64 = con.run(xd)
+    r = con.route(xd)
+    c = con.compact(torch.from_numpy(ids).cuda(), torch.from_numpy(emb).to(torch.bfloat16).cuda(),
+                    r["use64"], o256, o64, synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    say("  gpu done")
+    gate = r["gate"].cpu().numpy()
+    use = r["use64"].cpu().numpy()
+    # batch-wide steps on every tile, on the GPU's gates: bit-exact
+    thr, e_use = O.decide(gate[:, 0], cfg)
+    assert float(r["thr"].item()) == thr
+    assert np.array_equal(use, e_use)
+    frac = use.mean()
+    say(f"  routed fraction {frac:.3f}")
+    assert 0.2 < frac < 0.8
+    emb_bf = synth.to_bf16_exact(emb)
+    _check_compact(cfg, ids, emb_bf, use, o256, o64, c)
+    # float outputs on sampled tiles, plus the tiles nearest each threshold
+    g0 = gate[:, 0].astype(np.float64)
+    near = {int(np.argmin(np.abs(g0 - thr))), int(np.argmin(np.abs(g0 - 0.5)))}
+    tiles = sorted(set(synth.sample_tiles(cfg["T"], n=12)) | near)
+    x = synth.make_vit_tiles(cfg, tiles)
+    e256, e64 = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256[tiles]), e256, "bf16", "out256")
+    assert_close(to_np(o64[tiles]), e64, "bf16", "out64")
+    e_gate, _, _, e_pooled = O.connector_route(x, cfg, w)
+    assert_close(to_np(r["pooled"][tiles]), e_pooled, "bf16", "pooled")
+    dg = np.abs(gate[tiles] - e_gate).max()
+    say(f"  gate max abs diff {dg:.3e}")
+    assert dg <= GATE_TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 13, 100, 208, 999, 1024, 1025, 5000])
+def test_route_decide_bit_exact(T):
+    # the quantile + decision step on many gate sets, ties included
+    from vlm_visual_token_amd import ivc
+    say(f"route_decide T={T}")
+    rng = np.random.default_rng(T)
+    for trial in range(4):
+        p0 = rng.random(T).astype(np.float32)
+        if trial == 1:
+            p0 = (np.round(p0 * 8) / 8).astype(np.float32)   # many ties
+        if trial == 2:
+            p0[:] = np.float32(0.5)
+        if trial == 3:
+            p0 = (0.5 + (p0 - 0.5) * 1e-6).astype(np.float32)  # values straddling 0.5
+        gate = np.stack([p0, 1 - p0], axis=1).astype(np.float32)
+        gd = torch.from_numpy(gate).cuda()
+        thr_d = torch.empty(1, dtype=torch.float64, device="cuda")
+        use_d = torch.empty(T, dtype=torch.uint8, device="cuda")
+        ivc.ivc_route_decide(gd, T, 0.1, 0.5, thr_d, use_d)
+        torch.cuda.synchronize()
+        thr, use = O.decide(p0, {"rel_quantile": 0.1, "abs_threshold": 0.5})
+        assert float(thr_d.item()) == thr, (trial, float(thr_d.item()), thr)
+        assert np.array_equal(use_d.cpu().numpy(), use), trial
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_edge_cases():
+    cfg = workload("tiny_flash_f32")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, cfg["T"], 200)
+    x = torch.from_numpy(synth.make_vit(cfg)).cuda()
+    say("edge: T=0 run/route are no-ops")
+    con.run(x[:0])
+    con.route(x[:0])
+    say("edge: T=1 route compresses nothing")
+    r = con.route(x[:1])
+    torch.cuda.synchronize()
+    assert int(r["use64"].item()) == 0
+    assert float(r["thr"].item()) == float(r["gate"][0, 0].item())
+    say("edge: valid_tokens out of range sets the status bit")
+    bad = torch.tensor([0, 64, 65, 1, 2, 3, 4, 5], dtype=torch.int32, device="cuda")
+    r = con.route(x, valid=bad)
+    torch.cuda.synchronize()
+    assert int(r["status"].item()) & 2
+    say("edge: IMG_CONTEXT count mismatch sets the status bit")
+    ids, emb = synth.make_sequence(cfg)
+    o256, o64 = con.run(x)
+    use = torch.zeros(cfg["T"], dtype=torch.uint8, device="cuda")
+    ids_bad = ids.copy()
+    ids_bad[np.flatnonzero(ids == synth.IMG_CONTEXT)[3]] = 5
+    c = con.compact(torch.from_numpy(ids_bad).cuda(), torch.from_numpy(emb).cuda(), use, o256, o64,
+                    synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    assert int(c["status"].item()) == 1 and int(c["len"].item()) == 0
+    say("edge: empty sequence")
+    c = con.compact(torch.from_numpy(ids[:0]).cuda(), torch.from_numpy(emb[:0]).cuda(), use[:0],
+                    o256, o64, synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    assert int(c["len"].item()) == 0
+    say("edge: nothing routed keeps every slot")
+    c = con.compact(torch.from_numpy(ids).cuda(), torch.from_numpy(emb).cuda(), use, o256, o64,
+                    synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    assert int(c["len"].item()) == len(ids)
+    assert np.array_equal(c["ids"].cpu().numpy(), ids)
+
+
+def test_deterministic():
+    cfg = workload("tiny_flash_f32")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, cfg["T"])
+    x = torch.from_numpy(synth.make_vit(cfg)).cuda()
+    say("determinism")
+    a = [t.clone() for t in con.run(x)] + [con.route(x)["gate"].clone()]
+    b = [t.clone() for t in con.run(x)] + [con.route(x)["gate"].clone()]
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)

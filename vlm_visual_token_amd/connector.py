@@ -1,0 +1,81 @@
+"""Convenience wrapper over the C ABI: owns a handle and a workspace, and
+allocates output tensors with torch (device memory only; every step of the
+computation runs in the library's kernels)."""
+from __future__ import annotations
+
+import torch
+
+from . import ivc
+
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+class Connector:
+    def __init__(self, cfg: dict, weights: dict, max_tiles: int, max_seq_len: int = 0,
+                 device: str = "cuda", stream=None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.dtype = _TORCH_DT[cfg["dtype"]]
+        self._weights = weights  # keep the source tensors alive until create() has copied them
+        self.c_cfg = ivc.make_config(cfg)
+        self.c_w = ivc.make_weights(cfg, weights)
+        self.h = ivc.ivc_connector_create(self.c_cfg, self.c_w, stream)
+        self._weights = None
+        self.ws_bytes = ivc.ivc_connector_workspace_bytes(self.h, max_tiles, max_seq_len)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.S = (cfg["P"] // 2) ** 2
+        self.S64 = (cfg["P"] // 4) ** 2
+
+    def close(self):
+        if self.h:
+            ivc.ivc_connector_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def run(self, vit: torch.Tensor, out256=None, out64=None, stream=None):
+        T = vit.shape[0]
+        D = self.cfg["D"]
+        if out256 is None:
+            out256 = torch.empty((T, self.S, D), dtype=self.dtype, device=self.device)
+        if self.cfg["flash"] and out64 is None:
+            out64 = torch.empty((T, self.S64, D), dtype=self.dtype, device=self.device)
+        ivc.ivc_connector_run(self.h, vit, T, out256, out64, self.ws, self.ws_bytes, stream)
+        return out256, out64
+
+    def route(self, vit: torch.Tensor, valid=None, with_pooled=True, stream=None, out=None):
+        T = vit.shape[0]
+        if out is None:
+            out = dict(
+                gate=torch.empty((T, 2), dtype=torch.float32, device=self.device),
+                thr=torch.empty(1, dtype=torch.float64, device=self.device),
+                use64=torch.empty(T, dtype=torch.uint8, device=self.device),
+                pooled=(torch.empty((T, self.cfg["C"]), dtype=torch.float32, device=self.device)
+                        if with_pooled else None),
+                status=torch.zeros(1, dtype=torch.int32, device=self.device),
+            )
+        ivc.ivc_connector_route(self.h, vit, valid, T, out["gate"], out["thr"], out["use64"],
+                                out["pooled"], out["status"], self.ws, self.ws_bytes, stream)
+        return out
+
+    def compact(self, ids, embeds, use64, out256, out64, img_context_id: int, stream=None,
+                out=None):
+        L = ids.shape[0]
+        T = use64.shape[0]
+        if out is None:
+            out = dict(
+                ids=torch.empty(L, dtype=torch.int32, device=self.device),
+                pos=torch.empty(L, dtype=torch.int32, device=self.device),
+                keep_map=torch.empty(L, dtype=torch.int32, device=self.device),
+                embeds=torch.empty((L, self.cfg["D"]), dtype=self.dtype, device=self.device),
+                len=torch.zeros(1, dtype=torch.int64, device=self.device),
+                status=torch.zeros(1, dtype=torch.int32, device=self.device),
+            )
+        ivc.ivc_connector_compact(self.h, ids, embeds, L, img_context_id, use64, out256, out64, T,
+                                  out["ids"], out["pos"], out["keep_map"], out["embeds"],
+                                  out["len"], out["status"], self.ws, self.ws_bytes, stream)
+        return out

@@ -1,0 +1,80 @@
+// Device helpers shared by the connector's gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define IVC_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+// Native 16-byte vector (HIP's uint4 struct makes arrays of it spill to scratch).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- element conversions ---------------------------------------------------
+IVC_DEV float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+IVC_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename E> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  IVC_DEV static float load(const float* p) { return *p; }
+  IVC_DEV static float to_f(float v) { return v; }
+  IVC_DEV static float from_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kPerVec = 8;
+  IVC_DEV static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  IVC_DEV static float to_f(bf16_t v) { return bf16_to_f32(v); }
+  IVC_DEV static bf16_t from_f(float v) { return f32_to_bf16(v); }
+};
+
+// Unpack a 16-byte vector of E into floats (kPerVec of them).
+IVC_DEV void unpack16(const u32x4& v, float* f, float*) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+IVC_DEV void unpack16(const u32x4& v, float* f, bf16_t*) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+template <typename E> IVC_DEV void unpack(const u32x4& v, float* f) { unpack16(v, f, (E*)nullptr); }
+
+IVC_DEV u32x4 pack16(const float* f, float*) {
+  u32x4 v;
+  v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+  v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
+  return v;
+}
+IVC_DEV u32x4 pack16(const float* f, bf16_t*) {
+  u32x4 v;
+  v.x = (uint32_t)f32_to_bf16(f[0]) | ((uint32_t)f32_to_bf16(f[1]) << 16);
+  v.y = (uint32_t)f32_to_bf16(f[2]) | ((uint32_t)f32_to_bf16(f[3]) << 16);
+  v.z = (uint32_t)f32_to_bf16(f[4]) | ((uint32_t)f32_to_bf16(f[5]) << 16);
+  v.w = (uint32_t)f32_to_bf16(f[6]) | ((uint32_t)f32_to_bf16(f[7]) << 16);
+  return v;
+}
+template <typename E> IVC_DEV u32x4 pack(const float* f) { return pack16(f, (E*)nullptr); }
+
+// ---- wavefront reductions (64 lanes) ---------------------------------------
+IVC_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+IVC_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Exact GELU, 0.5 x (1 + erf(x / sqrt 2)).
+IVC_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }

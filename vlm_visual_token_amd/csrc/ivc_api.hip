@@ -1,0 +1,770 @@
+// Host side of the C ABI declared in include/ivc.h: validation, weight
+// ownership, workspace planning and the kernel sequence of each call.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/ivc.h"
+#include "kernels.h"
+
+using namespace ivc;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_last_error;
+
+static ivc_status fail(ivc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+#define HIP_OK(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(IVC_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_),       \
+                  __FILE__, __LINE__);                                                      \
+  } while (0)
+
+// Launch wrapper: optional per-kernel timing, then the launch's status.
+#define LAUNCH(name, stream, expr)   \
+  do {                               \
+    prof_begin(name, stream);        \
+    hipError_t le_ = (expr);         \
+    prof_end(stream);                \
+    HIP_OK(le_);                     \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// per-kernel timing
+// ---------------------------------------------------------------------------
+namespace {
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pending;
+std::vector<hipEvent_t> g_prof_free;
+std::vector<std::string> g_prof_names;
+std::vector<double> g_prof_ms;
+std::vector<long long> g_prof_n;
+hipEvent_t take_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  (void)hipEventCreate(&e);
+  return e;
+}
+}  // namespace
+
+namespace ivc {
+void prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof_on) return;
+  ProfRec r{name, take_event(), take_event()};
+  (void)hipEventRecord(r.a, s);
+  g_prof_pending.push_back(r);
+}
+void prof_end(hipStream_t s) {
+  if (!g_prof_on || g_prof_pending.empty()) return;
+  (void)hipEventRecord(g_prof_pending.back().b, s);
+}
+}  // namespace ivc
+
+static void prof_collect() {
+  for (auto& r : g_prof_pending) {
+    (void)hipEventSynchronize(r.b);
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, r.a, r.b);
+    size_t i = 0;
+    for (; i < g_prof_names.size(); ++i)
+      if (g_prof_names[i] == r.name) break;
+    if (i == g_prof_names.size()) {
+      g_prof_names.push_back(r.name);
+      g_prof_ms.push_back(0.0);
+      g_prof_n.push_back(0);
+    }
+    g_prof_ms[i] += ms;
+    g_prof_n[i] += 1;
+    g_prof_free.push_back(r.a);
+    g_prof_free.push_back(r.b);
+  }
+  g_prof_pending.clear();
+}
+
+extern "C" void ivc_profile_enable(int on) { g_prof_on = on != 0; }
+extern "C" void ivc_profile_reset(void) {
+  prof_collect();
+  g_prof_names.clear();
+  g_prof_ms.clear();
+  g_prof_n.clear();
+}
+extern "C" int32_t ivc_profile_read(const char** names, double* total_ms, int64_t* launches,
+                                    int32_t cap) {
+  prof_collect();
+  const int32_t n = (int32_t)g_prof_names.size();
+  for (int32_t i = 0; i < n && i < cap; ++i) {
+    if (names) names[i] = g_prof_names[i].c_str();
+    if (total_ms) total_ms[i] = g_prof_ms[i];
+    if (launches) launches[i] = g_prof_n[i];
+  }
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// handle
+// ---------------------------------------------------------------------------
+struct ivc_connector {
+  ivc_config cfg;
+  int esz;
+  char* blob = nullptr;
+  // mlp1 / mlp2
+  float *m1_ln_w, *m1_ln_b, *m1_b1, *m1_b2;
+  void *m1_w1, *m1_w2;
+  float *m2_ln_w, *m2_ln_b, *m2_b1, *m2_b2, *m2_b3;
+  void *m2_w1, *m2_w2, *m2_w3;
+  // router
+  void* query;
+  void *wq[IVC_MAX_POOL_LAYERS], *wo[IVC_MAX_POOL_LAYERS];
+  float *bq[IVC_MAX_POOL_LAYERS], *bo[IVC_MAX_POOL_LAYERS];
+  void* wkv;   // [2 * layers * C, C]: Wk_0; Wv_0; Wk_1; Wv_1; ...
+  float* bkv;  // [2 * layers * C]
+  void *g_w1[IVC_GATE_BLOCKS], *g_w2[IVC_GATE_BLOCKS], *g_cw;
+  float *g_b1[IVC_GATE_BLOCKS], *g_b2[IVC_GATE_BLOCKS], *g_lw[IVC_GATE_BLOCKS],
+      *g_lb[IVC_GATE_BLOCKS], *g_cb;
+};
+
+namespace {
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += al256(bytes);
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+__global__ void k_widen(const void* src, int dtype, float* dst, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (dtype == DT_BF16) {
+    const uint16_t h = ((const uint16_t*)src)[i];
+    dst[i] = __uint_as_float(((uint32_t)h) << 16);
+  } else {
+    dst[i] = ((const float*)src)[i];
+  }
+}
+
+ivc_status widen(const void* src, int dtype, float* dst, long long n, hipStream_t s) {
+  if (n == 0) return IVC_OK;
+  hipLaunchKernelGGL(k_widen, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, dtype,
+                     dst, n);
+  HIP_OK(hipGetLastError());
+  return IVC_OK;
+}
+
+ivc_status copy_mat(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  HIP_OK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
+  return IVC_OK;
+}
+
+ivc_status check_cfg(const ivc_config& c) {
+  if (c.dtype != IVC_F32 && c.dtype != IVC_BF16) return fail(IVC_ERR_INVALID_ARG, "dtype %d", c.dtype);
+  const int esz = c.dtype == IVC_BF16 ? 2 : 4;
+  if (c.vit_width <= 0 || c.grid <= 0 || c.llm_width <= 0 || c.mlp1_hidden <= 0)
+    return fail(IVC_ERR_INVALID_ARG, "widths and grid must be positive");
+  if (c.has_cls != 0 && c.has_cls != 1) return fail(IVC_ERR_INVALID_ARG, "has_cls must be 0 or 1");
+  if (c.grid % (c.flash ? 4 : 2) != 0)
+    return fail(IVC_ERR_INVALID_ARG, "grid %d not divisible by %d", c.grid, c.flash ? 4 : 2);
+  if ((long long)c.vit_width * esz % 16 || (long long)c.llm_width * esz % 16 ||
+      (long long)c.mlp1_hidden * esz % 16)
+    return fail(IVC_ERR_MISALIGNED, "row widths must be multiples of 16 bytes");
+  if (c.vit_width > shuffle_max_width(c.dtype))
+    return fail(IVC_ERR_UNSUPPORTED, "vit_width %d above the loader's %d", c.vit_width,
+                shuffle_max_width(c.dtype));
+  if (!(c.ln_eps >= 0.f)) return fail(IVC_ERR_INVALID_ARG, "ln_eps");
+  if (c.flash) {
+    if (c.mlp2_hidden <= 0 || (long long)c.mlp2_hidden * esz % 16)
+      return fail(IVC_ERR_INVALID_ARG, "mlp2_hidden");
+    if (c.pool_layers < 1 || c.pool_layers > IVC_MAX_POOL_LAYERS)
+      return fail(IVC_ERR_INVALID_ARG, "pool_layers %d", c.pool_layers);
+    if (c.pool_heads <= 0 || c.vit_width % c.pool_heads)
+      return fail(IVC_ERR_INVALID_ARG, "pool_heads %d does not divide C", c.pool_heads);
+    if (!pool_attn_supported(c.vit_width, c.pool_heads))
+      return fail(IVC_ERR_UNSUPPORTED, "pooling with C=%d, heads=%d", c.vit_width, c.pool_heads);
+    if (c.gate_hidden != c.vit_width)
+      return fail(IVC_ERR_INVALID_ARG, "gate_hidden %d must equal C %d", c.gate_hidden, c.vit_width);
+    if (c.gate_hidden > 4096) return fail(IVC_ERR_UNSUPPORTED, "gate_hidden above 4096");
+    if (c.gate_expansion < 1) return fail(IVC_ERR_INVALID_ARG, "gate_expansion");
+    if (c.pool_mode != IVC_POOL_KV && c.pool_mode != IVC_POOL_FOLDED)
+      return fail(IVC_ERR_INVALID_ARG, "pool_mode %d", c.pool_mode);
+    if (c.pool_mode == IVC_POOL_FOLDED)
+      return fail(IVC_ERR_UNSUPPORTED, "folded pooling is not built in this library version");
+    if (!(c.rel_quantile >= 0.0 && c.rel_quantile <= 1.0))
+      return fail(IVC_ERR_INVALID_ARG, "rel_quantile outside [0, 1]");
+  }
+  return IVC_OK;
+}
+
+// GEMM dispatch: MFMA for bf16 operands with K % 64 == 0, SIMT otherwise.
+hipError_t gemm(const char*, GemmArgs g, hipStream_t s) {
+  if (gemm_mfma_supported(g)) return launch_gemm_mfma(g, s);
+  return launch_gemm_simt(g, s);
+}
+
+GemmArgs mk_gemm(const void* A, long long lda, int a_dt, const void* W, int w_dt,
+                 const float* bias, void* Cm, int c_dt, int M, int N, int K, int act) {
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.W = W;
+  g.ldw = K;
+  g.bias = bias;
+  g.Cm = Cm;
+  g.ldc = N;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.act = act;
+  g.a_dtype = a_dt;
+  g.w_dtype = w_dt;
+  g.c_dtype = c_dt;
+  return g;
+}
+
+int pool_splits(int T, int N) {
+  // enough workgroups to cover 256 CUs a few times over, at least 64 tokens each
+  int s = 1;
+  while ((long long)T * s < 1024 && N / (2 * s) >= 64) s *= 2;
+  return s;
+}
+
+// ---- workspace plans ----
+struct RunWs {
+  void *a2, *a4, *h1, *g1, *g2;
+};
+size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
+  const ivc_config& c = h->cfg;
+  const size_t e = h->esz;
+  const size_t S = (size_t)(c.grid / 2) * (c.grid / 2), S4 = (size_t)(c.grid / 4) * (c.grid / 4);
+  Carver cv(base);
+  RunWs r{};
+  r.a2 = cv.take((size_t)T * S * 4 * c.vit_width * e);
+  r.h1 = cv.take((size_t)T * S * c.mlp1_hidden * e);
+  if (c.flash) {
+    r.a4 = cv.take((size_t)T * S4 * 16 * c.vit_width * e);
+    r.g1 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
+    r.g2 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
+  }
+  if (w) *w = r;
+  return cv.off;
+}
+
+struct RouteWs {
+  void* kv;
+  float *q, *qp, *o, *part, *y1, *y2, *x;
+};
+size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
+  const ivc_config& c = h->cfg;
+  const size_t C = c.vit_width, N = (size_t)c.grid * c.grid, L = c.pool_layers;
+  const size_t hh = c.gate_hidden, he = hh * c.gate_expansion;
+  Carver cv(base);
+  RouteWs r{};
+  if (!c.flash) return 0;
+  r.kv = cv.take((size_t)T * N * 2 * L * C * h->esz);
+  r.q = (float*)cv.take((size_t)T * C * 4);
+  r.qp = (float*)cv.take((size_t)T * C * 4);
+  r.o = (float*)cv.take((size_t)T * C * 4);
+  const int sp = pool_splits(T, (int)N);
+  r.part = (float*)cv.take((size_t)T * sp * (2 * c.pool_heads + C) * 4);
+  r.y1 = (float*)cv.take((size_t)T * he * 4);
+  r.y2 = (float*)cv.take((size_t)T * hh * 4);
+  r.x = (float*)cv.take((size_t)T * hh * 4);
+  if (w) *w = r;
+  return cv.off;
+}
+
+struct CompactWs {
+  int32_t *cnt, *off, *rb;
+  long long* src;
+};
+size_t plan_compact(int T, long long L, void* base, CompactWs* w) {
+  Carver cv(base);
+  CompactWs r{};
+  const long long nb = compact_blocks(L);
+  r.cnt = (int32_t*)cv.take((size_t)nb * 4);
+  r.off = (int32_t*)cv.take((size_t)nb * 4);
+  r.rb = (int32_t*)cv.take((size_t)(T + 1) * 4);
+  r.src = (long long*)cv.take((size_t)L * 8);
+  if (w) *w = r;
+  return cv.off;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// create / destroy
+// ---------------------------------------------------------------------------
+extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weights* w,
+                                           void* stream, ivc_connector** out) {
+  if (!cfg || !w || !out) return fail(IVC_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  ivc_status st = check_cfg(*cfg);
+  if (st != IVC_OK) return st;
+  const ivc_config& c = *cfg;
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = c.dtype;
+  const size_t e = dt == IVC_BF16 ? 2 : 4;
+  const size_t C = c.vit_width, D = c.llm_width, H1 = c.mlp1_hidden, H2 = c.mlp2_hidden;
+  const size_t Lp = c.pool_layers, hh = c.gate_hidden, he = hh * c.gate_expansion;
+
+  // required pointers
+  const void* req1[] = {w->mlp1_ln_w, w->mlp1_ln_b, w->mlp1_w1, w->mlp1_b1, w->mlp1_w2, w->mlp1_b2};
+  for (const void* p : req1) {
+    if (!p) return fail(IVC_ERR_INVALID_ARG, "missing mlp1 weight");
+    if (!aligned16(p)) return fail(IVC_ERR_MISALIGNED, "weight pointer not 16-byte aligned");
+  }
+  if (c.flash) {
+    const void* req2[] = {w->mlp2_ln_w, w->mlp2_ln_b, w->mlp2_w1, w->mlp2_b1, w->mlp2_w2,
+                          w->mlp2_b2,   w->mlp2_w3,   w->mlp2_b3, w->pool_query, w->gate_cls_w,
+                          w->gate_cls_b};
+    for (const void* p : req2) {
+      if (!p) return fail(IVC_ERR_INVALID_ARG, "missing mlp2/router weight");
+      if (!aligned16(p)) return fail(IVC_ERR_MISALIGNED, "weight pointer not 16-byte aligned");
+    }
+    for (size_t l = 0; l < Lp; ++l) {
+      const void* pl[] = {w->pool_wq[l], w->pool_bq[l], w->pool_wk[l], w->pool_bk[l],
+                          w->pool_wv[l], w->pool_bv[l], w->pool_wo[l], w->pool_bo[l]};
+      for (const void* p : pl)
+        if (!p) return fail(IVC_ERR_INVALID_ARG, "missing pooling weight of layer %zu", l);
+    }
+    for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
+      const void* pb[] = {w->gate_w1[b], w->gate_b1[b], w->gate_w2[b],
+                          w->gate_b2[b], w->gate_ln_w[b], w->gate_ln_b[b]};
+      for (const void* p : pb)
+        if (!p) return fail(IVC_ERR_INVALID_ARG, "missing gating weight of block %d", b);
+    }
+  }
+
+  ivc_connector* h = new ivc_connector();
+  h->cfg = c;
+  h->esz = (int)e;
+  Carver plan(nullptr);
+  auto layout = [&](Carver& cv) {
+    h->m1_ln_w = (float*)cv.take(4 * C * 4);
+    h->m1_ln_b = (float*)cv.take(4 * C * 4);
+    h->m1_w1 = cv.take(H1 * 4 * C * e);
+    h->m1_b1 = (float*)cv.take(H1 * 4);
+    h->m1_w2 = cv.take(D * H1 * e);
+    h->m1_b2 = (float*)cv.take(D * 4);
+    if (c.flash) {
+      h->m2_ln_w = (float*)cv.take(16 * C * 4);
+      h->m2_ln_b = (float*)cv.take(16 * C * 4);
+      h->m2_w1 = cv.take(H2 * 16 * C * e);
+      h->m2_b1 = (float*)cv.take(H2 * 4);
+      h->m2_w2 = cv.take(H2 * H2 * e);
+      h->m2_b2 = (float*)cv.take(H2 * 4);
+      h->m2_w3 = cv.take(D * H2 * e);
+      h->m2_b3 = (float*)cv.take(D * 4);
+      h->query = cv.take(C * e);
+      for (size_t l = 0; l < Lp; ++l) {
+        h->wq[l] = cv.take(C * C * e);
+        h->bq[l] = (float*)cv.take(C * 4);
+        h->wo[l] = cv.take(C * C * e);
+        h->bo[l] = (float*)cv.take(C * 4);
+      }
+      h->wkv = cv.take(2 * Lp * C * C * e);
+      h->bkv = (float*)cv.take(2 * Lp * C * 4);
+      for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
+        h->g_w1[b] = cv.take(he * hh * e);
+        h->g_b1[b] = (float*)cv.take(he * 4);
+        h->g_w2[b] = cv.take(hh * he * e);
+        h->g_b2[b] = (float*)cv.take(hh * 4);
+        h->g_lw[b] = (float*)cv.take(hh * 4);
+        h->g_lb[b] = (float*)cv.take(hh * 4);
+      }
+      h->g_cw = cv.take(2 * hh * e);
+      h->g_cb = (float*)cv.take(2 * 4);
+    }
+  };
+  layout(plan);
+  if (hipMalloc((void**)&h->blob, plan.off) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return fail(IVC_ERR_OOM, "hipMalloc of %zu bytes for weights failed", plan.off);
+  }
+  Carver real(h->blob);
+  layout(real);
+
+#define STEP(x)                   \
+  do {                            \
+    ivc_status s_ = (x);          \
+    if (s_ != IVC_OK) {           \
+      ivc_connector_destroy(h);   \
+      return s_;                  \
+    }                             \
+  } while (0)
+  STEP(widen(w->mlp1_ln_w, dt, h->m1_ln_w, 4 * C, s));
+  STEP(widen(w->mlp1_ln_b, dt, h->m1_ln_b, 4 * C, s));
+  STEP(copy_mat(w->mlp1_w1, h->m1_w1, H1 * 4 * C * e, s));
+  STEP(widen(w->mlp1_b1, dt, h->m1_b1, H1, s));
+  STEP(copy_mat(w->mlp1_w2, h->m1_w2, D * H1 * e, s));
+  STEP(widen(w->mlp1_b2, dt, h->m1_b2, D, s));
+  if (c.flash) {
+    STEP(widen(w->mlp2_ln_w, dt, h->m2_ln_w, 16 * C, s));
+    STEP(widen(w->mlp2_ln_b, dt, h->m2_ln_b, 16 * C, s));
+    STEP(copy_mat(w->mlp2_w1, h->m2_w1, H2 * 16 * C * e, s));
+    STEP(widen(w->mlp2_b1, dt, h->m2_b1, H2, s));
+    STEP(copy_mat(w->mlp2_w2, h->m2_w2, H2 * H2 * e, s));
+    STEP(widen(w->mlp2_b2, dt, h->m2_b2, H2, s));
+    STEP(copy_mat(w->mlp2_w3, h->m2_w3, D * H2 * e, s));
+    STEP(widen(w->mlp2_b3, dt, h->m2_b3, D, s));
+    STEP(copy_mat(w->pool_query, h->query, C * e, s));
+    for (size_t l = 0; l < Lp; ++l) {
+      STEP(copy_mat(w->pool_wq[l], h->wq[l], C * C * e, s));
+      STEP(widen(w->pool_bq[l], dt, h->bq[l], C, s));
+      STEP(copy_mat(w->pool_wo[l], h->wo[l], C * C * e, s));
+      STEP(widen(w->pool_bo[l], dt, h->bo[l], C, s));
+      STEP(copy_mat(w->pool_wk[l], (char*)h->wkv + (2 * l) * C * C * e, C * C * e, s));
+      STEP(copy_mat(w->pool_wv[l], (char*)h->wkv + (2 * l + 1) * C * C * e, C * C * e, s));
+      STEP(widen(w->pool_bk[l], dt, h->bkv + (2 * l) * C, C, s));
+      STEP(widen(w->pool_bv[l], dt, h->bkv + (2 * l + 1) * C, C, s));
+    }
+    for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
+      STEP(copy_mat(w->gate_w1[b], h->g_w1[b], he * hh * e, s));
+      STEP(widen(w->gate_b1[b], dt, h->g_b1[b], he, s));
+      STEP(copy_mat(w->gate_w2[b], h->g_w2[b], hh * he * e, s));
+      STEP(widen(w->gate_b2[b], dt, h->g_b2[b], hh, s));
+      STEP(widen(w->gate_ln_w[b], dt, h->g_lw[b], hh, s));
+      STEP(widen(w->gate_ln_b[b], dt, h->g_lb[b], hh, s));
+    }
+    STEP(copy_mat(w->gate_cls_w, h->g_cw, 2 * hh * e, s));
+    STEP(widen(w->gate_cls_b, dt, h->g_cb, 2, s));
+  }
+#undef STEP
+  if (hipStreamSynchronize(s) != hipSuccess) {
+    hipError_t er = hipGetLastError();
+    ivc_connector_destroy(h);
+    return fail(IVC_ERR_HIP, "weight copy failed: %s", hipGetErrorString(er));
+  }
+  *out = h;
+  return IVC_OK;
+}
+
+extern "C" void ivc_connector_destroy(ivc_connector* h) {
+  if (!h) return;
+  if (h->blob) {
+    (void)hipDeviceSynchronize();
+    (void)hipFree(h->blob);
+  }
+  delete h;
+}
+
+extern "C" size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t max_tiles,
+                                                int64_t max_seq_len) {
+  if (!h || max_tiles < 0 || max_seq_len < 0) return 0;
+  size_t a = plan_run(h, max_tiles, nullptr, nullptr);
+  size_t b = plan_route(h, max_tiles, nullptr, nullptr);
+  size_t c = plan_compact(max_tiles, max_seq_len, nullptr, nullptr);
+  size_t m = a > b ? a : b;
+  return m > c ? m : c;
+}
+
+// ---------------------------------------------------------------------------
+// run
+// ---------------------------------------------------------------------------
+extern "C" ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32_t T,
+                                        void* out256, void* out64, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  const ivc_config& c = h->cfg;
+  if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
+  if (T == 0) return IVC_OK;
+  if (!vit || !out256 || (c.flash && !out64))
+    return fail(IVC_ERR_INVALID_ARG, "null vit/out256%s", c.flash ? "/out64" : "");
+  if (!aligned16(vit) || !aligned16(out256) || (out64 && !aligned16(out64)) || !aligned16(ws))
+    return fail(IVC_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+  const long long S = (long long)(c.grid / 2) * (c.grid / 2);
+  if ((long long)T * S * 16 * c.vit_width > (1ll << 40))
+    return fail(IVC_ERR_UNSUPPORTED, "T = %d too large", T);
+  const size_t need = plan_run(h, T, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(IVC_ERR_WORKSPACE, "run needs %zu workspace bytes, got %zu", need, ws_bytes);
+  RunWs w;
+  plan_run(h, T, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = c.dtype;
+  const int C = c.vit_width, D = c.llm_width, H1 = c.mlp1_hidden, H2 = c.mlp2_hidden;
+
+  ShuffleArgs sa{};
+  sa.dtype = dt;
+  sa.X = vit;
+  sa.T = T;
+  sa.P = c.grid;
+  sa.C = C;
+  sa.has_cls = c.has_cls;
+  sa.flash = c.flash;
+  sa.ln = 1;
+  sa.g2 = h->m1_ln_w;
+  sa.b2 = h->m1_ln_b;
+  sa.out2 = w.a2;
+  sa.g4 = h->m2_ln_w;
+  sa.b4 = h->m2_ln_b;
+  sa.out4 = w.a4;
+  sa.eps = c.ln_eps;
+  LAUNCH("shuffle_ln", s, launch_shuffle_ln(sa, s));
+
+  const int M2 = (int)(T * S);
+  LAUNCH("mlp1_gemm1", s, gemm("mlp1_gemm1",
+                              mk_gemm(w.a2, 4 * C, dt, h->m1_w1, dt, h->m1_b1, w.h1, dt, M2, H1,
+                                      4 * C, ACT_GELU), s));
+  LAUNCH("mlp1_gemm2", s, gemm("mlp1_gemm2",
+                              mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D,
+                                      H1, ACT_NONE), s));
+  if (c.flash) {
+    const int M4 = T * (c.grid / 4) * (c.grid / 4);
+    LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1",
+                                mk_gemm(w.a4, 16 * C, dt, h->m2_w1, dt, h->m2_b1, w.g1, dt, M4,
+                                        H2, 16 * C, ACT_GELU), s));
+    LAUNCH("mlp2_gemm2", s, gemm("mlp2_gemm2",
+                                mk_gemm(w.g1, H2, dt, h->m2_w2, dt, h->m2_b2, w.g2, dt, M4, H2,
+                                        H2, ACT_GELU), s));
+    LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3",
+                                mk_gemm(w.g2, H2, dt, h->m2_w3, dt, h->m2_b3, out64, dt, M4, D,
+                                        H2, ACT_NONE), s));
+  }
+  return IVC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// route
+// ---------------------------------------------------------------------------
+extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
+                                          const int32_t* valid_tokens, int32_t T, float* gate,
+                                          double* threshold, uint8_t* use64, float* pooled,
+                                          int32_t* dev_status, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  const ivc_config& c = h->cfg;
+  if (!c.flash) return fail(IVC_ERR_INVALID_ARG, "route needs a flash connector");
+  if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
+  if (T == 0) return IVC_OK;
+  if (!vit || !gate || !threshold || !use64)
+    return fail(IVC_ERR_INVALID_ARG, "null vit/gate/threshold/use64");
+  if (!aligned16(vit) || !aligned16(ws)) return fail(IVC_ERR_MISALIGNED, "vit/ws alignment");
+  const size_t need = plan_route(h, T, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(IVC_ERR_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws_bytes);
+  RouteWs w;
+  plan_route(h, T, ws, &w);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = c.dtype;
+  const int C = c.vit_width, N = c.grid * c.grid, L = c.pool_layers, H = c.pool_heads;
+  const int rows = c.has_cls + N;
+  const int hh = c.gate_hidden, he = hh * c.gate_expansion;
+
+  // K and V of every layer from the raw tokens (CLS skipped by the row remap)
+  GemmArgs kv = mk_gemm(vit, C, dt, h->wkv, dt, h->bkv, w.kv, dt, T * N, 2 * L * C, C, ACT_NONE);
+  kv.a_rpg = N;
+  kv.a_gstride = rows;
+  kv.a_goff = c.has_cls;
+  LAUNCH("pool_kv_gemm", s, gemm("pool_kv_gemm", kv, s));
+
+  LAUNCH("pool_query", s, launch_broadcast_rows(dt, h->query, w.q, T, C, s));
+  const int splits = pool_splits(T, N);
+  for (int l = 0; l < L; ++l) {
+    LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
+                                 mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32, T,
+                                         C, C, ACT_NONE), s));
+    PoolAttnArgs pa{};
+    pa.dtype = dt;
+    pa.KV = w.kv;
+    pa.kv_ld = 2ll * L * C;
+    pa.kcol = 2 * l * C;
+    pa.vcol = (2 * l + 1) * C;
+    pa.Q = w.qp;
+    pa.valid = valid_tokens;
+    pa.status = dev_status;
+    pa.T = T;
+    pa.N = N;
+    pa.C = C;
+    pa.H = H;
+    pa.splits = splits;
+    pa.part = w.part;
+    pa.O = w.o;
+    LAUNCH("pool_attn", s, launch_pool_attn(pa, s));
+    float* qn = (l == L - 1 && pooled) ? pooled : w.q;
+    LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
+                                 mk_gemm(w.o, C, DT_F32, h->wo[l], dt, h->bo[l], qn, DT_F32, T,
+                                         C, C, ACT_NONE), s));
+  }
+  const float* pooled_v = pooled ? pooled : w.q;
+
+  // Gating: x = pooled; 4 x (x += LN(W2 GELU(W1 x + b1) + b2)); softmax(Wc x + bc)
+  HIP_OK(hipMemcpyAsync(w.x, pooled_v, (size_t)T * hh * 4, hipMemcpyDeviceToDevice, s));
+  for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
+    LAUNCH("gate_fc1", s, gemm("gate_fc1",
+                              mk_gemm(w.x, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1, DT_F32,
+                                      T, he, hh, ACT_GELU), s));
+    LAUNCH("gate_fc2", s, gemm("gate_fc2",
+                              mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2, DT_F32,
+                                      T, hh, he, ACT_NONE), s));
+    LAUNCH("gate_res_ln", s,
+           launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));
+  }
+  LAUNCH("gate_head", s, launch_gate_head(dt, w.x, h->g_cw, h->g_cb, gate, T, hh, s));
+  LAUNCH("quantile_decide", s,
+         launch_quantile_decide(gate, T, c.rel_quantile, c.abs_threshold, threshold, use64, s));
+  return IVC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// compact
+// ---------------------------------------------------------------------------
+extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids,
+                                            const void* embeds, int64_t L, int32_t img_context_id,
+                                            const uint8_t* use64, const void* out256,
+                                            const void* out64, int32_t T, int32_t* out_ids,
+                                            int32_t* out_pos, int32_t* keep_map, void* out_embeds,
+                                            int64_t* out_len, int32_t* dev_status, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  const ivc_config& c = h->cfg;
+  if (L < 0 || T < 0) return fail(IVC_ERR_INVALID_ARG, "negative L or T");
+  if (L > 0x7fffffffll) return fail(IVC_ERR_UNSUPPORTED, "L above INT32_MAX");
+  if (!out_len || !dev_status) return fail(IVC_ERR_INVALID_ARG, "null out_len/dev_status");
+  const long long S = (long long)(c.grid / 2) * (c.grid / 2);
+  const long long S64 = (long long)(c.grid / 4) * (c.grid / 4);
+  if ((long long)T * S >= (1ll << 31)) return fail(IVC_ERR_UNSUPPORTED, "T * S too large");
+  if (L > 0 && (!ids || !embeds || !out_ids || !out_pos || !keep_map || !out_embeds))
+    return fail(IVC_ERR_INVALID_ARG, "null sequence pointer");
+  if (T > 0 && (!use64 || !out256)) return fail(IVC_ERR_INVALID_ARG, "null use64/out256");
+  if (T > 0 && !out64 && !c.flash) {
+    // a non-flash connector may compact with an all-zero use64 and no out64
+  } else if (T > 0 && !out64) {
+    return fail(IVC_ERR_INVALID_ARG, "null out64");
+  }
+  if (!aligned16(embeds) || !aligned16(out256) || !aligned16(out64) || !aligned16(out_embeds) ||
+      !aligned16(ws))
+    return fail(IVC_ERR_MISALIGNED, "embedding pointers must be 16-byte aligned");
+  const size_t need = plan_compact(T, L, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(IVC_ERR_WORKSPACE, "compact needs %zu workspace bytes, got %zu", need, ws_bytes);
+  CompactWs w;
+  plan_compact(T, L, ws, &w);
+  CompactArgs a{};
+  a.dtype = c.dtype;
+  a.ids = ids;
+  a.embeds = embeds;
+  a.L = L;
+  a.img_id = img_context_id;
+  a.use64 = use64;
+  a.out256 = out256;
+  a.out64 = out64 ? out64 : out256;
+  a.T = T;
+  a.S = (int)S;
+  a.S64 = c.flash ? (int)S64 : (int)S;
+  a.D = c.llm_width;
+  a.out_ids = out_ids;
+  a.out_pos = out_pos;
+  a.keep_map = keep_map;
+  a.out_embeds = out_embeds;
+  a.out_len = (long long*)out_len;
+  a.status = dev_status;
+  a.blk_cnt = w.cnt;
+  a.blk_off = w.off;
+  a.routed_before = w.rb;
+  a.src = w.src;
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("compact", s, launch_compact(a, s));
+  return IVC_OK;
+}
+
+extern "C" ivc_status ivc_route_decide(const float* gate, int32_t T, double rel_quantile,
+                                       double abs_threshold, double* threshold, uint8_t* use64,
+                                       void* stream) {
+  if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
+  if (!(rel_quantile >= 0.0 && rel_quantile <= 1.0))
+    return fail(IVC_ERR_INVALID_ARG, "rel_quantile outside [0, 1]");
+  if (T == 0) return IVC_OK;
+  if (!gate || !threshold || !use64) return fail(IVC_ERR_INVALID_ARG, "null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("quantile_decide", s,
+         launch_quantile_decide(gate, T, rel_quantile, abs_threshold, threshold, use64, s));
+  return IVC_OK;
+}
+
+extern "C" ivc_status ivc_tile_offsets(const int32_t* tiles_per_image, int32_t B, int32_t* offsets,
+                                       int32_t* dev_status, void* stream) {
+  if (B < 0) return fail(IVC_ERR_INVALID_ARG, "B = %d", B);
+  if (!offsets || (B > 0 && !tiles_per_image)) return fail(IVC_ERR_INVALID_ARG, "null pointer");
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("tile_offsets", s, launch_tile_offsets(tiles_per_image, B, offsets, dev_status, s));
+  return IVC_OK;
+}
+
+extern "C" ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t T, int32_t P,
+                                        int32_t C, int32_t has_cls, int32_t r, void* out,
+                                        void* stream) {
+  if (dtype != IVC_F32 && dtype != IVC_BF16) return fail(IVC_ERR_INVALID_ARG, "dtype");
+  if (T < 0 || P <= 0 || C <= 0 || (has_cls != 0 && has_cls != 1) || (r != 2 && r != 4))
+    return fail(IVC_ERR_INVALID_ARG, "bad shape");
+  if (P % r) return fail(IVC_ERR_INVALID_ARG, "P %% r != 0");
+  if (T == 0) return IVC_OK;
+  const int esz = dtype == IVC_BF16 ? 2 : 4;
+  if ((long long)C * esz % 16) return fail(IVC_ERR_MISALIGNED, "row width");
+  if (C > shuffle_max_width(dtype)) return fail(IVC_ERR_UNSUPPORTED, "C too large");
+  if (!vit || !out) return fail(IVC_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(vit) || !aligned16(out)) return fail(IVC_ERR_MISALIGNED, "alignment");
+  ShuffleArgs sa{};
+  sa.dtype = dtype;
+  sa.X = vit;
+  sa.T = T;
+  sa.P = P;
+  sa.C = C;
+  sa.has_cls = has_cls;
+  sa.flash = r == 4;
+  sa.ln = 0;
+  sa.out2 = r == 2 ? out : nullptr;
+  sa.out4 = r == 4 ? out : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("pixel_shuffle", s, launch_shuffle_ln(sa, s));
+  return IVC_OK;
+}
+
+extern "C" const char* ivc_status_string(ivc_status st) {
+  switch (st) {
+    case IVC_OK: return "ok";
+    case IVC_ERR_INVALID_ARG: return "invalid argument";
+    case IVC_ERR_UNSUPPORTED: return "unsupported shape";
+    case IVC_ERR_MISALIGNED: return "misaligned pointer or row";
+    case IVC_ERR_WORKSPACE: return "workspace too small";
+    case IVC_ERR_OOM: return "out of device memory";
+    case IVC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* ivc_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,283 @@
+// Sequence compaction after routing (compress_visual_tokens_in_sentence) and
+// IMG_CONTEXT embedding injection.
+//
+// InternVL3_5-4B-Flash Gating and CrossAttentionPooling page, section 4: a
+// tile routed to strong compression keeps only its first 64 visual tokens,
+// the other 192 are deleted from the input sequence, and positions are
+// corrected.  InternVL3-14B-Instruct page, token-injection section: the
+// visual vectors replace the IMG_CONTEXT positions in order, so the k-th
+// IMG_CONTEXT token is slot k % S of tile k / S.
+//
+// Closed form used here: with k(p) IMG_CONTEXT tokens before position p, the
+// slots deleted before p are
+//   f(k) = (S - S64) * routed_before[k / S] + use64[k / S] * max(0, k % S - S64),
+// so a kept token moves to j = p - f(k(p)).  Only one scan over the sequence
+// (the IMG_CONTEXT count) is needed, plus a scan of use64 over tiles:
+//   1. k_compact_count  per-1024-token block IMG_CONTEXT counts
+//   2. k_compact_plan   (one workgroup) block offsets, routed_before, L', status
+//   3. k_compact_map    per-position keep flag and destination; writes
+//                       out_ids, out_pos, keep_map and a source code per row
+//   4. k_compact_copy   one wave per output row, 16-byte copies of the row
+#include "common.h"
+#include "kernels.h"
+
+namespace ivc {
+
+constexpr int CB = 1024;  // positions per block
+constexpr int CT = 256;   // threads per block (4 positions each)
+
+long long compact_blocks(long long L) { return (L + CB - 1) / CB; }
+
+IVC_DEV int block_excl_scan(int v, int* sh /*[4]*/, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += sh[i];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return before + inc - v;
+}
+
+__global__ void __launch_bounds__(CT)
+k_compact_count(const int32_t* __restrict__ ids, long long L, int img, int32_t* __restrict__ cnt) {
+  const long long base = (long long)blockIdx.x * CB + threadIdx.x * 4;
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c += (base + e < L && ids[base + e] == img) ? 1 : 0;
+  __shared__ int sh[4];
+  int total;
+  block_excl_scan(c, sh, &total);
+  if (threadIdx.x == 0) cnt[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(1024)
+k_compact_plan(const int32_t* __restrict__ cnt, long long nblk, const uint8_t* __restrict__ use64,
+               int T, int S, int S64, long long L, int32_t* __restrict__ blk_off,
+               int32_t* __restrict__ routed_before, long long* __restrict__ out_len,
+               int32_t* __restrict__ status) {
+  __shared__ long long carry_s;
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // exclusive scans in chunks of 1024 with a running carry
+  auto scan = [&](auto get, auto put, long long n) -> long long {
+    if (threadIdx.x == 0) carry_s = 0;
+    __syncthreads();
+    for (long long c0 = 0; c0 < n; c0 += 1024) {
+      const long long i = c0 + threadIdx.x;
+      const int v = i < n ? get(i) : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+      }
+      if (lane == 63) wsum[w] = inc;
+      __syncthreads();
+      int before = 0, tot = 0;
+      for (int k = 0; k < 16; ++k) {
+        if (k < w) before += wsum[k];
+        tot += wsum[k];
+      }
+      const long long carry = carry_s;
+      if (i < n) put(i, carry + before + inc - v);
+      __syncthreads();
+      if (threadIdx.x == 0) carry_s = carry + tot;
+      __syncthreads();
+    }
+    return carry_s;
+  };
+  const long long n_img =
+      scan([&](long long i) { return (int)cnt[i]; },
+           [&](long long i, long long v) { blk_off[i] = (int32_t)v; }, nblk);
+  const long long n_routed =
+      scan([&](long long i) { return (int)(use64[i] != 0); },
+           [&](long long i, long long v) { routed_before[i] = (int32_t)v; }, (long long)T);
+  if (threadIdx.x == 0) {
+    routed_before[T] = (int32_t)n_routed;
+    const bool ok = n_img == (long long)T * S;
+    if (!ok) atomicOr(status, 1);
+    *out_len = ok ? L - (long long)(S - S64) * n_routed : 0;
+  }
+}
+
+__global__ void __launch_bounds__(CT)
+k_compact_map(const int32_t* __restrict__ ids, long long L, int img, const uint8_t* __restrict__ use64,
+              int T, int S, int S64, const int32_t* __restrict__ blk_off,
+              const int32_t* __restrict__ routed_before, const long long* __restrict__ out_len,
+              int32_t* __restrict__ out_ids, int32_t* __restrict__ out_pos,
+              int32_t* __restrict__ keep_map, long long* __restrict__ src) {
+  const long long base = (long long)blockIdx.x * CB + threadIdx.x * 4;
+  int tok[4], c = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    tok[e] = base + e < L ? ids[base + e] : 0;
+    c += (base + e < L && tok[e] == img) ? 1 : 0;
+  }
+  __shared__ int sh[4];
+  int total;
+  int k = blk_off[blockIdx.x] + block_excl_scan(c, sh, &total);
+  const long long Lp = *out_len;
+  const long long drop = S - S64;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const long long p = base + e;
+    if (p >= L) break;
+    const bool is_img = tok[e] == img;
+    const int tile = k / S, loc = k - tile * S;
+    long long f;  // slots deleted before p
+    bool keep = true;
+    long long code = 0;
+    if (tile < T) {
+      const int u = use64[tile] != 0;
+      f = drop * routed_before[tile] + (u ? max(0, loc - S64) : 0);
+      if (is_img) {
+        keep = !u || loc < S64;
+        code = u ? ((2ll << 60) | ((long long)tile * S64 + loc))
+                 : ((1ll << 60) | ((long long)tile * S + loc));
+      } else {
+        code = p;
+      }
+    } else {
+      // k == T*S exactly (text after the last slot) or a malformed sequence
+      f = drop * routed_before[T];
+      if (is_img) keep = false;  // more slots than tiles: status already set
+      code = p;
+    }
+    const long long j = p - f;
+    keep_map[p] = keep ? (int32_t)j : -1;
+    if (keep) {
+      out_ids[j] = tok[e];
+      src[j] = code;
+    }
+    out_pos[p] = p < Lp ? (int32_t)p : -1;
+    if (p >= Lp) out_ids[p] = -1;
+    if (is_img) ++k;
+  }
+}
+
+// One wave per output row, 16-byte vectors.
+template <int VPL>
+__global__ void __launch_bounds__(256)
+k_compact_copy(const long long* __restrict__ src, const long long* __restrict__ out_len,
+               const u32x4* __restrict__ embeds, const u32x4* __restrict__ o256,
+               const u32x4* __restrict__ o64, u32x4* __restrict__ out, int vpr, long long L) {
+  const long long j = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= L || j >= *out_len) return;
+  const long long code = src[j];
+  const int kind = (int)(code >> 60);
+  const long long idx = code & ((1ll << 60) - 1);
+  const u32x4* s = (kind == 0 ? embeds : kind == 1 ? o256 : o64) + idx * vpr;
+  u32x4* d = out + j * vpr;
+  u32x4 v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < vpr) v[i] = __builtin_nontemporal_load(s + c);
+  }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < vpr) __builtin_nontemporal_store(v[i], d + c);
+  }
+}
+
+__global__ void k_set_i64(long long* p, long long v) { *p = v; }
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  const long long nblk = compact_blocks(a.L);
+  if (a.L == 0) {
+    // nothing to scan; out_len = 0 (a kernel, not a memset, so the call can be graph-captured)
+    hipLaunchKernelGGL(k_set_i64, dim3(1), dim3(1), 0, s, a.out_len, 0ll);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_compact_count, dim3((unsigned)nblk), dim3(CT), 0, s, a.ids, a.L, a.img_id,
+                     a.blk_cnt);
+  hipLaunchKernelGGL(k_compact_plan, dim3(1), dim3(1024), 0, s, (const int32_t*)a.blk_cnt, nblk,
+                     a.use64, a.T, a.S, a.S64, a.L, a.blk_off, a.routed_before, a.out_len, a.status);
+  hipLaunchKernelGGL(k_compact_map, dim3((unsigned)nblk), dim3(CT), 0, s, a.ids, a.L, a.img_id,
+                     a.use64, a.T, a.S, a.S64, (const int32_t*)a.blk_off,
+                     (const int32_t*)a.routed_before, (const long long*)a.out_len, a.out_ids,
+                     a.out_pos, a.keep_map, a.src);
+  const int esz = a.dtype == DT_BF16 ? 2 : 4;
+  const int vpr = (int)((long long)a.D * esz / 16);
+  const int vpl = (vpr + 63) / 64;
+  dim3 grid((unsigned)((a.L + 3) / 4));
+#define IVC_COPY(n)                                                                              \
+  hipLaunchKernelGGL(k_compact_copy<n>, grid, dim3(256), 0, s, (const long long*)a.src,         \
+                     (const long long*)a.out_len, (const u32x4*)a.embeds, (const u32x4*)a.out256, \
+                     (const u32x4*)a.out64, (u32x4*)a.out_embeds, vpr, a.L)
+  if (vpl <= 1) IVC_COPY(1);
+  else if (vpl <= 2) IVC_COPY(2);
+  else if (vpl <= 4) IVC_COPY(4);
+  else if (vpl <= 8) IVC_COPY(8);
+  else if (vpl <= 16) IVC_COPY(16);
+  else return hipErrorInvalidValue;
+#undef IVC_COPY
+  return hipGetLastError();
+}
+
+// ---- ragged tile offsets -------------------------------------------------------
+__global__ void __launch_bounds__(1024)
+k_tile_offsets(const int32_t* __restrict__ tiles, int B, int32_t* __restrict__ off,
+               int32_t* __restrict__ status) {
+  __shared__ long long wsum[16];
+  __shared__ long long carry_s;
+  __shared__ int bad;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) {
+    carry_s = 0;
+    bad = 0;
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < B; c0 += 1024) {
+    const int i = c0 + threadIdx.x;
+    long long v = 0;
+    if (i < B) {
+      v = tiles[i];
+      if (v < 0) atomicOr(&bad, 1);
+    }
+    long long inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    long long before = 0, tot = 0;
+    for (int k = 0; k < 16; ++k) {
+      if (k < w) before += wsum[k];
+      tot += wsum[k];
+    }
+    const long long carry = carry_s;
+    const long long ex = carry + before + inc - v;
+    if (i < B) {
+      if (ex > 0x7fffffffll) atomicOr(&bad, 1);
+      off[i] = (int32_t)ex;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry_s = carry + tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (carry_s > 0x7fffffffll) bad = 1;
+    off[B] = (int32_t)carry_s;
+    if (bad && status != nullptr) atomicOr(status, 4);
+  }
+}
+
+hipError_t launch_tile_offsets(const int32_t* tiles, int B, int32_t* offsets, int32_t* status,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_tile_offsets, dim3(1), dim3(1024), 0, s, tiles, B, offsets, status);
+  return hipGetLastError();
+}
+
+}  // namespace ivc

@@ -1,0 +1,296 @@
+// GEMMs of the connector: C[M, N] = act(A[M, K] . W[N, K]^T + bias[N]).
+//
+// Both operands are K-contiguous (A row-major, W in nn.Linear [out, in]
+// layout), which is exactly what a CDNA MFMA lane wants: each lane feeds 8
+// consecutive K values of one row of A and one row of W to
+// v_mfma_f32_32x32x16_bf16.  mlp1, mlp2 and the pooling K/V projection all
+// use the MFMA kernel; the SIMT kernel covers fp32 workloads and the router's
+// fp32-activation products, whose M is the tile count.
+#include "common.h"
+#include "kernels.h"
+
+namespace ivc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA GEMM.
+//
+// Workgroup tile BM x BN, K step 64, WM x WN wavefronts each owning a
+// (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks.  Operand tiles are
+// staged through LDS with a 16-byte row pad (row stride 144 B) so that the
+// 16 lanes of each ds_read_b128 phase hit 16 distinct 4-bank groups.  Two
+// LDS buffers: the next K step's global loads are issued into registers
+// before the current step's MFMAs and written to the other buffer after
+// them, with one barrier per step.
+//
+// Grid mapping: workgroups are dealt round-robin to the 8 XCDs, so the linear
+// id is first regrouped so that consecutive tile ids land on one XCD, then
+// tiles are walked in bands of 8 tile-rows so an XCD's L2 sees the same A
+// rows and W rows many times.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int ACT>
+__global__ void __launch_bounds__(WM* WN * 64, 1)
+k_gemm_mfma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
+            int a_goff, const bf16_t* __restrict__ W, long long ldw,
+            const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
+            int K) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 64;
+  constexpr int LDK = BK + 8;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int AV = BM * (BK / 8) / NT;
+  constexpr int BV = BN * (BK / 8) / NT;
+  static_assert(AV * NT == BM * (BK / 8) && BV * NT == BN * (BK / 8), "tile/threads mismatch");
+
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDK];
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int nb = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int in_group = GM * tiles_n;
+  const int first_m = (bid / in_group) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int pid_m = first_m + (bid % in_group) % gsize;
+  const int pid_n = (bid % in_group) / gsize;
+  const int m0 = pid_m * BM, n0 = pid_n * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+
+  const bf16_t* a_src[AV];
+  const bf16_t* b_src[BV];
+  int a_dst[AV], b_dst[BV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * 8;
+    const int gm = min(m0 + r, M - 1);
+    const long long phys =
+        a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : (long long)gm;
+    a_src[i] = A + phys * lda + kc;
+    a_dst[i] = r * LDK + kc;
+  }
+#pragma unroll
+  for (int i = 0; i < BV; ++i) {
+    const int c = tid + i * NT, r = c >> 3, kc = (c & 7) * 8;
+    const int gn = min(n0 + r, N - 1);
+    b_src[i] = W + (long long)gn * ldw + kc;
+    b_dst[i] = r * LDK + kc;
+  }
+
+  u32x4 ra[AV], rb[BV];
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = K / BK;
+#pragma unroll
+  for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i]);
+#pragma unroll
+  for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i]);
+#pragma unroll
+  for (int i = 0; i < AV; ++i) *reinterpret_cast<u32x4*>(&sA[0][a_dst[i]]) = ra[i];
+#pragma unroll
+  for (int i = 0; i < BV; ++i) *reinterpret_cast<u32x4*>(&sB[0][b_dst[i]]) = rb[i];
+  __syncthreads();
+
+  const int frag_k = (lane >> 5) * 8;
+  const int frag_r = lane & 31;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const long long ko = (long long)(kt + 1) * BK;
+#pragma unroll
+      for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ko);
+#pragma unroll
+      for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + ko);
+    }
+    const bf16_t* tA = sA[cur];
+    const bf16_t* tB = sB[cur];
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(
+            &tA[(wm * TM + i * 32 + frag_r) * LDK + kk * 16 + frag_k]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
+            &tB[(wn * TN + j * 32 + frag_r) * LDK + kk * 16 + frag_k]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < AV; ++i) *reinterpret_cast<u32x4*>(&sA[cur ^ 1][a_dst[i]]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < BV; ++i) *reinterpret_cast<u32x4*>(&sB[cur ^ 1][b_dst[i]]) = rb[i];
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and rows
+  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = n0 + wn * TN + j * 32 + (lane & 31);
+    const bool col_ok = col < N;
+    const float bj = (bias != nullptr && col_ok) ? bias[col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * TM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (col_ok && row < M) {
+          float x = acc[i][j][v] + bj;
+          if (ACT == ACT_GELU) x = gelu_erf(x);
+          Cm[(long long)row * ldc + col] = f32_to_bf16(x);
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_mfma_cfg(const GemmArgs& g, hipStream_t s) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  dim3 grid((unsigned)tiles), block(WM * WN * 64);
+  if (g.act == ACT_GELU)
+    hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, ACT_GELU>), grid, block, 0, s,
+                       (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
+                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, ACT_NONE>), grid, block, 0, s,
+                       (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
+                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K);
+  return hipGetLastError();
+}
+
+bool gemm_mfma_supported(const GemmArgs& g) {
+  return g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % 64 == 0 &&
+         g.K > 0 && g.M > 0 && g.N > 0 && g.lda % 8 == 0 && g.ldw % 8 == 0;
+}
+
+hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s) {
+  if (!gemm_mfma_supported(g)) return hipErrorInvalidValue;
+  // Large products take 256x256 tiles; smaller ones 128x128 so that the
+  // grid still covers the 256 CUs.
+  const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  if (big_tiles >= 256) return launch_mfma_cfg<256, 256, 2, 2>(g, s);
+  return launch_mfma_cfg<128, 128, 2, 2>(g, s);
+}
+
+// ---------------------------------------------------------------------------
+// SIMT GEMM, fp32 FMA: 64x64 tile, K step 16, 256 threads with 4x4 outputs
+// each.  Operand tiles go to LDS K-major so each thread's 4 rows / 4 columns
+// are contiguous.
+// ---------------------------------------------------------------------------
+template <typename TA, typename TW, typename TC, int ACT>
+__global__ void __launch_bounds__(256)
+k_gemm_simt(const TA* __restrict__ A, long long lda, int a_rpg, long long a_gstride, int a_goff,
+            const TW* __restrict__ W, long long ldw, const float* __restrict__ bias,
+            TC* __restrict__ Cm, long long ldc, int M, int N, int K) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float sA[BK][BM + 4];
+  __shared__ float sW[BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+
+  // loader mapping: row lr = tid / 4 (0..63), k lk = (tid % 4) * 4 (0..12)
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  const int gm = m0 + lr, gn = n0 + lr;
+  const bool a_ok = gm < M, w_ok = gn < N;
+  long long a_row = 0;
+  if (a_ok) a_row = a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : gm;
+  const TA* a_ptr = A + a_row * lda;
+  const TW* w_ptr = W + (long long)(w_ok ? gn : 0) * ldw;
+
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k0 + lk + e;
+      sA[lk + e][lr] = (a_ok && k < K) ? Elem<TA>::to_f(a_ptr[k]) : 0.f;
+      sW[lk + e][lr] = (w_ok && k < K) ? Elem<TW>::to_f(w_ptr[k]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      float a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = sW[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= N) continue;
+      float x = acc[i][j] + (bias != nullptr ? bias[col] : 0.f);
+      if (ACT == ACT_GELU) x = gelu_erf(x);
+      Cm[(long long)row * ldc + col] = Elem<TC>::from_f(x);
+    }
+  }
+}
+
+template <typename TA, typename TW, typename TC>
+static hipError_t launch_simt_t(const GemmArgs& g, hipStream_t s) {
+  dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64)), block(256);
+  if (g.act == ACT_GELU)
+    hipLaunchKernelGGL((k_gemm_simt<TA, TW, TC, ACT_GELU>), grid, block, 0, s, (const TA*)g.A,
+                       g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const TW*)g.W, g.ldw, g.bias,
+                       (TC*)g.Cm, g.ldc, g.M, g.N, g.K);
+  else
+    hipLaunchKernelGGL((k_gemm_simt<TA, TW, TC, ACT_NONE>), grid, block, 0, s, (const TA*)g.A,
+                       g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const TW*)g.W, g.ldw, g.bias,
+                       (TC*)g.Cm, g.ldc, g.M, g.N, g.K);
+  return hipGetLastError();
+}
+
+template <typename TA, typename TW>
+static hipError_t launch_simt_c(const GemmArgs& g, hipStream_t s) {
+  return g.c_dtype == DT_BF16 ? launch_simt_t<TA, TW, bf16_t>(g, s)
+                              : launch_simt_t<TA, TW, float>(g, s);
+}
+template <typename TA>
+static hipError_t launch_simt_w(const GemmArgs& g, hipStream_t s) {
+  return g.w_dtype == DT_BF16 ? launch_simt_c<TA, bf16_t>(g, s) : launch_simt_c<TA, float>(g, s);
+}
+
+hipError_t launch_gemm_simt(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  return g.a_dtype == DT_BF16 ? launch_simt_w<bf16_t>(g, s) : launch_simt_w<float>(g, s);
+}
+
+}  // namespace ivc

@@ -1,0 +1,220 @@
+// Fused CLS drop + pixel_shuffle v2 + LayerNorm loader.
+//
+// pixel_shuffle v2 is a pure space-to-depth permutation of the P x P token
+// grid (InternVL3-14B-Instruct pixel-shuffle page, pixel_shuffle section;
+// InternVL3_5-2B-Flash page, three token levels):
+//   out[a*(P/r) + b][(r*m + k)*C + c] = grid[r*a + m][r*b + k][c],
+//   grid[i][j] = vit row has_cls + i*P + j.
+// An r=2 token is 4 input rows of C (a 2x2 cell block); an r=4 token is the
+// 4x4 block made of four r=2 blocks.  mlp1/mlp2 start with LayerNorm over the
+// concatenated row (4C or 16C), fused here so the permuted rows are written
+// once, already normalised, in the layout the projector GEMM reads.
+//
+// Work split (one wavefront = one r=2 token): the wave loads its 4 input rows
+// with 16-byte loads (a row is C contiguous elements, so every load is fully
+// coalesced), keeps them in registers, takes the r=2 statistics with two
+// passes over the registers, and writes the normalised 4C row.  With the
+// 64-token path on, a workgroup is the 4 waves of one r=4 block: they share
+// their partial sums through LDS for the 16C statistics (again two passes)
+// and each writes its 4 cells into the 16C row.  The ViT tensor is read
+// exactly once for both paths.
+#include "common.h"
+#include "kernels.h"
+
+namespace ivc {
+
+template <typename E, int CPL, bool FLASH, bool LN>
+__global__ void __launch_bounds__(256)
+k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
+             const float* __restrict__ g2, const float* __restrict__ b2, E* __restrict__ out2,
+             const float* __restrict__ g4, const float* __restrict__ b4, E* __restrict__ out4,
+             float eps) {
+  constexpr int V = Elem<E>::kPerVec;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int rows = has_cls + P * P;
+  const int Q2 = P >> 1, S2 = Q2 * Q2;
+  const int vpr = C / V;  // 16-byte vectors per input row
+
+  int t, a2, b2i, a4 = 0, b4i = 0;
+  if (FLASH) {
+    const int Q4 = P >> 2, S4 = Q4 * Q4;
+    const int blk = blockIdx.x;
+    t = blk / S4;
+    const int rem = blk - t * S4;
+    a4 = rem / Q4;
+    b4i = rem - a4 * Q4;
+    a2 = 2 * a4 + (w >> 1);
+    b2i = 2 * b4i + (w & 1);
+  } else {
+    const int tok = blockIdx.x * 4 + w;
+    if (tok >= T * S2) return;  // whole wave leaves; no barrier in this variant
+    t = tok / S2;
+    const int rem = tok - t * S2;
+    a2 = rem / Q2;
+    b2i = rem - a2 * Q2;
+  }
+
+  // ---- load the 2x2 cell block: cell q = 2m + k is grid (2*a2 + m, 2*b2 + k)
+  u32x4 raw[4][CPL];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int gi = 2 * a2 + (q >> 1), gj = 2 * b2i + (q & 1);
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(X + ((size_t)t * rows + has_cls + gi * P + gj) * C);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int v = lane + 64 * i;
+      raw[q][i] = (v < vpr) ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  float mean2 = 0.f, rstd2 = 1.f, mean4 = 0.f, rstd4 = 1.f;
+  if (LN) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        if (lane + 64 * i < vpr) {
+          float f[V];
+          unpack<E>(raw[q][i], f);
+#pragma unroll
+          for (int e = 0; e < V; ++e) s += f[e];
+        }
+      }
+    const float s2 = wave_sum(s);
+    mean2 = s2 / (float)(4 * C);
+    float d2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        if (lane + 64 * i < vpr) {
+          float f[V];
+          unpack<E>(raw[q][i], f);
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const float d = f[e] - mean2;
+            d2 += d * d;
+          }
+        }
+      }
+    rstd2 = 1.0f / sqrtf(wave_sum(d2) / (float)(4 * C) + eps);
+
+    if (FLASH) {
+      __shared__ float red[2][4];
+      if (lane == 0) red[0][w] = s2;
+      __syncthreads();
+      mean4 = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)(16 * C);
+      float d4 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          if (lane + 64 * i < vpr) {
+            float f[V];
+            unpack<E>(raw[q][i], f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+              const float d = f[e] - mean4;
+              d4 += d * d;
+            }
+          }
+        }
+      d4 = wave_sum(d4);
+      if (lane == 0) red[1][w] = d4;
+      __syncthreads();
+      rstd4 = 1.0f / sqrtf((red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)(16 * C) + eps);
+    }
+  }
+
+  // ---- r = 2 row: channel block q holds cell q
+  if (out2 != nullptr) {
+    E* dst = out2 + ((size_t)t * S2 + a2 * Q2 + b2i) * (size_t)(4 * C);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int v = lane + 64 * i;
+        if (v < vpr) {
+          const int ch = q * C + v * V;
+          u32x4 o = raw[q][i];
+          if (LN) {
+            float f[V];
+            unpack<E>(raw[q][i], f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = (f[e] - mean2) * rstd2 * g2[ch + e] + b2[ch + e];
+            o = pack<E>(f);
+          }
+          *reinterpret_cast<u32x4*>(dst + ch) = o;
+        }
+      }
+  }
+
+  // ---- r = 4 row: this wave's cell (m, k) sits at (2*(w>>1) + m, 2*(w&1) + k)
+  //      inside the 4x4 block, channel block 4*m4 + k4.
+  if (FLASH && out4 != nullptr) {
+    const int Q4 = P >> 2, S4 = Q4 * Q4;
+    E* dst = out4 + ((size_t)t * S4 + a4 * Q4 + b4i) * (size_t)(16 * C);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m4 = 2 * (w >> 1) + (q >> 1), k4 = 2 * (w & 1) + (q & 1);
+      const int base = (4 * m4 + k4) * C;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int v = lane + 64 * i;
+        if (v < vpr) {
+          const int ch = base + v * V;
+          u32x4 o = raw[q][i];
+          if (LN) {
+            float f[V];
+            unpack<E>(raw[q][i], f);
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = (f[e] - mean4) * rstd4 * g4[ch + e] + b4[ch + e];
+            o = pack<E>(f);
+          }
+          *reinterpret_cast<u32x4*>(dst + ch) = o;
+        }
+      }
+    }
+  }
+}
+
+template <typename E, int CPL, bool LN>
+static hipError_t launch_cpl(const ShuffleArgs& a, hipStream_t s) {
+  const int Q2 = a.P / 2, Q4 = a.P / 4;
+  if (a.flash) {
+    dim3 grid((unsigned)(a.T * Q4 * Q4));
+    hipLaunchKernelGGL((k_shuffle_ln<E, CPL, true, LN>), grid, dim3(256), 0, s, (const E*)a.X, a.T,
+                       a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4, a.eps);
+  } else {
+    const long long toks = (long long)a.T * Q2 * Q2;
+    dim3 grid((unsigned)((toks + 3) / 4));
+    hipLaunchKernelGGL((k_shuffle_ln<E, CPL, false, LN>), grid, dim3(256), 0, s, (const E*)a.X,
+                       a.T, a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4,
+                       a.eps);
+  }
+  return hipGetLastError();
+}
+
+template <typename E, bool LN>
+static hipError_t launch_e(const ShuffleArgs& a, hipStream_t s) {
+  const int vpr = a.C / Elem<E>::kPerVec;
+  const int need = (vpr + 63) / 64;
+  if (need <= 1) return launch_cpl<E, 1, LN>(a, s);
+  if (need <= 2) return launch_cpl<E, 2, LN>(a, s);
+  if (need <= 4) return launch_cpl<E, 4, LN>(a, s);
+  if (need <= 8) return launch_cpl<E, 8, LN>(a, s);
+  return hipErrorInvalidValue;
+}
+
+int shuffle_max_width(int dtype) { return 8 * 64 * (dtype == 1 ? 8 : 4); }
+
+hipError_t launch_shuffle_ln(const ShuffleArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.dtype == 1) return a.ln ? launch_e<bf16_t, true>(a, s) : launch_e<bf16_t, false>(a, s);
+  return a.ln ? launch_e<float, true>(a, s) : launch_e<float, false>(a, s);
+}
+
+}  // namespace ivc

@@ -1,0 +1,111 @@
+// Routing decision of the Visual Resolution Router.
+//
+// InternVL3_5-4B-Flash Gating and CrossAttentionPooling page, section 4, and
+// the InternVL3_5-2B-Flash page's routing-decision section: the threshold is
+// the 0.1-quantile of gate[:, 0] over the whole batch (linear interpolation
+// between order statistics, as torch.quantile), and a tile takes the 64-token
+// path only when gate[t, 0] > that quantile AND gate[t, 0] >= 0.5.
+//
+// One workgroup: the two order statistics come from an exact radix select
+// (four 8-bit passes over order-preserving uint32 keys of the fp32 gates),
+// the interpolation is done in fp64 with every operation rounded on its own
+// (contraction into fused multiply-add is switched off), so the threshold and every decision are bit-identical
+// to a host evaluation of the same formula on the same gates.
+#include "common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+namespace ivc {
+
+IVC_DEV uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+IVC_DEV float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+constexpr int QT = 1024;  // threads
+
+// k-th smallest key (0-based) among the T gates.
+IVC_DEV uint32_t radix_select(const float* gate, int T, int k, uint32_t* hist, uint32_t* sh) {
+  uint32_t prefix = 0;
+  for (int pass = 3; pass >= 0; --pass) {
+    const int shift = 8 * pass;
+    const uint32_t mask = pass == 3 ? 0u : (0xffffffffu << (shift + 8));
+    for (int i = threadIdx.x; i < 256; i += QT) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < T; i += QT) {
+      const uint32_t key = order_key(gate[2 * i]);
+      if ((key & mask) == (prefix & mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t cum = 0, b = 0;
+      for (; b < 255; ++b) {
+        if ((uint32_t)k < cum + hist[b]) break;
+        cum += hist[b];
+      }
+      k -= (int)cum;
+      sh[0] = prefix | (b << shift);
+      sh[1] = (uint32_t)k;
+    }
+    __syncthreads();
+    prefix = sh[0];
+    k = (int)sh[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__global__ void __launch_bounds__(QT)
+k_quantile_decide(const float* __restrict__ gate, int T, double q, double abs_thr,
+                  double* __restrict__ thr_out, uint8_t* __restrict__ use64) {
+  // Every product and sum below is rounded on its own: HIP's __dmul_rn and
+  // friends are plain operators that the compiler may fuse into an FMA, which
+  // moves the threshold by an ulp, so plain operators with contraction off.
+#pragma clang fp contract(off)
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[4];
+
+  const double pos = q * (double)(T - 1);
+  const double fl = floor(pos);
+  const int lo = (int)fl;
+  const int hi = (int)ceil(pos);
+  const double frac = pos - fl;
+
+  const uint32_t klo = radix_select(gate, T, lo, hist, sh);
+  // the next order statistic: equal to v[lo] if enough keys tie with it,
+  // otherwise the smallest key above it
+  if (threadIdx.x == 0) {
+    sh[2] = 0;
+    sh[3] = 0xffffffffu;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T; i += QT) {
+    const uint32_t key = order_key(gate[2 * i]);
+    if (key <= klo) atomicAdd(&sh[2], 1u);
+    else atomicMin(&sh[3], key);
+  }
+  __syncthreads();
+  const uint32_t khi = ((uint32_t)hi < sh[2]) ? klo : sh[3];
+
+  const double a = (double)key_value(klo), b = (double)key_value(khi);
+  const double diff = b - a;
+  const double thr = frac < 0.5 ? a + diff * frac : b - diff * (1.0 - frac);
+  if (threadIdx.x == 0) *thr_out = thr;
+  for (int i = threadIdx.x; i < T; i += QT) {
+    const double g = (double)gate[2 * i];
+    use64[i] = (g > thr && g >= abs_thr) ? 1 : 0;
+  }
+}
+
+hipError_t launch_quantile_decide(const float* gate, int T, double q, double abs_thr,
+                                  double* thr, uint8_t* use64, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantile_decide, dim3(1), dim3(QT), 0, s, gate, T, q, abs_thr, thr, use64);
+  return hipGetLastError();
+}
+
+}  // namespace ivc

@@ -1,0 +1,140 @@
+// Internal launch interface of the connector's kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ivc {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { ACT_NONE = 0, ACT_GELU = 1 };
+
+// ---- fused CLS drop + pixel_shuffle + LayerNorm ----------------------------
+struct ShuffleArgs {
+  int dtype;
+  const void* X;
+  int T, P, C, has_cls;
+  int flash;  // 1: one workgroup per r=4 block, writes out4 (and out2 if non-null)
+  int ln;     // 0: pure permutation (no normalisation)
+  const float *g2, *b2;
+  void* out2;
+  const float *g4, *b4;
+  void* out4;
+  float eps;
+};
+hipError_t launch_shuffle_ln(const ShuffleArgs& a, hipStream_t s);
+int shuffle_max_width(int dtype);
+
+// ---- GEMM: C[M, N] = act(A[M, K] . W[N, K]^T + bias[N]) ---------------------
+// A rows may be remapped: logical row m reads physical row
+//   (m / a_rpg) * a_gstride + a_goff + m % a_rpg      (a_rpg > 0)
+// which lets a GEMM read the ViT tensor with the CLS rows skipped.
+struct GemmArgs {
+  const void* A;
+  long long lda;
+  int a_rpg;
+  long long a_gstride;
+  int a_goff;
+  const void* W;
+  long long ldw;
+  const float* bias;
+  void* Cm;
+  long long ldc;
+  int M, N, K;
+  int act;
+  int a_dtype, w_dtype, c_dtype;
+};
+// bf16 A and W, fp32 accumulation on MFMA, bf16 out.  Needs K % 64 == 0.
+hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
+bool gemm_mfma_supported(const GemmArgs& g);
+// Any element types, fp32 FMA.  Used for fp32 workloads and fp32-activation
+// router products.
+hipError_t launch_gemm_simt(const GemmArgs& g, hipStream_t s);
+
+// ---- CrossAttentionPooling ---------------------------------------------------
+struct PoolAttnArgs {
+  int dtype;           // element type of KV
+  const void* KV;      // [T*N, kv_ld] with K_l at column kcol, V_l at vcol
+  long long kv_ld;
+  int kcol, vcol;
+  const float* Q;      // [T, C] projected queries of this layer
+  const int* valid;    // [T] or null
+  int* status;         // device status word or null
+  int T, N, C, H;
+  int splits;          // token splits per tile
+  float* part;         // [T, splits, H, 2 + d]: running max, sum, weighted V
+  float* O;            // [T, C] attention output (before out-projection)
+};
+hipError_t launch_pool_attn(const PoolAttnArgs& a, hipStream_t s);
+bool pool_attn_supported(int C, int H);
+
+// ---- Gating helpers ----------------------------------------------------------
+// x[t] += LayerNorm(y[t]) * gamma + beta   (rows of width h, fp32)
+hipError_t launch_residual_ln(float* x, const float* y, const float* gamma, const float* beta,
+                              int T, int h, float eps, hipStream_t s);
+// z = Wc x + bc, gate = softmax(z) for 2 classes; Wc element type dtype
+hipError_t launch_gate_head(int dtype, const float* x, const void* Wc, const float* bc,
+                            float* gate, int T, int h, hipStream_t s);
+// broadcast a [C] vector (element type dtype) into fp32 rows [T, C]
+hipError_t launch_broadcast_rows(int dtype, const void* v, float* out, int T, int C,
+                                 hipStream_t s);
+
+// ---- quantile + decision -----------------------------------------------------
+hipError_t launch_quantile_decide(const float* gate, int T, double q, double abs_thr,
+                                  double* thr, uint8_t* use64, hipStream_t s);
+
+// ---- compaction ----------------------------------------------------------------
+struct CompactArgs {
+  int dtype;
+  const int32_t* ids;
+  const void* embeds;
+  long long L;
+  int img_id;
+  const uint8_t* use64;
+  const void* out256;
+  const void* out64;
+  int T, S, S64, D;
+  int32_t* out_ids;
+  int32_t* out_pos;
+  int32_t* keep_map;
+  void* out_embeds;
+  long long* out_len;
+  int32_t* status;
+  // workspace
+  int32_t* blk_cnt;        // [nblk]
+  int32_t* blk_off;        // [nblk]
+  int32_t* routed_before;  // [T + 1]
+  long long* src;          // [L] source row code per output row
+};
+long long compact_blocks(long long L);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+hipError_t launch_tile_offsets(const int32_t* tiles, int B, int32_t* offsets, int32_t* status,
+                               hipStream_t s);
+
+// ---- folded pooling -------------------------------------------------------------
+struct FoldedArgs {
+  int dtype;
+  const void* X;      // ViT rows
+  int rows, has_cls;
+  const int* valid;
+  int* status;
+  int T, N, C, H;
+  const float* qt;    // [T, H, C] folded queries (already scaled by 1/sqrt(d))
+  int splits;
+  float* part;        // [T, splits, H, 2 + C]
+  float* xbar;        // [T, H, C] softmax-weighted token means
+};
+hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
+// qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :]
+hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, float* qt, int T, int C,
+                             int H, float scale, hipStream_t s);
+// o[t, h*d + i] = bv[h*d+i] + sum_c Wv[h*d + i, c] * xbar[t, h, c]
+hipError_t launch_fold_value(int dtype, const float* xbar, const void* Wv, const float* bv,
+                             float* o, int T, int C, int H, hipStream_t s);
+
+// ---- per-kernel timing (ivc_profile_*) -----------------------------------------
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+}  // namespace ivc
