@@ -262,6 +262,66 @@ def test_route_decide_bit_exact(T):
 
 
 # ---------------------------------------------------------------------------
+# folded pooling (key/value projections folded out of the token pass)
+# ---------------------------------------------------------------------------
+def _small_bf16_router(pool_mode):
+    cfg = workload("tiny_flash_f32", dtype="bf16", C=512, D=256, mlp1_hidden=256,
+                   mlp2_hidden=256, pool_heads=8, gate_hidden=512, pool_mode=pool_mode)
+    cfg["name"] = "small_bf16_router"
+    return cfg
+
+
+@pytest.mark.parametrize("padded", [False, True])
+def test_folded_pool_small_matches_oracle_and_kv(padded):
+    cfg = _small_bf16_router(1)
+    w = synth.make_weights(cfg)
+    x = synth.make_vit(cfg)
+    valid = synth.make_valid_tokens(cfg, seed=9) if padded else None
+    if padded:
+        x[:, 0, :] = np.nan
+        for t in range(cfg["T"]):
+            x[t, 1 + valid[t]:, :] = np.nan
+    say(f"folded small padded={padded}")
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    vd = torch.from_numpy(valid).cuda() if padded else None
+    rf = _connector(cfg, w, cfg["T"]).route(xd, valid=vd)
+    rk = _connector(dict(cfg, pool_mode=0), w, cfg["T"]).route(xd, valid=vd)
+    torch.cuda.synchronize()
+    assert int(rf["status"].item()) == 0
+    e_gate, _, _, e_pooled = O.connector_route(x, cfg, w, valid)
+    assert_close(to_np(rf["pooled"]), e_pooled, "bf16", "folded pooled")
+    assert_close(to_np(rk["pooled"]), e_pooled, "bf16", "kv pooled")
+    assert np.abs(rf["gate"].cpu().numpy() - e_gate).max() <= GATE_TOL
+    gate = rf["gate"].cpu().numpy()
+    thr, use = O.decide(gate[:, 0], cfg)
+    assert float(rf["thr"].item()) == thr
+    assert np.array_equal(rf["use64"].cpu().numpy(), use)
+
+
+def test_folded_pool_flash_workload():
+    cfg = workload("internvl35_2b_flash", pool_mode=1)
+    say(f"2B-Flash folded route: T={cfg['T']}")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, cfg["T"])
+    xd = dev_vit(cfg)
+    r = con.route(xd)
+    torch.cuda.synchronize()
+    gate = r["gate"].cpu().numpy()
+    thr, use = O.decide(gate[:, 0], cfg)
+    assert float(r["thr"].item()) == thr
+    assert np.array_equal(r["use64"].cpu().numpy(), use)
+    g0 = gate[:, 0].astype(np.float64)
+    near = {int(np.argmin(np.abs(g0 - thr))), int(np.argmin(np.abs(g0 - 0.5)))}
+    tiles = sorted(set(synth.sample_tiles(cfg["T"], n=12)) | near)
+    x = synth.make_vit_tiles(cfg, tiles)
+    e_gate, _, _, e_pooled = O.connector_route(x, cfg, w)
+    assert_close(to_np(r["pooled"][tiles]), e_pooled, "bf16", "pooled")
+    dg = np.abs(gate[tiles] - e_gate).max()
+    say(f"  gate max abs diff {dg:.3e}")
+    assert dg <= GATE_TOL
+
+
+# ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
 def test_edge_cases():

@@ -220,8 +220,9 @@ ivc_status check_cfg(const ivc_config& c) {
     if (c.gate_expansion < 1) return fail(IVC_ERR_INVALID_ARG, "gate_expansion");
     if (c.pool_mode != IVC_POOL_KV && c.pool_mode != IVC_POOL_FOLDED)
       return fail(IVC_ERR_INVALID_ARG, "pool_mode %d", c.pool_mode);
-    if (c.pool_mode == IVC_POOL_FOLDED)
-      return fail(IVC_ERR_UNSUPPORTED, "folded pooling is not built in this library version");
+    if (c.pool_mode == IVC_POOL_FOLDED && !pool_folded_supported(c.dtype, c.vit_width, c.pool_heads))
+      return fail(IVC_ERR_UNSUPPORTED,
+                  "folded pooling needs bf16, C in {512, 1024} and at most 16 heads");
     if (!(c.rel_quantile >= 0.0 && c.rel_quantile <= 1.0))
       return fail(IVC_ERR_INVALID_ARG, "rel_quantile outside [0, 1]");
   }
@@ -283,8 +284,8 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
 }
 
 struct RouteWs {
-  void* kv;
-  float *q, *qp, *o, *part, *y1, *y2, *x;
+  void *kv, *qt_hi, *qt_lo;
+  float *q, *qp, *o, *part, *xbar, *y1, *y2, *x;
 };
 size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   const ivc_config& c = h->cfg;
@@ -293,12 +294,19 @@ size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   Carver cv(base);
   RouteWs r{};
   if (!c.flash) return 0;
-  r.kv = cv.take((size_t)T * N * 2 * L * C * h->esz);
+  const int sp = pool_splits(T, (int)N);
+  if (c.pool_mode == IVC_POOL_FOLDED) {
+    r.qt_hi = cv.take((size_t)T * 16 * C * 2);
+    r.qt_lo = cv.take((size_t)T * 16 * C * 2);
+    r.part = (float*)cv.take((size_t)T * sp * 16 * (2 + C) * 4);
+    r.xbar = (float*)cv.take((size_t)T * c.pool_heads * C * 4);
+  } else {
+    r.kv = cv.take((size_t)T * N * 2 * L * C * h->esz);
+    r.part = (float*)cv.take((size_t)T * sp * (2 * c.pool_heads + C) * 4);
+  }
   r.q = (float*)cv.take((size_t)T * C * 4);
   r.qp = (float*)cv.take((size_t)T * C * 4);
   r.o = (float*)cv.take((size_t)T * C * 4);
-  const int sp = pool_splits(T, (int)N);
-  r.part = (float*)cv.take((size_t)T * sp * (2 * c.pool_heads + C) * 4);
   r.y1 = (float*)cv.take((size_t)T * he * 4);
   r.y2 = (float*)cv.take((size_t)T * hh * 4);
   r.x = (float*)cv.take((size_t)T * hh * 4);
@@ -585,36 +593,66 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
   const int rows = c.has_cls + N;
   const int hh = c.gate_hidden, he = hh * c.gate_expansion;
 
-  // K and V of every layer from the raw tokens (CLS skipped by the row remap)
-  GemmArgs kv = mk_gemm(vit, C, dt, h->wkv, dt, h->bkv, w.kv, dt, T * N, 2 * L * C, C, ACT_NONE);
-  kv.a_rpg = N;
-  kv.a_gstride = rows;
-  kv.a_goff = c.has_cls;
-  LAUNCH("pool_kv_gemm", s, gemm("pool_kv_gemm", kv, s));
+  const bool folded = c.pool_mode == IVC_POOL_FOLDED;
+  if (!folded) {
+    // K and V of every layer from the raw tokens (CLS skipped by the row remap)
+    GemmArgs kv = mk_gemm(vit, C, dt, h->wkv, dt, h->bkv, w.kv, dt, T * N, 2 * L * C, C, ACT_NONE);
+    kv.a_rpg = N;
+    kv.a_gstride = rows;
+    kv.a_goff = c.has_cls;
+    LAUNCH("pool_kv_gemm", s, gemm("pool_kv_gemm", kv, s));
+  }
 
   LAUNCH("pool_query", s, launch_broadcast_rows(dt, h->query, w.q, T, C, s));
   const int splits = pool_splits(T, N);
+  const float scale = 1.0f / sqrtf((float)(C / H));
   for (int l = 0; l < L; ++l) {
     LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
                                  mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32, T,
                                          C, C, ACT_NONE), s));
-    PoolAttnArgs pa{};
-    pa.dtype = dt;
-    pa.KV = w.kv;
-    pa.kv_ld = 2ll * L * C;
-    pa.kcol = 2 * l * C;
-    pa.vcol = (2 * l + 1) * C;
-    pa.Q = w.qp;
-    pa.valid = valid_tokens;
-    pa.status = dev_status;
-    pa.T = T;
-    pa.N = N;
-    pa.C = C;
-    pa.H = H;
-    pa.splits = splits;
-    pa.part = w.part;
-    pa.O = w.o;
-    LAUNCH("pool_attn", s, launch_pool_attn(pa, s));
+    const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * C * h->esz;
+    const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * C * h->esz;
+    const float* bv = h->bkv + (size_t)(2 * l + 1) * C;
+    if (folded) {
+      LAUNCH("pool_fold_query", s,
+             launch_fold_query(dt, w.qp, wk, w.qt_hi, w.qt_lo, T, C, H, scale, s));
+      FoldedArgs fa{};
+      fa.dtype = dt;
+      fa.X = vit;
+      fa.rows = rows;
+      fa.has_cls = c.has_cls;
+      fa.valid = valid_tokens;
+      fa.status = dev_status;
+      fa.T = T;
+      fa.N = N;
+      fa.C = C;
+      fa.H = H;
+      fa.qt_hi = w.qt_hi;
+      fa.qt_lo = w.qt_lo;
+      fa.splits = splits;
+      fa.part = w.part;
+      fa.xbar = w.xbar;
+      LAUNCH("pool_folded", s, launch_pool_folded(fa, s));
+      LAUNCH("pool_fold_value", s, launch_fold_value(dt, w.xbar, wv, bv, w.o, T, C, H, s));
+    } else {
+      PoolAttnArgs pa{};
+      pa.dtype = dt;
+      pa.KV = w.kv;
+      pa.kv_ld = 2ll * L * C;
+      pa.kcol = 2 * l * C;
+      pa.vcol = (2 * l + 1) * C;
+      pa.Q = w.qp;
+      pa.valid = valid_tokens;
+      pa.status = dev_status;
+      pa.T = T;
+      pa.N = N;
+      pa.C = C;
+      pa.H = H;
+      pa.splits = splits;
+      pa.part = w.part;
+      pa.O = w.o;
+      LAUNCH("pool_attn", s, launch_pool_attn(pa, s));
+    }
     float* qn = (l == L - 1 && pooled) ? pooled : w.q;
     LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
                                  mk_gemm(w.o, C, DT_F32, h->wo[l], dt, h->bo[l], qn, DT_F32, T,

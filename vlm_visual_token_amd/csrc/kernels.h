@@ -115,20 +115,22 @@ hipError_t launch_tile_offsets(const int32_t* tiles, int B, int32_t* offsets, in
 // ---- folded pooling -------------------------------------------------------------
 struct FoldedArgs {
   int dtype;
-  const void* X;      // ViT rows
+  const void* X;      // ViT rows [T, rows, C]
   int rows, has_cls;
   const int* valid;
   int* status;
   int T, N, C, H;
-  const float* qt;    // [T, H, C] folded queries (already scaled by 1/sqrt(d))
+  const void* qt_hi;  // [T, 16, C] bf16: folded queries (1/sqrt(d) applied), high part
+  const void* qt_lo;  // low part
   int splits;
-  float* part;        // [T, splits, H, 2 + C]
+  float* part;        // [T, splits, 16 * (2 + C)]
   float* xbar;        // [T, H, C] softmax-weighted token means
 };
+bool pool_folded_supported(int dtype, int C, int H);
 hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
-// qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :]
-hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, float* qt, int T, int C,
-                             int H, float scale, hipStream_t s);
+// qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
+hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt_hi, void* qt_lo,
+                             int T, int C, int H, float scale, hipStream_t s);
 // o[t, h*d + i] = bv[h*d+i] + sum_c Wv[h*d + i, c] * xbar[t, h, c]
 hipError_t launch_fold_value(int dtype, const float* xbar, const void* Wv, const float* bv,
                              float* o, int T, int C, int H, hipStream_t s);
