@@ -229,9 +229,31 @@ ivc_status check_cfg(const ivc_config& c) {
   return IVC_OK;
 }
 
-// GEMM dispatch: MFMA for bf16 operands with K % 64 == 0, SIMT otherwise.
-hipError_t gemm(const char*, GemmArgs g, hipStream_t s) {
-  if (gemm_mfma_supported(g)) return launch_gemm_mfma(g, s);
+// Scratch of the SIMT kernel's split-K reduction.
+struct SimtScratch {
+  float* part = nullptr;
+  size_t part_elems = 0;
+  void need(int M, int N, int K, int batch) {
+    const int ks = simt_ksplit(M, N, K, batch);
+    const size_t pe = simt_part_elems(M, N, batch, ks);
+    if (pe > part_elems) part_elems = pe;
+  }
+  void carve(Carver& cv) { part = (float*)cv.take(part_elems * 4); }
+};
+
+// GEMM dispatch: MFMA for bf16 operands with K % 64 == 0, SIMT otherwise
+// (split over K when the product is skinny and scratch is available).
+hipError_t gemm(const char*, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
+  if (g.batch <= 0) g.batch = 1;
+  if (g.batch == 1 && gemm_mfma_supported(g)) return launch_gemm_mfma(g, s);
+  g.ksplit = 1;
+  if (sc != nullptr && sc->part != nullptr) {
+    const int ks = simt_ksplit(g.M, g.N, g.K, g.batch);
+    if (ks > 1 && simt_part_elems(g.M, g.N, g.batch, ks) <= sc->part_elems) {
+      g.ksplit = ks;
+      g.part = sc->part;
+    }
+  }
   return launch_gemm_simt(g, s);
 }
 
@@ -252,6 +274,8 @@ GemmArgs mk_gemm(const void* A, long long lda, int a_dt, const void* W, int w_dt
   g.a_dtype = a_dt;
   g.w_dtype = w_dt;
   g.c_dtype = c_dt;
+  g.batch = 1;
+  g.ksplit = 1;
   return g;
 }
 
@@ -265,6 +289,7 @@ int pool_splits(int T, int N) {
 // ---- workspace plans ----
 struct RunWs {
   void *a2, *a4, *h1, *g1, *g2;
+  SimtScratch sc;
 };
 size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
   const ivc_config& c = h->cfg;
@@ -279,6 +304,17 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
     r.g1 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
     r.g2 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
   }
+  if (c.dtype == IVC_F32) {  // bf16 products all run on MFMA
+    const int M2 = (int)(T * S), M4 = (int)(T * S4);
+    r.sc.need(M2, c.mlp1_hidden, 4 * c.vit_width, 1);
+    r.sc.need(M2, c.llm_width, c.mlp1_hidden, 1);
+    if (c.flash) {
+      r.sc.need(M4, c.mlp2_hidden, 16 * c.vit_width, 1);
+      r.sc.need(M4, c.mlp2_hidden, c.mlp2_hidden, 1);
+      r.sc.need(M4, c.llm_width, c.mlp2_hidden, 1);
+    }
+    r.sc.carve(cv);
+  }
   if (w) *w = r;
   return cv.off;
 }
@@ -286,6 +322,7 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
 struct RouteWs {
   void *kv, *qt_hi, *qt_lo;
   float *q, *qp, *o, *part, *xbar, *y1, *y2, *x;
+  SimtScratch sc;
 };
 size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   const ivc_config& c = h->cfg;
@@ -310,6 +347,11 @@ size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   r.y1 = (float*)cv.take((size_t)T * he * 4);
   r.y2 = (float*)cv.take((size_t)T * hh * 4);
   r.x = (float*)cv.take((size_t)T * hh * 4);
+  r.sc.need(T, (int)C, (int)C, 1);
+  r.sc.need(T, (int)he, (int)hh, 1);
+  r.sc.need(T, (int)hh, (int)he, 1);
+  r.sc.need(T, (int)C / c.pool_heads, (int)C, c.pool_heads);
+  r.sc.carve(cv);
   if (w) *w = r;
   return cv.off;
 }
@@ -547,21 +589,21 @@ extern "C" ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32
   const int M2 = (int)(T * S);
   LAUNCH("mlp1_gemm1", s, gemm("mlp1_gemm1",
                               mk_gemm(w.a2, 4 * C, dt, h->m1_w1, dt, h->m1_b1, w.h1, dt, M2, H1,
-                                      4 * C, ACT_GELU), s));
+                                      4 * C, ACT_GELU), s, &w.sc));
   LAUNCH("mlp1_gemm2", s, gemm("mlp1_gemm2",
                               mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D,
-                                      H1, ACT_NONE), s));
+                                      H1, ACT_NONE), s, &w.sc));
   if (c.flash) {
     const int M4 = T * (c.grid / 4) * (c.grid / 4);
     LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1",
                                 mk_gemm(w.a4, 16 * C, dt, h->m2_w1, dt, h->m2_b1, w.g1, dt, M4,
-                                        H2, 16 * C, ACT_GELU), s));
+                                        H2, 16 * C, ACT_GELU), s, &w.sc));
     LAUNCH("mlp2_gemm2", s, gemm("mlp2_gemm2",
                                 mk_gemm(w.g1, H2, dt, h->m2_w2, dt, h->m2_b2, w.g2, dt, M4, H2,
-                                        H2, ACT_GELU), s));
+                                        H2, ACT_GELU), s, &w.sc));
     LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3",
                                 mk_gemm(w.g2, H2, dt, h->m2_w3, dt, h->m2_b3, out64, dt, M4, D,
-                                        H2, ACT_NONE), s));
+                                        H2, ACT_NONE), s, &w.sc));
   }
   return IVC_OK;
 }
@@ -609,7 +651,7 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
   for (int l = 0; l < L; ++l) {
     LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
                                  mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32, T,
-                                         C, C, ACT_NONE), s));
+                                         C, C, ACT_NONE), s, &w.sc));
     const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * C * h->esz;
     const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * C * h->esz;
     const float* bv = h->bkv + (size_t)(2 * l + 1) * C;
@@ -633,7 +675,17 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
       fa.part = w.part;
       fa.xbar = w.xbar;
       LAUNCH("pool_folded", s, launch_pool_folded(fa, s));
-      LAUNCH("pool_fold_value", s, launch_fold_value(dt, w.xbar, wv, bv, w.o, T, C, H, s));
+      // o_h = Wv_h xbar_h + bv_h for every head: one batched product over heads
+      const int d = C / H;
+      GemmArgs fv = mk_gemm(w.xbar, (long long)H * C, DT_F32, wv, dt, bv, w.o, DT_F32, T, d, C,
+                            ACT_NONE);
+      fv.ldc = C;
+      fv.batch = H;
+      fv.a_bs = C;
+      fv.w_bs = (long long)d * C;
+      fv.c_bs = d;
+      fv.bias_bs = d;
+      LAUNCH("pool_fold_value", s, gemm("pool_fold_value", fv, s, &w.sc));
     } else {
       PoolAttnArgs pa{};
       pa.dtype = dt;
@@ -656,7 +708,7 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
     float* qn = (l == L - 1 && pooled) ? pooled : w.q;
     LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
                                  mk_gemm(w.o, C, DT_F32, h->wo[l], dt, h->bo[l], qn, DT_F32, T,
-                                         C, C, ACT_NONE), s));
+                                         C, C, ACT_NONE), s, &w.sc));
   }
   const float* pooled_v = pooled ? pooled : w.q;
 
@@ -665,10 +717,10 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
   for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
     LAUNCH("gate_fc1", s, gemm("gate_fc1",
                               mk_gemm(w.x, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1, DT_F32,
-                                      T, he, hh, ACT_GELU), s));
+                                      T, he, hh, ACT_GELU), s, &w.sc));
     LAUNCH("gate_fc2", s, gemm("gate_fc2",
                               mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2, DT_F32,
-                                      T, hh, he, ACT_NONE), s));
+                                      T, hh, he, ACT_NONE), s, &w.sc));
     LAUNCH("gate_res_ln", s,
            launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));
   }

@@ -196,62 +196,138 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// SIMT GEMM, fp32 FMA: 64x64 tile, K step 16, 256 threads with 4x4 outputs
-// each.  Operand tiles go to LDS K-major so each thread's 4 rows / 4 columns
-// are contiguous.
+// SIMT GEMM, fp32 FMA, for fp32 workloads and the router's fp32-activation
+// products (M = tile count, a few hundred rows).  32 x 64 output tile, K step
+// 32, 256 threads with 2 x 4 outputs each; operand tiles go to LDS K-major.
+// Skinny products split K over grid.z so the grid covers the chip: each split
+// writes its partial tile and a second kernel adds the splits in order and
+// applies bias and activation (deterministic, and no device-scope fence,
+// which on a multi-XCD part would write back and invalidate whole L2s).
 // ---------------------------------------------------------------------------
+constexpr int SBM = 32, SBN = 64, SBK = 32;
+
+int simt_tiles(int M, int N) { return ((M + SBM - 1) / SBM) * ((N + SBN - 1) / SBN); }
+
+int simt_ksplit(int M, int N, int K, int batch) {
+  const long long tiles = (long long)simt_tiles(M, N) * batch;
+  int ks = 1;
+  while (tiles * ks < 512 && K / (ks * 2) >= 128) ks *= 2;
+  return ks;
+}
+
+size_t simt_part_elems(int M, int N, int batch, int ksplit) {
+  return ksplit > 1 ? (size_t)batch * ksplit * M * N : 0;
+}
+
+template <typename T> IVC_DEV void load4(const T* p, float* f);
+template <> IVC_DEV void load4<float>(const float* p, float* f) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  unpack<float>(v, f);
+}
+template <> IVC_DEV void load4<bf16_t>(const bf16_t* p, float* f) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
 template <typename TA, typename TW, typename TC, int ACT>
 __global__ void __launch_bounds__(256)
 k_gemm_simt(const TA* __restrict__ A, long long lda, int a_rpg, long long a_gstride, int a_goff,
             const TW* __restrict__ W, long long ldw, const float* __restrict__ bias,
-            TC* __restrict__ Cm, long long ldc, int M, int N, int K) {
-  constexpr int BM = 64, BN = 64, BK = 16;
-  __shared__ float sA[BK][BM + 4];
-  __shared__ float sW[BK][BN + 4];
+            TC* __restrict__ Cm, long long ldc, int M, int N, int K, long long a_bs,
+            long long w_bs, long long c_bs, long long bias_bs, int ksplit, int vec,
+            float* __restrict__ part) {
+  __shared__ float sA[SBK][SBM + 1];
+  __shared__ float sW[SBK][SBN + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * SBM, n0 = blockIdx.x * SBN;
+  const int b = blockIdx.z / ksplit, kz = blockIdx.z % ksplit;
+  A += b * a_bs;
+  W += b * w_bs;
 
-  // loader mapping: row lr = tid / 4 (0..63), k lk = (tid % 4) * 4 (0..12)
-  const int lr = tid >> 2, lk = (tid & 3) * 4;
-  const int gm = m0 + lr, gn = n0 + lr;
+  const int kchunk = ((K + ksplit - 1) / ksplit + SBK - 1) / SBK * SBK;
+  const int k_beg = kz * kchunk, k_end = min(K, k_beg + kchunk);
+
+  // loaders: A tile 32 x 32 (4 consecutive k per thread), W tile 64 x 32 (2 x 4)
+  const int ar = tid >> 3, ak = (tid & 7) * 4;
+  const int wr = tid >> 2, wk = (tid & 3) * 4;
+  const int gm = m0 + ar, gn = n0 + wr;
   const bool a_ok = gm < M, w_ok = gn < N;
   long long a_row = 0;
   if (a_ok) a_row = a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : gm;
   const TA* a_ptr = A + a_row * lda;
   const TW* w_ptr = W + (long long)(w_ok ? gn : 0) * ldw;
 
-  float acc[4][4];
+  float acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = k_beg; k0 < k_end; k0 += SBK) {
+    float av[4], wv[8];
+    if (vec && k0 + SBK <= k_end) {
+      if (a_ok) load4<TA>(a_ptr + k0 + ak, av);
+      else av[0] = av[1] = av[2] = av[3] = 0.f;
+      if (w_ok) {
+        load4<TW>(w_ptr + k0 + wk, wv);
+        load4<TW>(w_ptr + k0 + wk + 16, wv + 4);
+      } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k = k0 + lk + e;
-      sA[lk + e][lr] = (a_ok && k < K) ? Elem<TA>::to_f(a_ptr[k]) : 0.f;
-      sW[lk + e][lr] = (w_ok && k < K) ? Elem<TW>::to_f(w_ptr[k]) : 0.f;
+        for (int e = 0; e < 8; ++e) wv[e] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = k0 + ak + e;
+        av[e] = (a_ok && k < k_end) ? Elem<TA>::to_f(a_ptr[k]) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + wk + (e & 3) + 16 * (e >> 2);
+        wv[e] = (w_ok && k < k_end) ? Elem<TW>::to_f(w_ptr[k]) : 0.f;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < BK; ++k) {
-      float a[4], w[4];
+    for (int e = 0; e < 4; ++e) sA[ak + e][ar] = av[e];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sA[k][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = sW[k][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
-    }
+    for (int e = 0; e < 8; ++e) sW[wk + (e & 3) + 16 * (e >> 2)][wr] = wv[e];
     __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SBK; ++k) {
+      const float a0 = sA[k][ty * 2], a1 = sA[k][ty * 2 + 1];
+      float w4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w4[j] = sW[k][tx * 4 + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[0][j] = fmaf(a0, w4[j], acc[0][j]);
+        acc[1][j] = fmaf(a1, w4[j], acc[1][j]);
+      }
+    }
   }
+
+  if (ksplit > 1) {
+    float* pb = part + ((size_t)b * ksplit + kz) * M * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + ty * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int row = m0 + ty * 2 + i;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + tx * 4 + j;
+        if (col < N) pb[(size_t)row * N + col] = acc[i][j];
+      }
+    }
+    return;
+  }
+  Cm += b * c_bs;
+  if (bias != nullptr) bias += b * bias_bs;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + ty * 2 + i;
     if (row >= M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -264,17 +340,55 @@ k_gemm_simt(const TA* __restrict__ A, long long lda, int a_rpg, long long a_gstr
   }
 }
 
+// out = act(sum_z part[b][z] + bias), the splits added in order
+template <typename TC, int ACT>
+__global__ void __launch_bounds__(256)
+k_splitk_reduce(const float* __restrict__ part, int ksplit, int M, int N,
+                const float* __restrict__ bias, long long bias_bs, TC* __restrict__ Cm,
+                long long ldc, long long c_bs) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= (long long)M * N) return;
+  const int row = (int)(i / N), col = (int)(i % N);
+  const float* pb = part + (size_t)b * ksplit * M * N + i;
+  float x = 0.f;
+  for (int z = 0; z < ksplit; ++z) x += pb[(size_t)z * M * N];
+  if (bias != nullptr) x += bias[b * bias_bs + col];
+  if (ACT == ACT_GELU) x = gelu_erf(x);
+  Cm[b * c_bs + (long long)row * ldc + col] = Elem<TC>::from_f(x);
+}
+
 template <typename TA, typename TW, typename TC>
 static hipError_t launch_simt_t(const GemmArgs& g, hipStream_t s) {
-  dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64)), block(256);
+  const int batch = g.batch > 0 ? g.batch : 1;
+  const int ks = g.ksplit > 0 ? g.ksplit : 1;
+  if (ks > 1 && g.part == nullptr) return hipErrorInvalidValue;
+  // 16-byte-aligned rows and operands allow vector loads of 4 elements
+  auto al = [](const void* p, long long ld, long long bs, int es) {
+    return ((uintptr_t)p % 16 == 0) && (ld * es) % 16 == 0 && (bs * es) % 16 == 0;
+  };
+  const int vec = g.a_rpg == 0 && al(g.A, g.lda, g.a_bs, sizeof(TA)) &&
+                  al(g.W, g.ldw, g.w_bs, sizeof(TW)) && ((uintptr_t)g.W % 8 == 0);
+  dim3 grid((unsigned)((g.N + SBN - 1) / SBN), (unsigned)((g.M + SBM - 1) / SBM),
+            (unsigned)(batch * ks));
+  dim3 block(256);
+#define IVC_SIMT(ACTV)                                                                            \
+  hipLaunchKernelGGL((k_gemm_simt<TA, TW, TC, ACTV>), grid, block, 0, s, (const TA*)g.A, g.lda,  \
+                     g.a_rpg, g.a_gstride, g.a_goff, (const TW*)g.W, g.ldw, g.bias, (TC*)g.Cm,   \
+                     g.ldc, g.M, g.N, g.K, g.a_bs, g.w_bs, g.c_bs, g.bias_bs, ks, vec, g.part)
+  if (g.act == ACT_GELU && ks == 1) IVC_SIMT(ACT_GELU);
+  else IVC_SIMT(ACT_NONE);
+#undef IVC_SIMT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  const long long n = (long long)g.M * g.N;
+  dim3 rg((unsigned)((n + 255) / 256), (unsigned)batch);
   if (g.act == ACT_GELU)
-    hipLaunchKernelGGL((k_gemm_simt<TA, TW, TC, ACT_GELU>), grid, block, 0, s, (const TA*)g.A,
-                       g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const TW*)g.W, g.ldw, g.bias,
-                       (TC*)g.Cm, g.ldc, g.M, g.N, g.K);
+    hipLaunchKernelGGL((k_splitk_reduce<TC, ACT_GELU>), rg, dim3(256), 0, s, (const float*)g.part,
+                       ks, g.M, g.N, g.bias, g.bias_bs, (TC*)g.Cm, g.ldc, g.c_bs);
   else
-    hipLaunchKernelGGL((k_gemm_simt<TA, TW, TC, ACT_NONE>), grid, block, 0, s, (const TA*)g.A,
-                       g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const TW*)g.W, g.ldw, g.bias,
-                       (TC*)g.Cm, g.ldc, g.M, g.N, g.K);
+    hipLaunchKernelGGL((k_splitk_reduce<TC, ACT_NONE>), rg, dim3(256), 0, s, (const float*)g.part,
+                       ks, g.M, g.N, g.bias, g.bias_bs, (TC*)g.Cm, g.ldc, g.c_bs);
   return hipGetLastError();
 }
 

@@ -43,6 +43,14 @@ struct GemmArgs {
   int M, N, K;
   int act;
   int a_dtype, w_dtype, c_dtype;
+  // batched products (SIMT kernel): grid.z runs over `batch` independent
+  // problems whose operands start b * (a_bs, w_bs, c_bs, bias_bs) elements in
+  int batch;
+  long long a_bs, w_bs, c_bs, bias_bs;
+  // split-K (SIMT kernel): partial sums of the `ksplit` K ranges go to `part`
+  // ([batch][ksplit][M][N] fp32) and a second kernel adds them in order
+  int ksplit;
+  float* part;
 };
 // bf16 A and W, fp32 accumulation on MFMA, bf16 out.  Needs K % 64 == 0.
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
@@ -50,6 +58,10 @@ bool gemm_mfma_supported(const GemmArgs& g);
 // Any element types, fp32 FMA.  Used for fp32 workloads and fp32-activation
 // router products.
 hipError_t launch_gemm_simt(const GemmArgs& g, hipStream_t s);
+// split-K factor and workspace the SIMT kernel wants for a product
+int simt_ksplit(int M, int N, int K, int batch);
+size_t simt_part_elems(int M, int N, int batch, int ksplit);
+int simt_tiles(int M, int N);
 
 // ---- CrossAttentionPooling ---------------------------------------------------
 struct PoolAttnArgs {
