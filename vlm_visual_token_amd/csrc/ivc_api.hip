@@ -245,7 +245,12 @@ struct SimtScratch {
 // (split over K when the product is skinny and scratch is available).
 hipError_t gemm(const char*, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
   if (g.batch <= 0) g.batch = 1;
-  if (g.batch == 1 && gemm_mfma_supported(g)) return launch_gemm_mfma(g, s);
+  if (g.batch == 1 && gemm_mfma_supported(g)) {
+    // 256 x 256 LDS-DMA tiles when they fill the chip, else 128 x 128 tiles
+    const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    if (big_tiles >= 256 && gemm_dma_supported(g)) return launch_gemm_dma(g, s);
+    return launch_gemm_mfma(g, s);
+  }
   g.ksplit = 1;
   if (sc != nullptr && sc->part != nullptr) {
     const int ks = simt_ksplit(g.M, g.N, g.K, g.batch);

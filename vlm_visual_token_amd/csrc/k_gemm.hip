@@ -188,10 +188,7 @@ bool gemm_mfma_supported(const GemmArgs& g) {
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s) {
   if (!gemm_mfma_supported(g)) return hipErrorInvalidValue;
-  // Large products take 256x256 tiles; smaller ones 128x128 so that the
-  // grid still covers the 256 CUs.
-  const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-  if (big_tiles >= 256) return launch_mfma_cfg<256, 256, 2, 2>(g, s);
+  // 128 x 128 tiles (large products go to the LDS-DMA kernel instead)
   return launch_mfma_cfg<128, 128, 2, 2>(g, s);
 }
 

@@ -55,6 +55,9 @@ struct GemmArgs {
 // bf16 A and W, fp32 accumulation on MFMA, bf16 out.  Needs K % 64 == 0.
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
 bool gemm_mfma_supported(const GemmArgs& g);
+// Same product with 256 x 256 tiles fed by LDS DMA (large products).
+hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s);
+bool gemm_dma_supported(const GemmArgs& g);
 // Any element types, fp32 FMA.  Used for fp32 workloads and fp32-activation
 // router products.
 hipError_t launch_gemm_simt(const GemmArgs& g, hipStream_t s);
