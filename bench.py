@@ -56,6 +56,7 @@ def hbm_bytes(cfg: dict, L_seq: int, Lp: int) -> dict:
     return {
         "shuffle_ln": x_read + T * cfg["S"] * 4 * C * e + T * cfg["S64"] * 16 * C * e,
         "pool_attn": T * N * 2 * C * e,  # one layer's K and V
+        "pool_folded": T * N * C * e,  # one layer's pass over the tokens
         "compact": 2 * Lp * D * e + L_seq * 4 * 2 + Lp * 4 * 2,
     }
 
@@ -102,7 +103,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--pool-mode", type=int, default=0)
+    ap.add_argument("--pool-mode", type=int, default=1,
+                    help="0: K/V projection + attention, 1: folded pooling (same mathematics)")
+    ap.add_argument("--run-mode", choices=["routed", "both"], default="routed",
+                    help="routed: decide first, then run only each tile's chosen projector; "
+                         "both: run mlp1 and mlp2 on every tile, as the pages do")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tiles", type=int, default=32)
     ap.add_argument("--kernel-events", choices=["timed", "separate"], default="timed")
@@ -145,8 +150,11 @@ def main():
     def step():
         nonlocal rbuf, cbuf
         ivc.ivc_tile_offsets(tiles_d, len(cfg["tiles"]), off_d, st_d, stream)
-        con.run(x, o256, o64, stream=stream)
         rbuf = con.route(x, with_pooled=False, stream=stream, out=rbuf)
+        if args.run_mode == "routed":
+            con.run_routed(x, rbuf["use64"], o256, o64, stream=stream)
+        else:
+            con.run(x, o256, o64, stream=stream)
         cbuf = con.compact(ids_d, emb_d, rbuf["use64"], o256, o64, synth.IMG_CONTEXT,
                            stream=stream, out=cbuf)
 
@@ -186,6 +194,17 @@ def main():
     # roofline of the dominant kernel (largest share of the step's kernel time)
     flops = gemm_flops(cfg)
     hbm = hbm_bytes(cfg, L, Lp)
+    if args.run_mode == "routed":
+        # each projector runs on its own path's tiles only
+        n64 = int(use64.sum())
+        for k in ("mlp1_gemm1", "mlp1_gemm2"):
+            flops[k] *= (T - n64) / T
+        for k in ("mlp2_gemm1", "mlp2_gemm2", "mlp2_gemm3"):
+            flops[k] *= n64 / T
+        # the loader writes only the chosen path's rows
+        e, C = 2, cfg["C"]
+        hbm["shuffle_ln"] = (T * cfg["N"] * C * e + (T - n64) * cfg["S"] * 4 * C * e
+                             + n64 * cfg["S64"] * 16 * C * e)
     kern = {k: {"ms_avg": v[0] / v[1], "launches_per_step": v[1] / args.steps,
                 "ms_per_step": v[0] / args.steps} for k, v in prof.items()}
     dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
@@ -225,6 +244,7 @@ def main():
         "config": {"workload": WORKLOAD, "tiles": T, "images": len(cfg["tiles"]),
                    "vit_tokens_per_tile": cfg["N"], "vit_width": cfg["C"], "llm_width": cfg["D"],
                    "seq_len": L, "pool_mode": "kv" if args.pool_mode == 0 else "folded",
+                   "run_mode": args.run_mode,
                    "parallelism": "single GPU"},
         "visual_tokens_per_s": emitted / (ms_step / 1e3),
         "input_vit_tokens_per_s": T * cfg["N"] / (ms_step / 1e3),

@@ -159,6 +159,20 @@ size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t max_tiles,
 ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32_t T, void* out256,
                              void* out64, void* ws, size_t ws_bytes, void* stream);
 
+/* Route-first form of ivc_connector_run (flash = 1): with the decision use64
+ * [T] (device, from ivc_connector_route) already known, computes out256 only
+ * for tiles with use64[t] = 0 and out64 only for tiles with use64[t] = 1;
+ * rows of the other path are left untouched.  ivc_connector_compact reads
+ * exactly those rows, so the compacted sequence is the same as after
+ * ivc_connector_run, for about half of the projector work.  The pages
+ * compute both paths for every tile because the quantile needs the whole
+ * batch ([4B-Flash] section 5); deciding first removes that need.  The
+ * kernels size their grids for all T tiles and read the per-path tile counts
+ * from the device, so the call does not synchronise.  Same workspace as run. */
+ivc_status ivc_connector_run_routed(ivc_connector* h, const void* vit, int32_t T,
+                                    const uint8_t* use64, void* out256, void* out64, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* Visual Resolution Router ([4B-Flash] sections 2-4; [2B-Flash] routing
  * decision).  Requires flash = 1.
  *   vit          [T, has_cls + P*P, C] as for run

@@ -322,6 +322,65 @@ def test_folded_pool_flash_workload():
 
 
 # ---------------------------------------------------------------------------
+# route-first run: only the chosen path per tile
+# ---------------------------------------------------------------------------
+def _check_routed(con, cfg, xd, use_d):
+    use = use_d.cpu().numpy()
+    f256, f64 = con.run(xd)
+    r256 = torch.full_like(f256, float("nan"))
+    r64 = torch.full_like(f64, float("nan"))
+    con.run_routed(xd, use_d, r256, r64)
+    torch.cuda.synchronize()
+    keep256 = torch.from_numpy(use == 0).cuda()
+    keep64 = torch.from_numpy(use != 0).cuda()
+    # chosen path: bit-identical to the full run (same K order per output element)
+    assert torch.equal(r256[keep256], f256[keep256])
+    assert torch.equal(r64[keep64], f64[keep64])
+    # other path: untouched
+    assert torch.isnan(r256[~keep256].float()).all()
+    assert torch.isnan(r64[~keep64].float()).all()
+    return f256, f64, r256, r64
+
+
+@pytest.mark.parametrize("pattern", ["route", "none", "all", "alternate"])
+def test_run_routed_tiny(pattern):
+    cfg, w, x = _tiny_all()
+    say(f"run_routed tiny pattern={pattern}")
+    con = _connector(cfg, w, cfg["T"])
+    xd = torch.from_numpy(x).cuda()
+    if pattern == "route":
+        use_d = con.route(xd)["use64"]
+    else:
+        use = {"none": np.zeros(cfg["T"]), "all": np.ones(cfg["T"]),
+               "alternate": np.arange(cfg["T"]) % 2}[pattern].astype(np.uint8)
+        use_d = torch.from_numpy(use).cuda()
+    _check_routed(con, cfg, xd, use_d)
+
+
+def test_run_routed_flash_workload_and_compaction():
+    cfg = workload("internvl35_2b_flash", pool_mode=1)
+    say(f"2B-Flash run_routed: T={cfg['T']}")
+    w = host_weights(cfg)
+    ids, emb = synth.make_sequence(cfg)
+    con = _connector(cfg, w, cfg["T"], len(ids))
+    xd = dev_vit(cfg)
+    r = con.route(xd)
+    f256, f64, r256, r64 = _check_routed(con, cfg, xd, r["use64"])
+    ids_d = torch.from_numpy(ids).cuda()
+    emb_d = torch.from_numpy(emb).to(torch.bfloat16).cuda()
+    cf = con.compact(ids_d, emb_d, r["use64"], f256, f64, synth.IMG_CONTEXT)
+    cf = {k: v.clone() for k, v in cf.items()}
+    cr = con.compact(ids_d, emb_d, r["use64"], r256, r64, synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    n = int(cf["len"].item())
+    assert n == int(cr["len"].item())
+    for k in ("ids", "pos", "keep_map"):
+        assert torch.equal(cf[k], cr[k]), k
+    assert torch.equal(cf["embeds"][:n], cr["embeds"][:n])
+    assert not torch.isnan(cr["embeds"][:n].float()).any()
+
+
+# ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
 def test_edge_cases():

@@ -47,6 +47,18 @@ class Connector:
         ivc.ivc_connector_run(self.h, vit, T, out256, out64, self.ws, self.ws_bytes, stream)
         return out256, out64
 
+    def run_routed(self, vit: torch.Tensor, use64: torch.Tensor, out256=None, out64=None,
+                   stream=None):
+        T = vit.shape[0]
+        D = self.cfg["D"]
+        if out256 is None:
+            out256 = torch.empty((T, self.S, D), dtype=self.dtype, device=self.device)
+        if out64 is None:
+            out64 = torch.empty((T, self.S64, D), dtype=self.dtype, device=self.device)
+        ivc.ivc_connector_run_routed(self.h, vit, T, use64, out256, out64, self.ws, self.ws_bytes,
+                                     stream)
+        return out256, out64
+
     def route(self, vit: torch.Tensor, valid=None, with_pooled=True, stream=None, out=None):
         T = vit.shape[0]
         if out is None:

@@ -294,6 +294,7 @@ int pool_splits(int T, int N) {
 // ---- workspace plans ----
 struct RunWs {
   void *a2, *a4, *h1, *g1, *g2;
+  int *rank, *list256, *list64, *counts;  // route-first run only
   SimtScratch sc;
 };
 size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
@@ -308,6 +309,10 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
     r.a4 = cv.take((size_t)T * S4 * 16 * c.vit_width * e);
     r.g1 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
     r.g2 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
+    r.rank = (int*)cv.take((size_t)T * 4);
+    r.list256 = (int*)cv.take((size_t)T * 4);
+    r.list64 = (int*)cv.take((size_t)T * 4);
+    r.counts = (int*)cv.take(2 * 4);
   }
   if (c.dtype == IVC_F32) {  // bf16 products all run on MFMA
     const int M2 = (int)(T * S), M4 = (int)(T * S4);
@@ -550,9 +555,8 @@ extern "C" size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t 
 // ---------------------------------------------------------------------------
 // run
 // ---------------------------------------------------------------------------
-extern "C" ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32_t T,
-                                        void* out256, void* out64, void* ws, size_t ws_bytes,
-                                        void* stream) {
+static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const uint8_t* use64,
+                           void* out256, void* out64, void* ws, size_t ws_bytes, void* stream) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
@@ -572,6 +576,23 @@ extern "C" ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32
   hipStream_t s = (hipStream_t)stream;
   const int dt = c.dtype;
   const int C = c.vit_width, D = c.llm_width, H1 = c.mlp1_hidden, H2 = c.mlp2_hidden;
+  const int S4 = (c.grid / 4) * (c.grid / 4);
+
+  // route-first: per-path tile ranks and lists from the decision
+  RowMap rm256, rm64, rmh256, rmh64;
+  if (use64 != nullptr) {
+    LAUNCH("route_lists", s, launch_route_lists(use64, T, w.rank, w.list256, w.list64, w.counts, s));
+    rmh256.m_dev = w.counts;      // hidden rows of mlp1: n256 * S
+    rmh256.m_mult = (int)S;
+    rm256 = rmh256;               // final rows scatter back to the tile's slots
+    rm256.c_map = w.list256;
+    rm256.c_rpg = (int)S;
+    rmh64.m_dev = w.counts + 1;
+    rmh64.m_mult = S4;
+    rm64 = rmh64;
+    rm64.c_map = w.list64;
+    rm64.c_rpg = S4;
+  }
 
   ShuffleArgs sa{};
   sa.dtype = dt;
@@ -589,28 +610,48 @@ extern "C" ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32
   sa.b4 = h->m2_ln_b;
   sa.out4 = w.a4;
   sa.eps = c.ln_eps;
+  if (use64 != nullptr) {
+    sa.use64 = use64;
+    sa.rank = w.rank;
+  }
   LAUNCH("shuffle_ln", s, launch_shuffle_ln(sa, s));
 
   const int M2 = (int)(T * S);
-  LAUNCH("mlp1_gemm1", s, gemm("mlp1_gemm1",
-                              mk_gemm(w.a2, 4 * C, dt, h->m1_w1, dt, h->m1_b1, w.h1, dt, M2, H1,
-                                      4 * C, ACT_GELU), s, &w.sc));
-  LAUNCH("mlp1_gemm2", s, gemm("mlp1_gemm2",
-                              mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D,
-                                      H1, ACT_NONE), s, &w.sc));
+  GemmArgs g;
+  g = mk_gemm(w.a2, 4 * C, dt, h->m1_w1, dt, h->m1_b1, w.h1, dt, M2, H1, 4 * C, ACT_GELU);
+  g.rm = rmh256;
+  LAUNCH("mlp1_gemm1", s, gemm("mlp1_gemm1", g, s, &w.sc));
+  g = mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D, H1, ACT_NONE);
+  g.rm = rm256;
+  LAUNCH("mlp1_gemm2", s, gemm("mlp1_gemm2", g, s, &w.sc));
   if (c.flash) {
-    const int M4 = T * (c.grid / 4) * (c.grid / 4);
-    LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1",
-                                mk_gemm(w.a4, 16 * C, dt, h->m2_w1, dt, h->m2_b1, w.g1, dt, M4,
-                                        H2, 16 * C, ACT_GELU), s, &w.sc));
-    LAUNCH("mlp2_gemm2", s, gemm("mlp2_gemm2",
-                                mk_gemm(w.g1, H2, dt, h->m2_w2, dt, h->m2_b2, w.g2, dt, M4, H2,
-                                        H2, ACT_GELU), s, &w.sc));
-    LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3",
-                                mk_gemm(w.g2, H2, dt, h->m2_w3, dt, h->m2_b3, out64, dt, M4, D,
-                                        H2, ACT_NONE), s, &w.sc));
+    const int M4 = T * S4;
+    g = mk_gemm(w.a4, 16 * C, dt, h->m2_w1, dt, h->m2_b1, w.g1, dt, M4, H2, 16 * C, ACT_GELU);
+    g.rm = rmh64;
+    LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1", g, s, &w.sc));
+    g = mk_gemm(w.g1, H2, dt, h->m2_w2, dt, h->m2_b2, w.g2, dt, M4, H2, H2, ACT_GELU);
+    g.rm = rmh64;
+    LAUNCH("mlp2_gemm2", s, gemm("mlp2_gemm2", g, s, &w.sc));
+    g = mk_gemm(w.g2, H2, dt, h->m2_w3, dt, h->m2_b3, out64, dt, M4, D, H2, ACT_NONE);
+    g.rm = rm64;
+    LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3", g, s, &w.sc));
   }
   return IVC_OK;
+}
+
+extern "C" ivc_status ivc_connector_run(ivc_connector* h, const void* vit, int32_t T,
+                                        void* out256, void* out64, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  return run_impl(h, vit, T, nullptr, out256, out64, ws, ws_bytes, stream);
+}
+
+extern "C" ivc_status ivc_connector_run_routed(ivc_connector* h, const void* vit, int32_t T,
+                                               const uint8_t* use64, void* out256, void* out64,
+                                               void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "route-first run needs a flash connector");
+  if (T > 0 && !use64) return fail(IVC_ERR_INVALID_ARG, "null use64");
+  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

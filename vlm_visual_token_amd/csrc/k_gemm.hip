@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1)
 k_gemm_mfma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
             int a_goff, const bf16_t* __restrict__ W, long long ldw,
             const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-            int K) {
+            int K, RowMap rm) {
   constexpr int NT = WM * WN * 64;
   constexpr int BK = 64;
   constexpr int LDK = BK + 8;
@@ -48,8 +48,13 @@ k_gemm_mfma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDK];
 
+  // rows actually present (route-first products size the grid for all
+  // tiles): the tile grid is laid out over those rows only, so the active
+  // workgroups stay spread over all XCDs; the rest leave at once
+  if (rm.m_dev != nullptr) M = min(M, *rm.m_dev * rm.m_mult);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int nb = tiles_m * tiles_n;
+  if ((int)blockIdx.x >= nb) return;  // uniform over the workgroup, before any barrier
   int bid = blockIdx.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   constexpr int GM = 8;
@@ -159,7 +164,10 @@ k_gemm_mfma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
         if (col_ok && row < M) {
           float x = acc[i][j][v] + bj;
           if (ACT == ACT_GELU) x = gelu_erf(x);
-          Cm[(long long)row * ldc + col] = f32_to_bf16(x);
+          const long long orow =
+              rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg
+                                  : row;
+          Cm[orow * ldc + col] = f32_to_bf16(x);
         }
       }
     }
@@ -173,11 +181,13 @@ static hipError_t launch_mfma_cfg(const GemmArgs& g, hipStream_t s) {
   if (g.act == ACT_GELU)
     hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, ACT_GELU>), grid, block, 0, s,
                        (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
-                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K);
+                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K,
+                       g.rm);
   else
     hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, ACT_NONE>), grid, block, 0, s,
                        (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
-                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K);
+                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K,
+                       g.rm);
   return hipGetLastError();
 }
 
@@ -233,13 +243,16 @@ k_gemm_simt(const TA* __restrict__ A, long long lda, int a_rpg, long long a_gstr
             const TW* __restrict__ W, long long ldw, const float* __restrict__ bias,
             TC* __restrict__ Cm, long long ldc, int M, int N, int K, long long a_bs,
             long long w_bs, long long c_bs, long long bias_bs, int ksplit, int vec,
-            float* __restrict__ part) {
+            float* __restrict__ part, RowMap rm) {
   __shared__ float sA[SBK][SBM + 1];
   __shared__ float sW[SBK][SBN + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int m0 = blockIdx.y * SBM, n0 = blockIdx.x * SBN;
   const int b = blockIdx.z / ksplit, kz = blockIdx.z % ksplit;
+  const int Mfull = M;  // the split-K partial buffers are laid out for all rows
+  if (rm.m_dev != nullptr) M = min(M, *rm.m_dev * rm.m_mult);
+  if (m0 >= M) return;  // uniform over the workgroup, before any barrier
   A += b * a_bs;
   W += b * w_bs;
 
@@ -307,7 +320,7 @@ k_gemm_simt(const TA* __restrict__ A, long long lda, int a_rpg, long long a_gstr
   }
 
   if (ksplit > 1) {
-    float* pb = part + ((size_t)b * ksplit + kz) * M * N;
+    float* pb = part + ((size_t)b * ksplit + kz) * Mfull * N;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = m0 + ty * 2 + i;
@@ -332,7 +345,9 @@ k_gemm_simt(const TA* __restrict__ A, long long lda, int a_rpg, long long a_gstr
       if (col >= N) continue;
       float x = acc[i][j] + (bias != nullptr ? bias[col] : 0.f);
       if (ACT == ACT_GELU) x = gelu_erf(x);
-      Cm[(long long)row * ldc + col] = Elem<TC>::from_f(x);
+      const long long orow =
+          rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg : row;
+      Cm[orow * ldc + col] = Elem<TC>::from_f(x);
     }
   }
 }
@@ -342,17 +357,20 @@ template <typename TC, int ACT>
 __global__ void __launch_bounds__(256)
 k_splitk_reduce(const float* __restrict__ part, int ksplit, int M, int N,
                 const float* __restrict__ bias, long long bias_bs, TC* __restrict__ Cm,
-                long long ldc, long long c_bs) {
+                long long ldc, long long c_bs, RowMap rm) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   const int b = blockIdx.y;
-  if (i >= (long long)M * N) return;
+  const int Mact = rm.m_dev != nullptr ? min(M, *rm.m_dev * rm.m_mult) : M;
+  if (i >= (long long)Mact * N) return;
   const int row = (int)(i / N), col = (int)(i % N);
   const float* pb = part + (size_t)b * ksplit * M * N + i;
   float x = 0.f;
   for (int z = 0; z < ksplit; ++z) x += pb[(size_t)z * M * N];
   if (bias != nullptr) x += bias[b * bias_bs + col];
   if (ACT == ACT_GELU) x = gelu_erf(x);
-  Cm[b * c_bs + (long long)row * ldc + col] = Elem<TC>::from_f(x);
+  const long long orow =
+      rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg : row;
+  Cm[b * c_bs + orow * ldc + col] = Elem<TC>::from_f(x);
 }
 
 template <typename TA, typename TW, typename TC>
@@ -372,7 +390,7 @@ static hipError_t launch_simt_t(const GemmArgs& g, hipStream_t s) {
 #define IVC_SIMT(ACTV)                                                                            \
   hipLaunchKernelGGL((k_gemm_simt<TA, TW, TC, ACTV>), grid, block, 0, s, (const TA*)g.A, g.lda,  \
                      g.a_rpg, g.a_gstride, g.a_goff, (const TW*)g.W, g.ldw, g.bias, (TC*)g.Cm,   \
-                     g.ldc, g.M, g.N, g.K, g.a_bs, g.w_bs, g.c_bs, g.bias_bs, ks, vec, g.part)
+                     g.ldc, g.M, g.N, g.K, g.a_bs, g.w_bs, g.c_bs, g.bias_bs, ks, vec, g.part, g.rm)
   if (g.act == ACT_GELU && ks == 1) IVC_SIMT(ACT_GELU);
   else IVC_SIMT(ACT_NONE);
 #undef IVC_SIMT
@@ -382,10 +400,10 @@ static hipError_t launch_simt_t(const GemmArgs& g, hipStream_t s) {
   dim3 rg((unsigned)((n + 255) / 256), (unsigned)batch);
   if (g.act == ACT_GELU)
     hipLaunchKernelGGL((k_splitk_reduce<TC, ACT_GELU>), rg, dim3(256), 0, s, (const float*)g.part,
-                       ks, g.M, g.N, g.bias, g.bias_bs, (TC*)g.Cm, g.ldc, g.c_bs);
+                       ks, g.M, g.N, g.bias, g.bias_bs, (TC*)g.Cm, g.ldc, g.c_bs, g.rm);
   else
     hipLaunchKernelGGL((k_splitk_reduce<TC, ACT_NONE>), rg, dim3(256), 0, s, (const float*)g.part,
-                       ks, g.M, g.N, g.bias, g.bias_bs, (TC*)g.Cm, g.ldc, g.c_bs);
+                       ks, g.M, g.N, g.bias, g.bias_bs, (TC*)g.Cm, g.ldc, g.c_bs, g.rm);
   return hipGetLastError();
 }
 

@@ -86,14 +86,19 @@ __global__ void __launch_bounds__(DNT, 1)
 k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
            int a_goff, const bf16_t* __restrict__ W, long long ldw,
            const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-           int K) {
+           int K, RowMap rm) {
   __shared__ __attribute__((aligned(1024))) bf16_t sA0[TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16_t sB0[TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16_t sA1[TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16_t sB1[TILE_ELEMS];
 
+  // rows actually present (route-first products size the grid for all
+  // tiles): the tile grid is laid out over those rows only, so the active
+  // workgroups stay spread over all XCDs; the rest leave at once
+  if (rm.m_dev != nullptr) M = min(M, *rm.m_dev * rm.m_mult);
   const int tiles_m = (M + DBM - 1) / DBM, tiles_n = (N + DBN - 1) / DBN;
   const int nb = tiles_m * tiles_n;
+  if ((int)blockIdx.x >= nb) return;  // uniform over the workgroup, before any barrier
   int bid = blockIdx.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);  // consecutive ids on one XCD
   constexpr int GM = 8;
@@ -194,7 +199,10 @@ k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_g
         if (col_ok && row < M) {
           float x = acc[i][j][v] + bj;
           if (ACT == ACT_GELU) x = gelu_erf(x);
-          Cm[(long long)row * ldc + col] = f32_to_bf16(x);
+          const long long orow =
+              rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg
+                                  : row;
+          Cm[orow * ldc + col] = f32_to_bf16(x);
         }
       }
     }
@@ -213,11 +221,11 @@ hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
   if (g.act == ACT_GELU)
     hipLaunchKernelGGL(k_gemm_dma<ACT_GELU>, dim3((unsigned)tiles), dim3(DNT), 0, s,
                        (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
-                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K);
+                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm);
   else
     hipLaunchKernelGGL(k_gemm_dma<ACT_NONE>, dim3((unsigned)tiles), dim3(DNT), 0, s,
                        (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
-                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K);
+                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm);
   return hipGetLastError();
 }
 

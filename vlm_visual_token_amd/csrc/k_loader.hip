@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(256)
 k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
              const float* __restrict__ g2, const float* __restrict__ b2, E* __restrict__ out2,
              const float* __restrict__ g4, const float* __restrict__ b4, E* __restrict__ out4,
-             float eps) {
+             float eps, const uint8_t* __restrict__ use64, const int* __restrict__ rank) {
   constexpr int V = Elem<E>::kPerVec;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -129,9 +129,19 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
     }
   }
 
+  // route-first: only the tile's chosen path is written, at its rank in that path
+  bool want2 = out2 != nullptr, want4 = out4 != nullptr;
+  int t2 = t, t4 = t;
+  if (use64 != nullptr) {
+    const bool to64 = use64[t] != 0;
+    want2 = want2 && !to64;
+    want4 = want4 && to64;
+    t2 = t4 = rank[t];
+  }
+
   // ---- r = 2 row: channel block q holds cell q
-  if (out2 != nullptr) {
-    E* dst = out2 + ((size_t)t * S2 + a2 * Q2 + b2i) * (size_t)(4 * C);
+  if (want2) {
+    E* dst = out2 + ((size_t)t2 * S2 + a2 * Q2 + b2i) * (size_t)(4 * C);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -154,9 +164,9 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
 
   // ---- r = 4 row: this wave's cell (m, k) sits at (2*(w>>1) + m, 2*(w&1) + k)
   //      inside the 4x4 block, channel block 4*m4 + k4.
-  if (FLASH && out4 != nullptr) {
+  if (FLASH && want4) {
     const int Q4 = P >> 2, S4 = Q4 * Q4;
-    E* dst = out4 + ((size_t)t * S4 + a4 * Q4 + b4i) * (size_t)(16 * C);
+    E* dst = out4 + ((size_t)t4 * S4 + a4 * Q4 + b4i) * (size_t)(16 * C);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m4 = 2 * (w >> 1) + (q >> 1), k4 = 2 * (w & 1) + (q & 1);
@@ -187,13 +197,14 @@ static hipError_t launch_cpl(const ShuffleArgs& a, hipStream_t s) {
   if (a.flash) {
     dim3 grid((unsigned)(a.T * Q4 * Q4));
     hipLaunchKernelGGL((k_shuffle_ln<E, CPL, true, LN>), grid, dim3(256), 0, s, (const E*)a.X, a.T,
-                       a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4, a.eps);
+                       a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4, a.eps,
+                       a.use64, a.rank);
   } else {
     const long long toks = (long long)a.T * Q2 * Q2;
     dim3 grid((unsigned)((toks + 3) / 4));
     hipLaunchKernelGGL((k_shuffle_ln<E, CPL, false, LN>), grid, dim3(256), 0, s, (const E*)a.X,
                        a.T, a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4,
-                       a.eps);
+                       a.eps, a.use64, a.rank);
   }
   return hipGetLastError();
 }

@@ -101,6 +101,59 @@ k_quantile_decide(const float* __restrict__ gate, int T, double q, double abs_th
   }
 }
 
+// Per-path tile lists of a decision (one workgroup, chunked scan over tiles).
+__global__ void __launch_bounds__(1024)
+k_route_lists(const uint8_t* __restrict__ use64, int T, int* __restrict__ rank,
+              int* __restrict__ list256, int* __restrict__ list64, int* __restrict__ counts) {
+  __shared__ int wsum[16];
+  __shared__ int carry_s;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) carry_s = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < T; c0 += QT) {
+    const int t = c0 + threadIdx.x;
+    const int u = t < T ? (use64[t] != 0) : 0;
+    int inc = u;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int k = 0; k < 16; ++k) {
+      if (k < w) before += wsum[k];
+      tot += wsum[k];
+    }
+    const int carry = carry_s;
+    if (t < T) {
+      const int r64 = carry + before + inc - u;  // routed tiles before t
+      if (u) {
+        rank[t] = r64;
+        list64[r64] = t;
+      } else {
+        rank[t] = t - r64;
+        list256[t - r64] = t;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry_s = carry + tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = T - carry_s;
+    counts[1] = carry_s;
+  }
+}
+
+hipError_t launch_route_lists(const uint8_t* use64, int T, int* rank, int* list256, int* list64,
+                              int* counts, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_lists, dim3(1), dim3(QT), 0, s, use64, T, rank, list256, list64,
+                     counts);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantile_decide(const float* gate, int T, double q, double abs_thr,
                                   double* thr, uint8_t* use64, hipStream_t s) {
   if (T == 0) return hipSuccess;

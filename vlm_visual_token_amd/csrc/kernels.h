@@ -21,9 +21,24 @@ struct ShuffleArgs {
   const float *g4, *b4;
   void* out4;
   float eps;
+  // route-first: tile t writes only its chosen path's rows, at position rank[t]
+  const uint8_t* use64 = nullptr;
+  const int* rank = nullptr;
 };
 hipError_t launch_shuffle_ln(const ShuffleArgs& a, hipStream_t s);
 int shuffle_max_width(int dtype);
+
+// ---- route-first products -----------------------------------------------------
+// Optional device-side row count and output-row scatter of a GEMM: the grid
+// is sized for the host M (an upper bound); the product covers
+// min(M, *m_dev * m_mult) rows, and output row m is written to row
+// c_map[m / c_rpg] * c_rpg + m % c_rpg.
+struct RowMap {
+  const int* m_dev = nullptr;
+  int m_mult = 1;
+  const int* c_map = nullptr;
+  int c_rpg = 1;
+};
 
 // ---- GEMM: C[M, N] = act(A[M, K] . W[N, K]^T + bias[N]) ---------------------
 // A rows may be remapped: logical row m reads physical row
@@ -51,6 +66,7 @@ struct GemmArgs {
   // ([batch][ksplit][M][N] fp32) and a second kernel adds them in order
   int ksplit;
   float* part;
+  RowMap rm;
 };
 // bf16 A and W, fp32 accumulation on MFMA, bf16 out.  Needs K % 64 == 0.
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
@@ -123,6 +139,11 @@ struct CompactArgs {
 };
 long long compact_blocks(long long L);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+// Per-path tile lists of a routing decision: rank[t] = index of t among the
+// tiles of its path, list256 / list64 = tile ids in order, counts = {n256, n64}.
+hipError_t launch_route_lists(const uint8_t* use64, int T, int* rank, int* list256, int* list64,
+                              int* counts, hipStream_t s);
 
 hipError_t launch_tile_offsets(const int32_t* tiles, int B, int32_t* offsets, int32_t* status,
                                hipStream_t s);

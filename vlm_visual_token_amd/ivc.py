@@ -79,6 +79,7 @@ def load() -> ctypes.CDLL:
         "ivc_connector_destroy": (None, [P]),
         "ivc_connector_workspace_bytes": (c_size_t, [P, c_int32, c_int64]),
         "ivc_connector_run": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
+        "ivc_connector_run_routed": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P]),
         "ivc_connector_route": (c_int32, [P, P, P, c_int32, P, P, P, P, P, P, c_size_t, P]),
         "ivc_connector_compact": (c_int32, [P, P, P, c_int64, c_int32, P, P, P, c_int32, P, P, P,
                                             P, P, P, P, c_size_t, P]),
@@ -102,7 +103,7 @@ def load() -> ctypes.CDLL:
 def exported_symbols() -> list[str]:
     return [
         "ivc_connector_create", "ivc_connector_destroy", "ivc_connector_workspace_bytes",
-        "ivc_connector_run", "ivc_connector_route", "ivc_connector_compact", "ivc_route_decide",
+        "ivc_connector_run", "ivc_connector_run_routed", "ivc_connector_route", "ivc_connector_compact", "ivc_route_decide",
         "ivc_tile_offsets",
         "ivc_pixel_shuffle", "ivc_profile_enable", "ivc_profile_reset", "ivc_profile_read",
         "ivc_status_string", "ivc_last_error",
@@ -205,6 +206,12 @@ def ivc_connector_workspace_bytes(h: int, max_tiles: int, max_seq_len: int) -> i
 def ivc_connector_run(h, vit, T, out256, out64, ws, ws_bytes, stream=None) -> None:
     _check(load().ivc_connector_run(h, _ptr(vit), T, _ptr(out256), _ptr(out64), _ptr(ws),
                                     ws_bytes, _stream(stream)), "ivc_connector_run")
+
+
+def ivc_connector_run_routed(h, vit, T, use64, out256, out64, ws, ws_bytes, stream=None) -> None:
+    _check(load().ivc_connector_run_routed(h, _ptr(vit), T, _ptr(use64), _ptr(out256), _ptr(out64),
+                                           _ptr(ws), ws_bytes, _stream(stream)),
+           "ivc_connector_run_routed")
 
 
 def ivc_connector_route(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status, ws,
