@@ -13,16 +13,15 @@
 // (Wv xbar).  No K/V tensor is formed.
 //
 // Token pass (k_pool_folded): a workgroup takes a token range of one tile,
-// 16 tokens at a time.  Scores: the 4 waves each own C/4 channels and compute
-// partial [16 tokens x 16 heads] scores with v_mfma_f32_16x16x32_bf16, the
-// token rows as the A operand straight from HBM (8 consecutive channels per
-// lane = one 16-byte load) and q~ as the B operand, split into a bf16 high
-// part and a bf16 low part so the product keeps ~fp32 accuracy.  Partial
-// scores meet in LDS; every wave then runs the same online-softmax update.
-// The weighted sum is fp32 FMA from the token chunk staged in LDS: a lane
-// owns C/256 channels of its wave's slice and all 16 heads.  The pass is
-// bound by the HBM read of the tokens; the next chunk's loads are issued
-// before the current chunk is consumed.
+// 32 tokens at a time, 8 waves each owning C/8 channels.  Both products run
+// on v_mfma_f32_16x16x32_bf16: the scores with the token rows as the A
+// operand and q~ as B, split into a bf16 high and low part so the product
+// keeps ~fp32 accuracy; the weighted sum with the softmax weights (also split
+// hi + lo) as A and the token chunk, staged in LDS and read transposed, as B.
+// Partial scores of the 8 waves meet in LDS; every wave runs the same
+// online-softmax update (fp32).  An fp32 FMA weighted sum would make the pass
+// VALU-bound (wave64 fp32 FMA takes 4 cycles per instruction); on MFMA it is
+// bound by the HBM read of the tokens.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,19 +40,42 @@ bool pool_folded_supported(int dtype, int C, int H) {
 }
 
 // part layout per (tile, split): [FH] running max, [FH] running sum, [FH][C] weighted sums
+//
+// 8 waves per workgroup, wave w owning channels [w*C/8, (w+1)*C/8); chunks of
+// FT2 = 32 tokens.  Per chunk:
+//   load     the 32 token rows, row-contiguously (1 KB per wave instruction),
+//            into LDS; the next chunk's rows are loaded meanwhile;
+//   scores   S[token][head] (two 16-token tiles) with the token rows (from
+//            LDS) as the MFMA A operand and q~ (hi + lo) as B;
+//   softmax  a lane (head h = lane % 16, token group g = lane / 16) takes
+//            tokens 8g .. 8g+7 of head h: exactly the A-operand layout of the
+//            next product, so P (split into bf16 hi + lo) stays in registers;
+//   sum      xbar[h][c] += P[h][tokens] . X[tokens][c] on MFMA, the token
+//            chunk staged in LDS and read transposed (8 tokens of a channel).
+constexpr int FT2 = 32;
+
+IVC_DEV bf16x8_t pack_bf16x8(const bf16_t* v) {
+  u32x4 u;
+  u.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+  u.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+  u.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+  u.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 template <int C>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512, 2)
 k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __restrict__ valid,
               int* status, int N, const bf16_t* __restrict__ qt_hi,
               const bf16_t* __restrict__ qt_lo, int splits, float* __restrict__ part) {
-  constexpr int CW = C / 4;      // channels per wave
-  constexpr int KS = CW / 32;    // MFMA k-steps per wave
-  constexpr int CL = CW / 64;    // channels per lane in the weighted sum
+  constexpr int NW = 8;
+  constexpr int CW = C / NW;     // channels per wave
+  constexpr int KS = CW / 32;    // score MFMA k-steps per wave
+  constexpr int NT = CW / 16;    // 16-channel output tiles per wave
   constexpr int LDX = C + 8;     // padded LDS row (bf16)
 
-  __shared__ __attribute__((aligned(16))) bf16_t sX[FT * LDX];
-  __shared__ float sS[4][FT][FH];
-  __shared__ __attribute__((aligned(16))) float sP[4][FT][FH];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[FT2 * LDX];
+  __shared__ float sS[NW][FT2][FH];
 
   const int t = blockIdx.x / splits, sp = blockIdx.x % splits;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -71,7 +93,7 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
   const int n_beg = sp * per;
   const int n_end = min(nv, n_beg + per);
 
-  // q~ as B operand: lane holds head lo16, channels cw0 + 32*k + 8*hi4 + 0..7
+  // q~ as B operand of the score product: head lo16, channels cw0 + 32k + 8*hi4 + 0..7
   const int cw0 = w * CW;
   bf16x8_t qh[KS], ql[KS];
   {
@@ -83,98 +105,107 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
     }
   }
 
-  float acc[FH][CL];
+  // xbar accumulators: tile nt holds heads 4*hi4 + v, channel cw0 + 16*nt + lo16
+  f32x4_t acc[NT];
 #pragma unroll
-  for (int h = 0; h < FH; ++h)
-#pragma unroll
-    for (int i = 0; i < CL; ++i) acc[h][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;  // for head lo16 (lanes sharing lo16 agree)
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // head lo16 (lanes sharing lo16 agree)
 
   const bf16_t* xt = X + ((size_t)t * rows + has_cls) * C;
-  // token rows of the chunk as A operand: lane holds token n0 + lo16,
-  // channels cw0 + 32*k + 8*hi4 + 0..7
-  u32x4 xa[KS], xn[KS];
-  auto load_chunk = [&](int n0, u32x4* dst) {
-    const int n = n0 + lo16;
-    const bool ok = n < n_end;
-    const u32x4* src = reinterpret_cast<const u32x4*>(xt + (size_t)(ok ? n : n_beg) * C + cw0 + 8 * hi4);
+  // The chunk is loaded row-contiguously (a wave instruction covers 1 KB of
+  // one token row): thread i takes 16 bytes at token i / VPR + r * RPL,
+  // vector i % VPR, r = 0 .. LPT-1.  The next chunk is loaded while this one
+  // is processed.
+  constexpr int VPR = C / 8;               // 16-byte vectors per token row
+  constexpr int RPL = 512 / VPR;           // token rows per 512-thread pass
+  constexpr int LPT = FT2 / RPL;           // loads per thread per chunk
+  const int lrow = threadIdx.x / VPR, lvec = threadIdx.x % VPR;
+  u32x4 xg[LPT], xn[LPT];
+  auto load_chunk = [&](int n0, u32x4 (&dst)[LPT]) {
 #pragma unroll
-    for (int k = 0; k < KS; ++k) dst[k] = ok ? __builtin_nontemporal_load(src + 4 * k) : u32x4{0u, 0u, 0u, 0u};
-  };
-
-  if (n_beg < n_end) load_chunk(n_beg, xa);
-  for (int n0 = n_beg; n0 < n_end; n0 += FT) {
-    const bool more = n0 + FT < n_end;
-    if (more) load_chunk(n0 + FT, xn);
-
-    // partial scores over this wave's channels
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[k]);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[k], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[k], s, 0, 0, 0);
+    for (int r = 0; r < LPT; ++r) {
+      const int n = n0 + lrow + r * RPL;
+      dst[r] = n < n_end ? reinterpret_cast<const u32x4*>(xt + (size_t)n * C)[lvec]
+                         : u32x4{0u, 0u, 0u, 0u};
     }
-    // stage tokens (natural layout) and partial scores; s[v] is token 4*hi4+v, head lo16
+  };
+  if (n_beg < n_end) load_chunk(n_beg, xg);
+  for (int n0 = n_beg; n0 < n_end; n0 += FT2) {
+    if (n0 + FT2 < n_end) load_chunk(n0 + FT2, xn);
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
-      *reinterpret_cast<u32x4*>(&sX[lo16 * LDX + cw0 + 32 * k + 8 * hi4]) = xa[k];
+    for (int r = 0; r < LPT; ++r)
+      *reinterpret_cast<u32x4*>(&sX[(lrow + r * RPL) * LDX + 8 * lvec]) = xg[r];
+    __syncthreads();
+    // partial scores over this wave's channels; A operand = token 16*tt + lo16,
+    // channels cw0 + 32k + 8*hi4 (read from LDS); sc[v] = token 16*tt + 4*hi4 + v, head lo16
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sS[w][4 * hi4 + v][lo16] = s[v];
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            &sX[(16 * tt + lo16) * LDX + cw0 + 32 * k + 8 * hi4]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[k], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[k], sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sS[w][16 * tt + 4 * hi4 + v][lo16] = sc[v];
+    }
     __syncthreads();
 
-    // online softmax for head lo16 over tokens 4*hi4 .. 4*hi4+3 (every wave alike)
-    float sc[4], cmax = -INFINITY;
+    // online softmax: head lo16, tokens 8*hi4 .. 8*hi4+7 (all waves alike)
+    float sc8[8], cmax = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int tok = 4 * hi4 + v;
-      const float z = sS[0][tok][lo16] + sS[1][tok][lo16] + sS[2][tok][lo16] + sS[3][tok][lo16];
-      sc[v] = (n0 + tok < n_end) ? z : -INFINITY;
-      cmax = fmaxf(cmax, sc[v]);
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 8 * hi4 + j;
+      float z = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) z += sS[ww][tok][lo16];
+      sc8[j] = (n0 + tok < n_end) ? z : -INFINITY;
+      cmax = fmaxf(cmax, sc8[j]);
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
     const float m_new = fmaxf(m_run, cmax);
     const float corr = expf(m_run - m_new);
     float psum = 0.f;
+    bf16_t ph[8], pl[8];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float p = expf(sc[v] - m_new);
+    for (int j = 0; j < 8; ++j) {
+      const float p = expf(sc8[j] - m_new);
       psum += p;
-      sP[w][4 * hi4 + v][lo16] = p;
+      ph[j] = f32_to_bf16(p);
+      pl[j] = f32_to_bf16(p - bf16_to_f32(ph[j]));
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
     l_run = l_run * corr + psum;
     m_run = m_new;
-    __syncthreads();  // sP rows come from other lanes
+    const bf16x8_t pah = pack_bf16x8(ph), pal = pack_bf16x8(pl);
 
-    // weighted sum: lane owns channels cw0 + CL*lane + 0..CL-1, all heads
-    float cf[FH];
+    // rescale: accumulator row v of this lane is head 4*hi4 + v
+    float cr[4];
 #pragma unroll
-    for (int h = 0; h < FH; ++h) cf[h] = __shfl(corr, h, 64);
+    for (int v = 0; v < 4; ++v) cr[v] = __shfl(corr, 4 * hi4 + v, 64);
 #pragma unroll
-    for (int h = 0; h < FH; ++h)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int i = 0; i < CL; ++i) acc[h][i] *= cf[h];
-    const int nt = min(FT, n_end - n0);
-    for (int tok = 0; tok < nt; ++tok) {
-      float xv[CL];
-      const bf16_t* xr = &sX[tok * LDX + cw0 + CL * lane];
+      for (int v = 0; v < 4; ++v) acc[i][v] *= cr[v];
+
+    // xbar += P . X: B operand = tokens 8*hi4 .. +7 of channel cw0 + 16*nt + lo16
 #pragma unroll
-      for (int i = 0; i < CL; ++i) xv[i] = bf16_to_f32(xr[i]);
-      const f32x4_t* pr = reinterpret_cast<const f32x4_t*>(&sP[w][tok][0]);
-      f32x4_t p4[4] = {pr[0], pr[1], pr[2], pr[3]};
+    for (int nt = 0; nt < NT; ++nt) {
+      bf16_t xb[8];
+      const bf16_t* col = &sX[(8 * hi4) * LDX + cw0 + 16 * nt + lo16];
 #pragma unroll
-      for (int h = 0; h < FH; ++h) {
-        const float p = p4[h >> 2][h & 3];
-#pragma unroll
-        for (int i = 0; i < CL; ++i) acc[h][i] = fmaf(p, xv[i], acc[h][i]);
-      }
+      for (int j = 0; j < 8; ++j) xb[j] = col[j * LDX];
+      const bf16x8_t b = pack_bf16x8(xb);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, b, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, b, acc[nt], 0, 0, 0);
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < KS; ++k) xa[k] = xn[k];
+    for (int r = 0; r < LPT; ++r) xg[r] = xn[r];
   }
 
   float* pp = part + ((size_t)t * splits + sp) * (size_t)(FH * (2 + C));
@@ -183,9 +214,10 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
     pp[FH + lo16] = l_run;
   }
 #pragma unroll
-  for (int h = 0; h < FH; ++h)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int i = 0; i < CL; ++i) pp[2 * FH + (size_t)h * C + cw0 + CL * lane + i] = acc[h][i];
+    for (int v = 0; v < 4; ++v)
+      pp[2 * FH + (size_t)(4 * hi4 + v) * C + cw0 + 16 * nt + lo16] = acc[nt][v];
 }
 
 // xbar[t][h][c] = sum_s acc_s e^{m_s - M} / sum_s l_s e^{m_s - M}
@@ -218,11 +250,11 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s) {
   if (!pool_folded_supported(a.dtype, a.C, a.H)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.T * a.splits));
   if (a.C == 1024)
-    hipLaunchKernelGGL(k_pool_folded<1024>, grid, dim3(256), 0, s, (const bf16_t*)a.X, a.rows,
+    hipLaunchKernelGGL(k_pool_folded<1024>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
                        a.has_cls, a.valid, a.status, a.N, (const bf16_t*)a.qt_hi,
                        (const bf16_t*)a.qt_lo, a.splits, a.part);
   else
-    hipLaunchKernelGGL(k_pool_folded<512>, grid, dim3(256), 0, s, (const bf16_t*)a.X, a.rows,
+    hipLaunchKernelGGL(k_pool_folded<512>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
                        a.has_cls, a.valid, a.status, a.N, (const bf16_t*)a.qt_hi,
                        (const bf16_t*)a.qt_lo, a.splits, a.part);
   hipError_t e = hipGetLastError();
