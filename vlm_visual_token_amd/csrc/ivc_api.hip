@@ -132,6 +132,7 @@ extern "C" int32_t ivc_profile_read(const char** names, double* total_ms, int64_
 struct ivc_connector {
   ivc_config cfg;
   int esz;
+  int ncu = 256;  // compute units of the device the connector was created on
   char* blob = nullptr;
   // mlp1 / mlp2
   float *m1_ln_w, *m1_ln_b, *m1_b1, *m1_b2;
@@ -343,9 +344,11 @@ size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   if (!c.flash) return 0;
   const int sp = pool_splits(T, (int)N);
   if (c.pool_mode == IVC_POOL_FOLDED) {
+    int G, Q, segmax;
+    folded_geometry(T, (int)N, (int)C, h->ncu, &G, &Q, &segmax);
     r.qt_hi = cv.take((size_t)T * 16 * C * 2);
     r.qt_lo = cv.take((size_t)T * 16 * C * 2);
-    r.part = (float*)cv.take((size_t)T * sp * 16 * (2 + C) * 4);
+    r.part = (float*)cv.take((size_t)G * segmax * 16 * (2 + C) * 4);
     r.xbar = (float*)cv.take((size_t)T * c.pool_heads * C * 4);
   } else {
     r.kv = cv.take((size_t)T * N * 2 * L * C * h->esz);
@@ -431,6 +434,13 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
   ivc_connector* h = new ivc_connector();
   h->cfg = c;
   h->esz = (int)e;
+  {
+    // the token pass of folded pooling splits its work over the compute units
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      h->ncu = n;
+  }
   Carver plan(nullptr);
   auto layout = [&](Carver& cv) {
     h->m1_ln_w = (float*)cv.take(4 * C * 4);
@@ -694,6 +704,8 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
   LAUNCH("pool_query", s, launch_broadcast_rows(dt, h->query, w.q, T, C, s));
   const int splits = pool_splits(T, N);
   const float scale = 1.0f / sqrtf((float)(C / H));
+  int fG = 0, fQ = 0, fseg = 0;
+  if (folded) folded_geometry(T, N, C, h->ncu, &fG, &fQ, &fseg);
   for (int l = 0; l < L; ++l) {
     LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
                                  mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32, T,
@@ -703,7 +715,8 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
     const float* bv = h->bkv + (size_t)(2 * l + 1) * C;
     if (folded) {
       LAUNCH("pool_fold_query", s,
-             launch_fold_query(dt, w.qp, wk, w.qt_hi, w.qt_lo, T, C, H, scale, s));
+             launch_fold_query(dt, w.qp, wk, w.qt_hi, w.qt_lo, T, C, H,
+                               scale * 1.4426950408889634f, s));  // scores in log2 units
       FoldedArgs fa{};
       fa.dtype = dt;
       fa.X = vit;
@@ -717,7 +730,9 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
       fa.H = H;
       fa.qt_hi = w.qt_hi;
       fa.qt_lo = w.qt_lo;
-      fa.splits = splits;
+      fa.G = fG;
+      fa.Q = fQ;
+      fa.segmax = fseg;
       fa.part = w.part;
       fa.xbar = w.xbar;
       LAUNCH("pool_folded", s, launch_pool_folded(fa, s));

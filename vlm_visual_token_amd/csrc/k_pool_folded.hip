@@ -12,16 +12,34 @@
 // xbar_h for every head, plus small per-tile products before (q~) and after
 // (Wv xbar).  No K/V tensor is formed.
 //
-// Token pass (k_pool_folded): a workgroup takes a token range of one tile,
-// 32 tokens at a time, 8 waves each owning C/8 channels.  Both products run
-// on v_mfma_f32_16x16x32_bf16: the scores with the token rows as the A
-// operand and q~ as B, split into a bf16 high and low part so the product
-// keeps ~fp32 accuracy; the weighted sum with the softmax weights (also split
-// hi + lo) as A and the token chunk, staged in LDS and read transposed, as B.
-// Partial scores of the 8 waves meet in LDS; every wave runs the same
-// online-softmax update (fp32).  An fp32 FMA weighted sum would make the pass
-// VALU-bound (wave64 fp32 FMA takes 4 cycles per instruction); on MFMA it is
-// bound by the HBM read of the tokens.
+// Token pass (k_pool_folded): the chip's workgroups share the batch's
+// token chunks (16 tokens of one tile) evenly, each a contiguous range that
+// may cross tile boundaries; per tile touched a workgroup leaves one partial
+// (running max, running sum, weighted sums of every head) and a merge kernel
+// combines the partials of each tile in a fixed order.  8 waves per
+// workgroup, wave w owning channels [w*C/8, (w+1)*C/8).  Per chunk:
+//   load     LDS DMA (global_load_lds_dwordx4) into a 4-stage ring, three
+//            chunks ahead of the one in use;
+//   scores   partial S[token][head] over the wave's channels on
+//            v_mfma_f32_16x16x32_bf16, token rows (from LDS) as A, q~ as B,
+//            q~ split into bf16 high + low parts so the product keeps ~fp32
+//            accuracy; the 8 partials meet in LDS;
+//   softmax  lane (head h = lane % 16, g = lane / 16) takes tokens 4g..4g+3
+//            of head h, which is exactly the A-operand layout of the next
+//            product, so P (split into bf16 hi + lo) stays in registers;
+//            scores are in log2 units (q~ carries log2(e)), and the running
+//            max moves only when a chunk's max exceeds it by more than 8, so
+//            the rescale of the accumulators is rare;
+//   sum      xbar[h][c] += P[h][tokens] . X[tokens][c] on
+//            v_mfma_f32_16x16x16_bf16, the B operand (4 tokens of one
+//            channel) read with ds_read_b64_tr_b16 from the row-major chunk.
+// LDS rows are padded to 2*(C+16) bytes (32 mod 256) and 16-byte chunk c of
+// row r sits at c ^ ((r >> 3) & 1): the score operand reads (16 rows, one
+// 16-byte piece each) and the transposed reads (8 rows x 32 bytes per half
+// wave) are then free of bank conflicts.
+// An fp32 FMA weighted sum would make the pass VALU-bound (wave64 fp32 FMA
+// takes 4 cycles per instruction); on MFMA it is bound by the HBM read of the
+// tokens.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,234 +51,382 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int FH = 16;  // heads per MFMA column block (fewer heads are zero-padded)
-constexpr int FT = 16;  // tokens per chunk
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+typedef __attribute__((address_space(1))) const char gchar_t;
 
 bool pool_folded_supported(int dtype, int C, int H) {
   return dtype == DT_BF16 && (C == 512 || C == 1024) && H >= 1 && H <= FH && C % H == 0;
 }
 
-// part layout per (tile, split): [FH] running max, [FH] running sum, [FH][C] weighted sums
-//
-// 8 waves per workgroup, wave w owning channels [w*C/8, (w+1)*C/8); chunks of
-// FT2 = 32 tokens.  Per chunk:
-//   load     the 32 token rows, row-contiguously (1 KB per wave instruction),
-//            into LDS; the next chunk's rows are loaded meanwhile;
-//   scores   S[token][head] (two 16-token tiles) with the token rows (from
-//            LDS) as the MFMA A operand and q~ (hi + lo) as B;
-//   softmax  a lane (head h = lane % 16, token group g = lane / 16) takes
-//            tokens 8g .. 8g+7 of head h: exactly the A-operand layout of the
-//            next product, so P (split into bf16 hi + lo) stays in registers;
-//   sum      xbar[h][c] += P[h][tokens] . X[tokens][c] on MFMA, the token
-//            chunk staged in LDS and read transposed (8 tokens of a channel).
-constexpr int FT2 = 32;
+namespace {
+template <int C>
+struct PF {
+  static constexpr int NW = 8;                 // waves per workgroup
+  static constexpr int FT = 16;                // tokens per chunk
+  static constexpr int ST = 4;                 // LDS ring stages
+  static constexpr int CW = C / NW;            // channels per wave
+  static constexpr int KS = CW / 32;           // score k-steps per wave
+  static constexpr int NT = CW / 16;           // 16-channel output tiles per wave
+  static constexpr int RB = 2 * (C + 16);      // LDS row bytes (32 mod 256)
+  static constexpr int SB = FT * RB;           // stage bytes
+  static constexpr int IPR = C / 512;          // 1 KB DMA instructions per row
+  static constexpr int DPW = 2 * IPR;          // DMA instructions per wave per chunk
+  static constexpr int LDP = FT + 4;           // partial-score row (floats)
+  static constexpr int WG_PER_CU = C <= 512 ? 2 : 1;
+};
 
-IVC_DEV bf16x8_t pack_bf16x8(const bf16_t* v) {
-  u32x4 u;
-  u.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
-  u.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
-  u.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
-  u.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
-  return __builtin_bit_cast(bf16x8_t, u);
+IVC_DEV int clamp_valid(const int* valid, int t, int N) {
+  const int nv = valid != nullptr ? valid[t] : N;
+  return nv < 1 ? 1 : (nv > N ? N : nv);
 }
 
+// Walks the non-empty chunks of a workgroup's range [.., c_end) in order:
+// tile t, chunk j (tokens 16j .. 16j+15), nv valid tokens of tile t.
+struct ChunkIter {
+  int t, j, nv, nce;
+  IVC_DEV void enter(const int* valid, int N) {
+    nv = clamp_valid(valid, t, N);
+    nce = (nv + 15) / 16;
+  }
+  IVC_DEV void start(int c, int NC, int c_end, const int* valid, int N) {
+    t = c / NC;
+    j = c - t * NC;
+    if (c < c_end) {
+      enter(valid, N);
+      if (j >= nce) next_tile(NC, c_end, valid, N);
+    }
+  }
+  IVC_DEV void next_tile(int NC, int c_end, const int* valid, int N) {
+    ++t;
+    j = 0;
+    if (t * NC < c_end) enter(valid, N);  // chunk 0 of a tile is never empty
+  }
+  IVC_DEV void next(int NC, int c_end, const int* valid, int N) {
+    if (++j >= nce) next_tile(NC, c_end, valid, N);
+  }
+  IVC_DEV bool done(int NC, int c_end) const { return t * NC + j >= c_end; }
+};
+
+// reductions over the four lanes l, l^16, l^32, l^48 (v_permlane{16,32}_swap)
+IVC_DEV float max_x4(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+IVC_DEV float sum_x4(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt left alone
+#define IVC_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its outstanding global loads (__syncthreads' release fence would drain the
+// DMA ring); the signal fences keep the compiler from moving memory
+// operations across it.
+IVC_DEV void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+IVC_DEV float bf16_lo_f(uint32_t u) { return __uint_as_float(u << 16); }
+IVC_DEV float bf16_hi_f(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats to packed bf16 (v_cvt_pk_bf16_f32, round to nearest even)
+IVC_DEV uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+}  // namespace
+
+void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax) {
+  const int NC = (N + 15) / 16;
+  const long long total = (long long)T * NC;
+  const int wpc = C <= 512 ? 2 : 1;
+  long long g = (long long)(ncu > 0 ? ncu : 256) * wpc;
+  if (g > total) g = total;
+  if (g < 1) g = 1;
+  const long long q = (total + g - 1) / g;
+  *Q = (int)q;
+  *G = (int)((total + q - 1) / q);
+  *segmax = (int)((q + NC - 1) / NC) + 1;
+}
+
+// part layout per slot: [FH] running max (log2 units), [FH] running sum, [FH][C] weighted sums
 template <int C>
-__global__ void __launch_bounds__(512, 2)
+__global__ void __launch_bounds__(512, 2 * PF<C>::WG_PER_CU)
 k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __restrict__ valid,
-              int* status, int N, const bf16_t* __restrict__ qt_hi,
-              const bf16_t* __restrict__ qt_lo, int splits, float* __restrict__ part) {
-  constexpr int NW = 8;
-  constexpr int CW = C / NW;     // channels per wave
-  constexpr int KS = CW / 32;    // score MFMA k-steps per wave
-  constexpr int NT = CW / 16;    // 16-channel output tiles per wave
-  constexpr int LDX = C + 8;     // padded LDS row (bf16)
+              int T, int N, const bf16_t* __restrict__ qt_hi, const bf16_t* __restrict__ qt_lo,
+              int Q, int segmax, float* __restrict__ part) {
+  using P = PF<C>;
+  constexpr int NW = P::NW, KS = P::KS, NT = P::NT, RB = P::RB, SB = P::SB, DPW = P::DPW;
+  constexpr int LDP = P::LDP;
+  __shared__ __attribute__((aligned(1024))) char st0[SB];
+  __shared__ __attribute__((aligned(1024))) char st1[SB];
+  __shared__ __attribute__((aligned(1024))) char st2[SB];
+  __shared__ __attribute__((aligned(1024))) char st3[SB];
+  __shared__ __attribute__((aligned(16))) float sP[NW][FH][LDP];
 
-  __shared__ __attribute__((aligned(16))) bf16_t sX[FT2 * LDX];
-  __shared__ float sS[NW][FT2][FH];
-
-  const int t = blockIdx.x / splits, sp = blockIdx.x % splits;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo16 = lane & 15, hi4 = lane >> 4;
+  const int NC = (N + 15) / 16;
+  const int total = T * NC;
+  const int c_beg = blockIdx.x * Q;
+  const int c_end = min(total, c_beg + Q);
+  const int t_first = c_beg / NC;
+  const int cw0 = w * P::CW;
 
-  int nv = N;
-  if (valid != nullptr) {
-    nv = valid[t];
-    if (nv < 1 || nv > N) {
-      if (status != nullptr && sp == 0 && threadIdx.x == 0) atomicOr(status, 2);
-      nv = nv < 1 ? 1 : N;
-    }
-  }
-  const int per = (N + splits - 1) / splits;
-  const int n_beg = sp * per;
-  const int n_end = min(nv, n_beg + per);
-
-  // q~ as B operand of the score product: head lo16, channels cw0 + 32k + 8*hi4 + 0..7
-  const int cw0 = w * CW;
-  bf16x8_t qh[KS], ql[KS];
-  {
-    const size_t qrow = ((size_t)t * FH + lo16) * C + cw0 + 8 * hi4;
+  // ---- DMA of one chunk: wave w loads rows 2w, 2w+1 (IPR instructions each)
+  const int dma_f = (w >> 2) & 1;  // swizzle term of rows 2w, 2w+1
+  uint32_t dma_off[P::IPR];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      qh[k] = *reinterpret_cast<const bf16x8_t*>(qt_hi + qrow + 32 * k);
-      ql[k] = *reinterpret_cast<const bf16x8_t*>(qt_lo + qrow + 32 * k);
+  for (int hf = 0; hf < P::IPR; ++hf) dma_off[hf] = (uint32_t)(((hf * 64 + lane) ^ dma_f) * 16);
+  gchar_t* xg = (gchar_t*)X;
+  auto dma = [&](const ChunkIter& it, char* stage) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int R = 2 * w + r;
+      const int n = min(16 * it.j + R, it.nv - 1);  // tail rows repeat a valid row (masked later)
+      gchar_t* src = xg + ((long long)it.t * rows + has_cls + n) * (long long)(C * 2);
+#pragma unroll
+      for (int hf = 0; hf < P::IPR; ++hf)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(src + dma_off[hf]),
+                                         (lds_void_t*)(stage + R * RB + hf * 1024), 16, 0, 0);
     }
-  }
+  };
 
-  // xbar accumulators: tile nt holds heads 4*hi4 + v, channel cw0 + 16*nt + lo16
+  // ---- per-lane LDS offsets (bytes within a stage)
+  // score A operand: row lo16, 16-byte piece cw0/8 + 4k + hi4 (swizzled)
+  const int a_off = lo16 * RB + (cw0 / 8 + (hi4 ^ ((lo16 >> 3) & 1))) * 16;
+  // transposed B operand: lane (g = hi4, e = lo16/4, q = lo16%4) points at row
+  // 4g + e, channels n0c + 4q .. +3 of 16-channel tile n0c = cw0 + 16 nt
+  const int tr_row = 4 * hi4 + (lo16 >> 2), tr_q = lo16 & 3;
+  const int tr_off = tr_row * RB + (cw0 / 8 + ((tr_q >> 1) ^ ((tr_row >> 3) & 1))) * 16 + (tr_q & 1) * 8;
+
+  // ---- running state of the current tile.  A new tile only resets the
+  // running max and sum: its first chunk then rescales the accumulators by 0.
+  // l_run holds this lane's share (its 4 tokens per chunk) of head lo16's sum.
+  int cur_t = -1;
+  bf16x8_t qh[KS], ql[KS];
   f32x4_t acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;  // head lo16 (lanes sharing lo16 agree)
+  float m_run = -INFINITY, l_run = 0.f;
 
-  const bf16_t* xt = X + ((size_t)t * rows + has_cls) * C;
-  // The chunk is loaded row-contiguously (a wave instruction covers 1 KB of
-  // one token row): thread i takes 16 bytes at token i / VPR + r * RPL,
-  // vector i % VPR, r = 0 .. LPT-1.  The next chunk is loaded while this one
-  // is processed.
-  constexpr int VPR = C / 8;               // 16-byte vectors per token row
-  constexpr int RPL = 512 / VPR;           // token rows per 512-thread pass
-  constexpr int LPT = FT2 / RPL;           // loads per thread per chunk
-  const int lrow = threadIdx.x / VPR, lvec = threadIdx.x % VPR;
-  u32x4 xg[LPT], xn[LPT];
-  auto load_chunk = [&](int n0, u32x4 (&dst)[LPT]) {
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) {
-      const int n = n0 + lrow + r * RPL;
-      dst[r] = n < n_end ? reinterpret_cast<const u32x4*>(xt + (size_t)n * C)[lvec]
-                         : u32x4{0u, 0u, 0u, 0u};
+  auto flush = [&](int t) {
+    float* pp = part + ((size_t)blockIdx.x * segmax + (t - t_first)) * (size_t)(FH * (2 + C));
+    const float l_all = sum_x4(l_run);
+    if (w == 0 && hi4 == 0) {
+      pp[lo16] = m_run;
+      pp[FH + lo16] = l_all;
     }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        pp[2 * FH + (size_t)(4 * hi4 + v) * C + cw0 + 16 * nt + lo16] = acc[nt][v];
   };
-  if (n_beg < n_end) load_chunk(n_beg, xg);
-  for (int n0 = n_beg; n0 < n_end; n0 += FT2) {
-    if (n0 + FT2 < n_end) load_chunk(n0 + FT2, xn);
+
+  // ---- prologue: the first ST-1 chunks into stages 0..ST-2
+  ChunkIter pi, ci;
+  pi.start(c_beg, NC, c_end, valid, N);
+  ci = pi;
+  int issued = 0, consumed = 0;
+  if (!pi.done(NC, c_end)) { dma(pi, st0); pi.next(NC, c_end, valid, N); ++issued; }
+  if (!pi.done(NC, c_end)) { dma(pi, st1); pi.next(NC, c_end, valid, N); ++issued; }
+  if (!pi.done(NC, c_end)) { dma(pi, st2); pi.next(NC, c_end, valid, N); ++issued; }
+
+  auto step = [&](const char* stage, char* next_stage) {
+    // this chunk's DMA is done once at most (issued - consumed - 1) chunks remain in flight
+    const int ahead = issued - consumed - 1;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (ahead >= 2) IVC_WAIT_VM(2 * DPW);
+    else if (ahead == 1) IVC_WAIT_VM(DPW);
+    else IVC_WAIT_VM(0);
+    lds_barrier();
+    bf16x8_t a[KS];
 #pragma unroll
-    for (int r = 0; r < LPT; ++r)
-      *reinterpret_cast<u32x4*>(&sX[(lrow + r * RPL) * LDX + 8 * lvec]) = xg[r];
-    __syncthreads();
-    // partial scores over this wave's channels; A operand = token 16*tt + lo16,
-    // channels cw0 + 32k + 8*hi4 (read from LDS); sc[v] = token 16*tt + 4*hi4 + v, head lo16
+    for (int k = 0; k < KS; ++k) a[k] = *reinterpret_cast<const bf16x8_t*>(stage + a_off + 64 * k);
+
+    if (ci.t != cur_t) {
+      if (cur_t >= 0) flush(cur_t);
+      cur_t = ci.t;
+      const size_t qrow = ((size_t)ci.t * FH + lo16) * C + cw0 + 8 * hi4;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+      for (int k = 0; k < KS; ++k) {
+        qh[k] = *reinterpret_cast<const bf16x8_t*>(qt_hi + qrow + 32 * k);
+        ql[k] = *reinterpret_cast<const bf16x8_t*>(qt_lo + qrow + 32 * k);
+      }
+      // q~ is used at once; waiting here keeps the wait off the common path
+      IVC_WAIT_VM(0);
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+
+    // partial scores: sc[v] = token 4*hi4 + v, head lo16, over this wave's channels
+    {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            &sX[(16 * tt + lo16) * LDX + cw0 + 32 * k + 8 * hi4]);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[k], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[k], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], qh[k], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], ql[k], sc, 0, 0, 0);
       }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sS[w][16 * tt + 4 * hi4 + v][lo16] = sc[v];
+      *reinterpret_cast<f32x4_t*>(&sP[w][lo16][4 * hi4]) = sc;
     }
-    __syncthreads();
+    lds_barrier();
 
-    // online softmax: head lo16, tokens 8*hi4 .. 8*hi4+7 (all waves alike)
-    float sc8[8], cmax = -INFINITY;
+    // operands of the weighted sum first: they do not depend on the softmax
+    s16x4_t b[NT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = 8 * hi4 + j;
-      float z = 0.f;
+    for (int nt = 0; nt < NT; ++nt)
+      b[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(lds_void_t*)(stage + tr_off + 32 * nt));
+
+    // softmax over this chunk: lane (head lo16, tokens 4*hi4 .. +3)
+    f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&sP[0][lo16][4 * hi4]);
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) z += sS[ww][tok][lo16];
-      sc8[j] = (n0 + tok < n_end) ? z : -INFINITY;
-      cmax = fmaxf(cmax, sc8[j]);
+    for (int ww = 1; ww < NW; ++ww) s4 += *reinterpret_cast<const f32x4_t*>(&sP[ww][lo16][4 * hi4]);
+    // the next DMA goes out after this step's LDS reads: the compiler makes an
+    // LDS read that follows an LDS DMA wait for it
+    if (!pi.done(NC, c_end)) { dma(pi, next_stage); pi.next(NC, c_end, valid, N); ++issued; }
+    const int n0 = 16 * ci.j;
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (n0 + 4 * hi4 + e >= ci.nv) s4[e] = -INFINITY;
+      cmax = fmaxf(cmax, s4[e]);
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float corr = expf(m_run - m_new);
-    float psum = 0.f;
-    bf16_t ph[8], pl[8];
+    cmax = max_x4(cmax);  // the chunk's first token is valid, so cmax is finite
+    const bool need = cmax > m_run + 8.f;
+    if (__ballot(need) != 0) {
+      const float m_new = need ? cmax : m_run;
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+      m_run = m_new;
+      float cr[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = expf(sc8[j] - m_new);
-      psum += p;
-      ph[j] = f32_to_bf16(p);
-      pl[j] = f32_to_bf16(p - bf16_to_f32(ph[j]));
+      for (int v = 0; v < 4; ++v) cr[v] = __shfl(corr, 4 * hi4 + v, 64);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][v] = cr[v] == 0.f ? 0.f : acc[i][v] * cr[v];
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    const bf16x8_t pah = pack_bf16x8(ph), pal = pack_bf16x8(pl);
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(s4[e] - m_run);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    const uint32_t h01 = cvt_pk_bf16(p[0], p[1]), h23 = cvt_pk_bf16(p[2], p[3]);
+    const uint32_t l01 = cvt_pk_bf16(p[0] - bf16_lo_f(h01), p[1] - bf16_hi_f(h01));
+    const uint32_t l23 = cvt_pk_bf16(p[2] - bf16_lo_f(h23), p[3] - bf16_hi_f(h23));
+    s16x4_t pah, pal;
+    {
+      uint2 u{h01, h23}, v{l01, l23};
+      pah = __builtin_bit_cast(s16x4_t, u);
+      pal = __builtin_bit_cast(s16x4_t, v);
+    }
 
-    // rescale: accumulator row v of this lane is head 4*hi4 + v
-    float cr[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) cr[v] = __shfl(corr, 4 * hi4 + v, 64);
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][v] *= cr[v];
-
-    // xbar += P . X: B operand = tokens 8*hi4 .. +7 of channel cw0 + 16*nt + lo16
+    // xbar += P . X over this wave's 16-channel tiles
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      bf16_t xb[8];
-      const bf16_t* col = &sX[(8 * hi4) * LDX + cw0 + 16 * nt + lo16];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xb[j] = col[j * LDX];
-      const bf16x8_t b = pack_bf16x8(xb);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, b, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, b, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pah, b[nt], acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pal, b[nt], acc[nt], 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) xg[r] = xn[r];
-  }
+    ++consumed;
+    ci.next(NC, c_end, valid, N);
+  };
 
-  float* pp = part + ((size_t)t * splits + sp) * (size_t)(FH * (2 + C));
-  if (w == 0 && hi4 == 0) {
-    pp[lo16] = m_run;
-    pp[FH + lo16] = l_run;
+  // The first step is peeled: after the prologue's DMAs the compiler would
+  // otherwise make a partial-score read in the loop wait for every DMA in
+  // flight.
+  if (!ci.done(NC, c_end)) {
+    step(st0, st3);
+    while (!ci.done(NC, c_end)) {
+      step(st1, st0);
+      if (ci.done(NC, c_end)) break;
+      step(st2, st1);
+      if (ci.done(NC, c_end)) break;
+      step(st3, st2);
+      if (ci.done(NC, c_end)) break;
+      step(st0, st3);
+    }
   }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      pp[2 * FH + (size_t)(4 * hi4 + v) * C + cw0 + 16 * nt + lo16] = acc[nt][v];
+  if (cur_t >= 0) flush(cur_t);
 }
 
-// xbar[t][h][c] = sum_s acc_s e^{m_s - M} / sum_s l_s e^{m_s - M}
+// xbar[t][h][c] = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) over the
+// partials of tile t, in workgroup order.  Also flags invalid token counts.
 __global__ void __launch_bounds__(256)
-k_pool_folded_merge(const float* __restrict__ part, int splits, int C, int H,
-                    float* __restrict__ xbar) {
+k_pool_folded_merge(const float* __restrict__ part, const int* __restrict__ valid, int* status,
+                    int N, int C, int H, int Q, int segmax, float* __restrict__ xbar) {
   const int t = blockIdx.x, h = blockIdx.y;
+  const int NC = (N + 15) / 16;
+  int nv = valid != nullptr ? valid[t] : N;
+  if ((nv < 1 || nv > N) && status != nullptr && h == 0 && threadIdx.x == 0) atomicOr(status, 2);
+  nv = nv < 1 ? 1 : (nv > N ? N : nv);
+  const int lo_c = t * NC, hi_c = t * NC + (nv + 15) / 16;
+  const int g0 = lo_c / Q, g1 = (hi_c - 1) / Q;
   const size_t stride = (size_t)FH * (2 + C);
-  const float* pt = part + (size_t)t * splits * stride;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pt[s * stride + h]);
+  for (int g = g0; g <= g1; ++g) {
+    const float* pp = part + ((size_t)g * segmax + (t - (g * Q) / NC)) * stride;
+    M = fmaxf(M, pp[h]);
+  }
   float L = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = pt[s * stride + h];
-    L += (ms == -INFINITY) ? 0.f : pt[s * stride + FH + h] * expf(ms - M);
+  for (int g = g0; g <= g1; ++g) {
+    const float* pp = part + ((size_t)g * segmax + (t - (g * Q) / NC)) * stride;
+    L += pp[FH + h] * exp2f(pp[h] - M);
   }
   const float invL = 1.0f / L;
-  for (int c = threadIdx.x; c < C; c += 256) {
-    float A = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = pt[s * stride + h];
-      if (ms != -INFINITY) A += pt[s * stride + 2 * FH + (size_t)h * C + c] * expf(ms - M);
+  for (int c4 = threadIdx.x; c4 < C / 4; c4 += 256) {
+    float4 A = {0.f, 0.f, 0.f, 0.f};
+    for (int g = g0; g <= g1; ++g) {
+      const float* pp = part + ((size_t)g * segmax + (t - (g * Q) / NC)) * stride;
+      const float sc = exp2f(pp[h] - M);
+      const float4 v = *reinterpret_cast<const float4*>(pp + 2 * FH + (size_t)h * C + 4 * c4);
+      A.x += v.x * sc;
+      A.y += v.y * sc;
+      A.z += v.z * sc;
+      A.w += v.w * sc;
     }
-    xbar[((size_t)t * H + h) * C + c] = A * invL;
+    A.x *= invL;
+    A.y *= invL;
+    A.z *= invL;
+    A.w *= invL;
+    *reinterpret_cast<float4*>(xbar + ((size_t)t * H + h) * C + 4 * c4) = A;
   }
 }
 
 hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (!pool_folded_supported(a.dtype, a.C, a.H)) return hipErrorInvalidValue;
-  dim3 grid((unsigned)(a.T * a.splits));
+  if (a.G < 1 || a.Q < 1 || a.segmax < 1) return hipErrorInvalidValue;
+  dim3 grid((unsigned)a.G);
   if (a.C == 1024)
     hipLaunchKernelGGL(k_pool_folded<1024>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
-                       a.has_cls, a.valid, a.status, a.N, (const bf16_t*)a.qt_hi,
-                       (const bf16_t*)a.qt_lo, a.splits, a.part);
+                       a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,
+                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part);
   else
     hipLaunchKernelGGL(k_pool_folded<512>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
-                       a.has_cls, a.valid, a.status, a.N, (const bf16_t*)a.qt_hi,
-                       (const bf16_t*)a.qt_lo, a.splits, a.part);
+                       a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,
+                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_pool_folded_merge, dim3((unsigned)a.T, (unsigned)a.H), dim3(256), 0, s,
-                     (const float*)a.part, a.splits, a.C, a.H, a.xbar);
+                     (const float*)a.part, a.valid, a.status, a.N, a.C, a.H, a.Q, a.segmax,
+                     a.xbar);
   return hipGetLastError();
 }
 

@@ -156,12 +156,16 @@ struct FoldedArgs {
   const int* valid;
   int* status;
   int T, N, C, H;
-  const void* qt_hi;  // [T, 16, C] bf16: folded queries (1/sqrt(d) applied), high part
+  const void* qt_hi;  // [T, 16, C] bf16: folded queries (log2(e)/sqrt(d) applied), high part
   const void* qt_lo;  // low part
-  int splits;
-  float* part;        // [T, splits, 16 * (2 + C)]
+  int G, Q, segmax;   // from folded_geometry
+  float* part;        // [G * segmax, 16 * (2 + C)]
   float* xbar;        // [T, H, C] softmax-weighted token means
 };
+// Work split of the token pass: G workgroups of Q consecutive 16-token chunks
+// each (chunk index = tile * ceil(N/16) + chunk); a workgroup leaves at most
+// segmax partials.  ncu = compute units of the device.
+void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax);
 bool pool_folded_supported(int dtype, int C, int H);
 hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
 // qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
