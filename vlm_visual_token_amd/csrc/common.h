@@ -76,5 +76,22 @@ IVC_DEV float wave_max(float v) {
   return v;
 }
 
-// Exact GELU, 0.5 x (1 + erf(x / sqrt 2)).
-IVC_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// erf by the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x), x >= 0, odd extension.
+// Branch-free (a library erf branches per range, which costs the GEMM
+// epilogues dearly when the lanes of a wave fall in different ranges).
+IVC_DEV float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * ax * ax);  // exp(-x^2)
+  return copysignf(fmaf(-p * t, e, 1.0f), x);
+}
+
+// GELU, 0.5 x (1 + erf(x / sqrt 2)).
+IVC_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }

@@ -145,6 +145,7 @@ struct ivc_connector {
   float *bq[IVC_MAX_POOL_LAYERS], *bo[IVC_MAX_POOL_LAYERS];
   void* wkv;   // [2 * layers * C, C]: Wk_0; Wv_0; Wk_1; Wv_1; ...
   float* bkv;  // [2 * layers * C]
+  void* wkT;   // bf16 only: [layers][C, C], wkT[l][c][j] = Wk_l[j][c] (query fold)
   void *g_w1[IVC_GATE_BLOCKS], *g_w2[IVC_GATE_BLOCKS], *g_cw;
   float *g_b1[IVC_GATE_BLOCKS], *g_b2[IVC_GATE_BLOCKS], *g_lw[IVC_GATE_BLOCKS],
       *g_lb[IVC_GATE_BLOCKS], *g_cb;
@@ -246,6 +247,7 @@ struct SimtScratch {
 // (split over K when the product is skinny and scratch is available).
 hipError_t gemm(const char*, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
   if (g.batch <= 0) g.batch = 1;
+  if (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) return launch_gemm_f32a(g, 0, nullptr, 1.f, s);
   if (g.batch == 1 && gemm_mfma_supported(g)) {
     // 256 x 256 LDS-DMA tiles when they fill the chip, else 128 x 128 tiles
     const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
@@ -467,6 +469,7 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       }
       h->wkv = cv.take(2 * Lp * C * C * e);
       h->bkv = (float*)cv.take(2 * Lp * C * 4);
+      h->wkT = dt == IVC_BF16 ? cv.take(Lp * C * C * e) : nullptr;
       for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
         h->g_w1[b] = cv.take(he * hh * e);
         h->g_b1[b] = (float*)cv.take(he * 4);
@@ -519,6 +522,11 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       STEP(widen(w->pool_bo[l], dt, h->bo[l], C, s));
       STEP(copy_mat(w->pool_wk[l], (char*)h->wkv + (2 * l) * C * C * e, C * C * e, s));
       STEP(copy_mat(w->pool_wv[l], (char*)h->wkv + (2 * l + 1) * C * C * e, C * C * e, s));
+      if (h->wkT != nullptr)
+        STEP(launch_transpose_bf16(w->pool_wk[l], (char*)h->wkT + l * C * C * e, (int)C, (int)C, s)
+                     == hipSuccess
+                 ? IVC_OK
+                 : fail(IVC_ERR_HIP, "weight transpose launch failed"));
       STEP(widen(w->pool_bk[l], dt, h->bkv + (2 * l) * C, C, s));
       STEP(widen(w->pool_bv[l], dt, h->bkv + (2 * l + 1) * C, C, s));
     }
@@ -714,9 +722,26 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
     const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * C * h->esz;
     const float* bv = h->bkv + (size_t)(2 * l + 1) * C;
     if (folded) {
-      LAUNCH("pool_fold_query", s,
-             launch_fold_query(dt, w.qp, wk, w.qt_hi, w.qt_lo, T, C, H,
-                               scale * 1.4426950408889634f, s));  // scores in log2 units
+      // q~_h = Wk_h^T q_h * log2(e) / sqrt(d) (scores in log2 units), per head
+      // a product [T, d] x [d, C] with the transposed key weights
+      const float qscale = scale * 1.4426950408889634f;
+      if (h->wkT != nullptr) {
+        const int d = C / H;
+        GemmArgs fq = mk_gemm(w.qp, C, DT_F32, (const char*)h->wkT + (size_t)l * C * C * h->esz,
+                              DT_BF16, nullptr, w.qt_hi, DT_BF16, T, C, d, ACT_NONE);
+        fq.ldw = C;
+        fq.ldc = 16ll * C;
+        fq.batch = H;
+        fq.a_bs = d;
+        fq.w_bs = d;
+        fq.c_bs = C;
+        LAUNCH("pool_fold_query", s, launch_gemm_f32a(fq, 1, w.qt_lo, qscale, s));
+        if (l == 0 && H < 16)
+          LAUNCH("pool_fold_pad", s, launch_zero_heads(w.qt_hi, w.qt_lo, T, H, C, s));
+      } else {
+        LAUNCH("pool_fold_query", s,
+               launch_fold_query(dt, w.qp, wk, w.qt_hi, w.qt_lo, T, C, H, qscale, s));
+      }
       FoldedArgs fa{};
       fa.dtype = dt;
       fa.X = vit;

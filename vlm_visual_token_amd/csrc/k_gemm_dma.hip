@@ -18,7 +18,8 @@
 // Two LDS stages (2 x 64 KB).  Each K step first reads all of its MFMA
 // fragments from the current stage into registers, then issues the DMA of
 // the next K step into the other stage, then runs its 64 MFMAs, which hide
-// the DMA latency; one barrier per K step.
+// the DMA latency; one barrier per K step.  The finished tile goes out
+// through LDS with 16-byte stores.
 #include "common.h"
 #include "kernels.h"
 
@@ -184,27 +185,48 @@ k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_g
     __syncthreads();
   }
 
-  // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and rows
+  // Epilogue through LDS: the 256 x 256 bf16 tile (128 KB; rows 64q .. 64q+63
+  // in stage array q of sA0, sB0, sA1, sB1) is written from the accumulators,
+  // then stored with 16-byte row-contiguous writes (2-byte stores straight
+  // from the accumulator layout reach a fraction of the write bandwidth).
+  // 32x32 accumulator layout: lane l holds column l % 32 and rows
   // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  {
+    char* slab_lo = wm ? (char*)sA1 : (char*)sA0;
+    char* slab_hi = wm ? (char*)sB1 : (char*)sB0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-    const bool col_ok = col < N;
-    const float bj = (bias != nullptr && col_ok) ? bias[col] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const int cl = wn * 128 + j * 32 + (lane & 31);
+      const int col = n0 + cl;
+      const float bj = (bias != nullptr && col < N) ? bias[col] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        char* slab = i < 2 ? slab_lo : slab_hi;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (col_ok && row < M) {
+        for (int v = 0; v < 16; ++v) {
+          const int rl = (i & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);  // row in slab
           float x = acc[i][j][v] + bj;
           if (ACT == ACT_GELU) x = gelu_erf(x);
-          const long long orow =
-              rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg
-                                  : row;
-          Cm[orow * ldc + col] = f32_to_bf16(x);
+          *reinterpret_cast<bf16_t*>(slab + rl * 512 + cl * 2) = f32_to_bf16(x);
         }
       }
+    }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int r = it * 8 + (tid >> 5), c = tid & 31;
+    const char* slab = it < 8 ? (const char*)sA0 : it < 16 ? (const char*)sB0
+                     : it < 24 ? (const char*)sA1 : (const char*)sB1;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(slab + (r & 63) * 512 + c * 16);
+    const int row = m0 + r, col = n0 + 8 * c;
+    if (row < M && col < N) {
+      const long long orow =
+          rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg
+                              : row;
+      *reinterpret_cast<u32x4*>(Cm + orow * ldc + col) = val;
     }
   }
 }
@@ -212,7 +234,8 @@ k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_g
 bool gemm_dma_supported(const GemmArgs& g) {
   return g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % DBK == 0 &&
          g.K > 0 && g.M > 0 && g.N > 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
-         ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.W % 16) == 0;
+         ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.W % 16) == 0 && g.N % 8 == 0 &&
+         g.ldc % 8 == 0 && ((uintptr_t)g.Cm % 16) == 0;
 }
 
 hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {

@@ -77,6 +77,14 @@ bool gemm_dma_supported(const GemmArgs& g);
 // Any element types, fp32 FMA.  Used for fp32 workloads and fp32-activation
 // router products.
 hipError_t launch_gemm_simt(const GemmArgs& g, hipStream_t s);
+// fp32 A, bf16 W on MFMA (A split into bf16 high + low parts), fp32 C; with
+// out_split = 1 the result times `scale` goes out as bf16 high (Cm) and low (C2)
+// parts instead.  Batched via batch / a_bs / w_bs / c_bs / bias_bs.  K % 32 == 0.
+bool gemm_f32a_supported(const GemmArgs& g);
+hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float scale,
+                            hipStream_t s);
+// dst[c][r] = src[r][c], bf16 [R, Cc]
+hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int Cc, hipStream_t s);
 // split-K factor and workspace the SIMT kernel wants for a product
 int simt_ksplit(int M, int N, int K, int batch);
 size_t simt_part_elems(int M, int N, int batch, int ksplit);
@@ -171,6 +179,8 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
 // qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
 hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt_hi, void* qt_lo,
                              int T, int C, int H, float scale, hipStream_t s);
+// qt_hi / qt_lo [T, 16, C]: heads H .. 15 set to zero
+hipError_t launch_zero_heads(void* qt_hi, void* qt_lo, int T, int H, int C, hipStream_t s);
 // o[t, h*d + i] = bv[h*d+i] + sum_c Wv[h*d + i, c] * xbar[t, h, c]
 hipError_t launch_fold_value(int dtype, const float* xbar, const void* Wv, const float* bv,
                              float* o, int T, int C, int H, hipStream_t s);
