@@ -134,13 +134,19 @@ typedef struct ivc_connector ivc_connector;
  * library-owned device memory (biases and LayerNorm parameters widened to
  * float32; the K/V projections of all pooling layers packed into one
  * [2 * layers * C, C] matrix), synchronises `stream`, and returns the handle
- * in *out.  The handle is immutable afterwards and may be shared by calls on
- * several streams.  Errors: IVC_ERR_INVALID_ARG, IVC_ERR_UNSUPPORTED,
- * IVC_ERR_MISALIGNED, IVC_ERR_OOM, IVC_ERR_HIP. */
+ * in *out.  A bf16 flash connector also owns a second stream (default
+ * priority) and two events: run and run_routed fork the mlp1 chain onto that
+ * stream after the loader and join it back into the caller's stream, so the
+ * two projector chains share the chip.  The handle's weights are immutable
+ * afterwards; calls may use several streams, but one handle must not be used
+ * by two host threads at once (the fork/join events are shared).  Errors:
+ * IVC_ERR_INVALID_ARG, IVC_ERR_UNSUPPORTED, IVC_ERR_MISALIGNED, IVC_ERR_OOM,
+ * IVC_ERR_HIP. */
 ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weights* w, void* stream,
                                 ivc_connector** out);
 
-/* Release the handle's device memory (synchronises the device first). NULL is a no-op. */
+/* Release the handle's device memory, stream and events (synchronises the
+ * device first). NULL is a no-op. */
 void ivc_connector_destroy(ivc_connector* h);
 
 /* Bytes of device workspace that run, route and compact need for up to

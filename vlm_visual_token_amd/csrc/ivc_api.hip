@@ -133,6 +133,10 @@ struct ivc_connector {
   ivc_config cfg;
   int esz;
   int ncu = 256;  // compute units of the device the connector was created on
+  // second stream (default priority) on which the mlp1 chain runs beside the
+  // mlp2 chain; forked from and joined back to the caller's stream by events
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   char* blob = nullptr;
   // mlp1 / mlp2
   float *m1_ln_w, *m1_ln_b, *m1_b1, *m1_b2;
@@ -443,6 +447,15 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       h->ncu = n;
   }
+  if (c.flash && dt == IVC_BF16) {
+    if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      ivc_connector_destroy(h);
+      return fail(IVC_ERR_HIP, "stream/event creation failed");
+    }
+  }
   Carver plan(nullptr);
   auto layout = [&](Carver& cv) {
     h->m1_ln_w = (float*)cv.take(4 * C * 4);
@@ -553,10 +566,11 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
 
 extern "C" void ivc_connector_destroy(ivc_connector* h) {
   if (!h) return;
-  if (h->blob) {
-    (void)hipDeviceSynchronize();
-    (void)hipFree(h->blob);
-  }
+  if (h->blob || h->aux) (void)hipDeviceSynchronize();
+  if (h->blob) (void)hipFree(h->blob);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->aux) (void)hipStreamDestroy(h->aux);
   delete h;
 }
 
@@ -634,14 +648,26 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   }
   LAUNCH("shuffle_ln", s, launch_shuffle_ln(sa, s));
 
+  // The mlp1 and mlp2 chains are independent: with a second stream the tail
+  // workgroups of one chain's products share the chip with the other's
+  // instead of leaving compute units idle.  (bf16 only: the fp32 products
+  // share one SIMT scratch buffer.)
+  const bool fork = c.flash && h->aux != nullptr;
+  hipStream_t s1 = s;
+  if (fork) {
+    HIP_OK(hipEventRecord(h->ev_fork, s));
+    HIP_OK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
+    s1 = h->aux;
+  }
   const int M2 = (int)(T * S);
   GemmArgs g;
   g = mk_gemm(w.a2, 4 * C, dt, h->m1_w1, dt, h->m1_b1, w.h1, dt, M2, H1, 4 * C, ACT_GELU);
   g.rm = rmh256;
-  LAUNCH("mlp1_gemm1", s, gemm("mlp1_gemm1", g, s, &w.sc));
+  LAUNCH("mlp1_gemm1", s1, gemm("mlp1_gemm1", g, s1, &w.sc));
   g = mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D, H1, ACT_NONE);
   g.rm = rm256;
-  LAUNCH("mlp1_gemm2", s, gemm("mlp1_gemm2", g, s, &w.sc));
+  LAUNCH("mlp1_gemm2", s1, gemm("mlp1_gemm2", g, s1, &w.sc));
+  if (fork) HIP_OK(hipEventRecord(h->ev_join, s1));
   if (c.flash) {
     const int M4 = T * S4;
     g = mk_gemm(w.a4, 16 * C, dt, h->m2_w1, dt, h->m2_b1, w.g1, dt, M4, H2, 16 * C, ACT_GELU);
@@ -654,6 +680,7 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     g.rm = rm64;
     LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3", g, s, &w.sc));
   }
+  if (fork) HIP_OK(hipStreamWaitEvent(s, h->ev_join, 0));
   return IVC_OK;
 }
 

@@ -28,9 +28,14 @@ IVC_DEV float key_value(uint32_t k) {
 
 constexpr int QT = 1024;  // threads
 
-// k-th smallest key (0-based) among the T gates.
-IVC_DEV uint32_t radix_select(const float* gate, int T, int k, uint32_t* hist, uint32_t* sh) {
+// k-th smallest key (0-based) among the T gates.  Per pass: histogram of
+// the next 8 key bits among the keys that match the prefix so far, then the
+// 256 bins are scanned in parallel (4 waves) and the bin holding the k-th
+// key extends the prefix.
+IVC_DEV uint32_t radix_select(const float* gate, int T, int k, uint32_t* hist, uint32_t* sh,
+                              uint32_t* wtot) {
   uint32_t prefix = 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int pass = 3; pass >= 0; --pass) {
     const int shift = 8 * pass;
     const uint32_t mask = pass == 3 ? 0u : (0xffffffffu << (shift + 8));
@@ -41,15 +46,26 @@ IVC_DEV uint32_t radix_select(const float* gate, int T, int k, uint32_t* hist, u
       if ((key & mask) == (prefix & mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t cum = 0, b = 0;
-      for (; b < 255; ++b) {
-        if ((uint32_t)k < cum + hist[b]) break;
-        cum += hist[b];
+    uint32_t h = 0, inc = 0;
+    if (threadIdx.x < 256) {
+      h = hist[threadIdx.x];
+      inc = h;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
       }
-      k -= (int)cum;
-      sh[0] = prefix | (b << shift);
-      sh[1] = (uint32_t)k;
+      if (lane == 63) wtot[w] = inc;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+      uint32_t before = 0;
+      for (int q = 0; q < w; ++q) before += wtot[q];
+      const uint32_t excl = before + inc - h;  // keys in lower bins
+      if ((uint32_t)k >= excl && (uint32_t)k < excl + h) {
+        sh[0] = prefix | ((uint32_t)threadIdx.x << shift);
+        sh[1] = (uint32_t)k - excl;
+      }
     }
     __syncthreads();
     prefix = sh[0];
@@ -68,6 +84,7 @@ k_quantile_decide(const float* __restrict__ gate, int T, double q, double abs_th
 #pragma clang fp contract(off)
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh[4];
+  __shared__ uint32_t wtot[4];
 
   const double pos = q * (double)(T - 1);
   const double fl = floor(pos);
@@ -75,7 +92,7 @@ k_quantile_decide(const float* __restrict__ gate, int T, double q, double abs_th
   const int hi = (int)ceil(pos);
   const double frac = pos - fl;
 
-  const uint32_t klo = radix_select(gate, T, lo, hist, sh);
+  const uint32_t klo = radix_select(gate, T, lo, hist, sh, wtot);
   // the next order statistic: equal to v[lo] if enough keys tie with it,
   // otherwise the smallest key above it
   if (threadIdx.x == 0) {
