@@ -1,25 +1,40 @@
 // bf16 GEMM for the projector MLPs: C[M, N] = act(A[M, K] . W[N, K]^T + bias[N]).
 //
-// 256 x 256 output tile per workgroup, K step 64, 4 wavefronts of 128 x 128
-// (a 4 x 4 grid of v_mfma_f32_32x32x16_bf16 blocks, 256 fp32 accumulators
-// per lane, held in AGPRs).
+// 256 x 256 output tile per workgroup, 4 wavefronts of 128 x 128 (a 4 x 4
+// grid of v_mfma_f32_32x32x16_bf16 blocks, 256 fp32 accumulators per lane,
+// held in AGPRs).  Operand tiles move from HBM/L2 to LDS with gfx950's LDS
+// DMA (global_load_lds_dwordx4): no staging registers, so the VGPRs hold the
+// MFMA fragments.  A DMA instruction writes one contiguous 1 KB block (64
+// lanes x 16 bytes); each lane picks the global 16-byte piece that belongs at
+// its fixed LDS position, which lets the tiles be stored XOR-swizzled, so the
+// fragment reads (ds_read_b128, one row per lane) are free of bank conflicts
+// without padding.
 //
-// Operand tiles move from HBM/L2 to LDS with gfx950's LDS DMA
-// (global_load_lds_dwordx4): no staging registers, so the VGPRs can hold a
-// whole K step of MFMA fragments.  A DMA instruction writes one contiguous
-// 1 KB block (64 lanes x 16 bytes), i.e. 8 tile rows of 128 bytes.  To keep
-// the fragment reads (ds_read_b128, one row per lane) free of bank conflicts
-// without padding, 16-byte chunk c of tile row r is stored at position
-// c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows (and any
-// 16 consecutive rows split by parity) then land in distinct bank groups.
-// Each lane of a DMA picks the global chunk that belongs at its fixed LDS
-// position, so every 8 lanes still read one full 128-byte row of A or W.
+// Two main loops:
+//  * 4-stage (K step 32, 4 x 32 KB): the DMA of step k+3 and the fragment
+//    reads of step k+1 (into a second register buffer) are interleaved with
+//    the 32 MFMAs of step k, one DMA instruction and two reads after every
+//    four MFMAs, so the memory pipeline is fed evenly and three steps of
+//    operands are in flight.  Used for K below 8192.
+//  * 2-stage (K step 64, 2 x 64 KB): full 128-byte rows per DMA request,
+//    which suits very long K; the next step's DMA and the next sub-step's
+//    fragment reads are likewise interleaved with the MFMAs.
+// In both, the compiler must not make an LDS read wait for the DMAs in
+// flight: each stage is a separate __shared__ array (the compiler tracks
+// LDS DMA targets per array), every 4-stage step issues its DMA (past the
+// end it reloads the last K step), and the barriers wait for this wave's LDS
+// operations only (the DMA completion is waited for explicitly).
 //
-// Two LDS stages (2 x 64 KB).  Each K step first reads all of its MFMA
-// fragments from the current stage into registers, then issues the DMA of
-// the next K step into the other stage, then runs its 64 MFMAs, which hide
-// the DMA latency; one barrier per K step.  The finished tile goes out
-// through LDS with 16-byte stores.
+// Epilogue: the 256 x 256 bf16 tile goes through LDS (the four 32 KB stage
+// arrays hold 64 rows each) and out with 16-byte row-contiguous stores;
+// 2-byte stores straight from the accumulator layout reach only a fraction
+// of the write bandwidth.
+//
+// Grid: workgroups are dealt round-robin to the 8 XCDs, so the linear id is
+// regrouped so consecutive tile ids land on one XCD, then tiles are walked in
+// bands of 8 tile-rows so an XCD's L2 sees the same A and W rows many times.
+// Route-first products read their row count from the device (RowMap) and lay
+// the tile grid over the rows present.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,170 +47,54 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 typedef __attribute__((address_space(1))) const char gchar_t;
 
 namespace {
-constexpr int DBM = 256, DBN = 256, DBK = 64;
-constexpr int DNT = 256;
-constexpr int TILE_ELEMS = DBM * DBK;  // one operand tile, bf16 elements (32 KB)
+constexpr int DBM = 256, DBN = 256, DNT = 256;
+constexpr int QB = 32768;  // bytes of one stage array (also one epilogue slab of 64 rows)
 
-IVC_DEV int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt left alone
+#define IVC_GWAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-struct Frags {
-  bf16x8_t a[4], b[4];
-};
-
-// Per-lane LDS byte addresses of one K step's fragments: fragment (i, kk) of
-// A sits at a_off[kk] + i * 4096 (rows i*32 + lane%32 of the wave's 128-row
-// slice), since the swizzle term depends only on lane % 32.
-struct FragAddr {
-  uint32_t a_off[4], b_off[4];
-};
-
-IVC_DEV void read_frags(uint32_t sa, uint32_t sb, const FragAddr& fa, int kk, Frags& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-        (uintptr_t)(sa + fa.a_off[kk] + i * 4096));
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    f.b[j] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-        (uintptr_t)(sb + fa.b_off[kk] + j * 4096));
+// Workgroup barrier waiting only for this wave's LDS operations
+IVC_DEV void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-IVC_DEV void mma(const Frags& f, f32x16_t (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-}
-
-// DMA one K step: the 8 A blocks and 8 W blocks of this wave.  a_base / b_base
-// are the tile's first rows at this K step (uniform); offsets are per lane.
-IVC_DEV void dma_tiles(gchar_t* a_base, gchar_t* b_base, const uint32_t* a_off,
-                       const uint32_t* b_off, bf16_t* sa, bf16_t* sb, int w) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_base + a_off[j]),
-                                     (lds_void_t*)(sa + (w * 8 + j) * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_base + b_off[j]),
-                                     (lds_void_t*)(sb + (w * 8 + j) * 512), 16, 0, 0);
-  }
-}
-}  // namespace
-
-template <int ACT>
-__global__ void __launch_bounds__(DNT, 1)
-k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
-           int a_goff, const bf16_t* __restrict__ W, long long ldw,
-           const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-           int K, RowMap rm) {
-  __shared__ __attribute__((aligned(1024))) bf16_t sA0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB0[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16_t sA1[TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB1[TILE_ELEMS];
-
-  // rows actually present (route-first products size the grid for all
-  // tiles): the tile grid is laid out over those rows only, so the active
-  // workgroups stay spread over all XCDs; the rest leave at once
+// Tile of this workgroup; false if it has none (uniform, before any barrier).
+IVC_DEV bool map_tile(int& M, int N, const RowMap& rm, int& m0, int& n0) {
   if (rm.m_dev != nullptr) M = min(M, *rm.m_dev * rm.m_mult);
   const int tiles_m = (M + DBM - 1) / DBM, tiles_n = (N + DBN - 1) / DBN;
   const int nb = tiles_m * tiles_n;
-  if ((int)blockIdx.x >= nb) return;  // uniform over the workgroup, before any barrier
+  if ((int)blockIdx.x >= nb) return false;
   int bid = blockIdx.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);  // consecutive ids on one XCD
   constexpr int GM = 8;
   const int in_group = GM * tiles_n;
   const int first_m = (bid / in_group) * GM;
   const int gsize = min(tiles_m - first_m, GM);
-  const int pid_m = first_m + (bid % in_group) % gsize;
-  const int pid_n = (bid % in_group) / gsize;
-  const int m0 = pid_m * DBM, n0 = pid_n * DBN;
+  m0 = (first_m + (bid % in_group) % gsize) * DBM;
+  n0 = ((bid % in_group) / gsize) * DBN;
+  return true;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+IVC_DEV long long phys_row(int gm, int a_rpg, long long a_gstride, int a_goff) {
+  return a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : (long long)gm;
+}
 
-  // DMA sources: load j of wave w fills tile rows (w*8 + j)*8 .. +7; lane
-  // takes row + lane/8 and the global chunk that belongs at position lane%8.
-  // Byte offsets are relative to the tile's first row (A rows may be
-  // remapped, so that row's physical index is computed like the others).
-  auto phys_a = [&](int gm) -> long long {
-    return a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : (long long)gm;
-  };
-  const long long a_row0 = phys_a(m0);
-  // global-address-space bases: the DMA then takes a uniform base plus a
-  // 32-bit per-lane offset (one VGPR per load)
-  gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
-  gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
-  uint32_t a_off[8], b_off[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (w * 8 + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    const int gm = min(m0 + r, M - 1);
-    a_off[j] = (uint32_t)(((phys_a(gm) - a_row0) * lda + c * 8) * 2);
-    const int gn = min(n0 + r, N - 1);
-    b_off[j] = (uint32_t)(((long long)(gn - n0) * ldw + c * 8) * 2);
-  }
-  // fragment addresses (bytes within a stage array)
-  FragAddr fa;
+// Writes the 256 x 256 tile (bias, activation, bf16) through LDS slabs
+// q0..q3 (rows 64s .. 64s+63 in slab s, 512 bytes per row) to C.
+// 32x32 accumulator layout: lane l holds column l % 32 and rows
+// 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+template <int ACT>
+IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q2, char* q3,
+                        int wm, int wn, int m0, int n0, int M, int N, const float* bias,
+                        bf16_t* Cm, long long ldc, const RowMap& rm) {
+  const int tid = threadIdx.x, lane = tid & 63;
   {
-    const int rl = lane & 31, half = lane >> 5, sw = swz(rl);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t p = (uint32_t)(((2 * kk + half) ^ sw) * 16);
-      fa.a_off[kk] = (uint32_t)((wm * 128 + rl) * 128) + p;
-      fa.b_off[kk] = (uint32_t)((wn * 128 + rl) * 128) + p;
-    }
-  }
-  const uint32_t la0 = (uint32_t)(uintptr_t)(lds_void_t*)sA0, lb0 = (uint32_t)(uintptr_t)(lds_void_t*)sB0;
-  const uint32_t la1 = (uint32_t)(uintptr_t)(lds_void_t*)sA1, lb1 = (uint32_t)(uintptr_t)(lds_void_t*)sB1;
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int KT = K / DBK;
-  const long long kstep = DBK * 2;  // bytes per K step along a row
-  dma_tiles(a_tile, b_tile, a_off, b_off, sA0, sB0, w);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool odd = kt & 1;
-    const uint32_t la = odd ? la1 : la0, lb = odd ? lb1 : lb0;
-    // all fragments of this K step first ...
-    Frags f[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) read_frags(la, lb, fa, kk, f[kk]);
-    // ... then the DMA of the next step into the other stage, hidden by the MFMAs
-    if (kt + 1 < KT) {
-      const long long ko = (long long)(kt + 1) * kstep;
-      if (odd) dma_tiles(a_tile + ko, b_tile + ko, a_off, b_off, sA0, sB0, w);
-      else dma_tiles(a_tile + ko, b_tile + ko, a_off, b_off, sA1, sB1, w);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) mma(f[kk], acc);
-    // keep the MFMAs above the wait: otherwise they sink below the barrier
-    // and the DMA latency is no longer hidden
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  // Epilogue through LDS: the 256 x 256 bf16 tile (128 KB; rows 64q .. 64q+63
-  // in stage array q of sA0, sB0, sA1, sB1) is written from the accumulators,
-  // then stored with 16-byte row-contiguous writes (2-byte stores straight
-  // from the accumulator layout reach a fraction of the write bandwidth).
-  // 32x32 accumulator layout: lane l holds column l % 32 and rows
-  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  {
-    char* slab_lo = wm ? (char*)sA1 : (char*)sA0;
-    char* slab_hi = wm ? (char*)sB1 : (char*)sB0;
+    char* slab_lo = wm ? q2 : q0;
+    char* slab_hi = wm ? q3 : q1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cl = wn * 128 + j * 32 + (lane & 31);
@@ -206,7 +105,7 @@ k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_g
         char* slab = i < 2 ? slab_lo : slab_hi;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int rl = (i & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);  // row in slab
+          const int rl = (i & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
           float x = acc[i][j][v] + bj;
           if (ACT == ACT_GELU) x = gelu_erf(x);
           *reinterpret_cast<bf16_t*>(slab + rl * 512 + cl * 2) = f32_to_bf16(x);
@@ -218,8 +117,7 @@ k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_g
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int r = it * 8 + (tid >> 5), c = tid & 31;
-    const char* slab = it < 8 ? (const char*)sA0 : it < 16 ? (const char*)sB0
-                     : it < 24 ? (const char*)sA1 : (const char*)sB1;
+    const char* slab = it < 8 ? q0 : it < 16 ? q1 : it < 24 ? q2 : q3;
     const u32x4 val = *reinterpret_cast<const u32x4*>(slab + (r & 63) * 512 + c * 16);
     const int row = m0 + r, col = n0 + 8 * c;
     if (row < M && col < N) {
@@ -230,9 +128,237 @@ k_gemm_dma(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_g
     }
   }
 }
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 4-stage kernel: K step 32.  Stage array s holds A rows at [0, 16 KB) and W
+// rows at [16 KB, 32 KB), 64 bytes per row; 16-byte piece c of row r sits at
+// c ^ ((r >> 2) & 3).
+// ---------------------------------------------------------------------------
+template <int ACT>
+__global__ void __launch_bounds__(DNT, 1)
+k_gemm_dma4(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
+            int a_goff, const bf16_t* __restrict__ W, long long ldw,
+            const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
+            int K, RowMap rm) {
+  constexpr int BK = 32, TB = QB / 2, DPW = 8;
+  __shared__ __attribute__((aligned(1024))) char s0[QB];
+  __shared__ __attribute__((aligned(1024))) char s1[QB];
+  __shared__ __attribute__((aligned(1024))) char s2[QB];
+  __shared__ __attribute__((aligned(1024))) char s3[QB];
+  int m0, n0;
+  if (!map_tile(M, N, rm, m0, n0)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+
+  // DMA j (0..3) of wave w fills rows (4w + j)*16 .. +15; lane: row + lane/4,
+  // LDS piece lane%4 holding global piece (lane%4) ^ swz(row)
+  const long long a_row0 = phys_row(m0, a_rpg, a_gstride, a_goff);
+  gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
+  gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (w * 4 + j) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    a_off[j] = (uint32_t)(((phys_row(min(m0 + r, M - 1), a_rpg, a_gstride, a_goff) - a_row0) * lda +
+                           c * 8) * 2);
+    b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
+  }
+  auto dma_one = [&](int q, long long ko, char* st) {  // q = 0..7: A block q/2 (even), W (odd)
+    const int j = q >> 1;
+    if ((q & 1) == 0)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ko + a_off[j]),
+                                       (lds_void_t*)(st + (w * 4 + j) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + ko + b_off[j]),
+                                       (lds_void_t*)(st + TB + (w * 4 + j) * 1024), 16, 0, 0);
+  };
+  auto dma = [&](int kt, char* st) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma_one(q, (long long)kt * (BK * 2), st);
+  };
+  // fragment (i, kk) of A at fa[kk] + i * 2048 within a stage (rows i*32 + lane%32)
+  uint32_t fa[2], fb[2];
+  {
+    const int rl = lane & 31, sw = (rl >> 2) & 3;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t p = (uint32_t)(((2 * kk + (lane >> 5)) ^ sw) * 16);
+      fa[kk] = (uint32_t)((wm * 128 + rl) * 64) + p;
+      fb[kk] = (uint32_t)(TB + (wn * 128 + rl) * 64) + p;
+    }
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = K / BK;  // a multiple of 4
+  dma(0, s0);
+  dma(min(1, KT - 1), s1);
+  dma(min(2, KT - 1), s2);
+  bf16x8_t fa0[2][4], fb0[2][4], fa1[2][4], fb1[2][4];
+#define IVC_DMA4_READ(ST, FA, FB)                                                           \
+  do {                                                                                      \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
+        FA[kk][i] = *reinterpret_cast<const bf16x8_t*>((ST) + fa[kk] + i * 2048);           \
+        FB[kk][i] = *reinterpret_cast<const bf16x8_t*>((ST) + fb[kk] + i * 2048);           \
+      }                                                                                     \
+    }                                                                                       \
+  } while (0)
+  // Iteration k: wait for step k+1's DMA, barrier, then step k's 32 MFMAs
+  // with, after every 4, one DMA instruction of step k+3 (into the stage read
+  // two iterations ago) and two fragment reads of step k+1.
+#define IVC_DMA4_ITER(K_, FAC, FBC, FAN, FBN, STN, STD)                                     \
+  do {                                                                                      \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                \
+    IVC_GWAIT_VM(DPW);                                                                      \
+    lds_barrier();                                                                          \
+    const long long ko_ = (long long)min((K_) + 3, KT - 1) * (BK * 2);                      \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                        \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] =                             \
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FAC[kk][i], FBC[kk][j], acc[i][j], 0, 0, 0); \
+      dma_one(kk * 4 + i, ko_, STD);                                                        \
+      FAN[kk][i] = *reinterpret_cast<const bf16x8_t*>((STN) + fa[kk] + i * 2048);           \
+      FBN[kk][i] = *reinterpret_cast<const bf16x8_t*>((STN) + fb[kk] + i * 2048);           \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+    }                                                                                       \
+  } while (0)
+  IVC_GWAIT_VM(2 * DPW);
+  lds_barrier();
+  IVC_DMA4_READ(s0, fa0, fb0);
+  for (int k = 0; k < KT; k += 4) {
+    IVC_DMA4_ITER(k, fa0, fb0, fa1, fb1, s1, s3);
+    IVC_DMA4_ITER(k + 1, fa1, fb1, fa0, fb0, s2, s0);
+    IVC_DMA4_ITER(k + 2, fa0, fb0, fa1, fb1, s3, s1);
+    IVC_DMA4_ITER(k + 3, fa1, fb1, fa0, fb0, s0, s2);
+  }
+#undef IVC_DMA4_ITER
+#undef IVC_DMA4_READ
+  IVC_GWAIT_VM(0);  // no DMA may land after the stages are reused
+  __syncthreads();
+  store_tile<ACT>(acc, s0, s1, s2, s3, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm);
+}
+
+// ---------------------------------------------------------------------------
+// 2-stage kernel: K step 64.  sA*/sB* hold 256 rows of 128 bytes; 16-byte
+// piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// ---------------------------------------------------------------------------
+template <int ACT>
+__global__ void __launch_bounds__(DNT, 1)
+k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
+            int a_goff, const bf16_t* __restrict__ W, long long ldw,
+            const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
+            int K, RowMap rm) {
+  constexpr int BK = 64;
+  __shared__ __attribute__((aligned(1024))) char sA0[QB];
+  __shared__ __attribute__((aligned(1024))) char sB0[QB];
+  __shared__ __attribute__((aligned(1024))) char sA1[QB];
+  __shared__ __attribute__((aligned(1024))) char sB1[QB];
+  int m0, n0;
+  if (!map_tile(M, N, rm, m0, n0)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+
+  // DMA j (0..7) of wave w fills rows (8w + j)*8 .. +7; lane: row + lane/8,
+  // LDS piece lane%8 holding global piece (lane%8) ^ f(row)
+  const long long a_row0 = phys_row(m0, a_rpg, a_gstride, a_goff);
+  gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
+  gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
+  uint32_t a_off[8], b_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (w * 8 + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
+    a_off[j] = (uint32_t)(((phys_row(min(m0 + r, M - 1), a_rpg, a_gstride, a_goff) - a_row0) * lda +
+                           c * 8) * 2);
+    b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
+  }
+  auto dma_one = [&](int q, long long ko, char* sa, char* sb) {  // q = 0..15
+    const int j = q >> 1;
+    if ((q & 1) == 0)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ko + a_off[j]),
+                                       (lds_void_t*)(sa + (w * 8 + j) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + ko + b_off[j]),
+                                       (lds_void_t*)(sb + (w * 8 + j) * 1024), 16, 0, 0);
+  };
+  // fragment (i, kk) of A at fa[kk] + i * 4096 within sA (rows i*32 + lane%32)
+  uint32_t fa[4], fb[4];
+  {
+    const int rl = lane & 31, sw = (rl & 7) ^ ((rl >> 3) & 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t p = (uint32_t)(((2 * kk + (lane >> 5)) ^ sw) * 16);
+      fa[kk] = (uint32_t)((wm * 128 + rl) * 128) + p;
+      fb[kk] = (uint32_t)((wn * 128 + rl) * 128) + p;
+    }
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = K / BK;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) dma_one(q, 0, sA0, sB0);
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool odd = kt & 1;
+    const char* sa = odd ? sA1 : sA0;
+    const char* sb = odd ? sB1 : sB0;
+    char* na = odd ? sA0 : sA1;
+    char* nb = odd ? sB0 : sB1;
+    const bool more = kt + 1 < KT;
+    const long long ko = (long long)(kt + 1) * (BK * 2);
+    // this step's tiles have landed and every wave is done with the other
+    // stage: barrier, then the next step's DMA spread over the MFMAs
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    bf16x8_t f[2][2][4];  // [buffer][A / W][block]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[0][0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[0] + i * 4096);
+      f[0][1][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[0] + i * 4096);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cb = kk & 1, nbuf = cb ^ 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (more) dma_one(kk * 4 + i, ko, na, nb);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[cb][0][i], f[cb][1][j], acc[i][j],
+                                                              0, 0, 0);
+        if (kk < 3) {
+          f[nbuf][0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[kk + 1] + i * 4096);
+          f[nbuf][1][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[kk + 1] + i * 4096);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  store_tile<ACT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm);
+}
 
 bool gemm_dma_supported(const GemmArgs& g) {
-  return g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % DBK == 0 &&
+  return g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % 64 == 0 &&
          g.K > 0 && g.M > 0 && g.N > 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
          ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.W % 16) == 0 && g.N % 8 == 0 &&
          g.ldc % 8 == 0 && ((uintptr_t)g.Cm % 16) == 0;
@@ -241,14 +367,19 @@ bool gemm_dma_supported(const GemmArgs& g) {
 hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
   if (!gemm_dma_supported(g)) return hipErrorInvalidValue;
   const int tiles = ((g.M + DBM - 1) / DBM) * ((g.N + DBN - 1) / DBN);
-  if (g.act == ACT_GELU)
-    hipLaunchKernelGGL(k_gemm_dma<ACT_GELU>, dim3((unsigned)tiles), dim3(DNT), 0, s,
-                       (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
-                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm);
-  else
-    hipLaunchKernelGGL(k_gemm_dma<ACT_NONE>, dim3((unsigned)tiles), dim3(DNT), 0, s,
-                       (const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff,
-                       (const bf16_t*)g.W, g.ldw, g.bias, (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm);
+  const bool four = g.K % 128 == 0 && g.K < 8192;
+#define IVC_DMA_LAUNCH(KERN)                                                                  \
+  hipLaunchKernelGGL(KERN, dim3((unsigned)tiles), dim3(DNT), 0, s, (const bf16_t*)g.A, g.lda, \
+                     g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw, g.bias,       \
+                     (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm)
+  if (four) {
+    if (g.act == ACT_GELU) IVC_DMA_LAUNCH(k_gemm_dma4<ACT_GELU>);
+    else IVC_DMA_LAUNCH(k_gemm_dma4<ACT_NONE>);
+  } else {
+    if (g.act == ACT_GELU) IVC_DMA_LAUNCH(k_gemm_dma2<ACT_GELU>);
+    else IVC_DMA_LAUNCH(k_gemm_dma2<ACT_NONE>);
+  }
+#undef IVC_DMA_LAUNCH
   return hipGetLastError();
 }
 
