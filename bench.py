@@ -61,6 +61,42 @@ def hbm_bytes(cfg: dict, L_seq: int, Lp: int) -> dict:
     }
 
 
+# source file of each timed kernel name (the committed traffic figures of a
+# kernel are valid only for the source they were measured on)
+KERNEL_SOURCE = {
+    "mlp1_gemm1": "k_gemm_dma.hip", "mlp1_gemm2": "k_gemm_dma.hip",
+    "mlp2_gemm1": "k_gemm_dma.hip", "mlp2_gemm2": "k_gemm_dma.hip",
+    "mlp2_gemm3": "k_gemm_dma.hip", "pool_folded": "k_pool_folded.hip",
+    "shuffle_ln": "k_loader.hip", "compact": "k_compact.hip",
+}
+
+
+def committed_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from its committed rocprofv3 counter
+    summary (profiles/traffic_<kernel>_<workload>.md: FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's counter reading), or None when there is none or
+    the kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{WORKLOAD}.md")
+    src = KERNEL_SOURCE.get(kernel)
+    if src is None or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    with open(os.path.join(ROOT, "vlm_visual_token_amd", "csrc", src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("source_sha256") != sha:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, w, seq, n_tiles: int) -> dict:
     """The CPU oracle as it stands, on a bounded sample: the per-tile steps
     (connector run + router pooling and gating) on ``n_tiles`` tiles, plus
@@ -110,7 +146,14 @@ def main():
                          "both: run mlp1 and mlp2 on every tile, as the pages do")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tiles", type=int, default=32)
-    ap.add_argument("--kernel-events", choices=["timed", "separate"], default="timed")
+    ap.add_argument("--kernel-events", choices=["timed", "separate"], default="separate",
+                    help="separate: the timed region runs without per-kernel events (the two "
+                         "projector chains overlap on two streams) and a second pass of the same "
+                         "steps records them (chains serialised, each kernel timed alone); "
+                         "timed: events inside the timed region")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run 4 device-to-device copies of 512 MiB (calibration "
+                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -180,11 +223,11 @@ def main():
     print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
     if args.kernel_events == "timed":
         ms, prof = timed(True)
-        ms_plain = None
+        ms_ev = None
     else:
         ms, _ = timed(False)
-        ms_plain = ms
-        _, prof = timed(True)
+        print(f"# per-kernel event pass ({args.steps} steps)", file=sys.stderr, flush=True)
+        ms_ev, prof = timed(True)
     ms_step = ms / args.steps
     use64 = rbuf["use64"].cpu().numpy()
     Lp = int(cbuf["len"].item())
@@ -223,6 +266,16 @@ def main():
         if k in hbm:
             v["gbs"] = hbm[k] / (v["ms_avg"] / 1e3) / 1e9
 
+    roof["traffic"] = committed_traffic(dom)
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"# cpu baseline ({args.cpu_tiles} tiles)", file=sys.stderr, flush=True)
@@ -252,10 +305,12 @@ def main():
         "compacted_len": Lp,
         "roofline": roof,
         "kernels": kern,
+        "kernel_events": ("separate pass, projector chains serialised"
+                          if args.kernel_events == "separate" else "inside the timed region"),
         "cpu_baseline": cpu,
     }
-    if ms_plain is not None:
-        out["ms_per_step_without_kernel_events"] = ms_plain / args.steps
+    if ms_ev is not None:
+        out["ms_per_step_event_pass"] = ms_ev / args.steps
     print(json.dumps(out))
 
 

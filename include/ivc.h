@@ -249,6 +249,8 @@ ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t T, int32_t 
 /* Per-kernel timing for measurement: when enabled, the library records a
  * hipEvent pair around each kernel it launches on the call's stream and
  * accumulates the elapsed time per kernel name after the events complete.
+ * While enabled, run and run_routed keep both projector chains on the call's
+ * stream (no fork), so each kernel is timed alone.
  * ivc_profile_read synchronises the recorded events, then returns up to
  * `cap` entries (name, total ms, launches).  Not thread-safe; off by default. */
 void ivc_profile_enable(int on);

@@ -13,6 +13,7 @@
 #include "../../include/ivc.h"
 #include "kernels.h"
 
+
 using namespace ivc;
 
 // ---------------------------------------------------------------------------
@@ -652,7 +653,9 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   // workgroups of one chain's products share the chip with the other's
   // instead of leaving compute units idle.  (bf16 only: the fp32 products
   // share one SIMT scratch buffer.)
-  const bool fork = c.flash && h->aux != nullptr;
+  // (While per-kernel timing is on, both chains stay on the caller's stream so
+  // each kernel's events time it alone.)
+  const bool fork = c.flash && h->aux != nullptr && !g_prof_on;
   hipStream_t s1 = s;
   if (fork) {
     HIP_OK(hipEventRecord(h->ev_fork, s));
