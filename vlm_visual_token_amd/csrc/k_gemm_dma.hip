@@ -17,8 +17,9 @@
 //    four MFMAs, so the memory pipeline is fed evenly and three steps of
 //    operands are in flight.  Used for K below 8192.
 //  * 2-stage (K step 64, 2 x 64 KB): full 128-byte rows per DMA request,
-//    which suits very long K; the next step's DMA and the next sub-step's
-//    fragment reads are likewise interleaved with the MFMAs.
+//    which suits very long K; the next step's DMA goes out over the first
+//    half of the step's MFMAs and the next sub-step's fragment reads are
+//    interleaved with them.
 // In both, the compiler must not make an LDS read wait for the DMAs in
 // flight: each stage is a separate __shared__ array (the compiler tracks
 // LDS DMA targets per array), every 4-stage step issues its DMA (past the
@@ -41,6 +42,8 @@
 namespace ivc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
@@ -83,47 +86,80 @@ IVC_DEV long long phys_row(int gm, int a_rpg, long long a_gstride, int a_goff) {
   return a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : (long long)gm;
 }
 
+// Byte XOR applied to a column offset in row r of an epilogue slab: one
+// 4-byte write instruction covers rows R, R+1, R+4, R+5 and 64 bytes of
+// columns, which this spreads over all 64 LDS banks (a permutation of the
+// 16-byte pieces within the row, so the 16-byte reads stay conflict-free).
+IVC_DEV int slab_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 6; }
+
 // Writes the 256 x 256 tile (bias, activation, bf16) through LDS slabs
 // q0..q3 (rows 64s .. 64s+63 in slab s, 512 bytes per row) to C.
 // 32x32 accumulator layout: lane l holds column l % 32 and rows
-// 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+// 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.  Values v, v+1 (rows R, R+1) are
+// converted together (v_cvt_pk_bf16_f32) and traded with the neighbouring
+// lane (column c ^ 1), so the even lane writes row R, columns c, c+1 and the
+// odd lane row R+1, columns c-1, c: one 4-byte LDS write per two values.
 template <int ACT>
 IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q2, char* q3,
                         int wm, int wn, int m0, int n0, int M, int N, const float* bias,
                         bf16_t* Cm, long long ldc, const RowMap& rm) {
   const int tid = threadIdx.x, lane = tid & 63;
+  const bool odd_lane = lane & 1;
+  // v_perm_b32 selectors: even lane keeps its low half and takes the
+  // neighbour's low half; odd lane takes the neighbour's high half and keeps
+  // its own high half
+  const uint32_t sel = odd_lane ? 0x07060302u : 0x05040100u;
   {
     char* slab_lo = wm ? q2 : q0;
     char* slab_hi = wm ? q3 : q1;
+    float bcol[4];  // all four loads in flight together
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      bcol[j] = (bias != nullptr && col < N) ? bias[col] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cl = wn * 128 + j * 32 + (lane & 31);
-      const int col = n0 + cl;
-      const float bj = (bias != nullptr && col < N) ? bias[col] : 0.f;
+      const float bj = bcol[j];
+      const int cw = cl & ~1;  // column of the pair this lane writes
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         char* slab = i < 2 ? slab_lo : slab_hi;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rl = (i & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          float x = acc[i][j][v] + bj;
-          if (ACT == ACT_GELU) x = gelu_erf(x);
-          *reinterpret_cast<bf16_t*>(slab + rl * 512 + cl * 2) = f32_to_bf16(x);
+        for (int v = 0; v < 16; v += 2) {
+          float x0 = acc[i][j][v] + bj, x1 = acc[i][j][v + 1] + bj;
+          if (ACT == ACT_GELU) {
+            x0 = gelu_erf(x0);
+            x1 = gelu_erf(x1);
+          }
+          const uint32_t own = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));  // rows R, R+1
+          const uint32_t nbr = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+          const uint32_t pair = __builtin_amdgcn_perm(odd_lane ? own : nbr, odd_lane ? nbr : own, sel);
+          const int rl = (i & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3) + (odd_lane ? 1 : 0);
+          *reinterpret_cast<uint32_t*>(slab + rl * 512 + ((cw * 2) ^ slab_swz(rl))) = pair;
         }
       }
     }
   }
   __syncthreads();
+  // output row of tile row r (route-first products scatter groups of c_rpg rows)
+  const bool pow2 = rm.c_map != nullptr && (rm.c_rpg & (rm.c_rpg - 1)) == 0;
+  const int sh = pow2 ? __builtin_ctz((unsigned)rm.c_rpg) : 0;
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
     const int r = it * 8 + (tid >> 5), c = tid & 31;
     const char* slab = it < 8 ? q0 : it < 16 ? q1 : it < 24 ? q2 : q3;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(slab + (r & 63) * 512 + c * 16);
+    const u32x4 val =
+        *reinterpret_cast<const u32x4*>(slab + (r & 63) * 512 + ((c * 16) ^ slab_swz(r & 63)));
     const int row = m0 + r, col = n0 + 8 * c;
     if (row < M && col < N) {
-      const long long orow =
-          rm.c_map != nullptr ? (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg
-                              : row;
+      long long orow = row;
+      if (pow2)
+        orow = ((long long)rm.c_map[row >> sh] << sh) + (row & (rm.c_rpg - 1));
+      else if (rm.c_map != nullptr)
+        orow = (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg;
       *reinterpret_cast<u32x4*>(Cm + orow * ldc + col) = val;
     }
   }
@@ -339,11 +375,15 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
       const int cb = kk & 1, nbuf = cb ^ 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (more) dma_one(kk * 4 + i, ko, na, nb);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+          // the next step's 16 DMA instructions go out over the first half of
+          // the step: late enough not to stall the MFMA issue on the address
+          // unit, early enough to land before the step ends
+          if (more && kk < 2 && (j & 1) == 0) dma_one(kk * 8 + i * 2 + (j >> 1), ko, na, nb);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[cb][0][i], f[cb][1][j], acc[i][j],
                                                               0, 0, 0);
+        }
         if (kk < 3) {
           f[nbuf][0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[kk + 1] + i * 4096);
           f[nbuf][1][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[kk + 1] + i * 4096);
