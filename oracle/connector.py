@@ -66,7 +66,7 @@ def token_grid(x, P: int, has_cls: int) -> np.ndarray:
     return x[:, has_cls:, :].reshape(T, P, P, C)
 
 
-def pixel_shuffle(G, r: int) -> np.ndarray:
+def pixel_shuffle(G, r: int, version: int = 2) -> np.ndarray:
     """Space-to-depth by r, written as explicit index math:
 
         out[a*(P/r) + b, (r*m + k)*C + c] = G[r*a + m, r*b + k, c]
@@ -76,18 +76,51 @@ def pixel_shuffle(G, r: int) -> np.ndarray:
     grid axis, then the other; v2 swaps the axes back so the grid is not
     transposed.  r = 2 is downsample ratio 0.5 (256 tokens of 4C); r = 4 is
     ratio 0.25 (64 tokens of 16C, [2B-Flash] three token levels).
+
+    version = 1 is the older ps_version of the same page (section on v1 and
+    v2): the axes are not swapped back, so the output token grid is the
+    transpose of v2's; channels are unchanged:
+
+        out_v1[b*(P/r) + a] = out_v2[a*(P/r) + b]
     """
     T, P, P2, C = G.shape
-    assert P == P2 and P % r == 0
+    assert P == P2 and P % r == 0 and version in (1, 2)
     Q = P // r
     out = np.empty((T, Q * Q, r * r * C), dtype=G.dtype)
     for a in range(Q):
         for b in range(Q):
+            tok = a * Q + b if version == 2 else b * Q + a
             for m in range(r):
                 for k in range(r):
                     blk = r * m + k
-                    out[:, a * Q + b, blk * C:(blk + 1) * C] = G[:, r * a + m, r * b + k, :]
+                    out[:, tok, blk * C:(blk + 1) * C] = G[:, r * a + m, r * b + k, :]
     return out
+
+
+SHUFFLE64_ORDERS = ("direct", "twice_r2")
+
+
+def shuffle64(G, order: str = "direct", version: int = 2) -> np.ndarray:
+    """The 64-token path's input, [T, (P/4)^2, 16C].
+
+    [2B-Flash] three token levels: scale 0.25 = 0.5 squared, described as
+    equivalent to two pixel_shuffles.  Both readings gather the same 4 x 4
+    cells into a token and differ only in channel order:
+
+    * "direct": pixel_shuffle(G, 4), the r = 4 formula
+      (channel block 4*M + K for cell (M, K) of the 4 x 4 block);
+    * "twice_r2": the r = 2 shuffle applied to the 16 x 16 grid of 4C
+      tokens that the first r = 2 shuffle makes (channel block
+      4*(2*m2 + k2) + (2*m + k) for cell (2*m2 + m, 2*k2 + k)).
+
+    version = 1 transposes the resulting token grid, as for pixel_shuffle.
+    """
+    assert order in SHUFFLE64_ORDERS
+    T, P, _, C = G.shape
+    if order == "direct":
+        return pixel_shuffle(G, 4, version)
+    Y2 = pixel_shuffle(G, 2).reshape(T, P // 2, P // 2, 4 * C)
+    return pixel_shuffle(Y2, 2, version)
 
 
 # ---------------------------------------------------------------------------
@@ -133,12 +166,23 @@ def mlp2(Y, w: dict, eps: float) -> np.ndarray:
     return linear(h, w["mlp2.l3.w"], w["mlp2.l3.b"])
 
 
+def shuffled(x, cfg: dict, r: int) -> np.ndarray:
+    """The projector input of one path, [T, (P/r)^2, r^2 C]: pixel_shuffle
+    (r = 2) or the 64-token shuffle (r = 4) of the token grid, with the
+    config's ps_version (default 2) and 64-path channel order (default
+    "direct")."""
+    G = token_grid(x, cfg["P"], cfg["has_cls"])
+    version = cfg.get("ps_version", 2)
+    if r == 2:
+        return pixel_shuffle(G, 2, version)
+    return shuffle64(G, cfg.get("shuffle64_order", "direct"), version)
+
+
 def shuffled_ln_rows(x, cfg: dict, w: dict, r: int) -> np.ndarray:
     """The LayerNorm'd pixel-shuffled rows (the first projector's input after
     its LayerNorm), [T, (P/r)^2, r^2 C]."""
-    Y = pixel_shuffle(token_grid(x, cfg["P"], cfg["has_cls"]), r)
     key = "mlp1.ln" if r == 2 else "mlp2.ln"
-    return layer_norm(Y, w[key + ".w"], w[key + ".b"], cfg["ln_eps"])
+    return layer_norm(shuffled(x, cfg, r), w[key + ".w"], w[key + ".b"], cfg["ln_eps"])
 
 
 def connector_run(x, cfg: dict, w: dict):
@@ -146,11 +190,10 @@ def connector_run(x, cfg: dict, w: dict):
     extract_feature_flash ([2B-Flash] dual pipeline, step 2):
 
         out256 = mlp1(pixel_shuffle(grid(x), 2))      [T, 256, D]
-        out64  = mlp2(pixel_shuffle(grid(x), 4))      [T, 64, D]  (Flash only)
+        out64  = mlp2(shuffle64(grid(x)))             [T, 64, D]  (Flash only)
     """
-    G = token_grid(x, cfg["P"], cfg["has_cls"])
-    out256 = mlp1(pixel_shuffle(G, 2), w, cfg["ln_eps"])
-    out64 = mlp2(pixel_shuffle(G, 4), w, cfg["ln_eps"]) if cfg["flash"] else None
+    out256 = mlp1(shuffled(x, cfg, 2), w, cfg["ln_eps"])
+    out64 = mlp2(shuffled(x, cfg, 4), w, cfg["ln_eps"]) if cfg["flash"] else None
     return out256, out64
 
 

@@ -20,9 +20,10 @@ def _grid_ids(T, P, C):
 @pytest.mark.parametrize("P", [4, 8, 32])
 @pytest.mark.parametrize("C", [1, 3, 8])
 @pytest.mark.parametrize("r", [2, 4])
-def test_bijection(P, C, r):
+@pytest.mark.parametrize("version", [1, 2])
+def test_bijection(P, C, r, version):
     G = _grid_ids(2, P, C)
-    Y = O.pixel_shuffle(G, r)
+    Y = O.pixel_shuffle(G, r, version)
     assert Y.shape == (2, (P // r) ** 2, r * r * C)
     assert np.array_equal(np.sort(Y.ravel()), G.ravel())
 
@@ -113,9 +114,9 @@ def test_token_levels(golden):
 
 
 def test_r4_differs_from_twice_r2_only_by_channel_order():
-    # Reading recorded in the design doc: the 64-token path uses the direct r=4
-    # formula.  Two successive r=2 shuffles gather the same 16 cells into each
-    # token, in a different channel order.
+    # The 64-token path's default is the direct r=4 formula.  Two successive
+    # r=2 shuffles gather the same 16 cells into each token, in a different
+    # channel order.
     P, C = 8, 2
     G = _grid_ids(1, P, C)
     direct = O.pixel_shuffle(G, 4)
@@ -123,3 +124,55 @@ def test_r4_differs_from_twice_r2_only_by_channel_order():
     assert direct.shape == twice.shape
     assert np.array_equal(np.sort(direct, axis=-1), np.sort(twice, axis=-1))
     assert not np.array_equal(direct, twice)
+
+
+def _torch_unshuffle(G, r):
+    """torch's pixel_unshuffle with channels reordered to the connector's
+    (m, k, c) order, as [T, P/r, P/r, r*r*C] (spatial axes a, b)."""
+    T, P, _, C = G.shape
+    Q = P // r
+    pu = torch.nn.functional.pixel_unshuffle(torch.from_numpy(G).permute(0, 3, 1, 2), r)
+    return pu.reshape(T, C, r, r, Q, Q).permute(0, 4, 5, 2, 3, 1).reshape(T, Q, Q, r * r * C).numpy()
+
+
+@pytest.mark.parametrize("P,C,r", [(8, 5, 2), (8, 3, 4), (32, 4, 2), (32, 2, 4)])
+def test_v1_is_transposed_token_grid(P, C, r):
+    # 14B page, v1/v2 section: v1 does not swap the two spatial axes back, so
+    # its output grid is the transpose of v2's (token (a, b) lands at b, a),
+    # channels unchanged.  Checked against torch's space-to-depth.
+    rng = np.random.default_rng(2)
+    G = rng.standard_normal((2, P, P, C))
+    Q = P // r
+    want = _torch_unshuffle(G, r).transpose(0, 2, 1, 3).reshape(2, Q * Q, r * r * C)
+    assert np.array_equal(O.pixel_shuffle(G, r, 1), want)
+    assert not np.array_equal(O.pixel_shuffle(G, r, 1), O.pixel_shuffle(G, r, 2))
+
+
+def test_shuffle64_orders_worked_example():
+    # P = 4, C = 1, cell (i, j) holds 10*i + j; the single 64-path token of
+    # the tile, channel by channel.  direct: the 4 x 4 block row by row.
+    # twice_r2: the r = 2 shuffle (2 x 2 cells in the order (0,0), (0,1),
+    # (1,0), (1,1)) applied to 2 x 2 blocks taken in that same order.
+    G = np.array([[10.0 * i + j for j in range(4)] for i in range(4)]).reshape(1, 4, 4, 1)
+    direct = [0, 1, 2, 3, 10, 11, 12, 13, 20, 21, 22, 23, 30, 31, 32, 33]
+    twice = [0, 1, 10, 11, 2, 3, 12, 13, 20, 21, 30, 31, 22, 23, 32, 33]
+    assert O.shuffle64(G, "direct")[0, 0].tolist() == direct
+    assert O.shuffle64(G, "twice_r2")[0, 0].tolist() == twice
+    for v in (1, 2):  # one token: the transpose changes nothing
+        assert O.shuffle64(G, "twice_r2", v)[0, 0].tolist() == twice
+
+
+@pytest.mark.parametrize("P,C", [(8, 3), (32, 2)])
+@pytest.mark.parametrize("version", [1, 2])
+def test_shuffle64_twice_matches_torch_twice(P, C, version):
+    rng = np.random.default_rng(3)
+    G = rng.standard_normal((2, P, P, C))
+    Q = P // 4
+    twice = _torch_unshuffle(_torch_unshuffle(G, 2), 2)
+    if version == 1:
+        twice = twice.transpose(0, 2, 1, 3)
+    assert np.array_equal(O.shuffle64(G, "twice_r2", version), twice.reshape(2, Q * Q, 16 * C))
+    direct = _torch_unshuffle(G, 4)
+    if version == 1:
+        direct = direct.transpose(0, 2, 1, 3)
+    assert np.array_equal(O.shuffle64(G, "direct", version), direct.reshape(2, Q * Q, 16 * C))
