@@ -157,7 +157,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(the connector's multi-GPU sharding is described in DESIGN.md, not built).",
+              f"(tiles are independent, so several GPUs would each run a whole-image tile range; "
+              f"that sharding is not built).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -73,6 +73,14 @@ typedef enum { IVC_F32 = 0, IVC_BF16 = 1 } ivc_dtype;
  * the tile's tokens are read once per layer and no K/V tensor exists. */
 typedef enum { IVC_POOL_KV = 0, IVC_POOL_FOLDED = 1 } ivc_pool_mode;
 
+/* Channel order of the 64-token path's 16C rows.  [2B-Flash] describes the
+ * scale 0.25 shuffle as equivalent to two 0.5 shuffles; both orders gather
+ * the same 4 x 4 cells into a token.  DIRECT is pixel_shuffle with r = 4:
+ * cell (M, K) of the block goes to channel block 4*M + K.  TWICE_R2 applies
+ * the r = 2 shuffle to the 16 x 16 grid of 4C tokens: cell
+ * (2*m2 + m, 2*k2 + k) goes to channel block 4*(2*m2 + k2) + (2*m + k). */
+typedef enum { IVC_SHUFFLE64_DIRECT = 0, IVC_SHUFFLE64_TWICE_R2 = 1 } ivc_shuffle64_order;
+
 /* Device status codes written by run/route/compact/ivc_tile_offsets. */
 #define IVC_DEV_OK 0
 #define IVC_DEV_ERR_IMG_COUNT 1    /* IMG_CONTEXT slots != T * (P/2)^2          */
@@ -96,7 +104,10 @@ typedef struct ivc_config {
   int32_t gate_hidden;    /* gating width; must equal C (the pooled vector's width)  */
   int32_t gate_expansion; /* inner width of a gating block = gate_hidden * this      */
   int32_t pool_mode;      /* ivc_pool_mode                                          */
-  int32_t reserved;
+  int32_t ps_version;     /* pixel_shuffle version: 2 (or 0) = v2; 1 = v1, whose
+                             token grid is transposed ([14B] v1/v2 section)     */
+  int32_t shuffle64_order;/* ivc_shuffle64_order: channel order of the 64-token path */
+  int32_t reserved;       /* 0                                                      */
   double rel_quantile;    /* relative threshold, a quantile level (0.1)             */
   double abs_threshold;   /* absolute threshold on gate[:, 0] (0.5)                 */
   float ln_eps;           /* LayerNorm epsilon (1e-5, torch's default)              */
@@ -238,13 +249,16 @@ ivc_status ivc_route_decide(const float* gate, int32_t T, double rel_quantile,
 ivc_status ivc_tile_offsets(const int32_t* tiles_per_image, int32_t B, int32_t* offsets,
                             int32_t* dev_status, void* stream);
 
-/* Stand-alone pixel_shuffle v2 ([14B] pixel_shuffle section), a pure
+/* Stand-alone pixel_shuffle ([14B] pixel_shuffle section), a pure
  * permutation with no normalisation:
  *   vit [T, has_cls + P*P, C] (element type dtype) -> out [T, (P/r)^2, r*r*C],
- *   out[t][a*(P/r)+b][(r*m+k)*C + c] = vit[t][has_cls + (r*a+m)*P + r*b+k][c].
- * r = 2 or 4. */
+ *   v2: out[t][a*(P/r)+b][(r*m+k)*C + c] = vit[t][has_cls + (r*a+m)*P + r*b+k][c];
+ *   v1 (ps_version = 1): the same row lands at token b*(P/r) + a.
+ * r = 2 or 4; for r = 4, shuffle64_order selects the channel order
+ * (ivc_shuffle64_order).  ps_version 0 means 2. */
 ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t T, int32_t P, int32_t C,
-                             int32_t has_cls, int32_t r, void* out, void* stream);
+                             int32_t has_cls, int32_t r, int32_t ps_version,
+                             int32_t shuffle64_order, void* out, void* stream);
 
 /* Per-kernel timing for measurement: when enabled, the library records a
  * hipEvent pair around each kernel it launches on the call's stream and

@@ -63,6 +63,7 @@ def _cfg(**kw):
     (dict(pool_heads=3), 1),
     (dict(C=62), 3),
     (dict(pool_layers=9), 1),
+    (dict(ps_version=3), 1),
 ])
 def test_create_rejects_bad_config_on_host(bad, status):
     c = ivc.make_config(_cfg(**bad))
@@ -70,6 +71,14 @@ def test_create_rejects_bad_config_on_host(bad, status):
     with pytest.raises(ivc.IvcError) as e:
         ivc.ivc_connector_create(c, w, 0)
     assert e.value.status == status
+
+
+def test_create_rejects_bad_shuffle64_order_on_host():
+    c = ivc.make_config(_cfg())
+    c.shuffle64_order = 2
+    with pytest.raises(ivc.IvcError) as e:
+        ivc.ivc_connector_create(c, ivc.ivc_weights(), 0)
+    assert e.value.status == 1
 
 
 def test_create_rejects_missing_weights_on_host():
@@ -87,6 +96,10 @@ def test_entry_points_reject_bad_arguments_on_host():
         ivc.ivc_pixel_shuffle(7, None, 1, 8, 64, 1, 2, None, 0)
     with pytest.raises(ivc.IvcError):
         ivc.ivc_pixel_shuffle(0, None, 1, 8, 64, 1, 3, None, 0)
+    with pytest.raises(ivc.IvcError):
+        ivc.ivc_pixel_shuffle(0, None, 1, 8, 64, 1, 2, None, 0, ps_version=3)
+    with pytest.raises(ivc.IvcError):
+        ivc.ivc_pixel_shuffle(0, None, 1, 8, 64, 1, 4, None, 0, shuffle64_order=2)
     with pytest.raises(ivc.IvcError) as e:
         ivc.ivc_pixel_shuffle(1, 18, 1, 8, 64, 1, 2, 34, 0)  # pointers not 16-byte aligned
     assert e.value.status == 3

@@ -59,6 +59,27 @@ def test_pixel_shuffle_bit_exact(dtype, P, C, T, has_cls, r):
     assert np.array_equal(got.view(np.uint32), exp.astype(np.float32).view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype,P,C,T,has_cls", [("f32", 8, 4, 5, 1), ("bf16", 32, 1024, 2, 1),
+                                                  ("bf16", 16, 8, 3, 0)])
+@pytest.mark.parametrize("r,version,order", [(2, 1, "direct"), (4, 1, "direct"), (4, 2, "twice_r2"),
+                                             (4, 1, "twice_r2")])
+def test_pixel_shuffle_variants_bit_exact(dtype, P, C, T, has_cls, r, version, order):
+    from vlm_visual_token_amd import ivc
+    say(f"pixel_shuffle variant dtype={dtype} P={P} C={C} T={T} r={r} v{version} {order}")
+    g = torch.Generator().manual_seed(7 * P + C + r + version)
+    x = torch.randn((T, has_cls + P * P, C), generator=g).to(TORCH_DT[dtype])
+    xd = x.cuda()
+    Q = P // r
+    out = torch.full((T, Q * Q, r * r * C), float("nan"), dtype=xd.dtype, device="cuda")
+    ivc.ivc_pixel_shuffle(1 if dtype == "bf16" else 0, xd, T, P, C, has_cls, r, out,
+                          ps_version=version, shuffle64_order=ivc.SHUFFLE64_ORDERS.index(order))
+    torch.cuda.synchronize()
+    G = O.token_grid(x.float().numpy(), P, has_cls)
+    exp = O.pixel_shuffle(G, 2, version) if r == 2 else O.shuffle64(G, order, version)
+    got = out.float().cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), exp.astype(np.float32).view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # tiny Flash workload, fp32: everything, every tile
 # ---------------------------------------------------------------------------
@@ -77,6 +98,20 @@ def _tiny_all(valid=None, poison=False):
 def test_tiny_run_matches_oracle():
     cfg, w, x = _tiny_all()
     say("tiny run")
+    con = _connector(cfg, w, cfg["T"])
+    o256, o64 = con.run(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    e256, e64 = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256), e256, "f32", "out256")
+    assert_close(to_np(o64), e64, "f32", "out64")
+
+
+@pytest.mark.parametrize("version,order", [(1, "direct"), (2, "twice_r2"), (1, "twice_r2")])
+def test_tiny_run_index_variants_match_oracle(version, order):
+    cfg = workload("tiny_flash_f32", ps_version=version, shuffle64_order=order)
+    w = host_weights(cfg)
+    x = synth.make_vit(cfg)
+    say(f"tiny run ps_version={version} order={order}")
     con = _connector(cfg, w, cfg["T"])
     o256, o64 = con.run(torch.from_numpy(x).cuda())
     torch.cuda.synchronize()

@@ -212,6 +212,11 @@ ivc_status check_cfg(const ivc_config& c) {
     return fail(IVC_ERR_UNSUPPORTED, "vit_width %d above the loader's %d", c.vit_width,
                 shuffle_max_width(c.dtype));
   if (!(c.ln_eps >= 0.f)) return fail(IVC_ERR_INVALID_ARG, "ln_eps");
+  if (c.ps_version < 0 || c.ps_version > 2)
+    return fail(IVC_ERR_INVALID_ARG, "ps_version %d", c.ps_version);
+  if (c.shuffle64_order != IVC_SHUFFLE64_DIRECT && c.shuffle64_order != IVC_SHUFFLE64_TWICE_R2)
+    return fail(IVC_ERR_INVALID_ARG, "shuffle64_order %d", c.shuffle64_order);
+  if (c.reserved != 0) return fail(IVC_ERR_INVALID_ARG, "reserved must be 0");
   if (c.flash) {
     if (c.mlp2_hidden <= 0 || (long long)c.mlp2_hidden * esz % 16)
       return fail(IVC_ERR_INVALID_ARG, "mlp2_hidden");
@@ -643,6 +648,8 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   sa.b4 = h->m2_ln_b;
   sa.out4 = w.a4;
   sa.eps = c.ln_eps;
+  sa.ps_v1 = c.ps_version == 1;
+  sa.twice_r2 = c.shuffle64_order == IVC_SHUFFLE64_TWICE_R2;
   if (use64 != nullptr) {
     sa.use64 = use64;
     sa.rank = w.rank;
@@ -932,9 +939,13 @@ extern "C" ivc_status ivc_tile_offsets(const int32_t* tiles_per_image, int32_t B
 }
 
 extern "C" ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t T, int32_t P,
-                                        int32_t C, int32_t has_cls, int32_t r, void* out,
+                                        int32_t C, int32_t has_cls, int32_t r,
+                                        int32_t ps_version, int32_t shuffle64_order, void* out,
                                         void* stream) {
   if (dtype != IVC_F32 && dtype != IVC_BF16) return fail(IVC_ERR_INVALID_ARG, "dtype");
+  if (ps_version < 0 || ps_version > 2) return fail(IVC_ERR_INVALID_ARG, "ps_version %d", ps_version);
+  if (shuffle64_order != IVC_SHUFFLE64_DIRECT && shuffle64_order != IVC_SHUFFLE64_TWICE_R2)
+    return fail(IVC_ERR_INVALID_ARG, "shuffle64_order %d", shuffle64_order);
   if (T < 0 || P <= 0 || C <= 0 || (has_cls != 0 && has_cls != 1) || (r != 2 && r != 4))
     return fail(IVC_ERR_INVALID_ARG, "bad shape");
   if (P % r) return fail(IVC_ERR_INVALID_ARG, "P %% r != 0");
@@ -955,6 +966,8 @@ extern "C" ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t 
   sa.ln = 0;
   sa.out2 = r == 2 ? out : nullptr;
   sa.out4 = r == 4 ? out : nullptr;
+  sa.ps_v1 = ps_version == 1;
+  sa.twice_r2 = shuffle64_order == IVC_SHUFFLE64_TWICE_R2;
   hipStream_t s = (hipStream_t)stream;
   LAUNCH("pixel_shuffle", s, launch_shuffle_ln(sa, s));
   return IVC_OK;

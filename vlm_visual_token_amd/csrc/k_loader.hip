@@ -6,9 +6,16 @@
 //   out[a*(P/r) + b][(r*m + k)*C + c] = grid[r*a + m][r*b + k][c],
 //   grid[i][j] = vit row has_cls + i*P + j.
 // An r=2 token is 4 input rows of C (a 2x2 cell block); an r=4 token is the
-// 4x4 block made of four r=2 blocks.  mlp1/mlp2 start with LayerNorm over the
-// concatenated row (4C or 16C), fused here so the permuted rows are written
-// once, already normalised, in the layout the projector GEMM reads.
+// 4x4 block made of four r=2 blocks.  Two index-math variants:
+//  * ps_version v1 (same page, v1/v2 section) leaves the two grid axes
+//    swapped, so token (a, b) is written at b*(P/r) + a;
+//  * the 64-token path as two successive r=2 shuffles (InternVL3_5-2B-Flash
+//    page: scale 0.25 is 0.5 squared) puts cell (2*m2 + m, 2*k2 + k) of the
+//    4x4 block in channel block 4*(2*m2 + k2) + (2*m + k) instead of the
+//    direct r=4 block 4*(2*m2 + m) + (2*k2 + k).
+// mlp1/mlp2 start with LayerNorm over the concatenated row (4C or 16C), fused
+// here so the permuted rows are written once, already normalised, in the
+// layout the projector GEMM reads.
 //
 // Work split (one wavefront = one r=2 token): the wave loads its 4 input rows
 // with 16-byte loads (a row is C contiguous elements, so every load is fully
@@ -28,7 +35,8 @@ __global__ void __launch_bounds__(256)
 k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
              const float* __restrict__ g2, const float* __restrict__ b2, E* __restrict__ out2,
              const float* __restrict__ g4, const float* __restrict__ b4, E* __restrict__ out4,
-             float eps, const uint8_t* __restrict__ use64, const int* __restrict__ rank) {
+             float eps, int ps_v1, int twice_r2, const uint8_t* __restrict__ use64,
+             const int* __restrict__ rank) {
   constexpr int V = Elem<E>::kPerVec;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -141,7 +149,8 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
 
   // ---- r = 2 row: channel block q holds cell q
   if (want2) {
-    E* dst = out2 + ((size_t)t2 * S2 + a2 * Q2 + b2i) * (size_t)(4 * C);
+    const int tok2 = ps_v1 ? b2i * Q2 + a2 : a2 * Q2 + b2i;
+    E* dst = out2 + ((size_t)t2 * S2 + tok2) * (size_t)(4 * C);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -162,15 +171,17 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
       }
   }
 
-  // ---- r = 4 row: this wave's cell (m, k) sits at (2*(w>>1) + m, 2*(w&1) + k)
-  //      inside the 4x4 block, channel block 4*m4 + k4.
+  // ---- r = 4 row: this wave's cell q = (m, k) sits at (2*(w>>1) + m, 2*(w&1) + k)
+  //      inside the 4x4 block: channel block 4*m4 + k4 (direct) or 4*w + q
+  //      (two r=2 shuffles).
   if (FLASH && want4) {
     const int Q4 = P >> 2, S4 = Q4 * Q4;
-    E* dst = out4 + ((size_t)t4 * S4 + a4 * Q4 + b4i) * (size_t)(16 * C);
+    const int tok4 = ps_v1 ? b4i * Q4 + a4 : a4 * Q4 + b4i;
+    E* dst = out4 + ((size_t)t4 * S4 + tok4) * (size_t)(16 * C);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m4 = 2 * (w >> 1) + (q >> 1), k4 = 2 * (w & 1) + (q & 1);
-      const int base = (4 * m4 + k4) * C;
+      const int base = (twice_r2 ? 4 * w + q : 4 * m4 + k4) * C;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int v = lane + 64 * i;
@@ -198,13 +209,13 @@ static hipError_t launch_cpl(const ShuffleArgs& a, hipStream_t s) {
     dim3 grid((unsigned)(a.T * Q4 * Q4));
     hipLaunchKernelGGL((k_shuffle_ln<E, CPL, true, LN>), grid, dim3(256), 0, s, (const E*)a.X, a.T,
                        a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4, a.eps,
-                       a.use64, a.rank);
+                       a.ps_v1, a.twice_r2, a.use64, a.rank);
   } else {
     const long long toks = (long long)a.T * Q2 * Q2;
     dim3 grid((unsigned)((toks + 3) / 4));
     hipLaunchKernelGGL((k_shuffle_ln<E, CPL, false, LN>), grid, dim3(256), 0, s, (const E*)a.X,
                        a.T, a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4,
-                       a.eps, a.use64, a.rank);
+                       a.eps, a.ps_v1, a.twice_r2, a.use64, a.rank);
   }
   return hipGetLastError();
 }

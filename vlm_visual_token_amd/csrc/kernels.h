@@ -21,6 +21,8 @@ struct ShuffleArgs {
   const float *g4, *b4;
   void* out4;
   float eps;
+  int ps_v1 = 0;     // 1: pixel_shuffle v1, token grid transposed (token b*(P/r) + a)
+  int twice_r2 = 0;  // 1: 64-path channel order of two successive r=2 shuffles
   // route-first: tile t writes only its chosen path's rows, at position rank[t]
   const uint8_t* use64 = nullptr;
   const int* rank = nullptr;

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libivc.so")
 IVC_OK = 0
 IVC_F32, IVC_BF16 = 0, 1
 IVC_POOL_KV, IVC_POOL_FOLDED = 0, 1
+SHUFFLE64_ORDERS = ("direct", "twice_r2")  # ivc_shuffle64_order values 0, 1
 IVC_DEV_OK = 0
 IVC_DEV_ERR_IMG_COUNT = 1
 IVC_DEV_ERR_VALID_TOKENS = 2
@@ -37,7 +38,8 @@ class ivc_config(ctypes.Structure):
         ("llm_width", c_int32), ("mlp1_hidden", c_int32), ("flash", c_int32),
         ("mlp2_hidden", c_int32), ("pool_layers", c_int32), ("pool_heads", c_int32),
         ("gate_hidden", c_int32), ("gate_expansion", c_int32), ("pool_mode", c_int32),
-        ("reserved", c_int32), ("rel_quantile", c_double), ("abs_threshold", c_double),
+        ("ps_version", c_int32), ("shuffle64_order", c_int32), ("reserved", c_int32),
+        ("rel_quantile", c_double), ("abs_threshold", c_double),
         ("ln_eps", c_float),
     ]
 
@@ -85,7 +87,8 @@ def load() -> ctypes.CDLL:
                                             P, P, P, P, c_size_t, P]),
         "ivc_route_decide": (c_int32, [P, c_int32, c_double, c_double, P, P, P]),
         "ivc_tile_offsets": (c_int32, [P, c_int32, P, P, P]),
-        "ivc_pixel_shuffle": (c_int32, [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32, P, P]),
+        "ivc_pixel_shuffle": (c_int32, [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                        c_int32, c_int32, P, P]),
         "ivc_profile_enable": (None, [c_int32]),
         "ivc_profile_reset": (None, []),
         "ivc_profile_read": (c_int32, [POINTER(c_char_p), POINTER(c_double), POINTER(c_int64), c_int32]),
@@ -152,6 +155,8 @@ def make_config(cfg: dict) -> ivc_config:
     c.gate_hidden = cfg["gate_hidden"]
     c.gate_expansion = cfg["gate_expansion"]
     c.pool_mode = cfg.get("pool_mode", IVC_POOL_KV)
+    c.ps_version = cfg.get("ps_version", 2)
+    c.shuffle64_order = SHUFFLE64_ORDERS.index(cfg.get("shuffle64_order", "direct"))
     c.rel_quantile = cfg["rel_quantile"]
     c.abs_threshold = cfg["abs_threshold"]
     c.ln_eps = cfg["ln_eps"]
@@ -242,8 +247,10 @@ def ivc_tile_offsets(tiles_per_image, B, offsets, dev_status, stream=None) -> No
                                    _stream(stream)), "ivc_tile_offsets")
 
 
-def ivc_pixel_shuffle(dtype, vit, T, P, C, has_cls, r, out, stream=None) -> None:
-    _check(load().ivc_pixel_shuffle(dtype, _ptr(vit), T, P, C, has_cls, r, _ptr(out),
+def ivc_pixel_shuffle(dtype, vit, T, P, C, has_cls, r, out, stream=None, ps_version=2,
+                      shuffle64_order=0) -> None:
+    _check(load().ivc_pixel_shuffle(dtype, _ptr(vit), T, P, C, has_cls, r, ps_version,
+                                    shuffle64_order, _ptr(out),
                                     _stream(stream)), "ivc_pixel_shuffle")
 
 
