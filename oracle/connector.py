@@ -34,6 +34,7 @@ from scipy.special import erf as _erf
 
 STATUS_OK = 0
 STATUS_IMG_COUNT = 1  # IMG_CONTEXT slots in the sequence != tiles * slots per tile
+STATUS_SEQ_LAYOUT = 8  # batch: sequence or tile offsets not an ordered partition
 
 
 def f64(a) -> np.ndarray:
@@ -366,3 +367,61 @@ def compact(ids, embeds, img_context_id: int, use64, out256, out64, S: int, S64:
     return dict(out_ids=out_ids, out_pos=out_pos, keep_map=keep_map,
                 out_embeds=out_emb, out_len=j, status=STATUS_OK)
 
+
+
+def compact_batch(ids, cu_seqlens, embeds, img_context_id: int, tile_offsets, use64, out256,
+                  out64, S: int, S64: int):
+    """Compaction of B prompts packed back to back (variable-length batch).
+
+    Sequence b is positions cu_seqlens[b] .. cu_seqlens[b+1]-1 of ``ids``
+    and its images own tiles tile_offsets[b] .. tile_offsets[b+1]-1 (image
+    order within the sequence, as for one prompt).  Every sequence is
+    compacted on its own exactly as ``compact`` does for one prompt: its
+    k-th IMG_CONTEXT slot is local slot k % S of its (k // S)-th tile, a
+    routed tile keeps its first S64 slots ([4B-Flash] section 4), and its
+    positions restart at 0.  The compacted sequences are packed back to back:
+    out_cu[0] = 0, out_cu[b+1] = out_cu[b] + L'_b, and keep_map holds packed
+    indices.  A sequence whose IMG_CONTEXT count differs from S times its
+    tile count compacts to length 0 (status STATUS_IMG_COUNT); the others
+    are unaffected.  Offsets that are not an ordered partition (cu_seqlens
+    from 0 to L, non-decreasing; tile_offsets non-decreasing within [0, T])
+    give status STATUS_SEQ_LAYOUT and an empty result.
+
+    Returns a dict like ``compact``'s, with out_pos holding per-sequence
+    positions and out_cu [B+1] in place of out_len.
+    """
+    ids = np.asarray(ids)
+    cu = [int(v) for v in cu_seqlens]
+    to = [int(v) for v in tile_offsets]
+    L = ids.shape[0]
+    B = len(cu) - 1
+    T = len(use64)
+    D = embeds.shape[1]
+    out_ids = np.full(L, -1, dtype=np.int64)
+    out_pos = np.full(L, -1, dtype=np.int64)
+    keep_map = np.full(L, -1, dtype=np.int64)
+    out_emb = np.zeros((L, D), dtype=np.float64)
+    out_cu = np.zeros(B + 1, dtype=np.int64)
+    layout_ok = (len(to) == B + 1 and cu[0] == 0 and cu[B] == L and to[0] >= 0 and to[B] <= T
+                 and all(cu[b] <= cu[b + 1] and to[b] <= to[b + 1] for b in range(B)))
+    if not layout_ok:
+        return dict(out_ids=out_ids, out_pos=out_pos, keep_map=keep_map, out_embeds=out_emb,
+                    out_cu=out_cu, status=STATUS_SEQ_LAYOUT)
+    status = STATUS_OK
+    for b in range(B):
+        p0, p1, t0, t1 = cu[b], cu[b + 1], to[b], to[b + 1]
+        one = compact(ids[p0:p1], embeds[p0:p1], img_context_id, use64[t0:t1],
+                      out256[t0:t1], None if out64 is None else out64[t0:t1], S, S64)
+        n = one["out_len"]
+        j0 = int(out_cu[b])
+        out_cu[b + 1] = j0 + n
+        if one["status"] != STATUS_OK:
+            status |= one["status"]
+            continue
+        out_ids[j0:j0 + n] = one["out_ids"][:n]
+        out_pos[j0:j0 + n] = one["out_pos"][:n]
+        out_emb[j0:j0 + n] = one["out_embeds"][:n]
+        kept = one["keep_map"] >= 0
+        keep_map[p0:p1][kept] = one["keep_map"][kept] + j0
+    return dict(out_ids=out_ids, out_pos=out_pos, keep_map=keep_map, out_embeds=out_emb,
+                out_cu=out_cu, status=status)

@@ -107,3 +107,88 @@ def test_tile_offsets():
     r = np.random.default_rng(0)
     t = r.integers(1, 13, 32) + 1
     assert np.array_equal(O.tile_offsets(t), np.concatenate([[0], np.cumsum(t)]))
+
+
+# ---------------------------------------------------------------------------
+# batched, ragged compaction: B prompts packed back to back
+# ---------------------------------------------------------------------------
+def _batch_case(tiles, S, S64, D, seed):
+    """Sequences with the given per-sequence tile counts (0 = text only),
+    concatenated; returns the packed inputs and the per-sequence pieces."""
+    seqs = [_case(t, S, S64, D, seed * 100 + b) if t else None for b, t in enumerate(tiles)]
+    r = np.random.default_rng(seed)
+    pieces = []
+    for t, c in zip(tiles, seqs):
+        if c is None:
+            n = int(r.integers(0, 4))  # text-only sequence, possibly empty
+            c = (r.integers(0, 1000, n).astype(np.int32), r.standard_normal((n, D)),
+                 np.zeros(0, np.uint8), np.zeros((0, S, D)), np.zeros((0, S64, D)))
+        pieces.append(c)
+    ids = np.concatenate([c[0] for c in pieces])
+    emb = np.concatenate([c[1] for c in pieces])
+    use64 = np.concatenate([c[2] for c in pieces])
+    o256 = np.concatenate([c[3] for c in pieces])
+    o64 = np.concatenate([c[4] for c in pieces])
+    cu = np.concatenate([[0], np.cumsum([len(c[0]) for c in pieces])])
+    to = np.concatenate([[0], np.cumsum(tiles)])
+    return ids, emb, use64, o256, o64, cu, to, pieces
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("tiles,S,S64", [([2, 0, 3, 1], 16, 4), ([1], 16, 4), ([0, 0], 4, 1),
+                                         ([3, 1, 0, 2, 5], 4, 1)])
+def test_compact_batch_matches_brute_force(seed, tiles, S, S64):
+    ids, emb, use64, o256, o64, cu, to, pieces = _batch_case(tiles, S, S64, 3, seed)
+    got = O.compact_batch(ids, cu, emb, IMG, to, use64, o256, o64, S, S64)
+    assert got["status"] == O.STATUS_OK
+    j = 0
+    for b, (sid, semb, suse, s256, s64) in enumerate(pieces):
+        bids, bkeep, brows = _brute(sid, semb, suse, s256, s64, S, S64)
+        n = len(bids)
+        assert got["out_cu"][b] == j and got["out_cu"][b + 1] == j + n
+        assert np.array_equal(got["out_ids"][j:j + n], bids)
+        assert np.array_equal(got["out_pos"][j:j + n], np.arange(n))
+        if n:
+            assert np.array_equal(got["out_embeds"][j:j + n], brows)
+        km = got["keep_map"][cu[b]:cu[b + 1]]
+        assert np.array_equal(np.flatnonzero(km >= 0), bkeep)
+        assert np.array_equal(km[bkeep], j + np.arange(n))
+        j += n
+    L = len(ids)
+    assert j == L - (S - S64) * int(use64.sum())
+    assert (got["out_ids"][j:] == -1).all() and (got["out_pos"][j:] == -1).all()
+
+
+def test_compact_batch_one_bad_sequence():
+    ids, emb, use64, o256, o64, cu, to, pieces = _batch_case([2, 2, 1], 16, 4, 2, 5)
+    # drop one IMG_CONTEXT slot from sequence 1: its count no longer matches its tiles
+    p = int(np.flatnonzero(ids[cu[1]:cu[2]] == IMG)[0]) + cu[1]
+    ids = np.delete(ids, p)
+    emb = np.delete(emb, p, axis=0)
+    cu = cu.copy()
+    cu[2:] -= 1
+    got = O.compact_batch(ids, cu, emb, IMG, to, use64, o256, o64, 16, 4)
+    assert got["status"] == O.STATUS_IMG_COUNT
+    lens = np.diff(got["out_cu"])
+    assert lens[1] == 0
+    for b in (0, 2):
+        sid, semb, suse, s256, s64 = pieces[b]
+        assert lens[b] == len(_brute(sid, semb, suse, s256, s64, 16, 4)[0])
+    assert (got["keep_map"][cu[1]:cu[2]] == -1).all()
+
+
+@pytest.mark.parametrize("bad", ["cu_end", "cu_order", "tile_order", "tile_range"])
+def test_compact_batch_rejects_bad_layout(bad):
+    ids, emb, use64, o256, o64, cu, to, _ = _batch_case([1, 2], 4, 1, 2, 6)
+    cu, to = cu.copy(), to.copy()
+    if bad == "cu_end":
+        cu[-1] -= 1
+    elif bad == "cu_order":
+        cu[1] = cu[2] + 1
+    elif bad == "tile_order":
+        to[1] = to[2] + 1
+    else:
+        to[-1] = len(use64) + 1
+    got = O.compact_batch(ids, cu, emb, IMG, to, use64, o256, o64, 4, 1)
+    assert got["status"] == O.STATUS_SEQ_LAYOUT
+    assert (got["out_cu"] == 0).all() and (got["keep_map"] == -1).all()
