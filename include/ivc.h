@@ -86,6 +86,7 @@ typedef enum { IVC_SHUFFLE64_DIRECT = 0, IVC_SHUFFLE64_TWICE_R2 = 1 } ivc_shuffl
 #define IVC_DEV_ERR_IMG_COUNT 1    /* IMG_CONTEXT slots != T * (P/2)^2          */
 #define IVC_DEV_ERR_VALID_TOKENS 2 /* a valid_tokens[t] outside [1, P*P]        */
 #define IVC_DEV_ERR_TILE_COUNT 4   /* a tiles_per_image[i] < 0, or sum > INT32_MAX */
+#define IVC_DEV_ERR_SEQ_LAYOUT 8   /* batch: cu_seqlens / tile_offsets not an ordered partition */
 
 #define IVC_MAX_POOL_LAYERS 8
 #define IVC_GATE_BLOCKS 4
@@ -231,6 +232,44 @@ ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids, const voi
                                  int32_t* out_ids, int32_t* out_pos, int32_t* keep_map,
                                  void* out_embeds, int64_t* out_len, int32_t* dev_status,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Variable-length batch form of ivc_connector_compact: B prompts packed
+ * back to back, as varlen attention takes them.  Sequence b is positions
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of ids/embeds, and its images own
+ * tiles tile_offsets[b] .. tile_offsets[b+1]-1 of use64/out256/out64
+ * (image order, as ivc_tile_offsets lays them out).  Every sequence is
+ * compacted on its own exactly as ivc_connector_compact does for one prompt
+ * ([4B-Flash] section 4): positions restart at 0 in each sequence, and the
+ * compacted sequences are packed back to back:
+ *   out_cu_seqlens [B+1] int32: out_cu_seqlens[0] = 0,
+ *                  out_cu_seqlens[b+1] = out_cu_seqlens[b] + L'_b
+ *   out_ids [L], out_pos [L]: packed ids and per-sequence positions 0..L'_b-1,
+ *                  -1 past out_cu_seqlens[B]
+ *   keep_map [L]:  packed index of each input position, or -1 if deleted
+ *   out_embeds [L, D]: rows 0..out_cu_seqlens[B]-1 written, the rest untouched
+ * All of cu_seqlens, tile_offsets and the outputs are device arrays.
+ * dev_status (required) gets IVC_DEV_ERR_IMG_COUNT when a sequence's
+ * IMG_CONTEXT count differs from (P/2)^2 times its tile count (that
+ * sequence then compacts to length 0, the others are unaffected), and
+ * IVC_DEV_ERR_SEQ_LAYOUT when cu_seqlens does not run from 0 to L without
+ * decreasing or tile_offsets decreases or leaves [0, T] (then every
+ * out_cu_seqlens entry is 0 and every keep_map, out_ids and out_pos entry
+ * -1).  B = 0 requires L = 0 and enqueues nothing.  Workspace:
+ * ivc_connector_compact_batch_workspace_bytes. */
+ivc_status ivc_connector_compact_batch(ivc_connector* h, const int32_t* ids,
+                                       const int32_t* cu_seqlens, int32_t B, const void* embeds,
+                                       int64_t L, int32_t img_context_id,
+                                       const int32_t* tile_offsets, const uint8_t* use64,
+                                       const void* out256, const void* out64, int32_t T,
+                                       int32_t* out_ids, int32_t* out_pos, int32_t* keep_map,
+                                       void* out_embeds, int32_t* out_cu_seqlens,
+                                       int32_t* dev_status, void* ws, size_t ws_bytes,
+                                       void* stream);
+
+/* Workspace bytes of ivc_connector_compact_batch for up to max_tiles tiles,
+ * max_total_len packed tokens and max_seqs sequences. */
+size_t ivc_connector_compact_batch_workspace_bytes(const ivc_connector* h, int32_t max_tiles,
+                                                   int64_t max_total_len, int32_t max_seqs);
 
 /* The router's batch-wide step alone ([4B-Flash] section 4): threshold =
  * rel_quantile-quantile of gate[:, 0] (linear interpolation between order

@@ -16,6 +16,7 @@ from .inputs import (  # noqa: F401
     make_vit_tiles,
     make_vit,
     make_sequence,
+    make_batch_sequences,
     make_valid_tokens,
     make_tiles_per_image,
     to_bf16_exact,

@@ -258,6 +258,43 @@ def make_sequence(cfg: dict, seed: int = 0, poison: bool = True):
     return ids, emb
 
 
+def make_batch_sequences(cfg: dict, images_per_seq, seed: int = 0, poison: bool = True,
+                         with_embeds: bool = True):
+    """B prompts packed back to back (a variable-length batch).
+
+    ``images_per_seq[b]`` lists the tile counts of sequence b's images (an
+    empty list gives a text-only prompt).  Each prompt is laid out as
+    ``make_sequence`` lays out one, with its own seeded text.  Returns
+    ``(ids int32 [L], embeds float32 [L, D] or None, cu_seqlens int32 [B+1],
+    tile_offsets int32 [B+1])``: sequence b is positions cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 and owns tiles tile_offsets[b] .. tile_offsets[b+1]-1.
+    """
+    S = cfg["S"]
+    n_text = cfg["text_per_image"]
+    parts, lens, tiles = [], [], []
+    for b, imgs in enumerate(images_per_seq):
+        g = _rng(seed, "batch.ids", b)
+        n0 = sum(len(p) for p in parts)
+        if not imgs:
+            parts.append(g.integers(0, TEXT_VOCAB, size=int(g.integers(0, n_text + 1))).astype(np.int32))
+        for nt in imgs:
+            txt = g.integers(0, TEXT_VOCAB, size=n_text).astype(np.int32)
+            h = n_text // 2
+            parts += [txt[:h], np.array([IMG_START], np.int32), np.full(nt * S, IMG_CONTEXT, np.int32),
+                      np.array([IMG_END], np.int32), txt[h:]]
+        lens.append(sum(len(p) for p in parts) - n0)
+        tiles.append(int(sum(imgs)))
+    ids = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    to = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int32)
+    emb = None
+    if with_embeds:
+        emb = _finish(cfg, _normal(seed, "batch.embeds", (ids.shape[0], cfg["D"])))
+        if poison:
+            emb[ids == IMG_CONTEXT] = np.float32(np.nan)
+    return ids, emb, cu, to
+
+
 def sample_tiles(T: int, seed: int = 0, n: int = 16) -> list[int]:
     """Tiles checked element by element on large workloads: the first, the
     last and ``n - 2`` more drawn without replacement."""

@@ -470,3 +470,133 @@ def test_deterministic():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# batched, ragged compaction (B prompts packed back to back)
+# ---------------------------------------------------------------------------
+def _compact_model(name):
+    """A connector whose compaction geometry (P, D, dtype) is the named
+    workload's, with small projector widths (compaction reads none of them)."""
+    if name == "tiny_flash_f32":
+        return workload(name)
+    return workload(name, C=64, mlp1_hidden=256, mlp2_hidden=256, gate_hidden=64, pool_heads=4)
+
+
+def _batch_case(cfg, images, seed):
+    ids, emb, cu, to = synth.make_batch_sequences(cfg, images, seed)
+    T = int(to[-1])
+    dt = TORCH_DT[cfg["dtype"]]
+    g = torch.Generator().manual_seed(seed)
+    o256 = torch.randn((T, cfg["S"], cfg["D"]), generator=g).to(dt)
+    o64 = torch.randn((T, cfg["S64"], cfg["D"]), generator=g).to(dt)
+    use = (torch.rand(T, generator=g) < 0.5).to(torch.uint8).numpy()
+    return ids, emb, cu, to, use, o256, o64
+
+
+def _run_batch(con, cfg, ids, emb_d, cu, to, use, o256, o64):
+    return con.compact_batch(torch.from_numpy(ids).cuda(), torch.from_numpy(cu).cuda(), emb_d,
+                             torch.from_numpy(to).cuda(), torch.from_numpy(use).cuda(),
+                             o256.cuda(), o64.cuda(), synth.IMG_CONTEXT)
+
+
+@pytest.mark.parametrize("name,images,seed", [
+    ("tiny_flash_f32", [[1, 2], [], [3], [1], [], [2]], 1),
+    ("tiny_flash_f32", [[1]], 2),
+    ("tiny_flash_f32", [[], []], 3),
+    ("internvl35_2b_flash", [[13, 1], [], [4, 4, 1], [13], [2]], 4),
+])
+def test_compact_batch_matches_oracle(name, images, seed):
+    cfg = _compact_model(name)
+    say(f"compact_batch {name} images={images}")
+    ids, emb, cu, to, use, o256, o64 = _batch_case(cfg, images, seed)
+    con = _connector(cfg, host_weights(cfg), 1)
+    emb_d = torch.from_numpy(emb).to(TORCH_DT[cfg["dtype"]]).cuda()
+    c = _run_batch(con, cfg, ids, emb_d, cu, to, use, o256, o64)
+    torch.cuda.synchronize()
+    ref = O.compact_batch(ids, cu, emb, synth.IMG_CONTEXT, to, use, to_np(o256), to_np(o64),
+                          cfg["S"], cfg["S64"])
+    assert int(c["status"].item()) == 0 and ref["status"] == 0
+    assert np.array_equal(c["cu"].cpu().numpy(), ref["out_cu"])
+    n = int(ref["out_cu"][-1])
+    assert n == len(ids) - (cfg["S"] - cfg["S64"]) * int(use.sum())
+    assert np.array_equal(c["ids"].cpu().numpy(), ref["out_ids"])
+    assert np.array_equal(c["pos"].cpu().numpy(), ref["out_pos"])
+    assert np.array_equal(c["keep_map"].cpu().numpy(), ref["keep_map"])
+    got = c["embeds"][:n].float().cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref["out_embeds"][:n].astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("bad", ["slot_count", "cu_end", "tile_order"])
+def test_compact_batch_errors(bad):
+    cfg = workload("tiny_flash_f32")
+    say(f"compact_batch error case {bad}")
+    ids, emb, cu, to, use, o256, o64 = _batch_case(cfg, [[1], [2], [1]], 5)
+    if bad == "slot_count":
+        p = int(np.flatnonzero(ids[cu[1]:cu[2]] == synth.IMG_CONTEXT)[0]) + int(cu[1])
+        ids = np.delete(ids, p)
+        emb = np.delete(emb, p, axis=0)
+        cu = cu.copy()
+        cu[2:] -= 1
+    elif bad == "cu_end":
+        cu = cu.copy()
+        cu[-1] -= 1
+    else:
+        to = to.copy()
+        to[1] = to[2] + 1
+    con = _connector(cfg, host_weights(cfg), 1)
+    c = _run_batch(con, cfg, ids, torch.from_numpy(emb).cuda(), cu, to, use, o256, o64)
+    torch.cuda.synchronize()
+    ref = O.compact_batch(ids, cu, emb, synth.IMG_CONTEXT, to, use, to_np(o256), to_np(o64),
+                          cfg["S"], cfg["S64"])
+    st = int(c["status"].item())
+    assert st == ref["status"] == (O.STATUS_IMG_COUNT if bad == "slot_count" else O.STATUS_SEQ_LAYOUT)
+    assert np.array_equal(c["cu"].cpu().numpy(), ref["out_cu"])
+    assert np.array_equal(c["keep_map"].cpu().numpy(), ref["keep_map"])
+    n = int(ref["out_cu"][-1])
+    assert np.array_equal(c["ids"].cpu().numpy(), ref["out_ids"])
+    assert np.array_equal(c["pos"].cpu().numpy(), ref["out_pos"])
+    got = c["embeds"][:n].float().cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref["out_embeds"][:n].astype(np.float32).view(np.uint32))
+
+
+def test_compact_batch_flash_layout_16_prompts():
+    # 16 prompts, each the 2B-Flash batch layout (16 images x 13 tiles), D = 2048:
+    # L = 860k.  Index outputs bit-exact against the oracle; every embedding row
+    # checked against the source row the oracle assigns it (the oracle runs
+    # on one-column stand-ins that name each source row).
+    cfg = _compact_model("internvl35_2b_flash")
+    B = 16
+    ids, _, cu, to = synth.make_batch_sequences(cfg, [cfg["tiles"]] * B, 6, with_embeds=False)
+    L, T, S, S64, D = len(ids), int(to[-1]), cfg["S"], cfg["S64"], cfg["D"]
+    say(f"compact_batch 2B-Flash layout x{B}: L={L} T={T}")
+    g = torch.Generator(device="cuda").manual_seed(6)
+    emb_d = torch.randn((L, D), generator=g, device="cuda").to(torch.bfloat16)
+    o256 = torch.randn((T, S, D), generator=g, device="cuda").to(torch.bfloat16)
+    o64 = torch.randn((T, S64, D), generator=g, device="cuda").to(torch.bfloat16)
+    use = (np.random.default_rng(6).random(T) < 0.5).astype(np.uint8)
+    con = _connector(cfg, host_weights(cfg), 1)
+    c = con.compact_batch(torch.from_numpy(ids).cuda(), torch.from_numpy(cu).cuda(), emb_d,
+                          torch.from_numpy(to).cuda(), torch.from_numpy(use).cuda(), o256, o64,
+                          synth.IMG_CONTEXT)
+    torch.cuda.synchronize()
+    code_e = np.arange(L, dtype=np.float64)[:, None]
+    code_256 = (L + np.arange(T * S, dtype=np.float64)).reshape(T, S, 1)
+    code_64 = (L + T * S + np.arange(T * S64, dtype=np.float64)).reshape(T, S64, 1)
+    ref = O.compact_batch(ids, cu, code_e, synth.IMG_CONTEXT, to, use, code_256, code_64, S, S64)
+    assert int(c["status"].item()) == 0 and ref["status"] == 0
+    assert np.array_equal(c["cu"].cpu().numpy(), ref["out_cu"])
+    n = int(ref["out_cu"][-1])
+    assert n == L - (S - S64) * int(use.sum())
+    assert np.array_equal(c["ids"].cpu().numpy(), ref["out_ids"])
+    assert np.array_equal(c["pos"].cpu().numpy(), ref["out_pos"])
+    assert np.array_equal(c["keep_map"].cpu().numpy(), ref["keep_map"])
+    code = torch.from_numpy(ref["out_embeds"][:n, 0].astype(np.int64)).cuda()
+    want = torch.empty((n, D), dtype=torch.bfloat16, device="cuda")
+    m = code < L
+    want[m] = emb_d[code[m]]
+    m2 = (code >= L) & (code < L + T * S)
+    want[m2] = o256.view(-1, D)[code[m2] - L]
+    m3 = code >= L + T * S
+    want[m3] = o64.view(-1, D)[code[m3] - L - T * S]
+    assert torch.equal(c["embeds"][:n].view(torch.int16), want.view(torch.int16))

@@ -91,3 +91,28 @@ class Connector:
                                   out["ids"], out["pos"], out["keep_map"], out["embeds"],
                                   out["len"], out["status"], self.ws, self.ws_bytes, stream)
         return out
+
+    def compact_batch(self, ids, cu_seqlens, embeds, tile_offsets, use64, out256, out64,
+                      img_context_id: int, stream=None, out=None, ws=None):
+        """Variable-length batch compaction (ivc_connector_compact_batch).
+        ``ws`` defaults to a workspace sized for this call."""
+        L = ids.shape[0]
+        B = cu_seqlens.shape[0] - 1
+        T = use64.shape[0]
+        if out is None:
+            out = dict(
+                ids=torch.empty(L, dtype=torch.int32, device=self.device),
+                pos=torch.empty(L, dtype=torch.int32, device=self.device),
+                keep_map=torch.empty(L, dtype=torch.int32, device=self.device),
+                embeds=torch.empty((L, self.cfg["D"]), dtype=self.dtype, device=self.device),
+                cu=torch.zeros(B + 1, dtype=torch.int32, device=self.device),
+                status=torch.zeros(1, dtype=torch.int32, device=self.device),
+            )
+        if ws is None:
+            n = ivc.ivc_connector_compact_batch_workspace_bytes(self.h, T, L, B)
+            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        ivc.ivc_connector_compact_batch(self.h, ids, cu_seqlens, B, embeds, L, img_context_id,
+                                        tile_offsets, use64, out256, out64, T, out["ids"],
+                                        out["pos"], out["keep_map"], out["embeds"], out["cu"],
+                                        out["status"], ws, ws.numel(), stream)
+        return out

@@ -390,9 +390,26 @@ size_t plan_compact(int T, long long L, void* base, CompactWs* w) {
   CompactWs r{};
   const long long nb = compact_blocks(L);
   r.cnt = (int32_t*)cv.take((size_t)nb * 4);
-  r.off = (int32_t*)cv.take((size_t)nb * 4);
+  r.off = (int32_t*)cv.take((size_t)(nb + 1) * 4);
   r.rb = (int32_t*)cv.take((size_t)(T + 1) * 4);
   r.src = (long long*)cv.take((size_t)L * 8);
+  if (w) *w = r;
+  return cv.off;
+}
+
+struct CompactBatchWs {
+  CompactWs c;
+  int32_t *seq_img, *seq_ok, *layout_ok;
+  long long* total;
+};
+size_t plan_compact_batch(int T, long long L, int B, void* base, CompactBatchWs* w) {
+  CompactBatchWs r{};
+  Carver cv(base);
+  cv.off = plan_compact(T, L, base, &r.c);
+  r.seq_img = (int32_t*)cv.take((size_t)(B + 1) * 4);
+  r.seq_ok = (int32_t*)cv.take((size_t)(B + 1) * 4);
+  r.total = (long long*)cv.take(8);
+  r.layout_ok = (int32_t*)cv.take(4);
   if (w) *w = r;
   return cv.off;
 }
@@ -912,6 +929,80 @@ extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids
   a.src = w.src;
   hipStream_t s = (hipStream_t)stream;
   LAUNCH("compact", s, launch_compact(a, s));
+  return IVC_OK;
+}
+
+extern "C" size_t ivc_connector_compact_batch_workspace_bytes(const ivc_connector* h,
+                                                             int32_t max_tiles,
+                                                             int64_t max_total_len,
+                                                             int32_t max_seqs) {
+  if (!h || max_tiles < 0 || max_total_len < 0 || max_seqs < 0) return 0;
+  return plan_compact_batch(max_tiles, max_total_len, max_seqs, nullptr, nullptr);
+}
+
+extern "C" ivc_status ivc_connector_compact_batch(
+    ivc_connector* h, const int32_t* ids, const int32_t* cu_seqlens, int32_t B, const void* embeds,
+    int64_t L, int32_t img_context_id, const int32_t* tile_offsets, const uint8_t* use64,
+    const void* out256, const void* out64, int32_t T, int32_t* out_ids, int32_t* out_pos,
+    int32_t* keep_map, void* out_embeds, int32_t* out_cu_seqlens, int32_t* dev_status, void* ws,
+    size_t ws_bytes, void* stream) {
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  const ivc_config& c = h->cfg;
+  if (L < 0 || T < 0 || B < 0) return fail(IVC_ERR_INVALID_ARG, "negative L, T or B");
+  if (L > 0x7fffffffll) return fail(IVC_ERR_UNSUPPORTED, "L above INT32_MAX");
+  if (B == 0 && L > 0) return fail(IVC_ERR_INVALID_ARG, "B = 0 with L = %lld", (long long)L);
+  if (!cu_seqlens || !tile_offsets || !out_cu_seqlens || !dev_status)
+    return fail(IVC_ERR_INVALID_ARG, "null cu_seqlens/tile_offsets/out_cu_seqlens/dev_status");
+  const long long S = (long long)(c.grid / 2) * (c.grid / 2);
+  const long long S64 = (long long)(c.grid / 4) * (c.grid / 4);
+  if ((long long)T * S >= (1ll << 31)) return fail(IVC_ERR_UNSUPPORTED, "T * S too large");
+  if (L > 0 && (!ids || !embeds || !out_ids || !out_pos || !keep_map || !out_embeds))
+    return fail(IVC_ERR_INVALID_ARG, "null sequence pointer");
+  if (T > 0 && (!use64 || !out256)) return fail(IVC_ERR_INVALID_ARG, "null use64/out256");
+  if (T > 0 && !out64 && c.flash) return fail(IVC_ERR_INVALID_ARG, "null out64");
+  if (!aligned16(embeds) || !aligned16(out256) || !aligned16(out64) || !aligned16(out_embeds) ||
+      !aligned16(ws))
+    return fail(IVC_ERR_MISALIGNED, "embedding pointers must be 16-byte aligned");
+  const size_t need = plan_compact_batch(T, L, B, nullptr, nullptr);
+  if (!ws || ws_bytes < need)
+    return fail(IVC_ERR_WORKSPACE, "compact_batch needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
+  if (B == 0) return IVC_OK;  // nothing to write: out_cu_seqlens[0] is the caller's 0
+  CompactBatchWs w;
+  plan_compact_batch(T, L, B, ws, &w);
+  CompactBatchArgs ba{};
+  CompactArgs& a = ba.base;
+  a.dtype = c.dtype;
+  a.ids = ids;
+  a.embeds = embeds;
+  a.L = L;
+  a.img_id = img_context_id;
+  a.use64 = use64;
+  a.out256 = out256;
+  a.out64 = out64 ? out64 : out256;
+  a.T = T;
+  a.S = (int)S;
+  a.S64 = c.flash ? (int)S64 : (int)S;
+  a.D = c.llm_width;
+  a.out_ids = out_ids;
+  a.out_pos = out_pos;
+  a.keep_map = keep_map;
+  a.out_embeds = out_embeds;
+  a.status = dev_status;
+  a.blk_cnt = w.c.cnt;
+  a.blk_off = w.c.off;
+  a.routed_before = w.c.rb;
+  a.src = w.c.src;
+  ba.cu = cu_seqlens;
+  ba.tile_off = tile_offsets;
+  ba.B = B;
+  ba.out_cu = out_cu_seqlens;
+  ba.seq_img = w.seq_img;
+  ba.seq_ok = w.seq_ok;
+  ba.total = w.total;
+  ba.layout_ok = w.layout_ok;
+  hipStream_t s = (hipStream_t)stream;
+  LAUNCH("compact_batch", s, launch_compact_batch(ba, s));
   return IVC_OK;
 }
 

@@ -101,9 +101,12 @@ k_compact_plan(const int32_t* __restrict__ cnt, long long nblk, const uint8_t* _
            [&](long long i, long long v) { routed_before[i] = (int32_t)v; }, (long long)T);
   if (threadIdx.x == 0) {
     routed_before[T] = (int32_t)n_routed;
-    const bool ok = n_img == (long long)T * S;
-    if (!ok) atomicOr(status, 1);
-    *out_len = ok ? L - (long long)(S - S64) * n_routed : 0;
+    blk_off[nblk] = (int32_t)n_img;
+    if (out_len != nullptr) {  // single sequence: check the slot count, set L'
+      const bool ok = n_img == (long long)T * S;
+      if (!ok) atomicOr(status, 1);
+      *out_len = ok ? L - (long long)(S - S64) * n_routed : 0;
+    }
   }
 }
 
@@ -191,6 +194,244 @@ k_compact_copy(const long long* __restrict__ src, const long long* __restrict__ 
 
 __global__ void k_set_i64(long long* p, long long v) { *p = v; }
 
+// ---- batched, ragged compaction ---------------------------------------------
+// Per sequence the closed form above holds with the sequence's own counters:
+// k = IMG_CONTEXT tokens of the sequence before p, tiles numbered from
+// tile_off[b], routed_before taken relative to tile_off[b], and the result
+// placed at out_cu[b] + (p - cu[b]) - f.  Kernels:
+//   k_compact_count (shared)  per-block IMG_CONTEXT counts
+//   k_compact_plan  (shared)  block offsets and routed_before, no L' / status
+//   k_cbatch_bounds           IMG_CONTEXT count before every sequence start
+//   k_cbatch_plan             layout check, per-sequence L'_b, slot check,
+//                             out_cu = exclusive scan of L'_b
+//   k_cbatch_map              keep flag, destination, ids, positions, source
+//   k_compact_copy  (shared)  the embedding rows
+
+// One wave per sequence boundary b <= B: IMG_CONTEXT tokens before cu[b].
+__global__ void __launch_bounds__(256)
+k_cbatch_bounds(const int32_t* __restrict__ ids, long long L, int img,
+                const int32_t* __restrict__ cu, int B, const int32_t* __restrict__ blk_off,
+                int32_t* __restrict__ seq_img) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b > B) return;
+  const long long p0 = min(max((long long)cu[b], 0ll), L);  // out-of-range offsets are flagged later
+  const long long blk = p0 / CB;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < CB / 64; ++i) {
+    const long long p = blk * CB + lane + 64 * i;
+    c += (p < p0 && ids[p] == img) ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  if (lane == 0) seq_img[b] = blk_off[blk] + c;
+}
+
+__global__ void __launch_bounds__(1024)
+k_cbatch_plan(const int32_t* __restrict__ cu, const int32_t* __restrict__ tile_off, int B,
+              long long L, int T, int S, int S64, const int32_t* __restrict__ seq_img,
+              const int32_t* __restrict__ routed_before, int32_t* __restrict__ out_cu,
+              int32_t* __restrict__ seq_ok, long long* __restrict__ total,
+              int32_t* __restrict__ layout_ok, int32_t* __restrict__ status) {
+  __shared__ int bad, any_miss;
+  __shared__ long long carry_s;
+  __shared__ long long wsum[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) {
+    bad = (cu[0] != 0 || (long long)cu[B] != L || tile_off[0] < 0 || tile_off[B] > T) ? 1 : 0;
+    any_miss = 0;
+    carry_s = 0;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += blockDim.x)
+    if (cu[b] > cu[b + 1] || tile_off[b] > tile_off[b + 1]) atomicOr(&bad, 1);
+  __syncthreads();
+  if (bad) {  // not an ordered partition: empty result
+    for (int b = threadIdx.x; b <= B; b += blockDim.x) out_cu[b] = 0;
+    if (threadIdx.x == 0) {
+      *total = 0;
+      *layout_ok = 0;
+      atomicOr(status, 8);
+    }
+    return;
+  }
+  const long long drop = S - S64;
+  for (int c0 = 0; c0 < B; c0 += 1024) {
+    const int b = c0 + threadIdx.x;
+    long long v = 0;
+    if (b < B) {
+      const int t0 = tile_off[b], t1 = tile_off[b + 1];
+      const bool ok = (long long)(seq_img[b + 1] - seq_img[b]) == (long long)S * (t1 - t0);
+      if (ok)
+        v = (long long)(cu[b + 1] - cu[b]) - drop * (routed_before[t1] - routed_before[t0]);
+      else
+        atomicOr(&any_miss, 1);
+      seq_ok[b] = ok ? 1 : 0;
+    }
+    long long inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    long long before = 0, tot = 0;
+    for (int k = 0; k < 16; ++k) {
+      if (k < w) before += wsum[k];
+      tot += wsum[k];
+    }
+    const long long carry = carry_s;
+    if (b < B) out_cu[b] = (int32_t)(carry + before + inc - v);
+    __syncthreads();
+    if (threadIdx.x == 0) carry_s = carry + tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out_cu[B] = (int32_t)carry_s;
+    *total = carry_s;
+    *layout_ok = 1;
+    if (any_miss) atomicOr(status, 1);
+  }
+}
+
+__global__ void __launch_bounds__(CT)
+k_cbatch_map(const int32_t* __restrict__ ids, long long L, int img,
+             const uint8_t* __restrict__ use64, int S, int S64, const int32_t* __restrict__ cu,
+             const int32_t* __restrict__ tile_off, int B, const int32_t* __restrict__ blk_off,
+             const int32_t* __restrict__ routed_before, const int32_t* __restrict__ seq_img,
+             const int32_t* __restrict__ seq_ok, const int32_t* __restrict__ out_cu,
+             const long long* __restrict__ total, const int32_t* __restrict__ layout_ok,
+             int32_t* __restrict__ out_ids, int32_t* __restrict__ out_pos,
+             int32_t* __restrict__ keep_map, long long* __restrict__ src) {
+  const long long base = (long long)blockIdx.x * CB + threadIdx.x * 4;
+  if (*layout_ok == 0) {  // uniform over the grid
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (base + e < L) keep_map[base + e] = out_ids[base + e] = out_pos[base + e] = -1;
+    return;
+  }
+  int tok[4], c = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    tok[e] = base + e < L ? ids[base + e] : 0;
+    c += (base + e < L && tok[e] == img) ? 1 : 0;
+  }
+  __shared__ int sh[4];
+  int blk_total;
+  int g = blk_off[blockIdx.x] + block_excl_scan(c, sh, &blk_total);  // IMG_CONTEXT before base
+  if (base >= L) return;
+  const long long Lp = *total;
+  const long long drop = S - S64;
+  // sequence holding position base: the last b with cu[b] <= base (cu[B] = L > base)
+  int lo = 0, hi = B;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)cu[mid] <= base) lo = mid;
+    else hi = mid - 1;
+  }
+  int b = -1;
+  long long c0 = 0, c1 = 0;
+  int t0 = 0, nt = 0, rb0 = 0, g0 = 0, ok = 0, oc = 0;
+  auto enter = [&](int nb) {
+    b = nb;
+    c0 = cu[b];
+    c1 = cu[b + 1];
+    t0 = tile_off[b];
+    nt = tile_off[b + 1] - t0;
+    rb0 = routed_before[t0];
+    g0 = seq_img[b];
+    ok = seq_ok[b];
+    oc = out_cu[b];
+  };
+  enter(lo);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const long long p = base + e;
+    if (p >= L) break;
+    if (p >= c1) {
+      int nb = b + 1;
+      while ((long long)cu[nb + 1] <= p) ++nb;  // skips empty sequences; ends since cu[B] = L
+      enter(nb);
+    }
+    const bool is_img = tok[e] == img;
+    const int k = g - g0;  // IMG_CONTEXT of this sequence before p
+    const int tl = k / S, loc = k - tl * S;
+    long long f;  // slots of this sequence deleted before p
+    bool keep = ok != 0;
+    long long code = p;
+    if (tl < nt) {
+      const int tile = t0 + tl;
+      const int u = use64[tile] != 0;
+      f = drop * (routed_before[tile] - rb0) + (u ? max(0, loc - S64) : 0);
+      if (is_img) {
+        keep = keep && (!u || loc < S64);
+        code = u ? ((2ll << 60) | ((long long)tile * S64 + loc))
+                 : ((1ll << 60) | ((long long)tile * S + loc));
+      }
+    } else {
+      // text after the sequence's last slot (an extra slot only occurs when ok = 0)
+      f = drop * (routed_before[t0 + nt] - rb0);
+      if (is_img) keep = false;
+    }
+    const long long jl = (p - c0) - f;
+    const long long j = oc + jl;
+    keep_map[p] = keep ? (int32_t)j : -1;
+    if (keep) {
+      out_ids[j] = tok[e];
+      out_pos[j] = (int32_t)jl;
+      src[j] = code;
+    }
+    if (p >= Lp) out_ids[p] = out_pos[p] = -1;
+    if (is_img) ++g;
+  }
+}
+
+static hipError_t launch_copy(const CompactArgs& a, const long long* len, hipStream_t s) {
+  const int esz = a.dtype == DT_BF16 ? 2 : 4;
+  const int vpr = (int)((long long)a.D * esz / 16);
+  const int vpl = (vpr + 63) / 64;
+  dim3 grid((unsigned)((a.L + 3) / 4));
+#define IVC_COPY(n)                                                                              \
+  hipLaunchKernelGGL(k_compact_copy<n>, grid, dim3(256), 0, s, (const long long*)a.src, len,    \
+                     (const u32x4*)a.embeds, (const u32x4*)a.out256, (const u32x4*)a.out64,     \
+                     (u32x4*)a.out_embeds, vpr, a.L)
+  if (vpl <= 1) IVC_COPY(1);
+  else if (vpl <= 2) IVC_COPY(2);
+  else if (vpl <= 4) IVC_COPY(4);
+  else if (vpl <= 8) IVC_COPY(8);
+  else if (vpl <= 16) IVC_COPY(16);
+  else return hipErrorInvalidValue;
+#undef IVC_COPY
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_batch(const CompactBatchArgs& ba, hipStream_t s) {
+  const CompactArgs& a = ba.base;
+  const long long nblk = compact_blocks(a.L);
+  if (a.L > 0) {
+    hipLaunchKernelGGL(k_compact_count, dim3((unsigned)nblk), dim3(CT), 0, s, a.ids, a.L, a.img_id,
+                       a.blk_cnt);
+  }
+  hipLaunchKernelGGL(k_compact_plan, dim3(1), dim3(1024), 0, s, (const int32_t*)a.blk_cnt, nblk,
+                     a.use64, a.T, a.S, a.S64, a.L, a.blk_off, a.routed_before,
+                     (long long*)nullptr, a.status);
+  hipLaunchKernelGGL(k_cbatch_bounds, dim3((unsigned)((ba.B + 1 + 3) / 4)), dim3(256), 0, s, a.ids,
+                     a.L, a.img_id, ba.cu, ba.B, (const int32_t*)a.blk_off, ba.seq_img);
+  hipLaunchKernelGGL(k_cbatch_plan, dim3(1), dim3(1024), 0, s, ba.cu, ba.tile_off, ba.B, a.L, a.T,
+                     a.S, a.S64, (const int32_t*)ba.seq_img, (const int32_t*)a.routed_before,
+                     ba.out_cu, ba.seq_ok, ba.total, ba.layout_ok, a.status);
+  if (a.L == 0) return hipGetLastError();
+  hipLaunchKernelGGL(k_cbatch_map, dim3((unsigned)nblk), dim3(CT), 0, s, a.ids, a.L, a.img_id,
+                     a.use64, a.S, a.S64, ba.cu, ba.tile_off, ba.B, (const int32_t*)a.blk_off,
+                     (const int32_t*)a.routed_before, (const int32_t*)ba.seq_img,
+                     (const int32_t*)ba.seq_ok, (const int32_t*)ba.out_cu,
+                     (const long long*)ba.total, (const int32_t*)ba.layout_ok, a.out_ids, a.out_pos,
+                     a.keep_map, a.src);
+  return launch_copy(a, ba.total, s);
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const long long nblk = compact_blocks(a.L);
   if (a.L == 0) {
@@ -206,22 +447,7 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
                      a.use64, a.T, a.S, a.S64, (const int32_t*)a.blk_off,
                      (const int32_t*)a.routed_before, (const long long*)a.out_len, a.out_ids,
                      a.out_pos, a.keep_map, a.src);
-  const int esz = a.dtype == DT_BF16 ? 2 : 4;
-  const int vpr = (int)((long long)a.D * esz / 16);
-  const int vpl = (vpr + 63) / 64;
-  dim3 grid((unsigned)((a.L + 3) / 4));
-#define IVC_COPY(n)                                                                              \
-  hipLaunchKernelGGL(k_compact_copy<n>, grid, dim3(256), 0, s, (const long long*)a.src,         \
-                     (const long long*)a.out_len, (const u32x4*)a.embeds, (const u32x4*)a.out256, \
-                     (const u32x4*)a.out64, (u32x4*)a.out_embeds, vpr, a.L)
-  if (vpl <= 1) IVC_COPY(1);
-  else if (vpl <= 2) IVC_COPY(2);
-  else if (vpl <= 4) IVC_COPY(4);
-  else if (vpl <= 8) IVC_COPY(8);
-  else if (vpl <= 16) IVC_COPY(16);
-  else return hipErrorInvalidValue;
-#undef IVC_COPY
-  return hipGetLastError();
+  return launch_copy(a, (const long long*)a.out_len, s);
 }
 
 // ---- ragged tile offsets -------------------------------------------------------

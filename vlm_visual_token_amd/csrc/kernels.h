@@ -143,12 +143,29 @@ struct CompactArgs {
   int32_t* status;
   // workspace
   int32_t* blk_cnt;        // [nblk]
-  int32_t* blk_off;        // [nblk]
+  int32_t* blk_off;        // [nblk + 1]
   int32_t* routed_before;  // [T + 1]
   long long* src;          // [L] source row code per output row
 };
 long long compact_blocks(long long L);
+
+// Batched form: B sequences packed back to back (sequence b = positions
+// cu[b] .. cu[b+1]-1, tiles tile_off[b] .. tile_off[b+1]-1), each compacted
+// on its own, outputs packed at out_cu[b].
+struct CompactBatchArgs {
+  CompactArgs base;          // out_len unused; status, sequence and embedding pointers as above
+  const int32_t* cu;         // [B + 1]
+  const int32_t* tile_off;   // [B + 1]
+  int B;
+  int32_t* out_cu;           // [B + 1]
+  // workspace
+  int32_t* seq_img;          // [B + 1] IMG_CONTEXT count before each sequence start
+  int32_t* seq_ok;           // [B] 1: the sequence's slot count matches its tiles
+  long long* total;          // [1] packed length (copy bound)
+  int32_t* layout_ok;        // [1]
+};
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_compact_batch(const CompactBatchArgs& a, hipStream_t s);
 
 // Per-path tile lists of a routing decision: rank[t] = index of t among the
 // tiles of its path, list256 / list64 = tile ids in order, counts = {n256, n64}.

@@ -22,6 +22,7 @@ IVC_DEV_OK = 0
 IVC_DEV_ERR_IMG_COUNT = 1
 IVC_DEV_ERR_VALID_TOKENS = 2
 IVC_DEV_ERR_TILE_COUNT = 4
+IVC_DEV_ERR_SEQ_LAYOUT = 8
 MAX_POOL_LAYERS = 8
 GATE_BLOCKS = 4
 
@@ -85,6 +86,9 @@ def load() -> ctypes.CDLL:
         "ivc_connector_route": (c_int32, [P, P, P, c_int32, P, P, P, P, P, P, c_size_t, P]),
         "ivc_connector_compact": (c_int32, [P, P, P, c_int64, c_int32, P, P, P, c_int32, P, P, P,
                                             P, P, P, P, c_size_t, P]),
+        "ivc_connector_compact_batch": (c_int32, [P, P, P, c_int32, P, c_int64, c_int32, P, P, P,
+                                                  P, c_int32, P, P, P, P, P, P, P, c_size_t, P]),
+        "ivc_connector_compact_batch_workspace_bytes": (c_size_t, [P, c_int32, c_int64, c_int32]),
         "ivc_route_decide": (c_int32, [P, c_int32, c_double, c_double, P, P, P]),
         "ivc_tile_offsets": (c_int32, [P, c_int32, P, P, P]),
         "ivc_pixel_shuffle": (c_int32, [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32,
@@ -106,7 +110,8 @@ def load() -> ctypes.CDLL:
 def exported_symbols() -> list[str]:
     return [
         "ivc_connector_create", "ivc_connector_destroy", "ivc_connector_workspace_bytes",
-        "ivc_connector_run", "ivc_connector_run_routed", "ivc_connector_route", "ivc_connector_compact", "ivc_route_decide",
+        "ivc_connector_run", "ivc_connector_run_routed", "ivc_connector_route", "ivc_connector_compact",
+        "ivc_connector_compact_batch", "ivc_connector_compact_batch_workspace_bytes", "ivc_route_decide",
         "ivc_tile_offsets",
         "ivc_pixel_shuffle", "ivc_profile_enable", "ivc_profile_reset", "ivc_profile_read",
         "ivc_status_string", "ivc_last_error",
@@ -235,6 +240,22 @@ def ivc_connector_compact(h, ids, embeds, L, img_context_id, use64, out256, out6
                                         _ptr(out_pos), _ptr(keep_map), _ptr(out_embeds),
                                         _ptr(out_len), _ptr(dev_status), _ptr(ws), ws_bytes,
                                         _stream(stream)), "ivc_connector_compact")
+
+
+def ivc_connector_compact_batch(h, ids, cu_seqlens, B, embeds, L, img_context_id, tile_offsets,
+                                use64, out256, out64, T, out_ids, out_pos, keep_map, out_embeds,
+                                out_cu_seqlens, dev_status, ws, ws_bytes, stream=None) -> None:
+    _check(load().ivc_connector_compact_batch(
+        h, _ptr(ids), _ptr(cu_seqlens), B, _ptr(embeds), L, img_context_id, _ptr(tile_offsets),
+        _ptr(use64), _ptr(out256), _ptr(out64), T, _ptr(out_ids), _ptr(out_pos), _ptr(keep_map),
+        _ptr(out_embeds), _ptr(out_cu_seqlens), _ptr(dev_status), _ptr(ws), ws_bytes,
+        _stream(stream)), "ivc_connector_compact_batch")
+
+
+def ivc_connector_compact_batch_workspace_bytes(h, max_tiles: int, max_total_len: int,
+                                                max_seqs: int) -> int:
+    return load().ivc_connector_compact_batch_workspace_bytes(h, max_tiles, max_total_len,
+                                                              max_seqs)
 
 
 def ivc_route_decide(gate, T, rel_quantile, abs_threshold, threshold, use64, stream=None) -> None:
