@@ -9,7 +9,9 @@ synthetic (seeded) and resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is tiles per second; ``roofline`` describes
 the dominant kernel, timed with HIP events on the launch stream inside the
-timed region; ``cpu_baseline`` times the CPU oracle on a bounded sample.
+timed region; ``cpu_baseline`` times the CPU oracle on a bounded sample;
+``compact_batch`` times the variable-length batch compaction on 64 prompts of
+the same layout packed back to back (3.4M tokens), outside the step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -134,9 +136,57 @@ def cpu_baseline(cfg, w, seq, n_tiles: int) -> dict:
                       f"({t3 - t2:.2f} s); scaled to one {T}-tile batch"}
 
 
+def compact_batch_stress(con, cfg, n_prompts, use64_one, torch, synth, ivc) -> dict:
+    """Batched compaction at serving scale: n_prompts prompts of this
+    workload's layout packed back to back (each with its own tiles, routed as
+    the timed batch was), one ivc_connector_compact_batch call per step.
+    Rows are copies, so the embedding and feature buffers are zero-filled."""
+    B = n_prompts
+    ids, _, cu, to = synth.make_batch_sequences(cfg, [cfg["tiles"]] * B, 0, with_embeds=False)
+    L, T, D, S, S64 = len(ids), int(to[-1]), cfg["D"], cfg["S"], cfg["S64"]
+    use = np.tile(use64_one, B).astype(np.uint8)
+    dev = "cuda"
+    ids_d = torch.from_numpy(ids).to(dev)
+    cu_d = torch.from_numpy(cu).to(dev)
+    to_d = torch.from_numpy(to).to(dev)
+    use_d = torch.from_numpy(use).to(dev)
+    emb = torch.zeros((L, D), dtype=torch.bfloat16, device=dev)
+    o256 = torch.zeros((T, S, D), dtype=torch.bfloat16, device=dev)
+    o64 = torch.zeros((T, S64, D), dtype=torch.bfloat16, device=dev)
+    n = ivc.ivc_connector_compact_batch_workspace_bytes(con.h, T, L, B)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = None
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        out = con.compact_batch(ids_d, cu_d, emb, to_d, use_d, o256, o64, synth.IMG_CONTEXT,
+                                stream=stream, out=out, ws=ws)
+    torch.cuda.synchronize()
+    reps = 10
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        con.compact_batch(ids_d, cu_d, emb, to_d, use_d, o256, o64, synth.IMG_CONTEXT,
+                          stream=stream, out=out, ws=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    Lp = int(out["cu"][-1].item())
+    assert int(out["status"].item()) == 0 and Lp == L - (S - S64) * int(use.sum())
+    byts = 2 * Lp * D * 2 + L * 4 * 2 + Lp * 4 * 2
+    gbs = byts / (ms / 1e3) / 1e9
+    res = {"prompts": B, "tiles": T, "L": L, "L_out": Lp, "ms": ms, "gbs": gbs,
+           "frac_hbm": gbs / PEAK_HBM_GBS, "algorithmic_bytes": byts}
+    del emb, o256, o64, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--compact-prompts", type=int, default=64,
+                    help="prompts in the batched-compaction measurement (0: skip)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--pool-mode", type=int, default=1,
@@ -269,6 +319,11 @@ def main():
 
     roof["traffic"] = committed_traffic(dom)
 
+    cb = None
+    if args.compact_prompts > 0:
+        print(f"# batched compaction, {args.compact_prompts} prompts", file=sys.stderr, flush=True)
+        cb = compact_batch_stress(con, cfg, args.compact_prompts, use64, torch, synth, ivc)
+
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
@@ -304,6 +359,7 @@ def main():
         "input_vit_tokens_per_s": T * cfg["N"] / (ms_step / 1e3),
         "routed_to_64": int(use64.sum()),
         "compacted_len": Lp,
+        "compact_batch": cb,
         "roofline": roof,
         "kernels": kern,
         "kernel_events": ("separate pass, projector chains serialised"
