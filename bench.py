@@ -185,6 +185,8 @@ def compact_batch_stress(con, cfg, n_prompts, use64_one, torch, synth, ivc) -> d
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--ln-fold", type=int, default=1,
+                    help="1: fold the projectors' LayerNorm into their first product")
     ap.add_argument("--compact-prompts", type=int, default=64,
                     help="prompts in the batched-compaction measurement (0: skip)")
     ap.add_argument("--steps", type=int, default=20)
@@ -219,7 +221,7 @@ def main():
 
     with open(os.path.join(ROOT, "tests", "golden", "gate_bias.json")) as f:
         bias = json.load(f)["gate_bias0"][WORKLOAD]
-    cfg = dict(synth.config(WORKLOAD), pool_mode=args.pool_mode)
+    cfg = dict(synth.config(WORKLOAD), pool_mode=args.pool_mode, ln_fold=args.ln_fold)
     T = cfg["T"]
     w = synth.make_weights(cfg, gate_bias0=bias)
     wd = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in w.items()}
@@ -299,6 +301,9 @@ def main():
         e, C = 2, cfg["C"]
         hbm["shuffle_ln"] = (T * cfg["N"] * C * e + (T - n64) * cfg["S"] * 4 * C * e
                              + n64 * cfg["S64"] * 16 * C * e)
+    if args.ln_fold:  # the loader reads the rows and writes 8 bytes of statistics per LN row
+        e, C = 2, cfg["C"]
+        hbm["shuffle_ln"] = T * cfg["N"] * C * e + T * (cfg["S"] + cfg["S64"]) * 8
     kern = {k: {"ms_avg": v[0] / v[1], "launches_per_step": v[1] / args.steps,
                 "ms_per_step": v[0] / args.steps} for k, v in prof.items()}
     dom = max(kern, key=lambda k: kern[k]["ms_per_step"])
@@ -353,7 +358,7 @@ def main():
         "config": {"workload": WORKLOAD, "tiles": T, "images": len(cfg["tiles"]),
                    "vit_tokens_per_tile": cfg["N"], "vit_width": cfg["C"], "llm_width": cfg["D"],
                    "seq_len": L, "pool_mode": "kv" if args.pool_mode == 0 else "folded",
-                   "run_mode": args.run_mode,
+                   "run_mode": args.run_mode, "ln_fold": bool(args.ln_fold),
                    "parallelism": "single GPU"},
         "visual_tokens_per_s": emitted / (ms_step / 1e3),
         "input_vit_tokens_per_s": T * cfg["N"] / (ms_step / 1e3),

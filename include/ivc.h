@@ -108,7 +108,8 @@ typedef struct ivc_config {
   int32_t ps_version;     /* pixel_shuffle version: 2 (or 0) = v2; 1 = v1, whose
                              token grid is transposed ([14B] v1/v2 section)     */
   int32_t shuffle64_order;/* ivc_shuffle64_order: channel order of the 64-token path */
-  int32_t reserved;       /* 0                                                      */
+  int32_t ln_fold;        /* 1: fold the projectors' LayerNorm into their first
+                             Linear (bf16 only; see ivc_connector_create)       */
   double rel_quantile;    /* relative threshold, a quantile level (0.1)             */
   double abs_threshold;   /* absolute threshold on gate[:, 0] (0.5)                 */
   float ln_eps;           /* LayerNorm epsilon (1e-5, torch's default)              */
@@ -141,6 +142,17 @@ typedef struct ivc_weights {
 } ivc_weights;
 
 typedef struct ivc_connector ivc_connector;
+
+/* LayerNorm fold (ln_fold = 1): mlp1 and mlp2 each start LayerNorm -> Linear,
+ * and LN(x) W^T + b = rstd (x . (gamma o W)^T) - rstd mean colsum(gamma o W)
+ * + (b + W beta).  create() stores gamma o W (rounded to bf16), its column
+ * sums and the folded bias; run and run_routed then write only each row's
+ * (mean, rstd) and the first product reads the raw ViT rows in pixel-shuffle
+ * order, so the normalised rows are never written.  Same results up to
+ * rounding (the bf16 rounding moves from the normalised rows to gamma o W).
+ * Needs bf16, C % 64 == 0 and the hidden widths % 8 == 0 (IVC_ERR_UNSUPPORTED
+ * otherwise); a call may then pass at most 2 GiB of ViT rows
+ * (T * (has_cls + P*P) * C * 2 bytes; IVC_ERR_UNSUPPORTED beyond). */
 
 /* Build a connector: validates the config, copies the weights into
  * library-owned device memory (biases and LayerNorm parameters widened to

@@ -64,6 +64,8 @@ def _cfg(**kw):
     (dict(C=62), 3),
     (dict(pool_layers=9), 1),
     (dict(ps_version=3), 1),
+    (dict(ln_fold=2), 1),
+    (dict(ln_fold=1), 2),  # the tiny workload is fp32: the fold needs bf16
 ])
 def test_create_rejects_bad_config_on_host(bad, status):
     c = ivc.make_config(_cfg(**bad))

@@ -600,3 +600,62 @@ def test_compact_batch_flash_layout_16_prompts():
     m3 = code >= L + T * S
     want[m3] = o64.view(-1, D)[code[m3] - L - T * S]
     assert torch.equal(c["embeds"][:n].view(torch.int16), want.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm folded into the first product of each projector (ln_fold)
+# ---------------------------------------------------------------------------
+def _tiny_bf16(T, **over):
+    cfg = workload("tiny_flash_f32", dtype="bf16", **over)
+    return dict(cfg, T=T, tiles=[T], name="tiny_bf16")
+
+
+@pytest.mark.parametrize("T,version,order,shift", [
+    (1, 2, "direct", 0.0), (5, 2, "direct", 0.0), (11, 2, "direct", 3.0), (5, 1, "direct", 0.0),
+    (5, 2, "twice_r2", 0.0), (7, 1, "twice_r2", 3.0)])
+def test_ln_fold_small_matches_oracle(T, version, order, shift):
+    # shift: LayerNorm ignores a constant added to a row, so a large common
+    # offset (mean >> spread) must cancel exactly in the folded epilogue
+    cfg = _tiny_bf16(T, ln_fold=1, ps_version=version, shuffle64_order=order)
+    w = synth.make_weights(cfg)
+    x = synth.to_bf16_exact(synth.make_vit_tiles(cfg, range(T)) + np.float32(shift))
+    say(f"ln_fold small T={T} v{version} {order} shift={shift}")
+    con = _connector(cfg, w, T)
+    o256, o64 = con.run(torch.from_numpy(x).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    e256, e64 = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256), e256, "bf16", "out256")
+    assert_close(to_np(o64), e64, "bf16", "out64")
+
+
+@pytest.mark.parametrize("pattern", ["none", "all", "alternate"])
+def test_ln_fold_run_routed_small(pattern):
+    T = 9
+    cfg = _tiny_bf16(T, ln_fold=1)
+    w = synth.make_weights(cfg)
+    x = synth.make_vit_tiles(cfg, range(T))
+    say(f"ln_fold run_routed small pattern={pattern}")
+    con = _connector(cfg, w, T)
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    use = {"none": np.zeros(T), "all": np.ones(T), "alternate": np.arange(T) % 2}[pattern]
+    _check_routed(con, cfg, xd, torch.from_numpy(use.astype(np.uint8)).cuda())
+
+
+def test_ln_fold_flash_workload_sampled():
+    cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
+    say(f"2B-Flash ln_fold run_routed: T={cfg['T']}")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, cfg["T"])
+    xd = dev_vit(cfg)
+    r = con.route(xd)
+    use_d = r["use64"]
+    f256, f64, r256, r64 = _check_routed(con, cfg, xd, use_d)
+    use = use_d.cpu().numpy()
+    tiles = synth.sample_tiles(cfg["T"])
+    x = synth.make_vit_tiles(cfg, tiles)
+    e256, e64 = O.connector_run(x, cfg, w)
+    t256 = [i for i, t in enumerate(tiles) if use[t] == 0]
+    t64 = [i for i, t in enumerate(tiles) if use[t] != 0]
+    assert t256 and t64
+    assert_close(to_np(r256[[tiles[i] for i in t256]]), e256[t256], "bf16", "out256 (ln_fold)")
+    assert_close(to_np(r64[[tiles[i] for i in t64]]), e64[t64], "bf16", "out64 (ln_fold)")

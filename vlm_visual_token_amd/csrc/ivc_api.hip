@@ -144,6 +144,8 @@ struct ivc_connector {
   void *m1_w1, *m1_w2;
   float *m2_ln_w, *m2_ln_b, *m2_b1, *m2_b2, *m2_b3;
   void *m2_w1, *m2_w2, *m2_w3;
+  // ln_fold: m*_w1 hold gamma o W1, m*_b1 the folded bias, m*_cs the column sums
+  float *m1_cs = nullptr, *m2_cs = nullptr;
   // router
   void* query;
   void *wq[IVC_MAX_POOL_LAYERS], *wo[IVC_MAX_POOL_LAYERS];
@@ -216,7 +218,12 @@ ivc_status check_cfg(const ivc_config& c) {
     return fail(IVC_ERR_INVALID_ARG, "ps_version %d", c.ps_version);
   if (c.shuffle64_order != IVC_SHUFFLE64_DIRECT && c.shuffle64_order != IVC_SHUFFLE64_TWICE_R2)
     return fail(IVC_ERR_INVALID_ARG, "shuffle64_order %d", c.shuffle64_order);
-  if (c.reserved != 0) return fail(IVC_ERR_INVALID_ARG, "reserved must be 0");
+  if (c.ln_fold != 0 && c.ln_fold != 1) return fail(IVC_ERR_INVALID_ARG, "ln_fold %d", c.ln_fold);
+  if (c.ln_fold) {
+    if (c.dtype != IVC_BF16) return fail(IVC_ERR_UNSUPPORTED, "ln_fold needs bf16");
+    if (c.vit_width % 64 || c.mlp1_hidden % 8 || (c.flash && c.mlp2_hidden % 8))
+      return fail(IVC_ERR_UNSUPPORTED, "ln_fold needs C %% 64 == 0 and hidden widths %% 8 == 0");
+  }
   if (c.flash) {
     if (c.mlp2_hidden <= 0 || (long long)c.mlp2_hidden * esz % 16)
       return fail(IVC_ERR_INVALID_ARG, "mlp2_hidden");
@@ -307,6 +314,7 @@ int pool_splits(int T, int N) {
 // ---- workspace plans ----
 struct RunWs {
   void *a2, *a4, *h1, *g1, *g2;
+  float *st2, *st4;  // ln_fold: (mean, rstd) per LayerNorm row instead of a2 / a4
   int *rank, *list256, *list64, *counts;  // route-first run only
   SimtScratch sc;
 };
@@ -316,10 +324,16 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
   const size_t S = (size_t)(c.grid / 2) * (c.grid / 2), S4 = (size_t)(c.grid / 4) * (c.grid / 4);
   Carver cv(base);
   RunWs r{};
-  r.a2 = cv.take((size_t)T * S * 4 * c.vit_width * e);
+  if (c.ln_fold)
+    r.st2 = (float*)cv.take((size_t)T * S * 2 * 4);
+  else
+    r.a2 = cv.take((size_t)T * S * 4 * c.vit_width * e);
   r.h1 = cv.take((size_t)T * S * c.mlp1_hidden * e);
   if (c.flash) {
-    r.a4 = cv.take((size_t)T * S4 * 16 * c.vit_width * e);
+    if (c.ln_fold)
+      r.st4 = (float*)cv.take((size_t)T * S4 * 2 * 4);
+    else
+      r.a4 = cv.take((size_t)T * S4 * 16 * c.vit_width * e);
     r.g1 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
     r.g2 = cv.take((size_t)T * S4 * c.mlp2_hidden * e);
     r.rank = (int*)cv.take((size_t)T * 4);
@@ -487,6 +501,10 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
     h->m1_b1 = (float*)cv.take(H1 * 4);
     h->m1_w2 = cv.take(D * H1 * e);
     h->m1_b2 = (float*)cv.take(D * 4);
+    if (c.ln_fold) {
+      h->m1_cs = (float*)cv.take(H1 * 4);
+      if (c.flash) h->m2_cs = (float*)cv.take(H2 * 4);
+    }
     if (c.flash) {
       h->m2_ln_w = (float*)cv.take(16 * C * 4);
       h->m2_ln_b = (float*)cv.take(16 * C * 4);
@@ -535,17 +553,25 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       return s_;                  \
     }                             \
   } while (0)
+  auto fold_or_copy = [&](const void* W1, void* dst, size_t N, size_t K, const float* g,
+                          const float* b, float* bias, float* cs) -> ivc_status {
+    if (!c.ln_fold) return copy_mat(W1, dst, N * K * e, s);
+    return launch_ln_fold_weights(W1, (int)N, (int)K, g, b, bias, dst, cs, bias, s) == hipSuccess
+               ? IVC_OK
+               : fail(IVC_ERR_HIP, "LayerNorm fold launch failed");
+  };
   STEP(widen(w->mlp1_ln_w, dt, h->m1_ln_w, 4 * C, s));
   STEP(widen(w->mlp1_ln_b, dt, h->m1_ln_b, 4 * C, s));
-  STEP(copy_mat(w->mlp1_w1, h->m1_w1, H1 * 4 * C * e, s));
   STEP(widen(w->mlp1_b1, dt, h->m1_b1, H1, s));
+  STEP(fold_or_copy(w->mlp1_w1, h->m1_w1, H1, 4 * C, h->m1_ln_w, h->m1_ln_b, h->m1_b1, h->m1_cs));
   STEP(copy_mat(w->mlp1_w2, h->m1_w2, D * H1 * e, s));
   STEP(widen(w->mlp1_b2, dt, h->m1_b2, D, s));
   if (c.flash) {
     STEP(widen(w->mlp2_ln_w, dt, h->m2_ln_w, 16 * C, s));
     STEP(widen(w->mlp2_ln_b, dt, h->m2_ln_b, 16 * C, s));
-    STEP(copy_mat(w->mlp2_w1, h->m2_w1, H2 * 16 * C * e, s));
     STEP(widen(w->mlp2_b1, dt, h->m2_b1, H2, s));
+    STEP(fold_or_copy(w->mlp2_w1, h->m2_w1, H2, 16 * C, h->m2_ln_w, h->m2_ln_b, h->m2_b1,
+                      h->m2_cs));
     STEP(copy_mat(w->mlp2_w2, h->m2_w2, H2 * H2 * e, s));
     STEP(widen(w->mlp2_b2, dt, h->m2_b2, H2, s));
     STEP(copy_mat(w->mlp2_w3, h->m2_w3, D * H2 * e, s));
@@ -649,6 +675,9 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     rm64.c_rpg = S4;
   }
 
+  const bool fold = c.ln_fold != 0;
+  if (fold && (long long)T * (c.has_cls + c.grid * c.grid) * C * 2 >= (1ll << 31) - (1ll << 24))
+    return fail(IVC_ERR_UNSUPPORTED, "ln_fold: %d tiles of ViT rows exceed 2 GiB", T);
   ShuffleArgs sa{};
   sa.dtype = dt;
   sa.X = vit;
@@ -660,10 +689,12 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   sa.ln = 1;
   sa.g2 = h->m1_ln_w;
   sa.b2 = h->m1_ln_b;
-  sa.out2 = w.a2;
+  sa.out2 = fold ? nullptr : w.a2;
   sa.g4 = h->m2_ln_w;
   sa.b4 = h->m2_ln_b;
-  sa.out4 = w.a4;
+  sa.out4 = fold ? nullptr : w.a4;
+  sa.st2 = fold ? w.st2 : nullptr;
+  sa.st4 = fold && c.flash ? w.st4 : nullptr;
   sa.eps = c.ln_eps;
   sa.ps_v1 = c.ps_version == 1;
   sa.twice_r2 = c.shuffle64_order == IVC_SHUFFLE64_TWICE_R2;
@@ -687,19 +718,54 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     s1 = h->aux;
   }
   const int M2 = (int)(T * S);
+  // first product of a projector: the LayerNorm'd rows, or (ln_fold) the raw
+  // ViT rows gathered in shuffle order with the LayerNorm applied in the epilogue
+  auto first_gemm = [&](int r, void* a_rows, const float* st, const int* list, const void* W1,
+                        const float* b1, const float* cs, void* out, int M, int N,
+                        const RowMap& rm) -> GemmArgs {
+    GemmArgs f;
+    if (!fold) {
+      f = mk_gemm(a_rows, (long long)r * r * C, dt, W1, dt, b1, out, dt, M, N, r * r * C, ACT_GELU);
+    } else {
+      f = mk_gemm(vit, C, dt, W1, dt, b1, out, dt, M, N, r * r * C, ACT_GELU);
+      f.fold = 1;
+      f.ag.list = list;
+      f.ag.rows = c.has_cls + c.grid * c.grid;
+      f.ag.has_cls = c.has_cls;
+      f.ag.P = c.grid;
+      f.ag.r = r;
+      f.ag.C = C;
+      f.ag.v1 = c.ps_version == 1;
+      f.ag.twice = r == 4 && c.shuffle64_order == IVC_SHUFFLE64_TWICE_R2;
+      f.ln_rows = st;
+      f.ln_colsum = cs;
+    }
+    f.rm = rm;
+    return f;
+  };
   GemmArgs g;
-  g = mk_gemm(w.a2, 4 * C, dt, h->m1_w1, dt, h->m1_b1, w.h1, dt, M2, H1, 4 * C, ACT_GELU);
-  g.rm = rmh256;
-  LAUNCH("mlp1_gemm1", s1, gemm("mlp1_gemm1", g, s1, &w.sc));
+  g = first_gemm(2, w.a2, w.st2, use64 ? w.list256 : nullptr, h->m1_w1, h->m1_b1, h->m1_cs, w.h1,
+                 M2, H1, rmh256);
+  if (fold) {
+    if (!gemm_dma_supported(g)) return fail(IVC_ERR_UNSUPPORTED, "ln_fold: mlp1 product shape");
+    LAUNCH("mlp1_gemm1", s1, launch_gemm_dma(g, s1));
+  } else {
+    LAUNCH("mlp1_gemm1", s1, gemm("mlp1_gemm1", g, s1, &w.sc));
+  }
   g = mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D, H1, ACT_NONE);
   g.rm = rm256;
   LAUNCH("mlp1_gemm2", s1, gemm("mlp1_gemm2", g, s1, &w.sc));
   if (fork) HIP_OK(hipEventRecord(h->ev_join, s1));
   if (c.flash) {
     const int M4 = T * S4;
-    g = mk_gemm(w.a4, 16 * C, dt, h->m2_w1, dt, h->m2_b1, w.g1, dt, M4, H2, 16 * C, ACT_GELU);
-    g.rm = rmh64;
-    LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1", g, s, &w.sc));
+    g = first_gemm(4, w.a4, w.st4, use64 ? w.list64 : nullptr, h->m2_w1, h->m2_b1, h->m2_cs, w.g1,
+                   M4, H2, rmh64);
+    if (fold) {
+      if (!gemm_dma_supported(g)) return fail(IVC_ERR_UNSUPPORTED, "ln_fold: mlp2 product shape");
+      LAUNCH("mlp2_gemm1", s, launch_gemm_dma(g, s));
+    } else {
+      LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1", g, s, &w.sc));
+    }
     g = mk_gemm(w.g1, H2, dt, h->m2_w2, dt, h->m2_b2, w.g2, dt, M4, H2, H2, ACT_GELU);
     g.rm = rmh64;
     LAUNCH("mlp2_gemm2", s, gemm("mlp2_gemm2", g, s, &w.sc));

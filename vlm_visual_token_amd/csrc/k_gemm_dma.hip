@@ -31,11 +31,21 @@
 // 2-byte stores straight from the accumulator layout reach only a fraction
 // of the write bandwidth.
 //
+// LayerNorm fold (FOLD): for the first Linear after a LayerNorm,
+//   LN(x) W^T + b = rstd * (x . (gamma o W)^T) - rstd * mean * colsum(gamma o W) + (b + W beta),
+// so A is the raw ViT rows, gathered in pixel-shuffle order by the DMA
+// addresses (each K step of 64 lies inside one C-wide cell, and a cell's row
+// offset within its grid block is the same for every token, so the gather
+// costs one scalar offset per step), and the epilogue applies the per-row
+// (mean, rstd) and per-column colsum.  The normalised rows are never written.
+//
 // Grid: workgroups are dealt round-robin to the 8 XCDs, so the linear id is
 // regrouped so consecutive tile ids land on one XCD, then tiles are walked in
 // bands of 8 tile-rows so an XCD's L2 sees the same A and W rows many times.
 // Route-first products read their row count from the device (RowMap) and lay
 // the tile grid over the rows present.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -86,6 +96,32 @@ IVC_DEV long long phys_row(int gm, int a_rpg, long long a_gstride, int a_goff) {
   return a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : (long long)gm;
 }
 
+// Gathered A: ViT row of cell 0 of logical row m's grid block.
+IVC_DEV long long gather_row0(const AGather& g, int m) {
+  const int Q = g.P / g.r, S = Q * Q;
+  const int rank = m / S, s = m - rank * S;
+  const int t = g.list != nullptr ? g.list[rank] : rank;
+  const int qa = s / Q, qb = s - qa * Q;
+  const int a = g.v1 ? qb : qa, b = g.v1 ? qa : qb;  // v1: token (a, b) sits at b*Q + a
+  return (long long)t * g.rows + g.has_cls + (long long)(g.r * a) * g.P + g.r * b;
+}
+
+// Gathered A: byte offset of K step kt (BK wide) relative to cell 0's row.
+IVC_DEV long long gather_koff(const AGather& g, int kt, int BK) {
+  const int k0 = kt * BK;
+  const int q = k0 / g.C, c0 = k0 - q * g.C;
+  int dm, dk;  // grid offset of cell q inside the block
+  if (g.twice) {  // r = 4 as two r = 2 shuffles: q = 4*(2*m2 + k2) + (2*m + k)
+    const int w = q >> 2, qq = q & 3;
+    dm = 2 * (w >> 1) + (qq >> 1);
+    dk = 2 * (w & 1) + (qq & 1);
+  } else {
+    dm = q / g.r;
+    dk = q - dm * g.r;
+  }
+  return ((long long)(dm * g.P + dk) * g.C + c0) * 2;
+}
+
 // Byte XOR applied to a column offset in row r of an epilogue slab: one
 // 4-byte write instruction covers rows R, R+1, R+4, R+5 and 64 bytes of
 // columns, which this spreads over all 64 LDS banks (a permutation of the
@@ -99,12 +135,30 @@ IVC_DEV int slab_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 6; }
 // converted together (v_cvt_pk_bf16_f32) and traded with the neighbouring
 // lane (column c ^ 1), so the even lane writes row R, columns c, c+1 and the
 // odd lane row R+1, columns c-1, c: one 4-byte LDS write per two values.
-template <int ACT>
+// FOLD: value = rstd_row * acc - rstd_row * mean_row * colsum[col] + bias[col],
+// with the tile's 256 (mean, rstd) pairs staged in LDS first.
+template <int ACT, bool FOLD>
 IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q2, char* q3,
                         int wm, int wn, int m0, int n0, int M, int N, const float* bias,
-                        bf16_t* Cm, long long ldc, const RowMap& rm) {
+                        bf16_t* Cm, long long ldc, const RowMap& rm, const float* ln_rows,
+                        const float* ln_colsum) {
   const int tid = threadIdx.x, lane = tid & 63;
   const bool odd_lane = lane & 1;
+  __shared__ float2 rowst[FOLD ? DBM : 1];  // (rstd, -rstd * mean) per tile row
+  float ccol[4];
+  if (FOLD) {
+    if (tid < DBM) {
+      const int row = min(m0 + tid, M - 1);
+      const float2 mr = *reinterpret_cast<const float2*>(ln_rows + 2 * (long long)row);
+      rowst[tid] = make_float2(mr.y, -mr.y * mr.x);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      ccol[j] = col < N ? ln_colsum[col] : 0.f;
+    }
+    __syncthreads();
+  }
   // v_perm_b32 selectors: even lane keeps its low half and takes the
   // neighbour's low half; odd lane takes the neighbour's high half and keeps
   // its own high half
@@ -128,7 +182,16 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
         char* slab = i < 2 ? slab_lo : slab_hi;
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
-          float x0 = acc[i][j][v] + bj, x1 = acc[i][j][v + 1] + bj;
+          float x0, x1;
+          if (FOLD) {
+            const int r0 = wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            const float2 s0 = rowst[r0], s1 = rowst[r0 + 1];
+            x0 = fmaf(s0.x, acc[i][j][v], fmaf(s0.y, ccol[j], bj));
+            x1 = fmaf(s1.x, acc[i][j][v + 1], fmaf(s1.y, ccol[j], bj));
+          } else {
+            x0 = acc[i][j][v] + bj;
+            x1 = acc[i][j][v + 1] + bj;
+          }
           if (ACT == ACT_GELU) {
             x0 = gelu_erf(x0);
             x1 = gelu_erf(x1);
@@ -171,13 +234,15 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
 // rows at [16 KB, 32 KB), 64 bytes per row; 16-byte piece c of row r sits at
 // c ^ ((r >> 2) & 3).
 // ---------------------------------------------------------------------------
-template <int ACT>
+template <int ACT, bool FOLD>
 __global__ void __launch_bounds__(DNT, 1)
 k_gemm_dma4(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
             int a_goff, const bf16_t* __restrict__ W, long long ldw,
             const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-            int K, RowMap rm) {
+            int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
+            const float* __restrict__ ln_colsum) {
   constexpr int BK = 32, TB = QB / 2, DPW = 8;
+  using aoff_t = typename std::conditional<FOLD, int32_t, uint32_t>::type;
   __shared__ __attribute__((aligned(1024))) char s0[QB];
   __shared__ __attribute__((aligned(1024))) char s1[QB];
   __shared__ __attribute__((aligned(1024))) char s2[QB];
@@ -190,30 +255,37 @@ k_gemm_dma4(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 
   // DMA j (0..3) of wave w fills rows (4w + j)*16 .. +15; lane: row + lane/4,
   // LDS piece lane%4 holding global piece (lane%4) ^ swz(row)
-  const long long a_row0 = phys_row(m0, a_rpg, a_gstride, a_goff);
+  const long long a_row0 = FOLD ? gather_row0(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
   gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
   gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
-  uint32_t a_off[4], b_off[4];
+  aoff_t a_off[4];
+  uint32_t b_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = (w * 4 + j) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    a_off[j] = (uint32_t)(((phys_row(min(m0 + r, M - 1), a_rpg, a_gstride, a_goff) - a_row0) * lda +
-                           c * 8) * 2);
+    const int gm = min(m0 + r, M - 1);
+    const long long pr = FOLD ? gather_row0(ag, gm) : phys_row(gm, a_rpg, a_gstride, a_goff);
+    a_off[j] = (aoff_t)(((pr - a_row0) * lda + c * 8) * 2);
     b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
   }
-  auto dma_one = [&](int q, long long ko, char* st) {  // q = 0..7: A block q/2 (even), W (odd)
+  // byte offsets of K step kt in A (gathered: the step's cell and column) and W
+  auto koa = [&](int kt) -> long long {
+    return FOLD ? gather_koff(ag, kt, BK) : (long long)kt * (BK * 2);
+  };
+  auto dma_one = [&](int q, long long ka, long long kb, char* st) {  // q = 0..7: A block q/2 (even), W (odd)
     const int j = q >> 1;
     if ((q & 1) == 0)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ko + a_off[j]),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ka + a_off[j]),
                                        (lds_void_t*)(st + (w * 4 + j) * 1024), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + ko + b_off[j]),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + kb + b_off[j]),
                                        (lds_void_t*)(st + TB + (w * 4 + j) * 1024), 16, 0, 0);
   };
   auto dma = [&](int kt, char* st) {
+    const long long ka = koa(kt), kb = (long long)kt * (BK * 2);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dma_one(q, (long long)kt * (BK * 2), st);
+    for (int q = 0; q < 8; ++q) dma_one(q, ka, kb, st);
   };
   // fragment (i, kk) of A at fa[kk] + i * 2048 within a stage (rows i*32 + lane%32)
   uint32_t fa[2], fb[2];
@@ -257,12 +329,13 @@ k_gemm_dma4(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
     __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                \
     IVC_GWAIT_VM(DPW);                                                                      \
     lds_barrier();                                                                          \
-    const long long ko_ = (long long)min((K_) + 3, KT - 1) * (BK * 2);                      \
+    const int kn_ = min((K_) + 3, KT - 1);                                                  \
+    const long long ka_ = koa(kn_), kb_ = (long long)kn_ * (BK * 2);                        \
     _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                        \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] =                             \
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(FAC[kk][i], FBC[kk][j], acc[i][j], 0, 0, 0); \
-      dma_one(kk * 4 + i, ko_, STD);                                                        \
+      dma_one(kk * 4 + i, ka_, kb_, STD);                                                   \
       FAN[kk][i] = *reinterpret_cast<const bf16x8_t*>((STN) + fa[kk] + i * 2048);           \
       FBN[kk][i] = *reinterpret_cast<const bf16x8_t*>((STN) + fb[kk] + i * 2048);           \
       __builtin_amdgcn_sched_barrier(0);                                                    \
@@ -281,20 +354,23 @@ k_gemm_dma4(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 #undef IVC_DMA4_READ
   IVC_GWAIT_VM(0);  // no DMA may land after the stages are reused
   __syncthreads();
-  store_tile<ACT>(acc, s0, s1, s2, s3, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm);
+  store_tile<ACT, FOLD>(acc, s0, s1, s2, s3, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm, ln_rows,
+                        ln_colsum);
 }
 
 // ---------------------------------------------------------------------------
 // 2-stage kernel: K step 64.  sA*/sB* hold 256 rows of 128 bytes; 16-byte
 // piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
 // ---------------------------------------------------------------------------
-template <int ACT>
+template <int ACT, bool FOLD>
 __global__ void __launch_bounds__(DNT, 1)
 k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
             int a_goff, const bf16_t* __restrict__ W, long long ldw,
             const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-            int K, RowMap rm) {
+            int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
+            const float* __restrict__ ln_colsum) {
   constexpr int BK = 64;
+  using aoff_t = typename std::conditional<FOLD, int32_t, uint32_t>::type;
   __shared__ __attribute__((aligned(1024))) char sA0[QB];
   __shared__ __attribute__((aligned(1024))) char sB0[QB];
   __shared__ __attribute__((aligned(1024))) char sA1[QB];
@@ -307,25 +383,27 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 
   // DMA j (0..7) of wave w fills rows (8w + j)*8 .. +7; lane: row + lane/8,
   // LDS piece lane%8 holding global piece (lane%8) ^ f(row)
-  const long long a_row0 = phys_row(m0, a_rpg, a_gstride, a_goff);
+  const long long a_row0 = FOLD ? gather_row0(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
   gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
   gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
-  uint32_t a_off[8], b_off[8];
+  aoff_t a_off[8];
+  uint32_t b_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (w * 8 + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
-    a_off[j] = (uint32_t)(((phys_row(min(m0 + r, M - 1), a_rpg, a_gstride, a_goff) - a_row0) * lda +
-                           c * 8) * 2);
+    const int gm = min(m0 + r, M - 1);
+    const long long pr = FOLD ? gather_row0(ag, gm) : phys_row(gm, a_rpg, a_gstride, a_goff);
+    a_off[j] = (aoff_t)(((pr - a_row0) * lda + c * 8) * 2);
     b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
   }
-  auto dma_one = [&](int q, long long ko, char* sa, char* sb) {  // q = 0..15
+  auto dma_one = [&](int q, long long ka, long long kb, char* sa, char* sb) {  // q = 0..15
     const int j = q >> 1;
     if ((q & 1) == 0)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ko + a_off[j]),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ka + a_off[j]),
                                        (lds_void_t*)(sa + (w * 8 + j) * 1024), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + ko + b_off[j]),
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + kb + b_off[j]),
                                        (lds_void_t*)(sb + (w * 8 + j) * 1024), 16, 0, 0);
   };
   // fragment (i, kk) of A at fa[kk] + i * 4096 within sA (rows i*32 + lane%32)
@@ -350,7 +428,7 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 
   const int KT = K / BK;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) dma_one(q, 0, sA0, sB0);
+  for (int q = 0; q < 16; ++q) dma_one(q, FOLD ? gather_koff(ag, 0, BK) : 0, 0, sA0, sB0);
   for (int kt = 0; kt < KT; ++kt) {
     const bool odd = kt & 1;
     const char* sa = odd ? sA1 : sA0;
@@ -358,7 +436,8 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
     char* na = odd ? sA0 : sA1;
     char* nb = odd ? sB0 : sB1;
     const bool more = kt + 1 < KT;
-    const long long ko = (long long)(kt + 1) * (BK * 2);
+    const long long kb = (long long)(kt + 1) * (BK * 2);
+    const long long ka = FOLD ? gather_koff(ag, kt + 1, BK) : kb;
     // this step's tiles have landed and every wave is done with the other
     // stage: barrier, then the next step's DMA spread over the MFMAs
     __builtin_amdgcn_s_waitcnt(0);
@@ -380,7 +459,7 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
           // the next step's 16 DMA instructions go out over the first half of
           // the step: late enough not to stall the MFMA issue on the address
           // unit, early enough to land before the step ends
-          if (more && kk < 2 && (j & 1) == 0) dma_one(kk * 8 + i * 2 + (j >> 1), ko, na, nb);
+          if (more && kk < 2 && (j & 1) == 0) dma_one(kk * 8 + i * 2 + (j >> 1), ka, kb, na, nb);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[cb][0][i], f[cb][1][j], acc[i][j],
                                                               0, 0, 0);
         }
@@ -394,14 +473,68 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  store_tile<ACT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm);
+  store_tile<ACT, FOLD>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm, ln_rows,
+                        ln_colsum);
+}
+
+// One workgroup per output n: the folded weights of the first Linear after a
+// LayerNorm, the column sum the epilogue subtracts, and the folded bias.
+__global__ void __launch_bounds__(256)
+k_ln_fold_weights(const bf16_t* __restrict__ W, int K, const float* __restrict__ gamma,
+                  const float* __restrict__ beta, const float* __restrict__ b,
+                  bf16_t* __restrict__ Wg, float* __restrict__ colsum, float* __restrict__ bfold) {
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const bf16_t* wr = W + (long long)n * K;
+  bf16_t* gr = Wg + (long long)n * K;
+  float s = 0.f, c = 0.f;
+  for (int k = tid; k < K; k += 256) {
+    const float wv = bf16_to_f32(wr[k]);
+    const bf16_t g = f32_to_bf16(gamma[k] * wv);
+    gr[k] = g;
+    s += bf16_to_f32(g);
+    c = fmaf(beta[k], wv, c);
+  }
+  __shared__ float rs[256], rc[256];
+  rs[tid] = s;
+  rc[tid] = c;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      rs[tid] += rs[tid + o];
+      rc[tid] += rc[tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    colsum[n] = rs[0];
+    bfold[n] = b[n] + rc[0];
+  }
+}
+
+hipError_t launch_ln_fold_weights(const void* W, int N, int K, const float* gamma,
+                                  const float* beta, const float* b, void* Wg, float* colsum,
+                                  float* bfold, hipStream_t s) {
+  if (N <= 0 || K <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ln_fold_weights, dim3((unsigned)N), dim3(256), 0, s, (const bf16_t*)W, K,
+                     gamma, beta, b, (bf16_t*)Wg, colsum, bfold);
+  return hipGetLastError();
 }
 
 bool gemm_dma_supported(const GemmArgs& g) {
-  return g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % 64 == 0 &&
-         g.K > 0 && g.M > 0 && g.N > 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
-         ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.W % 16) == 0 && g.N % 8 == 0 &&
-         g.ldc % 8 == 0 && ((uintptr_t)g.Cm % 16) == 0;
+  const bool base =
+      g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % 64 == 0 &&
+      g.K > 0 && g.M > 0 && g.N > 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
+      ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.W % 16) == 0 && g.N % 8 == 0 &&
+      g.ldc % 8 == 0 && ((uintptr_t)g.Cm % 16) == 0;
+  if (!base || !g.fold) return base;
+  // gathered A: C-wide cells hold whole K steps; K = r*r*C; lda = C; signed
+  // 32-bit offsets inside the gathered tensor; row statistics and colsum given
+  const AGather& a = g.ag;
+  return (a.r == 2 || (a.r == 4)) && a.C > 0 && a.C % 64 == 0 && g.K == a.r * a.r * a.C &&
+         g.lda == a.C && a.P % a.r == 0 && (!a.twice || a.r == 4) && g.ln_rows != nullptr &&
+         g.ln_colsum != nullptr && g.a_rpg == 0 &&
+         (long long)a.rows * a.C * 2 * ((long long)g.M / ((a.P / a.r) * (a.P / a.r)) + 1) <
+             (1ll << 31);
 }
 
 hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
@@ -411,13 +544,17 @@ hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
 #define IVC_DMA_LAUNCH(KERN)                                                                  \
   hipLaunchKernelGGL(KERN, dim3((unsigned)tiles), dim3(DNT), 0, s, (const bf16_t*)g.A, g.lda, \
                      g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw, g.bias,       \
-                     (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm)
-  if (four) {
-    if (g.act == ACT_GELU) IVC_DMA_LAUNCH(k_gemm_dma4<ACT_GELU>);
-    else IVC_DMA_LAUNCH(k_gemm_dma4<ACT_NONE>);
+                     (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm, g.ag, g.ln_rows, g.ln_colsum)
+  if (g.fold) {  // the folded products are the GELU'd first Linears
+    if (g.act != ACT_GELU) return hipErrorInvalidValue;
+    if (four) IVC_DMA_LAUNCH((k_gemm_dma4<ACT_GELU, true>));
+    else IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, true>));
+  } else if (four) {
+    if (g.act == ACT_GELU) IVC_DMA_LAUNCH((k_gemm_dma4<ACT_GELU, false>));
+    else IVC_DMA_LAUNCH((k_gemm_dma4<ACT_NONE, false>));
   } else {
-    if (g.act == ACT_GELU) IVC_DMA_LAUNCH(k_gemm_dma2<ACT_GELU>);
-    else IVC_DMA_LAUNCH(k_gemm_dma2<ACT_NONE>);
+    if (g.act == ACT_GELU) IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, false>));
+    else IVC_DMA_LAUNCH((k_gemm_dma2<ACT_NONE, false>));
   }
 #undef IVC_DMA_LAUNCH
   return hipGetLastError();

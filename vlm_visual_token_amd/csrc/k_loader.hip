@@ -15,7 +15,9 @@
 //    direct r=4 block 4*(2*m2 + m) + (2*k2 + k).
 // mlp1/mlp2 start with LayerNorm over the concatenated row (4C or 16C), fused
 // here so the permuted rows are written once, already normalised, in the
-// layout the projector GEMM reads.
+// layout the projector GEMM reads.  In statistics mode (LayerNorm folded into
+// the first product, which then reads the raw rows itself) only each row's
+// mean and 1/sqrt(var + eps) are written.
 //
 // Work split (one wavefront = one r=2 token): the wave loads its 4 input rows
 // with 16-byte loads (a row is C contiguous elements, so every load is fully
@@ -30,13 +32,14 @@
 
 namespace ivc {
 
-template <typename E, int CPL, bool FLASH, bool LN>
+template <typename E, int CPL, bool FLASH, bool LN, bool STATS>
 __global__ void __launch_bounds__(256)
 k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
              const float* __restrict__ g2, const float* __restrict__ b2, E* __restrict__ out2,
              const float* __restrict__ g4, const float* __restrict__ b4, E* __restrict__ out4,
              float eps, int ps_v1, int twice_r2, const uint8_t* __restrict__ use64,
-             const int* __restrict__ rank) {
+             const int* __restrict__ rank, float* __restrict__ st2, float* __restrict__ st4) {
+  static_assert(!STATS || LN, "statistics mode computes the LayerNorm statistics");
   constexpr int V = Elem<E>::kPerVec;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -138,13 +141,27 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
   }
 
   // route-first: only the tile's chosen path is written, at its rank in that path
-  bool want2 = out2 != nullptr, want4 = out4 != nullptr;
+  bool want2 = (STATS ? (void*)st2 : (void*)out2) != nullptr;
+  bool want4 = (STATS ? (void*)st4 : (void*)out4) != nullptr;
   int t2 = t, t4 = t;
   if (use64 != nullptr) {
     const bool to64 = use64[t] != 0;
     want2 = want2 && !to64;
     want4 = want4 && to64;
     t2 = t4 = rank[t];
+  }
+
+  if (STATS) {
+    if (want2 && lane == 0) {
+      const int tok2 = ps_v1 ? b2i * Q2 + a2 : a2 * Q2 + b2i;
+      *reinterpret_cast<float2*>(st2 + 2 * ((size_t)t2 * S2 + tok2)) = make_float2(mean2, rstd2);
+    }
+    if (FLASH && want4 && threadIdx.x == 0) {
+      const int Q4 = P >> 2, S4 = Q4 * Q4;
+      const int tok4 = ps_v1 ? b4i * Q4 + a4 : a4 * Q4 + b4i;
+      *reinterpret_cast<float2*>(st4 + 2 * ((size_t)t4 * S4 + tok4)) = make_float2(mean4, rstd4);
+    }
+    return;
   }
 
   // ---- r = 2 row: channel block q holds cell q
@@ -202,32 +219,32 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
   }
 }
 
-template <typename E, int CPL, bool LN>
+template <typename E, int CPL, bool LN, bool STATS>
 static hipError_t launch_cpl(const ShuffleArgs& a, hipStream_t s) {
   const int Q2 = a.P / 2, Q4 = a.P / 4;
   if (a.flash) {
     dim3 grid((unsigned)(a.T * Q4 * Q4));
-    hipLaunchKernelGGL((k_shuffle_ln<E, CPL, true, LN>), grid, dim3(256), 0, s, (const E*)a.X, a.T,
+    hipLaunchKernelGGL((k_shuffle_ln<E, CPL, true, LN, STATS>), grid, dim3(256), 0, s, (const E*)a.X, a.T,
                        a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4, a.eps,
-                       a.ps_v1, a.twice_r2, a.use64, a.rank);
+                       a.ps_v1, a.twice_r2, a.use64, a.rank, a.st2, a.st4);
   } else {
     const long long toks = (long long)a.T * Q2 * Q2;
     dim3 grid((unsigned)((toks + 3) / 4));
-    hipLaunchKernelGGL((k_shuffle_ln<E, CPL, false, LN>), grid, dim3(256), 0, s, (const E*)a.X,
+    hipLaunchKernelGGL((k_shuffle_ln<E, CPL, false, LN, STATS>), grid, dim3(256), 0, s, (const E*)a.X,
                        a.T, a.P, a.C, a.has_cls, a.g2, a.b2, (E*)a.out2, a.g4, a.b4, (E*)a.out4,
-                       a.eps, a.ps_v1, a.twice_r2, a.use64, a.rank);
+                       a.eps, a.ps_v1, a.twice_r2, a.use64, a.rank, a.st2, a.st4);
   }
   return hipGetLastError();
 }
 
-template <typename E, bool LN>
+template <typename E, bool LN, bool STATS>
 static hipError_t launch_e(const ShuffleArgs& a, hipStream_t s) {
   const int vpr = a.C / Elem<E>::kPerVec;
   const int need = (vpr + 63) / 64;
-  if (need <= 1) return launch_cpl<E, 1, LN>(a, s);
-  if (need <= 2) return launch_cpl<E, 2, LN>(a, s);
-  if (need <= 4) return launch_cpl<E, 4, LN>(a, s);
-  if (need <= 8) return launch_cpl<E, 8, LN>(a, s);
+  if (need <= 1) return launch_cpl<E, 1, LN, STATS>(a, s);
+  if (need <= 2) return launch_cpl<E, 2, LN, STATS>(a, s);
+  if (need <= 4) return launch_cpl<E, 4, LN, STATS>(a, s);
+  if (need <= 8) return launch_cpl<E, 8, LN, STATS>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -235,8 +252,13 @@ int shuffle_max_width(int dtype) { return 8 * 64 * (dtype == 1 ? 8 : 4); }
 
 hipError_t launch_shuffle_ln(const ShuffleArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.dtype == 1) return a.ln ? launch_e<bf16_t, true>(a, s) : launch_e<bf16_t, false>(a, s);
-  return a.ln ? launch_e<float, true>(a, s) : launch_e<float, false>(a, s);
+  if (a.st2 != nullptr || a.st4 != nullptr) {  // statistics only (bf16: the folded products)
+    if (a.dtype != 1 || !a.ln) return hipErrorInvalidValue;
+    return launch_e<bf16_t, true, true>(a, s);
+  }
+  if (a.dtype == 1)
+    return a.ln ? launch_e<bf16_t, true, false>(a, s) : launch_e<bf16_t, false, false>(a, s);
+  return a.ln ? launch_e<float, true, false>(a, s) : launch_e<float, false, false>(a, s);
 }
 
 }  // namespace ivc

@@ -21,6 +21,11 @@ struct ShuffleArgs {
   const float *g4, *b4;
   void* out4;
   float eps;
+  // statistics mode: (mean, rstd) of each LayerNorm row go to st2 / st4
+  // ([rows][2] fp32) instead of the normalised rows (LayerNorm folded into
+  // the products)
+  float* st2 = nullptr;
+  float* st4 = nullptr;
   int ps_v1 = 0;     // 1: pixel_shuffle v1, token grid transposed (token b*(P/r) + a)
   int twice_r2 = 0;  // 1: 64-path channel order of two successive r=2 shuffles
   // route-first: tile t writes only its chosen path's rows, at position rank[t]
@@ -40,6 +45,17 @@ struct RowMap {
   int m_mult = 1;
   const int* c_map = nullptr;
   int c_rpg = 1;
+};
+
+// A operand gathered straight from the ViT rows: logical row m is shuffled
+// token m % S of tile list[m / S] (list null: tile m / S), and K block q
+// (C wide) is cell q of the token's r x r grid block (pixel_shuffle order, or
+// the two-r=2 order for r = 4), so no shuffled copy of the rows is written.
+struct AGather {
+  const int* list = nullptr;
+  int rows = 0;  // has_cls + P*P
+  int has_cls = 0, P = 0, r = 2, C = 0;
+  int v1 = 0, twice = 0;
 };
 
 // ---- GEMM: C[M, N] = act(A[M, K] . W[N, K]^T + bias[N]) ---------------------
@@ -69,6 +85,14 @@ struct GemmArgs {
   int ksplit;
   float* part;
   RowMap rm;
+  // LayerNorm folded into the product (DMA kernels): A is gathered by `ag`
+  // from the raw rows, W holds gamma (.) W, and the epilogue computes
+  //   rstd_m * acc - rstd_m * mean_m * ln_colsum[n] + bias[n]
+  // with ln_rows[m] = (mean_m, rstd_m)
+  int fold = 0;
+  AGather ag;
+  const float* ln_rows = nullptr;
+  const float* ln_colsum = nullptr;
 };
 // bf16 A and W, fp32 accumulation on MFMA, bf16 out.  Needs K % 64 == 0.
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
@@ -85,6 +109,12 @@ hipError_t launch_gemm_simt(const GemmArgs& g, hipStream_t s);
 bool gemm_f32a_supported(const GemmArgs& g);
 hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float scale,
                             hipStream_t s);
+// LayerNorm fold of a Linear that follows LayerNorm(gamma, beta):
+//   Wg[n][k] = bf16(gamma[k] * W[n][k]),  colsum[n] = sum_k Wg[n][k],
+//   bfold[n] = b[n] + sum_k beta[k] * W[n][k]        (W, Wg bf16 [N, K])
+hipError_t launch_ln_fold_weights(const void* W, int N, int K, const float* gamma,
+                                  const float* beta, const float* b, void* Wg, float* colsum,
+                                  float* bfold, hipStream_t s);
 // dst[c][r] = src[r][c], bf16 [R, Cc]
 hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int Cc, hipStream_t s);
 // split-K factor and workspace the SIMT kernel wants for a product

@@ -39,7 +39,7 @@ class ivc_config(ctypes.Structure):
         ("llm_width", c_int32), ("mlp1_hidden", c_int32), ("flash", c_int32),
         ("mlp2_hidden", c_int32), ("pool_layers", c_int32), ("pool_heads", c_int32),
         ("gate_hidden", c_int32), ("gate_expansion", c_int32), ("pool_mode", c_int32),
-        ("ps_version", c_int32), ("shuffle64_order", c_int32), ("reserved", c_int32),
+        ("ps_version", c_int32), ("shuffle64_order", c_int32), ("ln_fold", c_int32),
         ("rel_quantile", c_double), ("abs_threshold", c_double),
         ("ln_eps", c_float),
     ]
@@ -162,6 +162,7 @@ def make_config(cfg: dict) -> ivc_config:
     c.pool_mode = cfg.get("pool_mode", IVC_POOL_KV)
     c.ps_version = cfg.get("ps_version", 2)
     c.shuffle64_order = SHUFFLE64_ORDERS.index(cfg.get("shuffle64_order", "direct"))
+    c.ln_fold = int(cfg.get("ln_fold", 0))
     c.rel_quantile = cfg["rel_quantile"]
     c.abs_threshold = cfg["abs_threshold"]
     c.ln_eps = cfg["ln_eps"]
