@@ -180,14 +180,18 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         char* slab = i < 2 ? slab_lo : slab_hi;
+        float2 rs[16];  // this lane's 16 rows of block row i, read together
+        if (FOLD) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            rs[v] = rowst[wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)];
+        }
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           float x0, x1;
           if (FOLD) {
-            const int r0 = wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            const float2 s0 = rowst[r0], s1 = rowst[r0 + 1];
-            x0 = fmaf(s0.x, acc[i][j][v], fmaf(s0.y, ccol[j], bj));
-            x1 = fmaf(s1.x, acc[i][j][v + 1], fmaf(s1.y, ccol[j], bj));
+            x0 = fmaf(rs[v].x, acc[i][j][v], fmaf(rs[v].y, ccol[j], bj));
+            x1 = fmaf(rs[v + 1].x, acc[i][j][v + 1], fmaf(rs[v + 1].y, ccol[j], bj));
           } else {
             x0 = acc[i][j][v] + bj;
             x1 = acc[i][j][v + 1] + bj;
