@@ -10,21 +10,15 @@
 // fragment reads (ds_read_b128, one row per lane) are free of bank conflicts
 // without padding.
 //
-// Two main loops:
-//  * 4-stage (K step 32, 4 x 32 KB): the DMA of step k+3 and the fragment
-//    reads of step k+1 (into a second register buffer) are interleaved with
-//    the 32 MFMAs of step k, one DMA instruction and two reads after every
-//    four MFMAs, so the memory pipeline is fed evenly and three steps of
-//    operands are in flight.  Used for K below 8192.
-//  * 2-stage (K step 64, 2 x 64 KB): full 128-byte rows per DMA request,
-//    which suits very long K; the next step's DMA goes out over the first
-//    half of the step's MFMAs and the next sub-step's fragment reads are
-//    interleaved with them.
-// In both, the compiler must not make an LDS read wait for the DMAs in
-// flight: each stage is a separate __shared__ array (the compiler tracks
-// LDS DMA targets per array), every 4-stage step issues its DMA (past the
-// end it reloads the last K step), and the barriers wait for this wave's LDS
-// operations only (the DMA completion is waited for explicitly).
+// Main loop: K step 64, two stages of 64 KB (A and W, 256 rows of 128 bytes
+// each): full 128-byte rows per DMA request.  The next step's 16 DMA
+// instructions go out over the first half of the step's MFMAs and the next
+// sub-step's fragment reads are interleaved with them.  (A four-stage ring
+// of K step 32 was measured slower on every shape here: its 64-byte row
+// requests cost more than the deeper prefetch gains.)
+// The compiler must not make an LDS read wait for the DMAs in flight: each
+// stage is a separate __shared__ array (the compiler tracks LDS DMA targets
+// per array).
 //
 // Epilogue: the 256 x 256 bf16 tile goes through LDS (the four 32 KB stage
 // arrays hold 64 rows each) and out with 16-byte row-contiguous stores;
@@ -62,18 +56,6 @@ typedef __attribute__((address_space(1))) const char gchar_t;
 namespace {
 constexpr int DBM = 256, DBN = 256, DNT = 256;
 constexpr int QB = 32768;  // bytes of one stage array (also one epilogue slab of 64 rows)
-
-// s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt left alone
-#define IVC_GWAIT_VM(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// Workgroup barrier waiting only for this wave's LDS operations
-IVC_DEV void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Tile of this workgroup; false if it has none (uniform, before any barrier).
 IVC_DEV bool map_tile(int& M, int N, const RowMap& rm, int& m0, int& n0) {
@@ -232,135 +214,6 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
   }
 }
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// 4-stage kernel: K step 32.  Stage array s holds A rows at [0, 16 KB) and W
-// rows at [16 KB, 32 KB), 64 bytes per row; 16-byte piece c of row r sits at
-// c ^ ((r >> 2) & 3).
-// ---------------------------------------------------------------------------
-template <int ACT, bool FOLD>
-__global__ void __launch_bounds__(DNT, 1)
-k_gemm_dma4(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
-            int a_goff, const bf16_t* __restrict__ W, long long ldw,
-            const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-            int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
-            const float* __restrict__ ln_colsum) {
-  constexpr int BK = 32, TB = QB / 2, DPW = 8;
-  using aoff_t = typename std::conditional<FOLD, int32_t, uint32_t>::type;
-  __shared__ __attribute__((aligned(1024))) char s0[QB];
-  __shared__ __attribute__((aligned(1024))) char s1[QB];
-  __shared__ __attribute__((aligned(1024))) char s2[QB];
-  __shared__ __attribute__((aligned(1024))) char s3[QB];
-  int m0, n0;
-  if (!map_tile(M, N, rm, m0, n0)) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 1, wn = w & 1;
-
-  // DMA j (0..3) of wave w fills rows (4w + j)*16 .. +15; lane: row + lane/4,
-  // LDS piece lane%4 holding global piece (lane%4) ^ swz(row)
-  const long long a_row0 = FOLD ? gather_row0(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
-  gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
-  gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
-  aoff_t a_off[4];
-  uint32_t b_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (w * 4 + j) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    const int gm = min(m0 + r, M - 1);
-    const long long pr = FOLD ? gather_row0(ag, gm) : phys_row(gm, a_rpg, a_gstride, a_goff);
-    a_off[j] = (aoff_t)(((pr - a_row0) * lda + c * 8) * 2);
-    b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
-  }
-  // byte offsets of K step kt in A (gathered: the step's cell and column) and W
-  auto koa = [&](int kt) -> long long {
-    return FOLD ? gather_koff(ag, kt, BK) : (long long)kt * (BK * 2);
-  };
-  auto dma_one = [&](int q, long long ka, long long kb, char* st) {  // q = 0..7: A block q/2 (even), W (odd)
-    const int j = q >> 1;
-    if ((q & 1) == 0)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ka + a_off[j]),
-                                       (lds_void_t*)(st + (w * 4 + j) * 1024), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + kb + b_off[j]),
-                                       (lds_void_t*)(st + TB + (w * 4 + j) * 1024), 16, 0, 0);
-  };
-  auto dma = [&](int kt, char* st) {
-    const long long ka = koa(kt), kb = (long long)kt * (BK * 2);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) dma_one(q, ka, kb, st);
-  };
-  // fragment (i, kk) of A at fa[kk] + i * 2048 within a stage (rows i*32 + lane%32)
-  uint32_t fa[2], fb[2];
-  {
-    const int rl = lane & 31, sw = (rl >> 2) & 3;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t p = (uint32_t)(((2 * kk + (lane >> 5)) ^ sw) * 16);
-      fa[kk] = (uint32_t)((wm * 128 + rl) * 64) + p;
-      fb[kk] = (uint32_t)(TB + (wn * 128 + rl) * 64) + p;
-    }
-  }
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int KT = K / BK;  // a multiple of 4
-  dma(0, s0);
-  dma(min(1, KT - 1), s1);
-  dma(min(2, KT - 1), s2);
-  bf16x8_t fa0[2][4], fb0[2][4], fa1[2][4], fb1[2][4];
-#define IVC_DMA4_READ(ST, FA, FB)                                                           \
-  do {                                                                                      \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                      \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
-        FA[kk][i] = *reinterpret_cast<const bf16x8_t*>((ST) + fa[kk] + i * 2048);           \
-        FB[kk][i] = *reinterpret_cast<const bf16x8_t*>((ST) + fb[kk] + i * 2048);           \
-      }                                                                                     \
-    }                                                                                       \
-  } while (0)
-  // Iteration k: wait for step k+1's DMA, barrier, then step k's 32 MFMAs
-  // with, after every 4, one DMA instruction of step k+3 (into the stage read
-  // two iterations ago) and two fragment reads of step k+1.
-#define IVC_DMA4_ITER(K_, FAC, FBC, FAN, FBN, STN, STD)                                     \
-  do {                                                                                      \
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                                \
-    IVC_GWAIT_VM(DPW);                                                                      \
-    lds_barrier();                                                                          \
-    const int kn_ = min((K_) + 3, KT - 1);                                                  \
-    const long long ka_ = koa(kn_), kb_ = (long long)kn_ * (BK * 2);                        \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] =                             \
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FAC[kk][i], FBC[kk][j], acc[i][j], 0, 0, 0); \
-      dma_one(kk * 4 + i, ka_, kb_, STD);                                                   \
-      FAN[kk][i] = *reinterpret_cast<const bf16x8_t*>((STN) + fa[kk] + i * 2048);           \
-      FBN[kk][i] = *reinterpret_cast<const bf16x8_t*>((STN) + fb[kk] + i * 2048);           \
-      __builtin_amdgcn_sched_barrier(0);                                                    \
-    }                                                                                       \
-  } while (0)
-  IVC_GWAIT_VM(2 * DPW);
-  lds_barrier();
-  IVC_DMA4_READ(s0, fa0, fb0);
-  for (int k = 0; k < KT; k += 4) {
-    IVC_DMA4_ITER(k, fa0, fb0, fa1, fb1, s1, s3);
-    IVC_DMA4_ITER(k + 1, fa1, fb1, fa0, fb0, s2, s0);
-    IVC_DMA4_ITER(k + 2, fa0, fb0, fa1, fb1, s3, s1);
-    IVC_DMA4_ITER(k + 3, fa1, fb1, fa0, fb0, s0, s2);
-  }
-#undef IVC_DMA4_ITER
-#undef IVC_DMA4_READ
-  IVC_GWAIT_VM(0);  // no DMA may land after the stages are reused
-  __syncthreads();
-  store_tile<ACT, FOLD>(acc, s0, s1, s2, s3, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm, ln_rows,
-                        ln_colsum);
-}
 
 // ---------------------------------------------------------------------------
 // 2-stage kernel: K step 64.  sA*/sB* hold 256 rows of 128 bytes; 16-byte
@@ -544,21 +397,17 @@ bool gemm_dma_supported(const GemmArgs& g) {
 hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
   if (!gemm_dma_supported(g)) return hipErrorInvalidValue;
   const int tiles = ((g.M + DBM - 1) / DBM) * ((g.N + DBN - 1) / DBN);
-  const bool four = g.K % 128 == 0 && g.K < 8192;
 #define IVC_DMA_LAUNCH(KERN)                                                                  \
   hipLaunchKernelGGL(KERN, dim3((unsigned)tiles), dim3(DNT), 0, s, (const bf16_t*)g.A, g.lda, \
                      g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw, g.bias,       \
                      (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm, g.ag, g.ln_rows, g.ln_colsum)
   if (g.fold) {  // the folded products are the GELU'd first Linears
     if (g.act != ACT_GELU) return hipErrorInvalidValue;
-    if (four) IVC_DMA_LAUNCH((k_gemm_dma4<ACT_GELU, true>));
-    else IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, true>));
-  } else if (four) {
-    if (g.act == ACT_GELU) IVC_DMA_LAUNCH((k_gemm_dma4<ACT_GELU, false>));
-    else IVC_DMA_LAUNCH((k_gemm_dma4<ACT_NONE, false>));
+    IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, true>));
+  } else if (g.act == ACT_GELU) {
+    IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, false>));
   } else {
-    if (g.act == ACT_GELU) IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, false>));
-    else IVC_DMA_LAUNCH((k_gemm_dma2<ACT_NONE, false>));
+    IVC_DMA_LAUNCH((k_gemm_dma2<ACT_NONE, false>));
   }
 #undef IVC_DMA_LAUNCH
   return hipGetLastError();
