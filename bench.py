@@ -194,7 +194,7 @@ def main():
     ap.add_argument("--pool-mode", type=int, default=1,
                     help="0: K/V projection + attention, 1: folded pooling (same mathematics)")
     ap.add_argument("--run-mode", choices=["routed", "both"], default="routed",
-                    help="routed: decide first, then run only each tile's chosen projector; "
+                    help="routed: decide first, then run only each tile's chosen projector (one forward call); "
                          "both: run mlp1 and mlp2 on every tile, as the pages do")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tiles", type=int, default=32)
@@ -246,10 +246,18 @@ def main():
     def step():
         nonlocal rbuf, cbuf
         ivc.ivc_tile_offsets(tiles_d, len(cfg["tiles"]), off_d, st_d, stream)
-        rbuf = con.route(x, with_pooled=False, stream=stream, out=rbuf)
         if args.run_mode == "routed":
-            con.run_routed(x, rbuf["use64"], o256, o64, stream=stream)
+            # route + route-first run in one call (the LayerNorm statistics
+            # pass runs beside the router)
+            if rbuf is None:
+                rbuf = dict(gate=torch.empty((T, 2), dtype=torch.float32, device="cuda"),
+                            thr=torch.empty(1, dtype=torch.float64, device="cuda"),
+                            use64=torch.empty(T, dtype=torch.uint8, device="cuda"), pooled=None,
+                            status=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                            out256=o256, out64=o64)
+            rbuf = con.forward(x, with_pooled=False, stream=stream, out=rbuf)
         else:
+            rbuf = con.route(x, with_pooled=False, stream=stream, out=rbuf)
             con.run(x, o256, o64, stream=stream)
         cbuf = con.compact(ids_d, emb_d, rbuf["use64"], o256, o64, synth.IMG_CONTEXT,
                            stream=stream, out=cbuf)

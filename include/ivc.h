@@ -222,6 +222,15 @@ ivc_status ivc_connector_route(ivc_connector* h, const void* vit, const int32_t*
                                float* pooled, int32_t* dev_status, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ivc_connector_route followed by ivc_connector_run_routed in one call
+ * ([4B-Flash] sections 2-5; [2B-Flash] dual pipeline), with the same outputs
+ * and one workspace of ivc_connector_workspace_bytes.  Requires flash = 1;
+ * out256 and out64 are both required. */
+ivc_status ivc_connector_forward(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
+                                 int32_t T, float* gate, double* threshold, uint8_t* use64,
+                                 float* pooled, int32_t* dev_status, void* out256, void* out64,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 /* compress_visual_tokens_in_sentence plus the IMG_CONTEXT embedding
  * injection ([4B-Flash] section 4; [2B-Flash] routing decision; [14B] token
  * injection).  The k-th IMG_CONTEXT token of `ids` is slot k % S of tile

@@ -659,3 +659,50 @@ def test_ln_fold_flash_workload_sampled():
     assert t256 and t64
     assert_close(to_np(r256[[tiles[i] for i in t256]]), e256[t256], "bf16", "out256 (ln_fold)")
     assert_close(to_np(r64[[tiles[i] for i in t64]]), e64[t64], "bf16", "out64 (ln_fold)")
+
+
+# ---------------------------------------------------------------------------
+# forward = route + route-first run in one call
+# ---------------------------------------------------------------------------
+def _check_forward(cfg, w, xd, valid=None):
+    con = _connector(cfg, w, cfg["T"])
+    r = con.route(xd, valid=valid)
+    r = {k: (v.clone() if v is not None else None) for k, v in r.items()}
+    r256 = torch.full((cfg["T"], cfg["S"], cfg["D"]), float("nan"), dtype=xd.dtype, device="cuda")
+    r64 = torch.full((cfg["T"], cfg["S64"], cfg["D"]), float("nan"), dtype=xd.dtype, device="cuda")
+    con.run_routed(xd, r["use64"], r256, r64)
+    f = con.forward(xd, valid=valid)
+    torch.cuda.synchronize()
+    for k in ("gate", "thr", "use64", "pooled", "status"):
+        assert torch.equal(f[k], r[k]), k
+    use = r["use64"].cpu().numpy()
+    keep256 = torch.from_numpy(use == 0).cuda()
+    keep64 = torch.from_numpy(use != 0).cuda()
+    assert torch.equal(f["out256"][keep256], r256[keep256])
+    assert torch.equal(f["out64"][keep64], r64[keep64])
+    return f
+
+
+def test_forward_matches_route_then_run_tiny():
+    cfg, w, x = _tiny_all()
+    say("forward tiny fp32")
+    _check_forward(cfg, w, torch.from_numpy(x).cuda())
+
+
+@pytest.mark.parametrize("version,order", [(2, "direct"), (1, "twice_r2")])
+def test_forward_matches_route_then_run_ln_fold_small(version, order):
+    T = 9
+    cfg = _tiny_bf16(T, ln_fold=1, ps_version=version, shuffle64_order=order)
+    w = synth.make_weights(cfg)
+    x = synth.make_vit_tiles(cfg, range(T))
+    say(f"forward ln_fold small v{version} {order}")
+    _check_forward(cfg, w, torch.from_numpy(x).to(torch.bfloat16).cuda())
+
+
+def test_forward_flash_workload_ln_fold():
+    cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
+    say(f"2B-Flash forward (ln_fold): T={cfg['T']}")
+    w = host_weights(cfg)
+    f = _check_forward(cfg, w, dev_vit(cfg))
+    use = f["use64"].cpu().numpy()
+    assert 0 < use.sum() < cfg["T"]

@@ -74,6 +74,26 @@ class Connector:
                                 out["pooled"], out["status"], self.ws, self.ws_bytes, stream)
         return out
 
+    def forward(self, vit: torch.Tensor, valid=None, with_pooled=True, stream=None, out=None):
+        """route + route-first run in one call (ivc_connector_forward)."""
+        T = vit.shape[0]
+        D = self.cfg["D"]
+        if out is None:
+            out = dict(
+                gate=torch.empty((T, 2), dtype=torch.float32, device=self.device),
+                thr=torch.empty(1, dtype=torch.float64, device=self.device),
+                use64=torch.empty(T, dtype=torch.uint8, device=self.device),
+                pooled=(torch.empty((T, self.cfg["C"]), dtype=torch.float32, device=self.device)
+                        if with_pooled else None),
+                status=torch.zeros(1, dtype=torch.int32, device=self.device),
+                out256=torch.empty((T, self.S, D), dtype=self.dtype, device=self.device),
+                out64=torch.empty((T, self.S64, D), dtype=self.dtype, device=self.device),
+            )
+        ivc.ivc_connector_forward(self.h, vit, valid, T, out["gate"], out["thr"], out["use64"],
+                                  out["pooled"], out["status"], out["out256"], out["out64"],
+                                  self.ws, self.ws_bytes, stream)
+        return out
+
     def compact(self, ids, embeds, use64, out256, out64, img_context_id: int, stream=None,
                 out=None):
         L = ids.shape[0]

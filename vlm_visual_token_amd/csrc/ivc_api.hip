@@ -795,11 +795,10 @@ extern "C" ivc_status ivc_connector_run_routed(ivc_connector* h, const void* vit
 // ---------------------------------------------------------------------------
 // route
 // ---------------------------------------------------------------------------
-extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
-                                          const int32_t* valid_tokens, int32_t T, float* gate,
-                                          double* threshold, uint8_t* use64, float* pooled,
-                                          int32_t* dev_status, void* ws, size_t ws_bytes,
-                                          void* stream) {
+static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
+                             int32_t T, float* gate, double* threshold, uint8_t* use64,
+                             float* pooled, int32_t* dev_status, void* ws, size_t ws_bytes,
+                             void* stream) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (!c.flash) return fail(IVC_ERR_INVALID_ARG, "route needs a flash connector");
@@ -934,6 +933,33 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
   LAUNCH("quantile_decide", s,
          launch_quantile_decide(gate, T, c.rel_quantile, c.abs_threshold, threshold, use64, s));
   return IVC_OK;
+}
+
+extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
+                                          const int32_t* valid_tokens, int32_t T, float* gate,
+                                          double* threshold, uint8_t* use64, float* pooled,
+                                          int32_t* dev_status, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  return route_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status, ws,
+                    ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// forward = route + route-first run in one call
+// ---------------------------------------------------------------------------
+
+extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
+                                            const int32_t* valid_tokens, int32_t T, float* gate,
+                                            double* threshold, uint8_t* use64, float* pooled,
+                                            int32_t* dev_status, void* out256, void* out64,
+                                            void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward needs a flash connector");
+  if (T > 0 && (!out256 || !out64)) return fail(IVC_ERR_INVALID_ARG, "null out256/out64");
+  ivc_status st = route_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status,
+                             ws, ws_bytes, stream);
+  if (st != IVC_OK) return st;
+  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

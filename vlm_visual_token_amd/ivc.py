@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
         "ivc_connector_run": (c_int32, [P, P, c_int32, P, P, P, c_size_t, P]),
         "ivc_connector_run_routed": (c_int32, [P, P, c_int32, P, P, P, P, c_size_t, P]),
         "ivc_connector_route": (c_int32, [P, P, P, c_int32, P, P, P, P, P, P, c_size_t, P]),
+        "ivc_connector_forward": (c_int32, [P, P, P, c_int32, P, P, P, P, P, P, P, P, c_size_t, P]),
         "ivc_connector_compact": (c_int32, [P, P, P, c_int64, c_int32, P, P, P, c_int32, P, P, P,
                                             P, P, P, P, c_size_t, P]),
         "ivc_connector_compact_batch": (c_int32, [P, P, P, c_int32, P, c_int64, c_int32, P, P, P,
@@ -110,7 +111,8 @@ def load() -> ctypes.CDLL:
 def exported_symbols() -> list[str]:
     return [
         "ivc_connector_create", "ivc_connector_destroy", "ivc_connector_workspace_bytes",
-        "ivc_connector_run", "ivc_connector_run_routed", "ivc_connector_route", "ivc_connector_compact",
+        "ivc_connector_run", "ivc_connector_run_routed", "ivc_connector_route", "ivc_connector_forward",
+        "ivc_connector_compact",
         "ivc_connector_compact_batch", "ivc_connector_compact_batch_workspace_bytes", "ivc_route_decide",
         "ivc_tile_offsets",
         "ivc_pixel_shuffle", "ivc_profile_enable", "ivc_profile_reset", "ivc_profile_read",
@@ -231,6 +233,14 @@ def ivc_connector_route(h, vit, valid_tokens, T, gate, threshold, use64, pooled,
                                       _ptr(threshold), _ptr(use64), _ptr(pooled),
                                       _ptr(dev_status), _ptr(ws), ws_bytes, _stream(stream)),
            "ivc_connector_route")
+
+
+def ivc_connector_forward(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status,
+                          out256, out64, ws, ws_bytes, stream=None) -> None:
+    _check(load().ivc_connector_forward(h, _ptr(vit), _ptr(valid_tokens), T, _ptr(gate),
+                                        _ptr(threshold), _ptr(use64), _ptr(pooled),
+                                        _ptr(dev_status), _ptr(out256), _ptr(out64), _ptr(ws),
+                                        ws_bytes, _stream(stream)), "ivc_connector_forward")
 
 
 def ivc_connector_compact(h, ids, embeds, L, img_context_id, use64, out256, out64, T, out_ids,
