@@ -641,6 +641,21 @@ def test_ln_fold_run_routed_small(pattern):
     _check_routed(con, cfg, xd, torch.from_numpy(use.astype(np.uint8)).cuda())
 
 
+@pytest.mark.parametrize("name", ["internvl35_4b_std", "internvl3_38b"])
+def test_ln_fold_standard_connector_sampled(name):
+    # standard (non-Flash) connectors: the statistics pass for r = 2 only, C = 1024 and 3200
+    cfg = workload(name, ln_fold=1)
+    say(f"{name} ln_fold: T={cfg['T']} C={cfg['C']} D={cfg['D']}")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, cfg["T"])
+    o256, _ = con.run(dev_vit(cfg))
+    torch.cuda.synchronize()
+    tiles = synth.sample_tiles(cfg["T"])
+    x = synth.make_vit_tiles(cfg, tiles)
+    e256, _ = O.connector_run(x, cfg, w)
+    assert_close(to_np(o256[tiles]), e256, "bf16", f"{name} out256 (ln_fold)")
+
+
 def test_ln_fold_flash_workload_sampled():
     cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
     say(f"2B-Flash ln_fold run_routed: T={cfg['T']}")
