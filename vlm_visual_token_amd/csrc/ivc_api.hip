@@ -926,10 +926,14 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     LAUNCH("gate_fc2", s, gemm("gate_fc2",
                               mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2, DT_F32,
                                       T, hh, he, ACT_NONE), s, &w.sc));
-    LAUNCH("gate_res_ln", s,
-           launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));
+    if (b + 1 < IVC_GATE_BLOCKS)
+      LAUNCH("gate_res_ln", s,
+             launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));
+    else  // the last block's residual LayerNorm and the classifier head in one launch
+      LAUNCH("gate_res_ln_head", s,
+             launch_residual_ln_head(dt, w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps,
+                                     h->g_cw, h->g_cb, gate, s));
   }
-  LAUNCH("gate_head", s, launch_gate_head(dt, w.x, h->g_cw, h->g_cb, gate, T, hh, s));
   LAUNCH("quantile_decide", s,
          launch_quantile_decide(gate, T, c.rel_quantile, c.abs_threshold, threshold, use64, s));
   return IVC_OK;

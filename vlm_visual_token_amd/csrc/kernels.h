@@ -143,9 +143,11 @@ bool pool_attn_supported(int C, int H);
 // x[t] += LayerNorm(y[t]) * gamma + beta   (rows of width h, fp32)
 hipError_t launch_residual_ln(float* x, const float* y, const float* gamma, const float* beta,
                               int T, int h, float eps, hipStream_t s);
-// z = Wc x + bc, gate = softmax(z) for 2 classes; Wc element type dtype
-hipError_t launch_gate_head(int dtype, const float* x, const void* Wc, const float* bc,
-                            float* gate, int T, int h, hipStream_t s);
+// the same for the last block, then z = Wc x + bc and gate = softmax(z) for 2
+// classes on the updated rows (one launch; Wc element type dtype)
+hipError_t launch_residual_ln_head(int dtype, float* x, const float* y, const float* gamma,
+                                   const float* beta, int T, int h, float eps, const void* Wc,
+                                   const float* bc, float* gate, hipStream_t s);
 // broadcast a [C] vector (element type dtype) into fp32 rows [T, C]
 hipError_t launch_broadcast_rows(int dtype, const void* v, float* out, int T, int C,
                                  hipStream_t s);
