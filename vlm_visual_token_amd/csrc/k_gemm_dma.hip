@@ -1,8 +1,8 @@
 // bf16 GEMM for the projector MLPs: C[M, N] = act(A[M, K] . W[N, K]^T + bias[N]).
 //
-// 256 x 256 output tile per workgroup, 4 wavefronts of 128 x 128 (a 4 x 4
-// grid of v_mfma_f32_32x32x16_bf16 blocks, 256 fp32 accumulators per lane,
-// held in AGPRs).  Operand tiles move from HBM/L2 to LDS with gfx950's LDS
+// 256 x 256 output tile per workgroup, 8 wavefronts of 128 x 64 (a 4 x 2
+// grid of v_mfma_f32_32x32x16_bf16 blocks, 128 fp32 accumulators per lane),
+// two wavefronts per SIMD.  Operand tiles move from HBM/L2 to LDS with gfx950's LDS
 // DMA (global_load_lds_dwordx4): no staging registers, so the VGPRs hold the
 // MFMA fragments.  A DMA instruction writes one contiguous 1 KB block (64
 // lanes x 16 bytes); each lane picks the global 16-byte piece that belongs at
@@ -11,7 +11,7 @@
 // without padding.
 //
 // Main loop: K step 64, two stages of 64 KB (A and W, 256 rows of 128 bytes
-// each): full 128-byte rows per DMA request.  The next step's 16 DMA
+// each): full 128-byte rows per DMA request.  The next step's DMA
 // instructions go out over the first half of the step's MFMAs and the next
 // sub-step's fragment reads are interleaved with them.  (A four-stage ring
 // of K step 32 was measured slower on every shape here: its 64-byte row
@@ -54,7 +54,7 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 typedef __attribute__((address_space(1))) const char gchar_t;
 
 namespace {
-constexpr int DBM = 256, DBN = 256, DNT = 256;
+constexpr int DBM = 256, DBN = 256, DNT = 512;  // tile rows, columns; threads
 constexpr int QB = 32768;  // bytes of one stage array (also one epilogue slab of 64 rows)
 
 // Tile of this workgroup; false if it has none (uniform, before any barrier).
@@ -119,15 +119,18 @@ IVC_DEV int slab_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 6; }
 // odd lane row R+1, columns c-1, c: one 4-byte LDS write per two values.
 // FOLD: value = rstd_row * acc - rstd_row * mean_row * colsum[col] + bias[col],
 // with the tile's 256 (mean, rstd) pairs staged in LDS first.
-template <int ACT, bool FOLD>
-IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q2, char* q3,
+// NJ: 32-column blocks per wave (4: waves of 128 x 128, 4 per tile; 2: waves
+// of 128 x 64, 8 per tile); NTH: threads of the workgroup.
+template <int ACT, bool FOLD, int NJ = 2, int NTH = DNT>
+IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* q2, char* q3,
                         int wm, int wn, int m0, int n0, int M, int N, const float* bias,
                         bf16_t* Cm, long long ldc, const RowMap& rm, const float* ln_rows,
                         const float* ln_colsum) {
+  constexpr int WC = 32 * NJ;  // columns per wave
   const int tid = threadIdx.x, lane = tid & 63;
   const bool odd_lane = lane & 1;
   __shared__ float2 rowst[FOLD ? DBM : 1];  // (rstd, -rstd * mean) per tile row
-  float ccol[4];
+  float ccol[NJ];
   if (FOLD) {
     if (tid < DBM) {
       const int row = min(m0 + tid, M - 1);
@@ -135,8 +138,8 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
       rowst[tid] = make_float2(mr.y, -mr.y * mr.x);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * WC + j * 32 + (lane & 31);
       ccol[j] = col < N ? ln_colsum[col] : 0.f;
     }
     __syncthreads();
@@ -148,15 +151,15 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
   {
     char* slab_lo = wm ? q2 : q0;
     char* slab_hi = wm ? q3 : q1;
-    float bcol[4];  // all four loads in flight together
+    float bcol[NJ];  // all loads in flight together
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * WC + j * 32 + (lane & 31);
       bcol[j] = (bias != nullptr && col < N) ? bias[col] : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cl = wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int cl = wn * WC + j * 32 + (lane & 31);
       const float bj = bcol[j];
       const int cw = cl & ~1;  // column of the pair this lane writes
 #pragma unroll
@@ -196,10 +199,12 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
   // output row of tile row r (route-first products scatter groups of c_rpg rows)
   const bool pow2 = rm.c_map != nullptr && (rm.c_rpg & (rm.c_rpg - 1)) == 0;
   const int sh = pow2 ? __builtin_ctz((unsigned)rm.c_rpg) : 0;
+  constexpr int RPI = NTH / 32;  // rows per iteration (32 threads x 16 bytes per row)
 #pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int r = it * 8 + (tid >> 5), c = tid & 31;
-    const char* slab = it < 8 ? q0 : it < 16 ? q1 : it < 24 ? q2 : q3;
+  for (int it = 0; it < DBM / RPI; ++it) {
+    const int r = it * RPI + (tid >> 5), c = tid & 31;
+    const int sl = r >> 6;
+    const char* slab = sl == 0 ? q0 : sl == 1 ? q1 : sl == 2 ? q2 : q3;
     const u32x4 val =
         *reinterpret_cast<const u32x4*>(slab + (r & 63) * 512 + ((c * 16) ^ slab_swz(r & 63)));
     const int row = m0 + r, col = n0 + 8 * c;
@@ -216,12 +221,18 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][4], char* q0, char* q1, char* q
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// 2-stage kernel: K step 64.  sA*/sB* hold 256 rows of 128 bytes; 16-byte
-// piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// The kernel: K step 64, two stages; sA*/sB* hold 256 rows of 128 bytes, and
+// 16-byte piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// 8 waves of 128 x 64 (4 x 2 MFMA blocks, 128 accumulators each), two per
+// SIMD, so while one wave of a SIMD waits to issue its share of the operand
+// DMA the other issues MFMAs (4 waves of 128 x 128 with all 256 AGPRs were
+// 3-8% slower: nothing could cover their DMA issue stalls).  Each wave
+// issues 8 of the step's 64 DMA instructions over the first half of the
+// step's MFMAs.
 // ---------------------------------------------------------------------------
 template <int ACT, bool FOLD>
 __global__ void __launch_bounds__(DNT, 1)
-k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
+k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
             int a_goff, const bf16_t* __restrict__ W, long long ldw,
             const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
             int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
@@ -235,35 +246,36 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
   int m0, n0;
   if (!map_tile(M, N, rm, m0, n0)) return;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
+  const int wm = w >> 2, wn = w & 3;  // rows wm*128 .., columns wn*64 ..
 
-  // DMA j (0..7) of wave w fills rows (8w + j)*8 .. +7; lane: row + lane/8,
-  // LDS piece lane%8 holding global piece (lane%8) ^ f(row)
+  // DMA j (0..3) of wave w fills rows (4w + j)*8 .. +7 of A and of W; lane:
+  // row + lane/8, LDS piece lane%8 holding global piece (lane%8) ^ f(row)
   const long long a_row0 = FOLD ? gather_row0(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
   gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
   gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
-  aoff_t a_off[8];
-  uint32_t b_off[8];
+  aoff_t a_off[4];
+  uint32_t b_off[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (w * 8 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {
+    const int r = (w * 4 + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
     const int gm = min(m0 + r, M - 1);
     const long long pr = FOLD ? gather_row0(ag, gm) : phys_row(gm, a_rpg, a_gstride, a_goff);
     a_off[j] = (aoff_t)(((pr - a_row0) * lda + c * 8) * 2);
     b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
   }
-  auto dma_one = [&](int q, long long ka, long long kb, char* sa, char* sb) {  // q = 0..15
+  auto dma_one = [&](int q, long long ka, long long kb, char* sa, char* sb) {  // q = 0..7
     const int j = q >> 1;
     if ((q & 1) == 0)
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ka + a_off[j]),
-                                       (lds_void_t*)(sa + (w * 8 + j) * 1024), 16, 0, 0);
+                                       (lds_void_t*)(sa + (w * 4 + j) * 1024), 16, 0, 0);
     else
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + kb + b_off[j]),
-                                       (lds_void_t*)(sb + (w * 8 + j) * 1024), 16, 0, 0);
+                                       (lds_void_t*)(sb + (w * 4 + j) * 1024), 16, 0, 0);
   };
-  // fragment (i, kk) of A at fa[kk] + i * 4096 within sA (rows i*32 + lane%32)
+  // fragment (i, kk) of A at fa[kk] + i * 4096 (rows wm*128 + i*32 + lane%32),
+  // of W at fb[kk] + j * 4096 (rows wn*64 + j*32 + lane%32)
   uint32_t fa[4], fb[4];
   {
     const int rl = lane & 31, sw = (rl & 7) ^ ((rl >> 3) & 1);
@@ -271,21 +283,21 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
     for (int kk = 0; kk < 4; ++kk) {
       const uint32_t p = (uint32_t)(((2 * kk + (lane >> 5)) ^ sw) * 16);
       fa[kk] = (uint32_t)((wm * 128 + rl) * 128) + p;
-      fb[kk] = (uint32_t)((wn * 128 + rl) * 128) + p;
+      fb[kk] = (uint32_t)((wn * 64 + rl) * 128) + p;
     }
   }
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int KT = K / BK;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) dma_one(q, FOLD ? gather_koff(ag, 0, BK) : 0, 0, sA0, sB0);
+  for (int q = 0; q < 8; ++q) dma_one(q, FOLD ? gather_koff(ag, 0, BK) : 0, 0, sA0, sB0);
   for (int kt = 0; kt < KT; ++kt) {
     const bool odd = kt & 1;
     const char* sa = odd ? sA1 : sA0;
@@ -295,16 +307,13 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
     const bool more = kt + 1 < KT;
     const long long kb = (long long)(kt + 1) * (BK * 2);
     const long long ka = FOLD ? gather_koff(ag, kt + 1, BK) : kb;
-    // this step's tiles have landed and every wave is done with the other
-    // stage: barrier, then the next step's DMA spread over the MFMAs
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bf16x8_t f[2][2][4];  // [buffer][A / W][block]
+    bf16x8_t fa_[2][4], fb_[2][2];  // [buffer][block]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[0][0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[0] + i * 4096);
-      f[0][1][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[0] + i * 4096);
-    }
+    for (int i = 0; i < 4; ++i) fa_[0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[0] + i * 4096);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb_[0][j] = *reinterpret_cast<const bf16x8_t*>(sb + fb[0] + j * 4096);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -312,17 +321,15 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // the next step's 16 DMA instructions go out over the first half of
-          // the step: late enough not to stall the MFMA issue on the address
-          // unit, early enough to land before the step ends
-          if (more && kk < 2 && (j & 1) == 0) dma_one(kk * 8 + i * 2 + (j >> 1), ka, kb, na, nb);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[cb][0][i], f[cb][1][j], acc[i][j],
+        for (int j = 0; j < 2; ++j) {
+          // 8 DMA instructions over the first 16 MFMAs of the step
+          if (more && kk < 2 && j == 0) dma_one(kk * 4 + i, ka, kb, na, nb);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[cb][i], fb_[cb][j], acc[i][j],
                                                               0, 0, 0);
         }
         if (kk < 3) {
-          f[nbuf][0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[kk + 1] + i * 4096);
-          f[nbuf][1][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[kk + 1] + i * 4096);
+          fa_[nbuf][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[kk + 1] + i * 4096);
+          if (i < 2) fb_[nbuf][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[kk + 1] + i * 4096);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -330,8 +337,8 @@ k_gemm_dma2(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  store_tile<ACT, FOLD>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, M, N, bias, Cm, ldc, rm, ln_rows,
-                        ln_colsum);
+  store_tile<ACT, FOLD, 2, DNT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, M, N, bias, Cm, ldc,
+                                    rm, ln_rows, ln_colsum);
 }
 
 // One workgroup per output n: the folded weights of the first Linear after a
@@ -398,16 +405,16 @@ hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
   if (!gemm_dma_supported(g)) return hipErrorInvalidValue;
   const int tiles = ((g.M + DBM - 1) / DBM) * ((g.N + DBN - 1) / DBN);
 #define IVC_DMA_LAUNCH(KERN)                                                                  \
-  hipLaunchKernelGGL(KERN, dim3((unsigned)tiles), dim3(DNT), 0, s, (const bf16_t*)g.A, g.lda, \
-                     g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw, g.bias,       \
+  hipLaunchKernelGGL(KERN, dim3((unsigned)tiles), dim3(DNT), 0, s, (const bf16_t*)g.A,    \
+                     g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw, g.bias,\
                      (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm, g.ag, g.ln_rows, g.ln_colsum)
   if (g.fold) {  // the folded products are the GELU'd first Linears
     if (g.act != ACT_GELU) return hipErrorInvalidValue;
-    IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, true>));
+    IVC_DMA_LAUNCH((k_gemm_dma8<ACT_GELU, true>));
   } else if (g.act == ACT_GELU) {
-    IVC_DMA_LAUNCH((k_gemm_dma2<ACT_GELU, false>));
+    IVC_DMA_LAUNCH((k_gemm_dma8<ACT_GELU, false>));
   } else {
-    IVC_DMA_LAUNCH((k_gemm_dma2<ACT_NONE, false>));
+    IVC_DMA_LAUNCH((k_gemm_dma8<ACT_NONE, false>));
   }
 #undef IVC_DMA_LAUNCH
   return hipGetLastError();
