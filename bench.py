@@ -187,6 +187,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--ln-fold", type=int, default=1,
                     help="1: fold the projectors' LayerNorm into their first product")
+    ap.add_argument("--mall-flush-steps", type=int, default=10,
+                    help="also time this many single steps, each after writing 1 GiB to evict "
+                         "the memory-side cache (median reported; 0: skip)")
     ap.add_argument("--compact-prompts", type=int, default=64,
                     help="prompts in the batched-compaction measurement (0: skip)")
     ap.add_argument("--steps", type=int, default=20)
@@ -290,6 +293,28 @@ def main():
         print(f"# per-kernel event pass ({args.steps} steps)", file=sys.stderr, flush=True)
         ms_ev, prof = timed(True)
     ms_step = ms / args.steps
+
+    # the same steps with the 256 MB memory-side cache (MALL) evicted before
+    # each one (a 1 GiB buffer written between steps, outside the timed spans):
+    # weights and activations then come from HBM at every step
+    ms_cold = None
+    if args.mall_flush_steps > 0:
+        print(f"# {args.mall_flush_steps} steps after a cache flush each", file=sys.stderr, flush=True)
+        junk = torch.empty(512 << 20, dtype=torch.int16, device="cuda")
+        evs = []
+        for i in range(args.mall_flush_steps):  # all enqueued, one synchronisation
+            junk.fill_(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms_cold = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        del junk
+        torch.cuda.empty_cache()
+
     use64 = rbuf["use64"].cpu().numpy()
     Lp = int(cbuf["len"].item())
     emitted = int((use64 == 0).sum()) * cfg["S"] + int(use64.sum()) * cfg["S64"]
@@ -381,6 +406,9 @@ def main():
     }
     if ms_ev is not None:
         out["ms_per_step_event_pass"] = ms_ev / args.steps
+    if ms_cold is not None:
+        out["ms_per_step_mall_flushed"] = ms_cold
+        out["tiles_per_s_mall_flushed"] = T / (ms_cold / 1e3)
     print(json.dumps(out))
 
 
