@@ -299,16 +299,18 @@ def test_route_decide_bit_exact(T):
 # ---------------------------------------------------------------------------
 # folded pooling (key/value projections folded out of the token pass)
 # ---------------------------------------------------------------------------
-def _small_bf16_router(pool_mode):
-    cfg = workload("tiny_flash_f32", dtype="bf16", C=512, D=256, mlp1_hidden=256,
-                   mlp2_hidden=256, pool_heads=8, gate_hidden=512, pool_mode=pool_mode)
+def _small_bf16_router(pool_mode, C=512, H=8):
+    cfg = workload("tiny_flash_f32", dtype="bf16", C=C, D=256, mlp1_hidden=256,
+                   mlp2_hidden=256, pool_heads=H, gate_hidden=C, pool_mode=pool_mode)
     cfg["name"] = "small_bf16_router"
     return cfg
 
 
+# (C, H): head widths 64, 32 and 128 of the fused query projection + key fold
+@pytest.mark.parametrize("C,H", [(512, 8), (512, 16), (1024, 8)])
 @pytest.mark.parametrize("padded", [False, True])
-def test_folded_pool_small_matches_oracle_and_kv(padded):
-    cfg = _small_bf16_router(1)
+def test_folded_pool_small_matches_oracle_and_kv(padded, C, H):
+    cfg = _small_bf16_router(1, C, H)
     w = synth.make_weights(cfg)
     x = synth.make_vit(cfg)
     valid = synth.make_valid_tokens(cfg, seed=9) if padded else None
@@ -316,7 +318,7 @@ def test_folded_pool_small_matches_oracle_and_kv(padded):
         x[:, 0, :] = np.nan
         for t in range(cfg["T"]):
             x[t, 1 + valid[t]:, :] = np.nan
-    say(f"folded small padded={padded}")
+    say(f"folded small padded={padded} C={C} H={H}")
     xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
     vd = torch.from_numpy(valid).cuda() if padded else None
     rf = _connector(cfg, w, cfg["T"]).route(xd, valid=vd)
@@ -354,6 +356,33 @@ def test_folded_pool_flash_workload():
     dg = np.abs(gate[tiles] - e_gate).max()
     say(f"  gate max abs diff {dg:.3e}")
     assert dg <= GATE_TOL
+
+
+# Batch sizes that split a tile's tokens over many token-pass workgroups (T = 3:
+# 64 per tile, the value fold then reads a merged xbar) or over up to four
+# (T = 100: the value fold merges the partials in its operand load), with a
+# padding mask on the second.
+@pytest.mark.parametrize("T,padded", [(3, False), (100, True)])
+def test_folded_pool_batch_sizes(T, padded):
+    cfg = workload("internvl35_2b_flash", pool_mode=1)
+    cfg["tiles"], cfg["T"] = [T], T
+    say(f"2B-Flash folded route: T={T} padded={padded}")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, T)
+    xd = dev_vit(cfg)
+    valid = synth.make_valid_tokens(cfg, seed=T) if padded else None
+    r = con.route(xd, valid=torch.from_numpy(valid).cuda() if padded else None)
+    torch.cuda.synchronize()
+    assert int(r["status"].item()) == 0
+    gate = r["gate"].cpu().numpy()
+    thr, use = O.decide(gate[:, 0], cfg)
+    assert float(r["thr"].item()) == thr
+    assert np.array_equal(r["use64"].cpu().numpy(), use)
+    tiles = sorted(set(synth.sample_tiles(T, n=6)))
+    x = synth.make_vit_tiles(cfg, tiles)
+    e_gate, _, _, e_pooled = O.connector_route(x, cfg, w, valid[tiles] if padded else None)
+    assert_close(to_np(r["pooled"][tiles]), e_pooled, "bf16", "pooled")
+    assert np.abs(gate[tiles] - e_gate).max() <= GATE_TOL
 
 
 # ---------------------------------------------------------------------------

@@ -833,18 +833,31 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
   const float scale = 1.0f / sqrtf((float)(C / H));
   int fG = 0, fQ = 0, fseg = 0;
   if (folded) folded_geometry(T, N, C, h->ncu, &fG, &fQ, &fseg);
+  // query projection and key fold in one launch where the shape allows it
+  const bool fq_fused = folded && h->wkT != nullptr && fold_query_fused_supported(C, H);
   for (int l = 0; l < L; ++l) {
-    LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
-                                 mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32, T,
-                                         C, C, ACT_NONE), s, &w.sc));
     const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * C * h->esz;
     const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * C * h->esz;
     const float* bv = h->bkv + (size_t)(2 * l + 1) * C;
+    // q~_h = Wk_h^T q_h * log2(e) / sqrt(d) (scores in log2 units), per head
+    // a product [T, d] x [d, C] with the transposed key weights
+    const float qscale = scale * 1.4426950408889634f;
+    if (fq_fused) {
+      LAUNCH("pool_query_fold", s,
+             launch_fold_query_fused(w.q, h->wq[l], h->bq[l],
+                                     (const char*)h->wkT + (size_t)l * C * C * h->esz, w.qt_hi,
+                                     w.qt_lo, T, C, H, qscale, s));
+      if (l == 0 && H < 16)
+        LAUNCH("pool_fold_pad", s, launch_zero_heads(w.qt_hi, w.qt_lo, T, H, C, s));
+    } else {
+      LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
+                                   mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32,
+                                           T, C, C, ACT_NONE), s, &w.sc));
+    }
     if (folded) {
-      // q~_h = Wk_h^T q_h * log2(e) / sqrt(d) (scores in log2 units), per head
-      // a product [T, d] x [d, C] with the transposed key weights
-      const float qscale = scale * 1.4426950408889634f;
-      if (h->wkT != nullptr) {
+      if (fq_fused) {
+        // q~ already written by the fused launch
+      } else if (h->wkT != nullptr) {
         const int d = C / H;
         GemmArgs fq = mk_gemm(w.qp, C, DT_F32, (const char*)h->wkT + (size_t)l * C * C * h->esz,
                               DT_BF16, nullptr, w.qt_hi, DT_BF16, T, C, d, ACT_NONE);
@@ -878,19 +891,28 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       fa.Q = fQ;
       fa.segmax = fseg;
       fa.part = w.part;
-      fa.xbar = w.xbar;
+      // o_h = Wv_h xbar_h + bv_h for every head: one batched product over heads,
+      // with bf16 weights reading the token pass's partials directly (the merge
+      // of a tile's partials happens in its operand load)
+      const bool merged_value = dt == IVC_BF16 && fold_value_merged_max_parts(T, N, fQ) <= 4;
+      fa.xbar = merged_value ? nullptr : w.xbar;
       LAUNCH("pool_folded", s, launch_pool_folded(fa, s));
-      // o_h = Wv_h xbar_h + bv_h for every head: one batched product over heads
-      const int d = C / H;
-      GemmArgs fv = mk_gemm(w.xbar, (long long)H * C, DT_F32, wv, dt, bv, w.o, DT_F32, T, d, C,
-                            ACT_NONE);
-      fv.ldc = C;
-      fv.batch = H;
-      fv.a_bs = C;
-      fv.w_bs = (long long)d * C;
-      fv.c_bs = d;
-      fv.bias_bs = d;
-      LAUNCH("pool_fold_value", s, gemm("pool_fold_value", fv, s, &w.sc));
+      if (merged_value) {
+        LAUNCH("pool_fold_value", s,
+               launch_fold_value_merged(w.part, valid_tokens, N, fQ, fseg, wv, bv, w.o, T, C, H,
+                                        s));
+      } else {
+        const int d = C / H;
+        GemmArgs fv = mk_gemm(w.xbar, (long long)H * C, DT_F32, wv, dt, bv, w.o, DT_F32, T, d, C,
+                              ACT_NONE);
+        fv.ldc = C;
+        fv.batch = H;
+        fv.a_bs = C;
+        fv.w_bs = (long long)d * C;
+        fv.c_bs = d;
+        fv.bias_bs = d;
+        LAUNCH("pool_fold_value", s, gemm("pool_fold_value", fv, s, &w.sc));
+      }
     } else {
       PoolAttnArgs pa{};
       pa.dtype = dt;

@@ -46,57 +46,65 @@ IVC_DEV void split8(const float4& x0, const float4& x1, bf16x8_t& hi, bf16x8_t& 
   hi = __builtin_bit_cast(bf16x8_t, h);
   lo = __builtin_bit_cast(bf16x8_t, l);
 }
-}  // namespace
 
-// Tile (16 MB) x (16 NB), NWV waves, PD K steps loaded per wave at once.
-// OUT: 0 = fp32 C, 1 = C * scale as bf16 high part (Cm) and low part (C2)
-template <int MB, int NB, int NWV, int PD, int ACT, int OUT>
-__global__ void __launch_bounds__(NWV * 64)
-k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
-            const bf16_t* __restrict__ W, long long ldw, long long w_bs,
-            const float* __restrict__ bias, long long bias_bs, void* __restrict__ Cm,
-            void* __restrict__ C2, long long ldc, long long c_bs, int M, int N, int K,
-            float scale) {
-  constexpr int BM = 16 * MB, BN = 16 * NB, LDR = BN + 4;
-  constexpr int NTH = NWV * 64, RPP = NTH / BN;  // epilogue rows per pass
-  static_assert(NTH % BN == 0 && BM % RPP == 0, "epilogue shape");
-  __shared__ __attribute__((aligned(16))) float red[NWV][BM][LDR];
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lo16 = lane & 15, hi4 = lane >> 4;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM, b = blockIdx.z;
-  A += b * a_bs;
-  W += b * w_bs;
-
-  // operand rows of this lane (clamped: rows past M or N are computed, not stored)
-  const float* arow[MB];
+// Activation row of one lane.  NS = 1: a plain fp32 row.  NS > 1: the
+// weighted sum of NS partial rows, (sum_s sc[s] * p[s][k]) * inv, accumulated
+// with fmaf in order s = 0, 1, ... (unused sources carry sc = 0).
+template <int NS>
+struct ARow {
+  const float* p[NS];
+  float sc[NS];
+  float inv;
+  struct Raw {
+    float4 v[NS][2];
+  };
+  IVC_DEV void load(int k0, Raw& r) const {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    arow[mb] = A + (long long)min(m0 + 16 * mb + lo16, M - 1) * lda + 8 * hi4;
-  const bf16_t* wrow[NB];
+    for (int i = 0; i < NS; ++i) {
+      r.v[i][0] = *reinterpret_cast<const float4*>(p[i] + k0);
+      r.v[i][1] = *reinterpret_cast<const float4*>(p[i] + k0 + 4);
+    }
+  }
+  IVC_DEV void get(const Raw& r, float4& x0, float4& x1) const {
+    if (NS == 1) {
+      x0 = r.v[0][0];
+      x1 = r.v[0][1];
+      return;
+    }
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    wrow[nb] = W + (long long)min(n0 + 16 * nb + lo16, N - 1) * ldw + 8 * hi4;
+    for (int i = 0; i < NS; ++i) {
+      const float* v0 = reinterpret_cast<const float*>(&r.v[i][0]);
+      const float* v1 = reinterpret_cast<const float*>(&r.v[i][1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = fmaf(v0[e], sc[i], a[e]);
+        a[4 + e] = fmaf(v1[e], sc[i], a[4 + e]);
+      }
+    }
+    x0 = make_float4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+    x1 = make_float4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
+  }
+};
 
-  f32x4_t acc[MB][NB];
+// Main loop of one wave: MB x NB blocks of 16 x 16, K steps w, w + NWV, ...
+// (each 32 wide), up to PD of them loaded at once.  arow / wrow: this lane's
+// operand rows, already offset by 8 * (lane / 16) elements.
+template <int MB, int NB, int NWV, int PD, int NS>
+IVC_DEV void f32a_mainloop(const ARow<NS> (&arow)[MB], const bf16_t* const (&wrow)[NB], int w,
+                           int nks, f32x4_t (&acc)[MB][NB]) {
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // wave w takes K steps w, w + NWV, ...; up to PD of them are loaded at once
-  const int nks = K / 32;
   for (int s0 = w; s0 < nks; s0 += NWV * PD) {
-    float4 xa[PD][MB][2];
+    typename ARow<NS>::Raw xa[PD][MB];
     u32x4 xw[PD][NB];
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
       const int k0 = 32 * min(s0 + NWV * i, nks - 1);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        xa[i][mb][0] = *reinterpret_cast<const float4*>(arow[mb] + k0);
-        xa[i][mb][1] = *reinterpret_cast<const float4*>(arow[mb] + k0 + 4);
-      }
+      for (int mb = 0; mb < MB; ++mb) arow[mb].load(k0, xa[i][mb]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) xw[i][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + k0);
     }
@@ -110,7 +118,8 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
       bf16x8_t ah[MB], al[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        float4 x0 = xa[i][mb][0], x1 = xa[i][mb][1];
+        float4 x0, x1;
+        arow[mb].get(xa[i][mb], x0, x1);
         x0.x *= keep; x0.y *= keep; x0.z *= keep; x0.w *= keep;
         x1.x *= keep; x1.y *= keep; x1.z *= keep; x1.w *= keep;
         split8(x0, x1, ah[mb], al[mb]);
@@ -125,6 +134,31 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
         }
     }
   }
+}
+
+// One output tile (16 MB) x (16 NB) of batch entry b with NWV waves, PD K
+// steps loaded per wave at once: the main loop, then the NWV partial tiles
+// summed through LDS in wave order, bias, activation and the store.
+// OUT: 0 = fp32 C, 1 = C * scale as bf16 high part (Cm) and low part (C2).
+template <int MB, int NB, int NWV, int PD, int ACT, int OUT, int NS>
+IVC_DEV void f32a_tile(const ARow<NS> (&arow)[MB], const bf16_t* __restrict__ W, long long ldw,
+                       const float* __restrict__ bias, void* __restrict__ Cm,
+                       void* __restrict__ C2, long long ldc, int M, int N, int K, float scale,
+                       int m0, int n0) {
+  constexpr int BM = 16 * MB, BN = 16 * NB, LDR = BN + 4;
+  constexpr int NTH = NWV * 64, RPP = NTH / BN;  // epilogue rows per pass
+  static_assert(NTH % BN == 0 && BM % RPP == 0, "epilogue shape");
+  __shared__ __attribute__((aligned(16))) float red[NWV][BM][LDR];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  const bf16_t* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    wrow[nb] = W + (long long)min(n0 + 16 * nb + lo16, N - 1) * ldw + 8 * hi4;
+
+  f32x4_t acc[MB][NB];
+  f32a_mainloop<MB, NB, NWV, PD, NS>(arow, wrow, w, K / 32, acc);
 
   // partial tiles -> LDS; output layout: lane holds column 16nb + lo16, rows 16mb + 4hi4 + v
 #pragma unroll
@@ -138,7 +172,7 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
   const int col = threadIdx.x % BN;
   const int n = n0 + col;
   if (n >= N) return;
-  const float bj = bias != nullptr ? bias[b * bias_bs + n] : 0.f;
+  const float bj = bias != nullptr ? bias[n] : 0.f;
 #pragma unroll
   for (int i = 0; i < BM / RPP; ++i) {
     const int r = (int)(threadIdx.x / BN) + RPP * i;
@@ -149,7 +183,7 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
     for (int ww = 0; ww < NWV; ++ww) v += red[ww][r][col];
     v += bj;
     if (ACT == ACT_GELU) v = gelu_erf(v);
-    const long long o = b * c_bs + (long long)m * ldc + n;
+    const long long o = (long long)m * ldc + n;
     if (OUT == 0) {
       reinterpret_cast<float*>(Cm)[o] = v;
     } else {
@@ -159,6 +193,106 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
       reinterpret_cast<bf16_t*>(C2)[o] = f32_to_bf16(v - bf16_to_f32(h));
     }
   }
+}
+}  // namespace
+
+template <int MB, int NB, int NWV, int PD, int ACT, int OUT>
+__global__ void __launch_bounds__(NWV * 64)
+k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
+            const bf16_t* __restrict__ W, long long ldw, long long w_bs,
+            const float* __restrict__ bias, long long bias_bs, void* __restrict__ Cm,
+            void* __restrict__ C2, long long ldc, long long c_bs, int M, int N, int K,
+            float scale) {
+  const int lane = threadIdx.x & 63;
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NB, m0 = blockIdx.y * 16 * MB, b = blockIdx.z;
+  A += b * a_bs;
+  // operand rows of this lane (clamped: rows past M or N are computed, not stored)
+  ARow<1> arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    arow[mb].p[0] = A + (long long)min(m0 + 16 * mb + lo16, M - 1) * lda + 8 * hi4;
+  f32a_tile<MB, NB, NWV, PD, ACT, OUT, 1>(
+      arow, W + b * w_bs, ldw, bias != nullptr ? bias + b * bias_bs : nullptr,
+      OUT == 0 ? (void*)((float*)Cm + b * c_bs) : (void*)((bf16_t*)Cm + b * c_bs),
+      OUT == 0 ? nullptr : (void*)((bf16_t*)C2 + b * c_bs), ldc, M, N, K, scale, m0, n0);
+}
+
+// Value fold of the folded pooling, reading the token pass's per-workgroup
+// partials directly (no merged xbar in between):
+//   o[t, h d + i] = bv[h d + i] + sum_c Wv[h d + i, c] xbar[t, h, c],
+//   xbar[t, h, :] = (sum_s 2^(m_s - M) acc_s) / (sum_s 2^(m_s - M) l_s),
+// over the partials s of tile t (workgroups g0 .. g1 of the token pass, in
+// order), M their largest running max: the same arithmetic as the merge
+// kernel of the token pass.  grid (ceil(d / 64), ceil(T / 16), H).
+template <int MAXS>
+__global__ void __launch_bounds__(512)
+k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ valid, int Ntok,
+                    int Q, int segmax, const bf16_t* __restrict__ Wv,
+                    const float* __restrict__ bv, float* __restrict__ o, int T, int C, int H) {
+  constexpr int FH = 16;
+  const int lane = threadIdx.x & 63;
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  const int d = C / H;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 16, h = blockIdx.z;
+  const int NC = (Ntok + 15) / 16;
+  const int t = min(m0 + lo16, T - 1);
+  int nv = valid != nullptr ? valid[t] : Ntok;
+  nv = nv < 1 ? 1 : (nv > Ntok ? Ntok : nv);
+  const int lo_c = t * NC, hi_c = t * NC + (nv + 15) / 16;
+  const int g0 = lo_c / Q, g1 = (hi_c - 1) / Q;
+  const size_t stride = (size_t)FH * (2 + C);
+  ARow<MAXS> arow[1];
+  float ms[MAXS], ls[MAXS];
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const int g = min(g0 + i, g1);
+    const float* pp = part + ((size_t)g * segmax + (t - (g * Q) / NC)) * stride;
+    ms[i] = pp[h];
+    ls[i] = pp[FH + h];
+    arow[0].p[i] = pp + 2 * FH + (size_t)h * C + 8 * hi4;
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i)
+    if (g0 + i <= g1) M = fmaxf(M, ms[i]);
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXS; ++i) {
+    const float e = g0 + i <= g1 ? exp2f(ms[i] - M) : 0.f;
+    arow[0].sc[i] = e;
+    L = fmaf(ls[i], e, L);
+  }
+  arow[0].inv = 1.0f / L;
+  f32a_tile<1, 4, 8, 2, ACT_NONE, 0, MAXS>(arow, Wv + (long long)h * d * C, C, bv + h * d,
+                                           o + h * d, nullptr, C, T, d, C, 1.f, m0, n0);
+}
+
+int fold_value_merged_max_parts(int T, int N, int Q) {
+  if (T <= 0 || N <= 0 || Q <= 0) return 0;
+  const int NC = (N + 15) / 16;
+  // a tile's chunks [t NC, t NC + NC) meet at most this many workgroups of Q chunks
+  return (NC - 1 + Q - 1) / Q + 1;
+}
+
+hipError_t launch_fold_value_merged(const float* part, const int* valid, int N, int Q, int segmax,
+                                    const void* Wv, const float* bv, float* o, int T, int C, int H,
+                                    hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int maxs = fold_value_merged_max_parts(T, N, Q);
+  if (maxs < 1 || maxs > 4 || H < 1 || C % H || (C / H) % 16 || C % 32 || (uintptr_t)part % 16 ||
+      (uintptr_t)Wv % 16 || ((size_t)C * 2) % 16)
+    return hipErrorInvalidValue;
+  const int d = C / H;
+  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((T + 15) / 16), (unsigned)H);
+#define IVC_FVM(S)                                                                                 \
+  hipLaunchKernelGGL(k_fold_value_merged<S>, grid, dim3(512), 0, s, part, valid, N, Q, segmax,     \
+                     (const bf16_t*)Wv, bv, o, T, C, H)
+  if (maxs <= 2) IVC_FVM(2);
+  else if (maxs == 3) IVC_FVM(3);
+  else IVC_FVM(4);
+#undef IVC_FVM
+  return hipGetLastError();
 }
 
 bool gemm_f32a_supported(const GemmArgs& g) {
@@ -202,6 +336,149 @@ hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float sc
   }
 #undef IVC_F32A
 #undef IVC_F32A_S
+  return hipGetLastError();
+}
+
+// Folded pooling query of one layer, the query projection and the key fold in
+// one launch (the same arithmetic, in the same order, as the two products
+// above: the query projection as a 16 x 64 tile of 8 waves x 4 K steps, the
+// fold as the short-K form, two K-step parities summed in order):
+//   qp = Wq q + bq                                  [T, C] (never stored)
+//   q~_h = scale * (Wk_h^T qp_h)   for every head h  [T, 16, C] bf16 hi + lo
+// Workgroup (16 tiles, head h): the 16 x D block of qp for head h (K = C)
+// summed through LDS, then the 16 x C block of q~_h with K = D = C / H,
+// wave w taking columns [w C/8, (w+1) C/8); the bf16 halves go through a
+// wave-private LDS slab so each row leaves with 16-byte stores.
+template <int D>
+__global__ void __launch_bounds__(512)
+k_fold_query_fused(const float* __restrict__ q, const bf16_t* __restrict__ Wq,
+                   const float* __restrict__ bq, const bf16_t* __restrict__ WkT,
+                   bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
+                   float scale) {
+  constexpr int NB = D / 16, LDR = D + 4, KS = D / 32;
+  constexpr int SR = 128 + 8;  // slab row (bf16): up to 128 columns per wave, 16 bytes of pad
+  __shared__ __attribute__((aligned(16))) float red[8][16][LDR];
+  __shared__ __attribute__((aligned(16))) float qp_s[16][D];
+  __shared__ __attribute__((aligned(16))) bf16_t slab[8][2][16][SR];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  const int m0 = blockIdx.x * 16, h = blockIdx.y;
+
+  const int CW = C / 8, nbw = CW / 16;  // columns and 16-column blocks of this wave (<= 8)
+  const int c0 = w * CW;
+  // key-fold weights of a group of GB column blocks (loaded ahead of their use)
+  constexpr int GB = KS <= 2 ? 8 : 4;
+  u32x4 xw[GB][KS];
+  auto load_group = [&](int g) {
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int n = c0 + 16 * min(g + j, nbw - 1) + lo16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        xw[j][ks] = *reinterpret_cast<const u32x4*>(WkT + (long long)n * C + h * D + 32 * ks +
+                                                    8 * hi4);
+    }
+  };
+
+  // ---- qp block [16, D] of head h
+  {
+    ARow<1> arow[1];
+    arow[0].p[0] = q + (long long)min(m0 + lo16, T - 1) * C + 8 * hi4;
+    const bf16_t* wrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      wrow[nb] = Wq + (long long)(h * D + 16 * nb + lo16) * C + 8 * hi4;
+    f32x4_t acc[1][NB];
+    f32a_mainloop<1, NB, 8, 4, 1>(arow, wrow, w, C / 32, acc);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][4 * hi4 + v][16 * nb + lo16] = acc[0][nb][v];
+  }
+  load_group(0);  // in flight across the reduction
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * D; i += 512) {
+    const int r = i / D, col = i - r * D;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) v += red[ww][r][col];
+    v += bq[h * D + col];
+    qp_s[r][col] = v;
+  }
+  __syncthreads();
+
+  // ---- q~_h block [16, C]: A = qp_s (hi + lo), B rows n of WkT at column offset h D
+  bf16x8_t ah[KS], al[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float4 x0 = *reinterpret_cast<const float4*>(&qp_s[lo16][32 * ks + 8 * hi4]);
+    const float4 x1 = *reinterpret_cast<const float4*>(&qp_s[lo16][32 * ks + 8 * hi4 + 4]);
+    split8(x0, x1, ah[ks], al[ks]);
+  }
+  bf16_t(*sh)[SR] = slab[w][0];
+  bf16_t(*sl)[SR] = slab[w][1];
+  for (int g = 0; g < nbw; g += GB) {
+    if (g > 0) load_group(g);
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      if (g + j >= nbw) break;
+      f32x4_t a0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, a1 = a0;  // K steps of even / odd index
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, xw[j][ks]);
+        f32x4_t& a = (ks & 1) ? a1 : a0;
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ks], bw, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ks], bw, a, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = 0.f;
+        x += a0[v];
+        x += a1[v];
+        x += 0.f;  // the missing bias, as the two-launch form adds it (-0 becomes +0)
+        x *= scale;
+        const bf16_t hv = f32_to_bf16(x);
+        sh[4 * hi4 + v][16 * (g + j) + lo16] = hv;
+        sl[4 * hi4 + v][16 * (g + j) + lo16] = f32_to_bf16(x - bf16_to_f32(hv));
+      }
+    }
+  }
+  __syncthreads();  // slab rows are read back by other lanes
+  const int ppr = CW / 8;  // 16-byte pieces per row
+  for (int i = lane; i < 16 * ppr; i += 64) {
+    const int r = i / ppr, p = i - r * ppr;
+    const int t = m0 + r;
+    if (t >= T) break;
+    const long long o = ((long long)t * 16 + h) * C + c0 + 8 * p;
+    *reinterpret_cast<u32x4*>(qt_hi + o) = *reinterpret_cast<const u32x4*>(&sh[r][8 * p]);
+    *reinterpret_cast<u32x4*>(qt_lo + o) = *reinterpret_cast<const u32x4*>(&sl[r][8 * p]);
+  }
+}
+
+bool fold_query_fused_supported(int C, int H) {
+  if (H < 1 || H > 16 || C % H != 0) return false;
+  const int d = C / H;
+  return (d == 32 || d == 64 || d == 128) && C % 128 == 0 && C <= 1024;
+}
+
+hipError_t launch_fold_query_fused(const float* q, const void* Wq, const float* bq,
+                                   const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
+                                   float scale, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!fold_query_fused_supported(C, H) || !q || !Wq || !bq || !WkT || !qt_hi || !qt_lo ||
+      (uintptr_t)q % 16 || (uintptr_t)Wq % 16 || (uintptr_t)WkT % 16 || (uintptr_t)qt_hi % 16 ||
+      (uintptr_t)qt_lo % 16)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((T + 15) / 16), (unsigned)H);
+  const int d = C / H;
+#define IVC_FQF(DV)                                                                                \
+  hipLaunchKernelGGL(k_fold_query_fused<DV>, grid, dim3(512), 0, s, q, (const bf16_t*)Wq, bq,      \
+                     (const bf16_t*)WkT, (bf16_t*)qt_hi, (bf16_t*)qt_lo, T, C, scale)
+  if (d == 32) IVC_FQF(32);
+  else if (d == 64) IVC_FQF(64);
+  else IVC_FQF(128);
+#undef IVC_FQF
   return hipGetLastError();
 }
 

@@ -169,7 +169,7 @@ template <int C>
 __global__ void __launch_bounds__(512, 2 * PF<C>::WG_PER_CU)
 k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __restrict__ valid,
               int T, int N, const bf16_t* __restrict__ qt_hi, const bf16_t* __restrict__ qt_lo,
-              int Q, int segmax, float* __restrict__ part) {
+              int Q, int segmax, float* __restrict__ part, int* __restrict__ status) {
   using P = PF<C>;
   constexpr int NW = P::NW, KS = P::KS, NT = P::NT, RB = P::RB, SB = P::SB, DPW = P::DPW;
   constexpr int LDP = P::LDP;
@@ -188,6 +188,13 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
   const int c_end = min(total, c_beg + Q);
   const int t_first = c_beg / NC;
   const int cw0 = w * P::CW;
+  // token counts out of range are clamped and flagged (every tile meets some workgroup)
+  if (valid != nullptr && status != nullptr && c_beg < c_end) {
+    for (int t = t_first + (int)threadIdx.x; t <= (c_end - 1) / NC; t += 512) {
+      const int nv = valid[t];
+      if (nv < 1 || nv > N) atomicOr(status, 2);
+    }
+  }
 
   // ---- DMA of one chunk: wave w loads rows 2w, 2w+1 (IPR instructions each)
   const int dma_f = (w >> 2) & 1;  // swizzle term of rows 2w, 2w+1
@@ -367,7 +374,8 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
 }
 
 // xbar[t][h][c] = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) over the
-// partials of tile t, in workgroup order.  Also flags invalid token counts.
+// partials of tile t, in workgroup order (fmaf accumulation, as the value fold
+// that reads the partials directly).  Also flags invalid token counts.
 __global__ void __launch_bounds__(256)
 k_pool_folded_merge(const float* __restrict__ part, const int* __restrict__ valid, int* status,
                     int N, int C, int H, int Q, int segmax, float* __restrict__ xbar) {
@@ -387,7 +395,7 @@ k_pool_folded_merge(const float* __restrict__ part, const int* __restrict__ vali
   float L = 0.f;
   for (int g = g0; g <= g1; ++g) {
     const float* pp = part + ((size_t)g * segmax + (t - (g * Q) / NC)) * stride;
-    L += pp[FH + h] * exp2f(pp[h] - M);
+    L = fmaf(pp[FH + h], exp2f(pp[h] - M), L);
   }
   const float invL = 1.0f / L;
   for (int c4 = threadIdx.x; c4 < C / 4; c4 += 256) {
@@ -396,10 +404,10 @@ k_pool_folded_merge(const float* __restrict__ part, const int* __restrict__ vali
       const float* pp = part + ((size_t)g * segmax + (t - (g * Q) / NC)) * stride;
       const float sc = exp2f(pp[h] - M);
       const float4 v = *reinterpret_cast<const float4*>(pp + 2 * FH + (size_t)h * C + 4 * c4);
-      A.x += v.x * sc;
-      A.y += v.y * sc;
-      A.z += v.z * sc;
-      A.w += v.w * sc;
+      A.x = fmaf(v.x, sc, A.x);
+      A.y = fmaf(v.y, sc, A.y);
+      A.z = fmaf(v.z, sc, A.z);
+      A.w = fmaf(v.w, sc, A.w);
     }
     A.x *= invL;
     A.y *= invL;
@@ -417,13 +425,14 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s) {
   if (a.C == 1024)
     hipLaunchKernelGGL(k_pool_folded<1024>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
                        a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,
-                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part);
+                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status);
   else
     hipLaunchKernelGGL(k_pool_folded<512>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
                        a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,
-                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part);
+                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.xbar == nullptr) return hipSuccess;  // the partials are read by the merged value fold
   hipLaunchKernelGGL(k_pool_folded_merge, dim3((unsigned)a.T, (unsigned)a.H), dim3(256), 0, s,
                      (const float*)a.part, a.valid, a.status, a.N, a.C, a.H, a.Q, a.segmax,
                      a.xbar);

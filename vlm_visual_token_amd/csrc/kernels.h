@@ -219,7 +219,7 @@ struct FoldedArgs {
   const void* qt_lo;  // low part
   int G, Q, segmax;   // from folded_geometry
   float* part;        // [G * segmax, 16 * (2 + C)]
-  float* xbar;        // [T, H, C] softmax-weighted token means
+  float* xbar;        // [T, H, C] softmax-weighted token means; nullptr: no merge launch
 };
 // Work split of the token pass: G workgroups of Q consecutive 16-token chunks
 // each (chunk index = tile * ceil(N/16) + chunk); a workgroup leaves at most
@@ -230,8 +230,21 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
 // qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
 hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt_hi, void* qt_lo,
                              int T, int C, int H, float scale, hipStream_t s);
+// qp = Wq q + bq, then q~_h = scale * Wk_h^T qp_h for every head, in one launch
+// (the same values as a query projection followed by the key fold).
+bool fold_query_fused_supported(int C, int H);
+hipError_t launch_fold_query_fused(const float* q, const void* Wq, const float* bq,
+                                   const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
+                                   float scale, hipStream_t s);
 // qt_hi / qt_lo [T, 16, C]: heads H .. 15 set to zero
 hipError_t launch_zero_heads(void* qt_hi, void* qt_lo, int T, int H, int C, hipStream_t s);
+// The value fold reading the token pass's partials directly (no merge launch):
+// o[t, h*d + i] = bv[h*d + i] + sum_c Wv[h*d + i, c] * xbar[t, h, c], bf16 Wv.
+// Usable when a tile's chunks meet at most 4 workgroups (max_parts <= 4).
+int fold_value_merged_max_parts(int T, int N, int Q);
+hipError_t launch_fold_value_merged(const float* part, const int* valid, int N, int Q, int segmax,
+                                    const void* Wv, const float* bv, float* o, int T, int C, int H,
+                                    hipStream_t s);
 // o[t, h*d + i] = bv[h*d+i] + sum_c Wv[h*d + i, c] * xbar[t, h, c]
 hipError_t launch_fold_value(int dtype, const float* xbar, const void* Wv, const float* bv,
                              float* o, int T, int C, int H, hipStream_t s);
