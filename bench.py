@@ -59,6 +59,8 @@ def hbm_bytes(cfg: dict, L_seq: int, Lp: int) -> dict:
         "shuffle_ln": x_read + T * cfg["S"] * 4 * C * e + T * cfg["S64"] * 16 * C * e,
         "pool_attn": T * N * 2 * C * e,  # one layer's K and V
         "pool_folded": T * N * C * e,  # one layer's pass over the tokens
+        "token_stats": x_read + T * N * 8,  # per-token LayerNorm moments
+        "ln_stats": T * N * 8 + T * (cfg["S"] + cfg["S64"]) * 8,
         "compact": 2 * Lp * D * e + L_seq * 4 * 2 + Lp * 4 * 2,
     }
 
@@ -69,7 +71,8 @@ KERNEL_SOURCE = {
     "mlp1_gemm1": "k_gemm_dma.hip", "mlp1_gemm2": "k_gemm_dma.hip",
     "mlp2_gemm1": "k_gemm_dma.hip", "mlp2_gemm2": "k_gemm_dma.hip",
     "mlp2_gemm3": "k_gemm_dma.hip", "pool_folded": "k_pool_folded.hip",
-    "shuffle_ln": "k_loader.hip", "compact": "k_compact.hip",
+    "shuffle_ln": "k_loader.hip", "compact": "k_compact.hip", "token_stats": "k_pool_folded.hip",
+    "ln_stats": "k_loader.hip",
 }
 
 

@@ -743,6 +743,29 @@ def test_forward_matches_route_then_run_ln_fold_small(version, order):
     _check_forward(cfg, w, torch.from_numpy(x).to(torch.bfloat16).cuda())
 
 
+# C = 512: LayerNorm statistics through per-token moments (from the first
+# token pass in forward, from their own kernel in run_routed), every index
+# variant; outputs bit-equal between the two calls and close to the oracle
+@pytest.mark.parametrize("version,order", [(2, "direct"), (1, "direct"), (2, "twice_r2"),
+                                           (1, "twice_r2")])
+def test_forward_ln_fold_token_stats_small(version, order):
+    cfg = workload("tiny_flash_f32", dtype="bf16", C=512, D=256, mlp1_hidden=256,
+                   mlp2_hidden=256, pool_heads=8, gate_hidden=512, pool_mode=1, ln_fold=1,
+                   ps_version=version, shuffle64_order=order)
+    cfg["name"] = "small_bf16_ln_fold"
+    w = synth.make_weights(cfg)
+    x = synth.make_vit(cfg)
+    say(f"forward token stats small v{version} {order}")
+    f = _check_forward(cfg, w, torch.from_numpy(x).to(torch.bfloat16).cuda())
+    use = f["use64"].cpu().numpy()
+    e256, e64 = O.connector_run(x, cfg, w)
+    t256, t64 = np.flatnonzero(use == 0), np.flatnonzero(use != 0)
+    if len(t256):
+        assert_close(to_np(f["out256"][t256]), e256[t256], "bf16", "out256 (forward)")
+    if len(t64):
+        assert_close(to_np(f["out64"][t64]), e64[t64], "bf16", "out64 (forward)")
+
+
 def test_forward_flash_workload_ln_fold():
     cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
     say(f"2B-Flash forward (ln_fold): T={cfg['T']}")

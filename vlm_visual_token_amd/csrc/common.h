@@ -76,6 +76,17 @@ IVC_DEV float wave_max(float v) {
   return v;
 }
 
+// ---- moments (mean, sum of squared deviations) of equal-sized groups -------
+// Two groups of n values each, (mean a.x, M2 a.y) and (b.x, b.y), combined
+// (Chan, Golub and LeVeque's pairwise update with n_a = n_b = n):
+//   mean = (a.x + b.x) / 2,  M2 = a.y + b.y + (a.x - b.x)^2 * n / 2.
+// half_n = n / 2.  The result depends on the operand order only through
+// a.y + b.y and a.x + b.x, both commutative.
+IVC_DEV float2 moments_pair(float2 a, float2 b, float half_n) {
+  const float d = a.x - b.x;
+  return make_float2((a.x + b.x) * 0.5f, fmaf(d * d, half_n, a.y + b.y));
+}
+
 // erf by the rational approximation of Abramowitz & Stegun, Handbook of
 // Mathematical Functions, formula 7.1.26 (absolute error <= 1.5e-7):
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),

@@ -623,21 +623,36 @@ extern "C" void ivc_connector_destroy(ivc_connector* h) {
   delete h;
 }
 
+// LayerNorm-fold statistics through per-token moments (bf16, C of 512 or
+// 1024): the moments live past both the run and the route layouts, so the
+// first token pass of forward can leave them for the run half.
+static bool use_token_stats(const ivc_connector* h) {
+  const ivc_config& c = h->cfg;
+  return c.ln_fold && token_stats_supported(c.dtype, c.vit_width, c.grid * c.grid);
+}
+static size_t tokst_offset(const ivc_connector* h, int T) {
+  const size_t a = plan_run(h, T, nullptr, nullptr), b = plan_route(h, T, nullptr, nullptr);
+  return ((a > b ? a : b) + 255) & ~(size_t)255;
+}
+static size_t tokst_bytes(const ivc_connector* h, int T) {
+  return use_token_stats(h) ? (size_t)T * h->cfg.grid * h->cfg.grid * 8 : 0;
+}
+
 extern "C" size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t max_tiles,
                                                 int64_t max_seq_len) {
   if (!h || max_tiles < 0 || max_seq_len < 0) return 0;
-  size_t a = plan_run(h, max_tiles, nullptr, nullptr);
-  size_t b = plan_route(h, max_tiles, nullptr, nullptr);
-  size_t c = plan_compact(max_tiles, max_seq_len, nullptr, nullptr);
-  size_t m = a > b ? a : b;
+  const size_t m = tokst_offset(h, max_tiles) + tokst_bytes(h, max_tiles);
+  const size_t c = plan_compact(max_tiles, max_seq_len, nullptr, nullptr);
   return m > c ? m : c;
 }
 
 // ---------------------------------------------------------------------------
 // run
 // ---------------------------------------------------------------------------
+// tokst_ready: the per-token moments are already in the workspace (forward)
 static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const uint8_t* use64,
-                           void* out256, void* out64, void* ws, size_t ws_bytes, void* stream) {
+                           void* out256, void* out64, void* ws, size_t ws_bytes, void* stream,
+                           bool tokst_ready = false) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
@@ -649,7 +664,8 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   const long long S = (long long)(c.grid / 2) * (c.grid / 2);
   if ((long long)T * S * 16 * c.vit_width > (1ll << 40))
     return fail(IVC_ERR_UNSUPPORTED, "T = %d too large", T);
-  const size_t need = plan_run(h, T, nullptr, nullptr);
+  const bool tstats = use_token_stats(h);
+  const size_t need = tstats ? tokst_offset(h, T) + tokst_bytes(h, T) : plan_run(h, T, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return fail(IVC_ERR_WORKSPACE, "run needs %zu workspace bytes, got %zu", need, ws_bytes);
   RunWs w;
@@ -702,7 +718,18 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     sa.use64 = use64;
     sa.rank = w.rank;
   }
-  LAUNCH("shuffle_ln", s, launch_shuffle_ln(sa, s));
+  if (fold && tstats) {
+    // per-token moments (unless the first token pass left them), then each
+    // shuffled row's (mean, rstd) from its 4 or 16 cells
+    float* tokst = (float*)((char*)ws + tokst_offset(h, T));
+    if (!tokst_ready)
+      LAUNCH("token_stats", s, launch_token_stats(vit, T, c.has_cls + c.grid * c.grid, c.has_cls,
+                                                  c.grid * c.grid, C, tokst, s));
+    LAUNCH("ln_stats", s, launch_ln_stats(tokst, T, c.grid, C, c.ln_eps, sa.ps_v1, c.flash,
+                                          sa.use64, sa.rank, sa.st2, sa.st4, s));
+  } else {
+    LAUNCH("shuffle_ln", s, launch_shuffle_ln(sa, s));
+  }
 
   // The mlp1 and mlp2 chains are independent: with a second stream the tail
   // workgroups of one chain's products share the chip with the other's
@@ -795,10 +822,12 @@ extern "C" ivc_status ivc_connector_run_routed(ivc_connector* h, const void* vit
 // ---------------------------------------------------------------------------
 // route
 // ---------------------------------------------------------------------------
+// tokst: if set, the first token pass also leaves every token's LayerNorm
+// moments there (forward; folded pooling, no padding mask)
 static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
                              int32_t T, float* gate, double* threshold, uint8_t* use64,
                              float* pooled, int32_t* dev_status, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             void* stream, float* tokst = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (!c.flash) return fail(IVC_ERR_INVALID_ARG, "route needs a flash connector");
@@ -891,6 +920,7 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       fa.Q = fQ;
       fa.segmax = fseg;
       fa.part = w.part;
+      fa.tokst = l == 0 ? tokst : nullptr;
       // o_h = Wv_h xbar_h + bv_h for every head: one batched product over heads,
       // with bf16 weights reading the token pass's partials directly (the merge
       // of a tile's partials happens in its operand load)
@@ -982,10 +1012,23 @@ extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward needs a flash connector");
   if (T > 0 && (!out256 || !out64)) return fail(IVC_ERR_INVALID_ARG, "null out256/out64");
+  // the LayerNorm-fold statistics come out of the first token pass when it
+  // reads every token (folded pooling, no padding mask): one less pass over
+  // the ViT tensor
+  const ivc_config& c = h->cfg;
+  float* tokst = nullptr;
+  if (T > 0 && use_token_stats(h) && c.pool_mode == IVC_POOL_FOLDED && valid_tokens == nullptr &&
+      pool_folded_supported(c.dtype, c.vit_width, c.pool_heads)) {
+    const size_t need = tokst_offset(h, T) + tokst_bytes(h, T);
+    if (!ws || ws_bytes < need)
+      return fail(IVC_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (!aligned16(ws)) return fail(IVC_ERR_MISALIGNED, "ws alignment");
+    tokst = (float*)((char*)ws + tokst_offset(h, T));
+  }
   ivc_status st = route_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status,
-                             ws, ws_bytes, stream);
+                             ws, ws_bytes, stream, tokst);
   if (st != IVC_OK) return st;
-  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream);
+  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream, tokst != nullptr);
 }
 
 // ---------------------------------------------------------------------------

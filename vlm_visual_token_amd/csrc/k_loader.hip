@@ -248,6 +248,71 @@ static hipError_t launch_e(const ShuffleArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// LayerNorm statistics of the shuffled rows from the per-token moments
+// tokst[t * N + n] = (mean, M2) of each grid cell's C channels: an r = 2 row
+// is a 2 x 2 cell block, an r = 4 row the 4 x 4 block of four of them
+// (whatever order the channel blocks take inside the row), combined
+// pairwise: the two cells of a grid row, then the two rows; the four 2 x 2
+// blocks likewise.  st2 / st4 get (mean, 1 / sqrt(M2 / n + eps)), n = 4C or
+// 16C, at the row the projector reads (route-first: the tile's rank in its
+// path, the other path skipped).  One thread per r = 2 row, then one per
+// r = 4 row.
+IVC_DEV float2 block2_moments(const float2* __restrict__ ts, int P, int gi, int gj, float C) {
+  const float2* c0 = ts + (size_t)gi * P + gj;
+  const float2 top = moments_pair(c0[0], c0[1], 0.5f * C);
+  const float2 bot = moments_pair(c0[P], c0[P + 1], 0.5f * C);
+  return moments_pair(top, bot, C);
+}
+
+__global__ void __launch_bounds__(256)
+k_ln_stats(const float2* __restrict__ tokst, int T, int P, int C, float eps, int ps_v1, int flash,
+           const uint8_t* __restrict__ use64, const int* __restrict__ rank,
+           float* __restrict__ st2, float* __restrict__ st4) {
+  const int Q2 = P / 2, S2 = Q2 * Q2, Q4 = P / 4, S4 = flash ? Q4 * Q4 : 0;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long n2 = (long long)T * S2;
+  const int N = P * P;
+  if (i < n2) {
+    const int t = (int)(i / S2), s = (int)(i - (long long)t * S2);
+    if (st2 == nullptr || (use64 != nullptr && use64[t] != 0)) return;
+    const int a = s / Q2, b = s - a * Q2;  // token (a, b) of the direct order
+    const float2 mo = block2_moments(tokst + (size_t)t * N, P, 2 * a, 2 * b, (float)C);
+    const int t2 = use64 != nullptr ? rank[t] : t;
+    const int tok = ps_v1 ? b * Q2 + a : s;
+    *reinterpret_cast<float2*>(st2 + 2 * ((size_t)t2 * S2 + tok)) =
+        make_float2(mo.x, 1.0f / sqrtf(mo.y / (float)(4 * C) + eps));
+    return;
+  }
+  const long long i4 = i - n2;
+  if (i4 >= (long long)T * S4) return;
+  const int t = (int)(i4 / S4), s = (int)(i4 - (long long)t * S4);
+  if (st4 == nullptr || (use64 != nullptr && use64[t] == 0)) return;
+  const int a = s / Q4, b = s - a * Q4;
+  const float2* ts = tokst + (size_t)t * N;
+  const float fc = (float)C;
+  const float2 b00 = block2_moments(ts, P, 4 * a, 4 * b, fc);
+  const float2 b01 = block2_moments(ts, P, 4 * a, 4 * b + 2, fc);
+  const float2 b10 = block2_moments(ts, P, 4 * a + 2, 4 * b, fc);
+  const float2 b11 = block2_moments(ts, P, 4 * a + 2, 4 * b + 2, fc);
+  const float2 mo = moments_pair(moments_pair(b00, b01, 2.f * fc), moments_pair(b10, b11, 2.f * fc),
+                                 4.f * fc);
+  const int t4 = use64 != nullptr ? rank[t] : t;
+  const int tok = ps_v1 ? b * Q4 + a : s;
+  *reinterpret_cast<float2*>(st4 + 2 * ((size_t)t4 * S4 + tok)) =
+      make_float2(mo.x, 1.0f / sqrtf(mo.y / (float)(16 * C) + eps));
+}
+
+hipError_t launch_ln_stats(const float* tokst, int T, int P, int C, float eps, int ps_v1,
+                           int flash, const uint8_t* use64, const int* rank, float* st2,
+                           float* st4, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!tokst || P % (flash ? 4 : 2) || (use64 != nullptr && rank == nullptr)) return hipErrorInvalidValue;
+  const long long n = (long long)T * ((P / 2) * (P / 2) + (flash ? (P / 4) * (P / 4) : 0));
+  hipLaunchKernelGGL(k_ln_stats, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const float2*)tokst, T, P, C, eps, ps_v1, flash, use64, rank, st2, st4);
+  return hipGetLastError();
+}
+
 int shuffle_max_width(int dtype) { return 8 * 64 * (dtype == 1 ? 8 : 4); }
 
 hipError_t launch_shuffle_ln(const ShuffleArgs& a, hipStream_t s) {

@@ -149,6 +149,61 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 IVC_DEV uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+
+// ---- per-token LayerNorm moments ------------------------------------------
+// A token's C channels as the token pass holds them: wave w (of 8) has
+// channels [w C/8, (w+1) C/8), its lane (token, g = lane / 16) the 8-channel
+// pieces g, g + 4, g + 8, ... of that range (KS = C / 256 of them).  Moments
+// (mean, M2) are taken per lane (two passes over its 8 KS values), combined
+// over the lane's 4 partners (v_permlane32_swap, then v_permlane16_swap) and
+// over the 8 waves in a fixed tree.  The token pass (first layer) and
+// k_token_stats both run exactly these steps, so their results are equal bit
+// for bit.
+template <int KS>
+IVC_DEV float2 lane_moments(const bf16x8_t (&a)[KS]) {
+  float f[KS][8];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const u32x4 u = __builtin_bit_cast(u32x4, a[k]);
+    unpack16(u, f[k], (bf16_t*)nullptr);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += f[k][e];
+  const float m = s / (float)(8 * KS);
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = f[k][e] - m;
+      q = fmaf(d, d, q);
+    }
+  return make_float2(m, q);
+}
+
+// lane l with l ^ 32, then with l ^ 16 (n values per lane); every one of the
+// four lanes ends with the same result (the swaps return the lower and the
+// upper partner's value in the same order on both sides)
+IVC_DEV float2 moments_x4(float2 mo, float n) {
+  auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mo.x), __float_as_uint(mo.x), false, false);
+  auto rq = __builtin_amdgcn_permlane32_swap(__float_as_uint(mo.y), __float_as_uint(mo.y), false, false);
+  mo = moments_pair(make_float2(__uint_as_float(rm[0]), __uint_as_float(rq[0])),
+                    make_float2(__uint_as_float(rm[1]), __uint_as_float(rq[1])), 0.5f * n);
+  auto sm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mo.x), __float_as_uint(mo.x), false, false);
+  auto sq = __builtin_amdgcn_permlane16_swap(__float_as_uint(mo.y), __float_as_uint(mo.y), false, false);
+  return moments_pair(make_float2(__uint_as_float(sm[0]), __uint_as_float(sq[0])),
+                      make_float2(__uint_as_float(sm[1]), __uint_as_float(sq[1])), n);
+}
+
+// the 8 waves' moments of one token (n values each): ((0,1),(2,3)),((4,5),(6,7))
+IVC_DEV float2 moments_8(const float2* w8, float n) {
+  const float2 a = moments_pair(w8[0], w8[1], 0.5f * n), b = moments_pair(w8[2], w8[3], 0.5f * n);
+  const float2 c = moments_pair(w8[4], w8[5], 0.5f * n), d = moments_pair(w8[6], w8[7], 0.5f * n);
+  return moments_pair(moments_pair(a, b, n), moments_pair(c, d, n), 2.f * n);
+}
 }  // namespace
 
 void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax) {
@@ -165,11 +220,14 @@ void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax) 
 }
 
 // part layout per slot: [FH] running max (log2 units), [FH] running sum, [FH][C] weighted sums
-template <int C>
+// STATS: also leave every token's LayerNorm moments (mean, M2 over its C
+// channels) in tokst[t * N + n] (all tokens valid).
+template <int C, bool STATS>
 __global__ void __launch_bounds__(512, 2 * PF<C>::WG_PER_CU)
 k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __restrict__ valid,
               int T, int N, const bf16_t* __restrict__ qt_hi, const bf16_t* __restrict__ qt_lo,
-              int Q, int segmax, float* __restrict__ part, int* __restrict__ status) {
+              int Q, int segmax, float* __restrict__ part, int* __restrict__ status,
+              float2* __restrict__ tokst) {
   using P = PF<C>;
   constexpr int NW = P::NW, KS = P::KS, NT = P::NT, RB = P::RB, SB = P::SB, DPW = P::DPW;
   constexpr int LDP = P::LDP;
@@ -178,6 +236,7 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
   __shared__ __attribute__((aligned(1024))) char st2[SB];
   __shared__ __attribute__((aligned(1024))) char st3[SB];
   __shared__ __attribute__((aligned(16))) float sP[NW][FH][LDP];
+  __shared__ float2 sTS[STATS ? NW * FH : 1];  // [token][wave] moments
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -293,7 +352,15 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
       }
       *reinterpret_cast<f32x4_t*>(&sP[w][lo16][4 * hi4]) = sc;
     }
+    if (STATS) {
+      const float2 mo = moments_x4(lane_moments<KS>(a), (float)(C / 32));
+      if (hi4 == 0) sTS[lo16 * NW + w] = mo;
+    }
     lds_barrier();
+    if (STATS && w == 0 && lane < 16) {
+      const int n = 16 * ci.j + lane;
+      if (n < N) tokst[(size_t)ci.t * N + n] = moments_8(&sTS[lane * NW], (float)(C / 8));
+    }
 
     // operands of the weighted sum first: they do not depend on the softmax
     s16x4_t b[NT];
@@ -417,19 +484,73 @@ k_pool_folded_merge(const float* __restrict__ part, const int* __restrict__ vali
   }
 }
 
+// Every token's LayerNorm moments without the pooling: workgroup = one
+// 16-token chunk (tile c / (N/16)), the 8 waves and lanes holding the same
+// channels as in the token pass, read straight from global memory.
+template <int C>
+__global__ void __launch_bounds__(512)
+k_token_stats(const bf16_t* __restrict__ X, int rows, int has_cls, int N,
+              float2* __restrict__ tokst) {
+  using P = PF<C>;
+  constexpr int NW = P::NW, KS = P::KS;
+  __shared__ float2 sTS[FH * NW];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  const int NC = N / 16;
+  const int t = blockIdx.x / NC, j = blockIdx.x - t * NC;
+  const int n = 16 * j + lo16;
+  const bf16_t* src = X + ((size_t)t * rows + has_cls + n) * C + w * P::CW + 8 * hi4;
+  bf16x8_t a[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+    a[k] = __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(
+                                            reinterpret_cast<const u32x4*>(src + 32 * k)));
+  const float2 mo = moments_x4(lane_moments<KS>(a), (float)(C / 32));
+  if (hi4 == 0) sTS[lo16 * NW + w] = mo;
+  __syncthreads();
+  if (w == 0 && lane < 16)
+    tokst[(size_t)t * N + 16 * j + lane] = moments_8(&sTS[lane * NW], (float)(C / 8));
+}
+
+bool token_stats_supported(int dtype, int C, int N) {
+  return dtype == DT_BF16 && (C == 512 || C == 1024) && N % 16 == 0 && N > 0;
+}
+
+hipError_t launch_token_stats(const void* X, int T, int rows, int has_cls, int N, int C,
+                              float* tokst, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!token_stats_supported(DT_BF16, C, N) || (uintptr_t)X % 16 || (uintptr_t)tokst % 8)
+    return hipErrorInvalidValue;
+  const long long nb = (long long)T * (N / 16);
+  if (nb > 0x7fffffffll) return hipErrorInvalidValue;
+  if (C == 1024)
+    hipLaunchKernelGGL(k_token_stats<1024>, dim3((unsigned)nb), dim3(512), 0, s,
+                       (const bf16_t*)X, rows, has_cls, N, (float2*)tokst);
+  else
+    hipLaunchKernelGGL(k_token_stats<512>, dim3((unsigned)nb), dim3(512), 0, s, (const bf16_t*)X,
+                       rows, has_cls, N, (float2*)tokst);
+  return hipGetLastError();
+}
+
 hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (!pool_folded_supported(a.dtype, a.C, a.H)) return hipErrorInvalidValue;
   if (a.G < 1 || a.Q < 1 || a.segmax < 1) return hipErrorInvalidValue;
   dim3 grid((unsigned)a.G);
-  if (a.C == 1024)
-    hipLaunchKernelGGL(k_pool_folded<1024>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
-                       a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,
-                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status);
-  else
-    hipLaunchKernelGGL(k_pool_folded<512>, grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,
-                       a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,
-                       (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status);
+  if (a.tokst != nullptr && (a.valid != nullptr || a.N % 16 != 0)) return hipErrorInvalidValue;
+#define IVC_PF(CV, ST)                                                                             \
+  hipLaunchKernelGGL((k_pool_folded<CV, ST>), grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,   \
+                     a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,                         \
+                     (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status, (float2*)a.tokst)
+  if (a.C == 1024) {
+    if (a.tokst) IVC_PF(1024, true);
+    else IVC_PF(1024, false);
+  } else {
+    if (a.tokst) IVC_PF(512, true);
+    else IVC_PF(512, false);
+  }
+#undef IVC_PF
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.xbar == nullptr) return hipSuccess;  // the partials are read by the merged value fold

@@ -33,6 +33,12 @@ struct ShuffleArgs {
   const int* rank = nullptr;
 };
 hipError_t launch_shuffle_ln(const ShuffleArgs& a, hipStream_t s);
+// (mean, rstd) of every shuffled LayerNorm row from the per-token moments
+// tokst [T, P*P] float2 (launch_token_stats or the first token pass), written
+// to st2 / st4 as the statistics mode of launch_shuffle_ln writes them.
+hipError_t launch_ln_stats(const float* tokst, int T, int P, int C, float eps, int ps_v1,
+                           int flash, const uint8_t* use64, const int* rank, float* st2,
+                           float* st4, hipStream_t s);
 int shuffle_max_width(int dtype);
 
 // ---- route-first products -----------------------------------------------------
@@ -220,12 +226,20 @@ struct FoldedArgs {
   int G, Q, segmax;   // from folded_geometry
   float* part;        // [G * segmax, 16 * (2 + C)]
   float* xbar;        // [T, H, C] softmax-weighted token means; nullptr: no merge launch
+  float* tokst;       // optional [T, N] float2: each token's LayerNorm moments (mean, M2);
+                      // needs valid == nullptr
 };
 // Work split of the token pass: G workgroups of Q consecutive 16-token chunks
 // each (chunk index = tile * ceil(N/16) + chunk); a workgroup leaves at most
 // segmax partials.  ncu = compute units of the device.
 void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax);
 bool pool_folded_supported(int dtype, int C, int H);
+// Each token's LayerNorm moments over its C channels, tokst[t * N + n] =
+// (mean, sum of squared deviations), with the same arithmetic as the token
+// pass's statistics; bf16, C of 512 or 1024, N a multiple of 16.
+bool token_stats_supported(int dtype, int C, int N);
+hipError_t launch_token_stats(const void* X, int T, int rows, int has_cls, int N, int C,
+                              float* tokst, hipStream_t s);
 hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
 // qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
 hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt_hi, void* qt_lo,
