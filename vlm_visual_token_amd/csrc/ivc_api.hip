@@ -148,6 +148,7 @@ struct ivc_connector {
   float *m1_cs = nullptr, *m2_cs = nullptr;
   // router
   void* query;
+  float* query_f;  // the learned query widened to fp32 (read by every tile's first layer)
   void *wq[IVC_MAX_POOL_LAYERS], *wo[IVC_MAX_POOL_LAYERS];
   float *bq[IVC_MAX_POOL_LAYERS], *bo[IVC_MAX_POOL_LAYERS];
   void* wkv;   // [2 * layers * C, C]: Wk_0; Wv_0; Wk_1; Wv_1; ...
@@ -358,7 +359,7 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
 
 struct RouteWs {
   void *kv, *qt_hi, *qt_lo;
-  float *q, *qp, *o, *part, *xbar, *y1, *y2, *x;
+  float *q, *qp, *o, *part, *xbar, *y1, *y2, *x, *x2;
   SimtScratch sc;
 };
 size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
@@ -386,6 +387,7 @@ size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   r.y1 = (float*)cv.take((size_t)T * he * 4);
   r.y2 = (float*)cv.take((size_t)T * hh * 4);
   r.x = (float*)cv.take((size_t)T * hh * 4);
+  r.x2 = (float*)cv.take((size_t)T * hh * 4);
   r.sc.need(T, (int)C, (int)C, 1);
   r.sc.need(T, (int)he, (int)hh, 1);
   r.sc.need(T, (int)hh, (int)he, 1);
@@ -515,6 +517,7 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       h->m2_w3 = cv.take(D * H2 * e);
       h->m2_b3 = (float*)cv.take(D * 4);
       h->query = cv.take(C * e);
+      h->query_f = (float*)cv.take(C * 4);
       for (size_t l = 0; l < Lp; ++l) {
         h->wq[l] = cv.take(C * C * e);
         h->bq[l] = (float*)cv.take(C * 4);
@@ -577,6 +580,7 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
     STEP(copy_mat(w->mlp2_w3, h->m2_w3, D * H2 * e, s));
     STEP(widen(w->mlp2_b3, dt, h->m2_b3, D, s));
     STEP(copy_mat(w->pool_query, h->query, C * e, s));
+    STEP(widen(w->pool_query, dt, h->query_f, C, s));
     for (size_t l = 0; l < Lp; ++l) {
       STEP(copy_mat(w->pool_wq[l], h->wq[l], C * C * e, s));
       STEP(widen(w->pool_bq[l], dt, h->bq[l], C, s));
@@ -649,10 +653,11 @@ extern "C" size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t 
 // ---------------------------------------------------------------------------
 // run
 // ---------------------------------------------------------------------------
-// tokst_ready: the per-token moments are already in the workspace (forward)
+// tokst_ready: the per-token moments are already in the workspace; lists_ready:
+// so are the per-path tile lists of use64 (both left by forward's route half)
 static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const uint8_t* use64,
                            void* out256, void* out64, void* ws, size_t ws_bytes, void* stream,
-                           bool tokst_ready = false) {
+                           bool tokst_ready = false, bool lists_ready = false) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
@@ -678,7 +683,9 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   // route-first: per-path tile ranks and lists from the decision
   RowMap rm256, rm64, rmh256, rmh64;
   if (use64 != nullptr) {
-    LAUNCH("route_lists", s, launch_route_lists(use64, T, w.rank, w.list256, w.list64, w.counts, s));
+    if (!lists_ready)
+      LAUNCH("route_lists", s,
+             launch_route_lists(use64, T, w.rank, w.list256, w.list64, w.counts, s));
     rmh256.m_dev = w.counts;      // hidden rows of mlp1: n256 * S
     rmh256.m_mult = (int)S;
     rm256 = rmh256;               // final rows scatter back to the tile's slots
@@ -824,10 +831,12 @@ extern "C" ivc_status ivc_connector_run_routed(ivc_connector* h, const void* vit
 // ---------------------------------------------------------------------------
 // tokst: if set, the first token pass also leaves every token's LayerNorm
 // moments there (forward; folded pooling, no padding mask)
+// lists: if set (rank, list256, list64, counts of the run workspace), the
+// decision kernel also writes the per-path tile lists (forward)
 static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
                              int32_t T, float* gate, double* threshold, uint8_t* use64,
                              float* pooled, int32_t* dev_status, void* ws, size_t ws_bytes,
-                             void* stream, float* tokst = nullptr) {
+                             void* stream, float* tokst = nullptr, const RunWs* lists = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (!c.flash) return fail(IVC_ERR_INVALID_ARG, "route needs a flash connector");
@@ -857,13 +866,15 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     LAUNCH("pool_kv_gemm", s, gemm("pool_kv_gemm", kv, s));
   }
 
-  LAUNCH("pool_query", s, launch_broadcast_rows(dt, h->query, w.q, T, C, s));
+  // query projection and key fold in one launch where the shape allows it;
+  // its first layer reads the learned query as a row of stride 0 for every tile
+  const bool fq_fused = c.pool_mode == IVC_POOL_FOLDED && h->wkT != nullptr &&
+                        fold_query_fused_supported(C, c.pool_heads);
+  if (!fq_fused) LAUNCH("pool_query", s, launch_broadcast_rows(dt, h->query, w.q, T, C, s));
   const int splits = pool_splits(T, N);
   const float scale = 1.0f / sqrtf((float)(C / H));
   int fG = 0, fQ = 0, fseg = 0;
   if (folded) folded_geometry(T, N, C, h->ncu, &fG, &fQ, &fseg);
-  // query projection and key fold in one launch where the shape allows it
-  const bool fq_fused = folded && h->wkT != nullptr && fold_query_fused_supported(C, H);
   for (int l = 0; l < L; ++l) {
     const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * C * h->esz;
     const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * C * h->esz;
@@ -873,9 +884,9 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     const float qscale = scale * 1.4426950408889634f;
     if (fq_fused) {
       LAUNCH("pool_query_fold", s,
-             launch_fold_query_fused(w.q, h->wq[l], h->bq[l],
-                                     (const char*)h->wkT + (size_t)l * C * C * h->esz, w.qt_hi,
-                                     w.qt_lo, T, C, H, qscale, s));
+             launch_fold_query_fused(l == 0 ? h->query_f : w.q, l == 0 ? 0 : C, h->wq[l],
+                                     h->bq[l], (const char*)h->wkT + (size_t)l * C * C * h->esz,
+                                     w.qt_hi, w.qt_lo, T, C, H, qscale, s));
       if (l == 0 && H < 16)
         LAUNCH("pool_fold_pad", s, launch_zero_heads(w.qt_hi, w.qt_lo, T, H, C, s));
     } else {
@@ -970,24 +981,54 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
   const float* pooled_v = pooled ? pooled : w.q;
 
   // Gating: x = pooled; 4 x (x += LN(W2 GELU(W1 x + b1) + b2)); softmax(Wc x + bc)
-  HIP_OK(hipMemcpyAsync(w.x, pooled_v, (size_t)T * hh * 4, hipMemcpyDeviceToDevice, s));
-  for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
-    LAUNCH("gate_fc1", s, gemm("gate_fc1",
-                              mk_gemm(w.x, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1, DT_F32,
-                                      T, he, hh, ACT_GELU), s, &w.sc));
-    LAUNCH("gate_fc2", s, gemm("gate_fc2",
-                              mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2, DT_F32,
-                                      T, hh, he, ACT_NONE), s, &w.sc));
-    if (b + 1 < IVC_GATE_BLOCKS)
-      LAUNCH("gate_res_ln", s,
-             launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));
-    else  // the last block's residual LayerNorm and the classifier head in one launch
-      LAUNCH("gate_res_ln_head", s,
-             launch_residual_ln_head(dt, w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps,
-                                     h->g_cw, h->g_cb, gate, s));
+  static_assert(IVC_GATE_BLOCKS >= 2, "the gating chain below alternates two row buffers");
+  if (dt == IVC_BF16 && f32a_ln_rows_supported(hh)) {
+    // block b > 0 takes block b-1's residual LayerNorm into its first Linear's
+    // prologue (rows alternate between two buffers; block 0 reads the pooled
+    // rows in place); the last block's LayerNorm runs with the classifier head
+    const float* xb = pooled_v;
+    for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
+      if (b == 0) {
+        LAUNCH("gate_fc1", s, gemm("gate_fc1",
+                                  mk_gemm(xb, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1,
+                                          DT_F32, T, he, hh, ACT_GELU), s, &w.sc));
+      } else {
+        float* xn = (b & 1) ? w.x : w.x2;
+        LAUNCH("gate_ln_fc1", s,
+               launch_f32a_ln_rows(xb, w.y2, h->g_lw[b - 1], h->g_lb[b - 1], c.ln_eps, xn,
+                                   h->g_w1[b], h->g_b1[b], w.y1, T, he, hh, ACT_GELU, s));
+        xb = xn;
+      }
+      LAUNCH("gate_fc2", s, gemm("gate_fc2",
+                                mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2,
+                                        DT_F32, T, hh, he, ACT_NONE), s, &w.sc));
+    }
+    const int b = IVC_GATE_BLOCKS - 1;
+    LAUNCH("gate_res_ln_head", s,
+           launch_residual_ln_head(dt, const_cast<float*>(xb), w.y2, h->g_lw[b], h->g_lb[b], T,
+                                   hh, c.ln_eps, h->g_cw, h->g_cb, gate, s));
+  } else {
+    HIP_OK(hipMemcpyAsync(w.x, pooled_v, (size_t)T * hh * 4, hipMemcpyDeviceToDevice, s));
+    for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
+      LAUNCH("gate_fc1", s, gemm("gate_fc1",
+                                mk_gemm(w.x, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1,
+                                        DT_F32, T, he, hh, ACT_GELU), s, &w.sc));
+      LAUNCH("gate_fc2", s, gemm("gate_fc2",
+                                mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2,
+                                        DT_F32, T, hh, he, ACT_NONE), s, &w.sc));
+      if (b + 1 < IVC_GATE_BLOCKS)
+        LAUNCH("gate_res_ln", s,
+               launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));
+      else  // the last block's residual LayerNorm and the classifier head in one launch
+        LAUNCH("gate_res_ln_head", s,
+               launch_residual_ln_head(dt, w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps,
+                                       h->g_cw, h->g_cb, gate, s));
+    }
   }
   LAUNCH("quantile_decide", s,
-         launch_quantile_decide(gate, T, c.rel_quantile, c.abs_threshold, threshold, use64, s));
+         launch_quantile_decide(gate, T, c.rel_quantile, c.abs_threshold, threshold, use64, s,
+                                lists ? lists->rank : nullptr, lists ? lists->list256 : nullptr,
+                                lists ? lists->list64 : nullptr, lists ? lists->counts : nullptr));
   return IVC_OK;
 }
 
@@ -1025,10 +1066,16 @@ extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
     if (!aligned16(ws)) return fail(IVC_ERR_MISALIGNED, "ws alignment");
     tokst = (float*)((char*)ws + tokst_offset(h, T));
   }
+  // the decision kernel also leaves the per-path tile lists where the run half
+  // reads them (the run layout may overlap the route scratch, which the
+  // decision kernel, the route's last, no longer reads)
+  RunWs rl{};
+  const bool lists = T > 0 && ws != nullptr && ws_bytes >= plan_run(h, T, nullptr, nullptr);
+  if (lists) plan_run(h, T, ws, &rl);
   ivc_status st = route_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status,
-                             ws, ws_bytes, stream, tokst);
+                             ws, ws_bytes, stream, tokst, lists ? &rl : nullptr);
   if (st != IVC_OK) return st;
-  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream, tokst != nullptr);
+  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream, tokst != nullptr, lists);
 }
 
 // ---------------------------------------------------------------------------

@@ -351,7 +351,7 @@ hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float sc
 // wave-private LDS slab so each row leaves with 16-byte stores.
 template <int D>
 __global__ void __launch_bounds__(512)
-k_fold_query_fused(const float* __restrict__ q, const bf16_t* __restrict__ Wq,
+k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __restrict__ Wq,
                    const float* __restrict__ bq, const bf16_t* __restrict__ WkT,
                    bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
                    float scale) {
@@ -384,7 +384,7 @@ k_fold_query_fused(const float* __restrict__ q, const bf16_t* __restrict__ Wq,
   // ---- qp block [16, D] of head h
   {
     ARow<1> arow[1];
-    arow[0].p[0] = q + (long long)min(m0 + lo16, T - 1) * C + 8 * hi4;
+    arow[0].p[0] = q + (long long)min(m0 + lo16, T - 1) * ldq + 8 * hi4;
     const bf16_t* wrow[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -456,24 +456,113 @@ k_fold_query_fused(const float* __restrict__ q, const bf16_t* __restrict__ Wq,
   }
 }
 
+// A Gating block's first Linear with the previous block's residual LayerNorm
+// in its prologue:
+//   x_out = x_in + LN(y) * gamma + beta        (rows of K values)
+//   C = act(x_out . W^T + bias)                 (the f32a product, 16 x 64 tiles)
+// Workgroup (16 rows, 64 columns): its 16 rows of x_out go to LDS (each wave
+// two rows: mean, then the mean square deviation, from registers, both
+// wave-reduced), the workgroups of the first column block also write them to
+// x_out (x_in and x_out must differ: the others still read x_in), and the
+// product reads its activation rows from LDS.
+template <int ACT>
+__global__ void __launch_bounds__(512)
+k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
+               const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
+               float* __restrict__ x_out, const bf16_t* __restrict__ W,
+               const float* __restrict__ bias, float* __restrict__ Cm, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) float xs[16 * 1024];  // [16][K], K <= 1024
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
+  const int vpl = K / 256;  // float4 vectors per lane (K % 256 == 0, K <= 1024)
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = 2 * w + rr;
+    const int t = min(m0 + r, M - 1);
+    const float4* yr = reinterpret_cast<const float4*>(y + (long long)t * K);
+    float4 v[4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < vpl) {
+        v[i] = yr[lane + 64 * i];
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+      }
+    }
+    const float mean = wave_sum(s) / (float)K;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < vpl) {
+        const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+        q += (a * a + b * b) + (c * c + d * d);
+      }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)K + eps);
+    const float4* xr = reinterpret_cast<const float4*>(x_in + (long long)t * K);
+    const float4* g4 = reinterpret_cast<const float4*>(gamma);
+    const float4* b4 = reinterpret_cast<const float4*>(beta);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < vpl) {
+        const int j = lane + 64 * i;
+        const float4 x = xr[j], g = g4[j], b = b4[j];
+        float4 o;
+        o.x = x.x + (v[i].x - mean) * rstd * g.x + b.x;
+        o.y = x.y + (v[i].y - mean) * rstd * g.y + b.y;
+        o.z = x.z + (v[i].z - mean) * rstd * g.z + b.z;
+        o.w = x.w + (v[i].w - mean) * rstd * g.w + b.w;
+        reinterpret_cast<float4*>(xs + r * K)[j] = o;
+        if (blockIdx.x == 0 && m0 + r < M) reinterpret_cast<float4*>(x_out + (long long)t * K)[j] = o;
+      }
+    }
+  }
+  __syncthreads();
+  ARow<1> arow[1];
+  arow[0].p[0] = xs + lo16 * K + 8 * hi4;
+  f32a_tile<1, 4, 8, 4, ACT, 0, 1>(arow, W, K, bias, Cm, nullptr, N, M, N, K, 1.f, m0, n0);
+}
+
+bool f32a_ln_rows_supported(int K) { return K % 256 == 0 && K >= 256 && K <= 1024; }
+
+hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* gamma,
+                               const float* beta, float eps, float* x_out, const void* W,
+                               const float* bias, float* Cm, int M, int N, int K, int act,
+                               hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (!f32a_ln_rows_supported(K) || x_in == x_out || N <= 0 || (uintptr_t)x_in % 16 ||
+      (uintptr_t)y % 16 || (uintptr_t)x_out % 16 || (uintptr_t)gamma % 16 ||
+      (uintptr_t)beta % 16 || (uintptr_t)W % 16 || (act != ACT_GELU && act != ACT_NONE))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16));
+  if (act == ACT_GELU)
+    hipLaunchKernelGGL(k_f32a_ln_rows<ACT_GELU>, grid, dim3(512), 0, s, x_in, y, gamma, beta, eps,
+                       x_out, (const bf16_t*)W, bias, Cm, M, N, K);
+  else
+    hipLaunchKernelGGL(k_f32a_ln_rows<ACT_NONE>, grid, dim3(512), 0, s, x_in, y, gamma, beta, eps,
+                       x_out, (const bf16_t*)W, bias, Cm, M, N, K);
+  return hipGetLastError();
+}
+
 bool fold_query_fused_supported(int C, int H) {
   if (H < 1 || H > 16 || C % H != 0) return false;
   const int d = C / H;
   return (d == 32 || d == 64 || d == 128) && C % 128 == 0 && C <= 1024;
 }
 
-hipError_t launch_fold_query_fused(const float* q, const void* Wq, const float* bq,
+hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, const float* bq,
                                    const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
                                    float scale, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (!fold_query_fused_supported(C, H) || !q || !Wq || !bq || !WkT || !qt_hi || !qt_lo ||
       (uintptr_t)q % 16 || (uintptr_t)Wq % 16 || (uintptr_t)WkT % 16 || (uintptr_t)qt_hi % 16 ||
-      (uintptr_t)qt_lo % 16)
+      (uintptr_t)qt_lo % 16 || ldq < 0 || ldq % 4)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((T + 15) / 16), (unsigned)H);
   const int d = C / H;
 #define IVC_FQF(DV)                                                                                \
-  hipLaunchKernelGGL(k_fold_query_fused<DV>, grid, dim3(512), 0, s, q, (const bf16_t*)Wq, bq,      \
+  hipLaunchKernelGGL(k_fold_query_fused<DV>, grid, dim3(512), 0, s, q, ldq, (const bf16_t*)Wq, bq, \
                      (const bf16_t*)WkT, (bf16_t*)qt_hi, (bf16_t*)qt_lo, T, C, scale)
   if (d == 32) IVC_FQF(32);
   else if (d == 64) IVC_FQF(64);

@@ -75,53 +75,13 @@ IVC_DEV uint32_t radix_select(const float* gate, int T, int k, uint32_t* hist, u
   return prefix;
 }
 
-__global__ void __launch_bounds__(QT)
-k_quantile_decide(const float* __restrict__ gate, int T, double q, double abs_thr,
-                  double* __restrict__ thr_out, uint8_t* __restrict__ use64) {
-  // Every product and sum below is rounded on its own: HIP's __dmul_rn and
-  // friends are plain operators that the compiler may fuse into an FMA, which
-  // moves the threshold by an ulp, so plain operators with contraction off.
-#pragma clang fp contract(off)
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[4];
-  __shared__ uint32_t wtot[4];
-
-  const double pos = q * (double)(T - 1);
-  const double fl = floor(pos);
-  const int lo = (int)fl;
-  const int hi = (int)ceil(pos);
-  const double frac = pos - fl;
-
-  const uint32_t klo = radix_select(gate, T, lo, hist, sh, wtot);
-  // the next order statistic: equal to v[lo] if enough keys tie with it,
-  // otherwise the smallest key above it
-  if (threadIdx.x == 0) {
-    sh[2] = 0;
-    sh[3] = 0xffffffffu;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < T; i += QT) {
-    const uint32_t key = order_key(gate[2 * i]);
-    if (key <= klo) atomicAdd(&sh[2], 1u);
-    else atomicMin(&sh[3], key);
-  }
-  __syncthreads();
-  const uint32_t khi = ((uint32_t)hi < sh[2]) ? klo : sh[3];
-
-  const double a = (double)key_value(klo), b = (double)key_value(khi);
-  const double diff = b - a;
-  const double thr = frac < 0.5 ? a + diff * frac : b - diff * (1.0 - frac);
-  if (threadIdx.x == 0) *thr_out = thr;
-  for (int i = threadIdx.x; i < T; i += QT) {
-    const double g = (double)gate[2 * i];
-    use64[i] = (g > thr && g >= abs_thr) ? 1 : 0;
-  }
-}
-
-// Per-path tile lists of a decision (one workgroup, chunked scan over tiles).
-__global__ void __launch_bounds__(1024)
-k_route_lists(const uint8_t* __restrict__ use64, int T, int* __restrict__ rank,
-              int* __restrict__ list256, int* __restrict__ list64, int* __restrict__ counts) {
+// Per-path tile lists of a decision (one workgroup of QT threads, chunked
+// scan over tiles): rank[t] = t's index in its own path, list256 / list64 the
+// tiles of each path in order, counts = (n256, n64).  u(t) gives tile t's
+// decision (0 or 1).
+template <typename U>
+IVC_DEV void route_lists_block(int T, U u_of, int* __restrict__ rank, int* __restrict__ list256,
+                               int* __restrict__ list64, int* __restrict__ counts) {
   __shared__ int wsum[16];
   __shared__ int carry_s;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -129,7 +89,7 @@ k_route_lists(const uint8_t* __restrict__ use64, int T, int* __restrict__ rank,
   __syncthreads();
   for (int c0 = 0; c0 < T; c0 += QT) {
     const int t = c0 + threadIdx.x;
-    const int u = t < T ? (use64[t] != 0) : 0;
+    const int u = t < T ? u_of(t) : 0;
     int inc = u;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -164,6 +124,60 @@ k_route_lists(const uint8_t* __restrict__ use64, int T, int* __restrict__ rank,
   }
 }
 
+__global__ void __launch_bounds__(1024)
+k_route_lists(const uint8_t* __restrict__ use64, int T, int* __restrict__ rank,
+              int* __restrict__ list256, int* __restrict__ list64, int* __restrict__ counts) {
+  route_lists_block(T, [&](int t) { return use64[t] != 0 ? 1 : 0; }, rank, list256, list64,
+                    counts);
+}
+
+// lists: also the per-path tile lists of the decision (rank != nullptr)
+__global__ void __launch_bounds__(QT)
+k_quantile_decide(const float* __restrict__ gate, int T, double q, double abs_thr,
+                  double* __restrict__ thr_out, uint8_t* __restrict__ use64, int* __restrict__ rank,
+                  int* __restrict__ list256, int* __restrict__ list64, int* __restrict__ counts) {
+  // Every product and sum below is rounded on its own: HIP's __dmul_rn and
+  // friends are plain operators that the compiler may fuse into an FMA, which
+  // moves the threshold by an ulp, so plain operators with contraction off.
+#pragma clang fp contract(off)
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[4];
+  __shared__ uint32_t wtot[4];
+
+  const double pos = q * (double)(T - 1);
+  const double fl = floor(pos);
+  const int lo = (int)fl;
+  const int hi = (int)ceil(pos);
+  const double frac = pos - fl;
+
+  const uint32_t klo = radix_select(gate, T, lo, hist, sh, wtot);
+  // the next order statistic: equal to v[lo] if enough keys tie with it,
+  // otherwise the smallest key above it
+  if (threadIdx.x == 0) {
+    sh[2] = 0;
+    sh[3] = 0xffffffffu;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T; i += QT) {
+    const uint32_t key = order_key(gate[2 * i]);
+    if (key <= klo) atomicAdd(&sh[2], 1u);
+    else atomicMin(&sh[3], key);
+  }
+  __syncthreads();
+  const uint32_t khi = ((uint32_t)hi < sh[2]) ? klo : sh[3];
+
+  const double a = (double)key_value(klo), b = (double)key_value(khi);
+  const double diff = b - a;
+  const double thr = frac < 0.5 ? a + diff * frac : b - diff * (1.0 - frac);
+  if (threadIdx.x == 0) *thr_out = thr;
+  auto decide = [&](int i) {
+    const double g = (double)gate[2 * i];
+    return (g > thr && g >= abs_thr) ? 1 : 0;
+  };
+  for (int i = threadIdx.x; i < T; i += QT) use64[i] = (uint8_t)decide(i);
+  if (rank != nullptr) route_lists_block(T, decide, rank, list256, list64, counts);
+}
+
 hipError_t launch_route_lists(const uint8_t* use64, int T, int* rank, int* list256, int* list64,
                               int* counts, hipStream_t s) {
   hipLaunchKernelGGL(k_route_lists, dim3(1), dim3(QT), 0, s, use64, T, rank, list256, list64,
@@ -172,9 +186,12 @@ hipError_t launch_route_lists(const uint8_t* use64, int T, int* rank, int* list2
 }
 
 hipError_t launch_quantile_decide(const float* gate, int T, double q, double abs_thr,
-                                  double* thr, uint8_t* use64, hipStream_t s) {
+                                  double* thr, uint8_t* use64, hipStream_t s, int* rank,
+                                  int* list256, int* list64, int* counts) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quantile_decide, dim3(1), dim3(QT), 0, s, gate, T, q, abs_thr, thr, use64);
+  if (rank != nullptr && (!list256 || !list64 || !counts)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quantile_decide, dim3(1), dim3(QT), 0, s, gate, T, q, abs_thr, thr, use64,
+                     rank, list256, list64, counts);
   return hipGetLastError();
 }
 

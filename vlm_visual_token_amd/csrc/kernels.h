@@ -159,8 +159,12 @@ hipError_t launch_broadcast_rows(int dtype, const void* v, float* out, int T, in
                                  hipStream_t s);
 
 // ---- quantile + decision -----------------------------------------------------
+// rank != nullptr: also the per-path tile lists of the decision, as
+// launch_route_lists writes them (one launch less in forward)
 hipError_t launch_quantile_decide(const float* gate, int T, double q, double abs_thr,
-                                  double* thr, uint8_t* use64, hipStream_t s);
+                                  double* thr, uint8_t* use64, hipStream_t s,
+                                  int* rank = nullptr, int* list256 = nullptr,
+                                  int* list64 = nullptr, int* counts = nullptr);
 
 // ---- compaction ----------------------------------------------------------------
 struct CompactArgs {
@@ -244,10 +248,20 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
 // qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
 hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt_hi, void* qt_lo,
                              int T, int C, int H, float scale, hipStream_t s);
+// C = act(x_out W^T + bias) with x_out = x_in + LN(y) * gamma + beta written
+// too (a Gating block's first Linear with the previous block's residual
+// LayerNorm in its prologue); fp32 rows of K (a multiple of 256, <= 1024),
+// bf16 W [N, K]; x_in and x_out distinct.
+bool f32a_ln_rows_supported(int K);
+hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* gamma,
+                               const float* beta, float eps, float* x_out, const void* W,
+                               const float* bias, float* Cm, int M, int N, int K, int act,
+                               hipStream_t s);
 // qp = Wq q + bq, then q~_h = scale * Wk_h^T qp_h for every head, in one launch
-// (the same values as a query projection followed by the key fold).
+// (the same values as a query projection followed by the key fold).  q: rows
+// of stride ldq (0: one row shared by every tile).
 bool fold_query_fused_supported(int C, int H);
-hipError_t launch_fold_query_fused(const float* q, const void* Wq, const float* bq,
+hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, const float* bq,
                                    const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
                                    float scale, hipStream_t s);
 // qt_hi / qt_lo [T, 16, C]: heads H .. 15 set to zero
