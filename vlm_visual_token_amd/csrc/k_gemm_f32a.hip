@@ -477,44 +477,60 @@ k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
   const int lo16 = lane & 15, hi4 = lane >> 4;
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
   const int vpl = K / 256;  // float4 vectors per lane (K % 256 == 0, K <= 1024)
+  // both rows' y, x, gamma and beta loaded up front (one round of latency)
+  float4 v[2][4], xv[2][4], gv[4], bv[4];
+  int tr[2];
+#pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
-    const int r = 2 * w + rr;
-    const int t = min(m0 + r, M - 1);
-    const float4* yr = reinterpret_cast<const float4*>(y + (long long)t * K);
-    float4 v[4];
-    float s = 0.f;
+    tr[rr] = min(m0 + 2 * w + rr, M - 1);
+    const float4* yr = reinterpret_cast<const float4*>(y + (long long)tr[rr] * K);
+    const float4* xr = reinterpret_cast<const float4*>(x_in + (long long)tr[rr] * K);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i < vpl) {
-        v[i] = yr[lane + 64 * i];
-        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        v[rr][i] = yr[lane + 64 * i];
+        xv[rr][i] = xr[lane + 64 * i];
       }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < vpl) {
+      gv[i] = reinterpret_cast<const float4*>(gamma)[lane + 64 * i];
+      bv[i] = reinterpret_cast<const float4*>(beta)[lane + 64 * i];
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int r = 2 * w + rr;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < vpl) s += (v[rr][i].x + v[rr][i].y) + (v[rr][i].z + v[rr][i].w);
     const float mean = wave_sum(s) / (float)K;
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i < vpl) {
-        const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+        const float a = v[rr][i].x - mean, b = v[rr][i].y - mean, c = v[rr][i].z - mean,
+                    d = v[rr][i].w - mean;
         q += (a * a + b * b) + (c * c + d * d);
       }
     }
     const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)K + eps);
-    const float4* xr = reinterpret_cast<const float4*>(x_in + (long long)t * K);
-    const float4* g4 = reinterpret_cast<const float4*>(gamma);
-    const float4* b4 = reinterpret_cast<const float4*>(beta);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i < vpl) {
         const int j = lane + 64 * i;
-        const float4 x = xr[j], g = g4[j], b = b4[j];
+        const float4 x = xv[rr][i], g = gv[i], b = bv[i];
         float4 o;
-        o.x = x.x + (v[i].x - mean) * rstd * g.x + b.x;
-        o.y = x.y + (v[i].y - mean) * rstd * g.y + b.y;
-        o.z = x.z + (v[i].z - mean) * rstd * g.z + b.z;
-        o.w = x.w + (v[i].w - mean) * rstd * g.w + b.w;
+        o.x = x.x + (v[rr][i].x - mean) * rstd * g.x + b.x;
+        o.y = x.y + (v[rr][i].y - mean) * rstd * g.y + b.y;
+        o.z = x.z + (v[rr][i].z - mean) * rstd * g.z + b.z;
+        o.w = x.w + (v[rr][i].w - mean) * rstd * g.w + b.w;
         reinterpret_cast<float4*>(xs + r * K)[j] = o;
-        if (blockIdx.x == 0 && m0 + r < M) reinterpret_cast<float4*>(x_out + (long long)t * K)[j] = o;
+        if (blockIdx.x == 0 && m0 + r < M)
+          reinterpret_cast<float4*>(x_out + (long long)tr[rr] * K)[j] = o;
       }
     }
   }
