@@ -359,10 +359,11 @@ def test_folded_pool_flash_workload():
 
 
 # Batch sizes that split a tile's tokens over many token-pass workgroups (T = 3:
-# 64 per tile, the value fold then reads a merged xbar) or over up to four
-# (T = 100: the value fold merges the partials in its operand load), with a
-# padding mask on the second.
-@pytest.mark.parametrize("T,padded", [(3, False), (100, True)])
+# 64 per tile, T = 13: up to 17, the value fold then reads a merged xbar) or
+# over up to four (T = 100: the value fold merges the partials in its operand
+# load), with padding masks (odd layers walk each workgroup's range backwards,
+# skipping the padded chunks from the other end).
+@pytest.mark.parametrize("T,padded", [(3, False), (13, True), (100, True)])
 def test_folded_pool_batch_sizes(T, padded):
     cfg = workload("internvl35_2b_flash", pool_mode=1)
     cfg["tiles"], cfg["T"] = [T], T

@@ -932,6 +932,9 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       fa.segmax = fseg;
       fa.part = w.part;
       fa.tokst = l == 0 ? tokst : nullptr;
+      // odd layers walk their ranges backwards: they start on the tokens the
+      // previous layer read last, which the 256 MB memory-side cache still holds
+      fa.reverse = l & 1;
       // o_h = Wv_h xbar_h + bv_h for every head: one batched product over heads,
       // with bf16 weights reading the token pass's partials directly (the merge
       // of a tile's partials happens in its operand load)

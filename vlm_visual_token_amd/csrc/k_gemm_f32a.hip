@@ -264,8 +264,10 @@ k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ vali
     L = fmaf(ls[i], e, L);
   }
   arow[0].inv = 1.0f / L;
-  f32a_tile<1, 4, 8, 2, ACT_NONE, 0, MAXS>(arow, Wv + (long long)h * d * C, C, bv + h * d,
-                                           o + h * d, nullptr, C, T, d, C, 1.f, m0, n0);
+  // all K steps of a wave in one round of loads while the registers allow it
+  constexpr int PD = MAXS <= 3 ? 4 : 2;
+  f32a_tile<1, 4, 8, PD, ACT_NONE, 0, MAXS>(arow, Wv + (long long)h * d * C, C, bv + h * d,
+                                            o + h * d, nullptr, C, T, d, C, 1.f, m0, n0);
 }
 
 int fold_value_merged_max_parts(int T, int N, int Q) {

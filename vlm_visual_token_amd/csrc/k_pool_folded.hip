@@ -84,15 +84,31 @@ IVC_DEV int clamp_valid(const int* valid, int t, int N) {
   return nv < 1 ? 1 : (nv > N ? N : nv);
 }
 
-// Walks the non-empty chunks of a workgroup's range [.., c_end) in order:
-// tile t, chunk j (tokens 16j .. 16j+15), nv valid tokens of tile t.
+// Walks the non-empty chunks of a workgroup's range [c_lo, c_end) in order,
+// or (rev) from the last one down: tile t, chunk j (tokens 16j .. 16j+15),
+// nv valid tokens of tile t.
 struct ChunkIter {
-  int t, j, nv, nce;
+  int t, j, nv, nce, rev, c_lo;
   IVC_DEV void enter(const int* valid, int N) {
     nv = clamp_valid(valid, t, N);
     nce = (nv + 15) / 16;
   }
+  IVC_DEV void rstart(int c_beg, int NC, int c_end, const int* valid, int N) {
+    rev = 1;
+    c_lo = c_beg;
+    if (c_end <= c_beg) {
+      t = -1;
+      j = 0;
+      return;
+    }
+    t = (c_end - 1) / NC;
+    j = c_end - 1 - t * NC;
+    enter(valid, N);
+    if (j >= nce) j = nce - 1;  // done() below if the range holds none of tile t's valid chunks
+  }
   IVC_DEV void start(int c, int NC, int c_end, const int* valid, int N) {
+    rev = 0;
+    c_lo = c;
     t = c / NC;
     j = c - t * NC;
     if (c < c_end) {
@@ -106,9 +122,18 @@ struct ChunkIter {
     if (t * NC < c_end) enter(valid, N);  // chunk 0 of a tile is never empty
   }
   IVC_DEV void next(int NC, int c_end, const int* valid, int N) {
+    if (rev) {
+      if (--j < 0 && --t >= 0) {
+        enter(valid, N);
+        j = nce - 1;
+      }
+      return;
+    }
     if (++j >= nce) next_tile(NC, c_end, valid, N);
   }
-  IVC_DEV bool done(int NC, int c_end) const { return t * NC + j >= c_end; }
+  IVC_DEV bool done(int NC, int c_end) const {
+    return rev ? t < 0 || t * NC + j < c_lo : t * NC + j >= c_end;
+  }
 };
 
 // reductions over the four lanes l, l^16, l^32, l^48 (v_permlane{16,32}_swap)
@@ -227,7 +252,7 @@ __global__ void __launch_bounds__(512, 2 * PF<C>::WG_PER_CU)
 k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __restrict__ valid,
               int T, int N, const bf16_t* __restrict__ qt_hi, const bf16_t* __restrict__ qt_lo,
               int Q, int segmax, float* __restrict__ part, int* __restrict__ status,
-              float2* __restrict__ tokst) {
+              float2* __restrict__ tokst, int rev) {
   using P = PF<C>;
   constexpr int NW = P::NW, KS = P::KS, NT = P::NT, RB = P::RB, SB = P::SB, DPW = P::DPW;
   constexpr int LDP = P::LDP;
@@ -308,7 +333,8 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
 
   // ---- prologue: the first ST-1 chunks into stages 0..ST-2
   ChunkIter pi, ci;
-  pi.start(c_beg, NC, c_end, valid, N);
+  if (rev) pi.rstart(c_beg, NC, c_end, valid, N);
+  else pi.start(c_beg, NC, c_end, valid, N);
   ci = pi;
   int issued = 0, consumed = 0;
   if (!pi.done(NC, c_end)) { dma(pi, st0); pi.next(NC, c_end, valid, N); ++issued; }
@@ -542,7 +568,8 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s) {
 #define IVC_PF(CV, ST)                                                                             \
   hipLaunchKernelGGL((k_pool_folded<CV, ST>), grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,   \
                      a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,                         \
-                     (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status, (float2*)a.tokst)
+                     (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status, (float2*)a.tokst, \
+                     a.reverse)
   if (a.C == 1024) {
     if (a.tokst) IVC_PF(1024, true);
     else IVC_PF(1024, false);

@@ -232,6 +232,8 @@ struct FoldedArgs {
   float* xbar;        // [T, H, C] softmax-weighted token means; nullptr: no merge launch
   float* tokst;       // optional [T, N] float2: each token's LayerNorm moments (mean, M2);
                       // needs valid == nullptr
+  int reverse;        // 1: each workgroup walks its chunk range from the end (alternating
+                      // directions between layers reuses what the memory-side cache kept)
 };
 // Work split of the token pass: G workgroups of Q consecutive 16-token chunks
 // each (chunk index = tile * ceil(N/16) + chunk); a workgroup leaves at most
