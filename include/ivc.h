@@ -224,8 +224,13 @@ ivc_status ivc_connector_route(ivc_connector* h, const void* vit, const int32_t*
 
 /* ivc_connector_route followed by ivc_connector_run_routed in one call
  * ([4B-Flash] sections 2-5; [2B-Flash] dual pipeline), with the same outputs
- * and one workspace of ivc_connector_workspace_bytes.  Requires flash = 1;
- * out256 and out64 are both required. */
+ * (bit for bit) and one workspace of ivc_connector_workspace_bytes.  Requires
+ * flash = 1; out256 and out64 are both required.  With ln_fold, folded
+ * pooling and no valid_tokens, the first pooling pass also takes the
+ * LayerNorm statistics the projectors need (the same arithmetic as run's own
+ * statistics pass, which is then skipped), and the decision kernel also
+ * writes the per-path tile lists, so the call reads the ViT tensor one time
+ * less than route + run_routed. */
 ivc_status ivc_connector_forward(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
                                  int32_t T, float* gate, double* threshold, uint8_t* use64,
                                  float* pooled, int32_t* dev_status, void* out256, void* out64,
