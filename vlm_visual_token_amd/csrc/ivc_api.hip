@@ -149,6 +149,10 @@ struct ivc_connector {
   // router
   void* query;
   float* query_f;  // the learned query widened to fp32 (read by every tile's first layer)
+  // folded pooling: the first layer's folded query, the same for every tile
+  // (the learned query projected and folded once at create), [16, C] bf16 hi / lo
+  void* qt0_hi;
+  void* qt0_lo;
   void *wq[IVC_MAX_POOL_LAYERS], *wo[IVC_MAX_POOL_LAYERS];
   float *bq[IVC_MAX_POOL_LAYERS], *bo[IVC_MAX_POOL_LAYERS];
   void* wkv;   // [2 * layers * C, C]: Wk_0; Wv_0; Wk_1; Wv_1; ...
@@ -527,6 +531,8 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       h->wkv = cv.take(2 * Lp * C * C * e);
       h->bkv = (float*)cv.take(2 * Lp * C * 4);
       h->wkT = dt == IVC_BF16 ? cv.take(Lp * C * C * e) : nullptr;
+      h->qt0_hi = dt == IVC_BF16 ? cv.take(16 * C * 2) : nullptr;
+      h->qt0_lo = dt == IVC_BF16 ? cv.take(16 * C * 2) : nullptr;
       for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
         h->g_w1[b] = cv.take(he * hh * e);
         h->g_b1[b] = (float*)cv.take(he * 4);
@@ -606,6 +612,21 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
     }
     STEP(copy_mat(w->gate_cls_w, h->g_cw, 2 * hh * e, s));
     STEP(widen(w->gate_cls_b, dt, h->g_cb, 2, s));
+    if (h->qt0_hi != nullptr && c.pool_mode == IVC_POOL_FOLDED &&
+        fold_query_fused_supported((int)C, c.pool_heads)) {
+      // the first layer's folded query: the same arithmetic as the per-tile
+      // launch of a route call, for one tile (every tile's would be equal)
+      const int H = c.pool_heads;
+      const float qscale = (1.0f / sqrtf((float)((int)C / H))) * 1.4426950408889634f;
+      STEP(launch_fold_query_fused(h->query_f, 0, h->wq[0], h->bq[0], h->wkT, h->qt0_hi,
+                                   h->qt0_lo, 1, (int)C, H, qscale, s) == hipSuccess
+               ? IVC_OK
+               : fail(IVC_ERR_HIP, "query fold launch failed"));
+      if (H < 16)
+        STEP(launch_zero_heads(h->qt0_hi, h->qt0_lo, 1, H, (int)C, s) == hipSuccess
+                 ? IVC_OK
+                 : fail(IVC_ERR_HIP, "query fold launch failed"));
+    }
   }
 #undef STEP
   if (hipStreamSynchronize(s) != hipSuccess) {
@@ -882,12 +903,15 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     // q~_h = Wk_h^T q_h * log2(e) / sqrt(d) (scores in log2 units), per head
     // a product [T, d] x [d, C] with the transposed key weights
     const float qscale = scale * 1.4426950408889634f;
+    // the first layer's folded query is the same for every tile: made once at create
+    const bool qt_shared = fq_fused && l == 0 && h->qt0_hi != nullptr;
     if (fq_fused) {
-      LAUNCH("pool_query_fold", s,
-             launch_fold_query_fused(l == 0 ? h->query_f : w.q, l == 0 ? 0 : C, h->wq[l],
-                                     h->bq[l], (const char*)h->wkT + (size_t)l * C * C * h->esz,
-                                     w.qt_hi, w.qt_lo, T, C, H, qscale, s));
-      if (l == 0 && H < 16)
+      if (!qt_shared)
+        LAUNCH("pool_query_fold", s,
+               launch_fold_query_fused(w.q, C, h->wq[l], h->bq[l],
+                                       (const char*)h->wkT + (size_t)l * C * C * h->esz, w.qt_hi,
+                                       w.qt_lo, T, C, H, qscale, s));
+      if (l == 0 && H < 16)  // heads H .. 15 of the per-tile buffers, read by the later layers
         LAUNCH("pool_fold_pad", s, launch_zero_heads(w.qt_hi, w.qt_lo, T, H, C, s));
     } else {
       LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
@@ -925,8 +949,9 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       fa.N = N;
       fa.C = C;
       fa.H = H;
-      fa.qt_hi = w.qt_hi;
-      fa.qt_lo = w.qt_lo;
+      fa.qt_hi = qt_shared ? h->qt0_hi : w.qt_hi;
+      fa.qt_lo = qt_shared ? h->qt0_lo : w.qt_lo;
+      fa.qt_shared = qt_shared;
       fa.G = fG;
       fa.Q = fQ;
       fa.segmax = fseg;

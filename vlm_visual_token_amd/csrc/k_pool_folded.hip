@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(512, 2 * PF<C>::WG_PER_CU)
 k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __restrict__ valid,
               int T, int N, const bf16_t* __restrict__ qt_hi, const bf16_t* __restrict__ qt_lo,
               int Q, int segmax, float* __restrict__ part, int* __restrict__ status,
-              float2* __restrict__ tokst, int rev) {
+              float2* __restrict__ tokst, int rev, int qt_shared) {
   using P = PF<C>;
   constexpr int NW = P::NW, KS = P::KS, NT = P::NT, RB = P::RB, SB = P::SB, DPW = P::DPW;
   constexpr int LDP = P::LDP;
@@ -356,7 +356,8 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
     if (ci.t != cur_t) {
       if (cur_t >= 0) flush(cur_t);
       cur_t = ci.t;
-      const size_t qrow = ((size_t)ci.t * FH + lo16) * C + cw0 + 8 * hi4;
+      // q~ rows of this tile (or the one block every tile shares)
+      const size_t qrow = (qt_shared ? 0 : (size_t)ci.t * FH * C) + (size_t)lo16 * C + cw0 + 8 * hi4;
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
         qh[k] = *reinterpret_cast<const bf16x8_t*>(qt_hi + qrow + 32 * k);
@@ -569,7 +570,7 @@ hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_pool_folded<CV, ST>), grid, dim3(512), 0, s, (const bf16_t*)a.X, a.rows,   \
                      a.has_cls, a.valid, a.T, a.N, (const bf16_t*)a.qt_hi,                         \
                      (const bf16_t*)a.qt_lo, a.Q, a.segmax, a.part, a.status, (float2*)a.tokst, \
-                     a.reverse)
+                     a.reverse, a.qt_shared)
   if (a.C == 1024) {
     if (a.tokst) IVC_PF(1024, true);
     else IVC_PF(1024, false);

@@ -227,6 +227,7 @@ struct FoldedArgs {
   int T, N, C, H;
   const void* qt_hi;  // [T, 16, C] bf16: folded queries (log2(e)/sqrt(d) applied), high part
   const void* qt_lo;  // low part
+  int qt_shared;      // 1: qt_hi / qt_lo are one [16, C] block shared by every tile
   int G, Q, segmax;   // from folded_geometry
   float* part;        // [G * segmax, 16 * (2 + C)]
   float* xbar;        // [T, H, C] softmax-weighted token means; nullptr: no merge launch
