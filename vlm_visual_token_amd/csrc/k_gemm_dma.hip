@@ -88,18 +88,19 @@ IVC_DEV long long gather_row0(const AGather& g, int m) {
   return (long long)t * g.rows + g.has_cls + (long long)(g.r * a) * g.P + g.r * b;
 }
 
-// Gathered A: byte offset of K step kt (BK wide) relative to cell 0's row.
-IVC_DEV long long gather_koff(const AGather& g, int kt, int BK) {
-  const int k0 = kt * BK;
-  const int q = k0 / g.C, c0 = k0 - q * g.C;
+// Gathered A: byte offset of channels [c0, c0 + BK) of cell q relative to
+// cell 0's row (r is 2 or 4, so the cell's grid offset is shifts and masks;
+// the main loop steps (q, c0) along K without dividing).
+IVC_DEV long long gather_koff(const AGather& g, int q, int c0) {
   int dm, dk;  // grid offset of cell q inside the block
   if (g.twice) {  // r = 4 as two r = 2 shuffles: q = 4*(2*m2 + k2) + (2*m + k)
     const int w = q >> 2, qq = q & 3;
     dm = 2 * (w >> 1) + (qq >> 1);
     dk = 2 * (w & 1) + (qq & 1);
   } else {
-    dm = q / g.r;
-    dk = q - dm * g.r;
+    const int sh = g.r == 4 ? 2 : 1;
+    dm = q >> sh;
+    dk = q & (g.r - 1);
   }
   return ((long long)(dm * g.P + dk) * g.C + c0) * 2;
 }
@@ -297,7 +298,8 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 
   const int KT = K / BK;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma_one(q, FOLD ? gather_koff(ag, 0, BK) : 0, 0, sA0, sB0);
+  for (int q = 0; q < 8; ++q) dma_one(q, FOLD ? gather_koff(ag, 0, 0) : 0, 0, sA0, sB0);
+  int cell_n = 0, c0_n = 0;  // (cell, channel) of the next K step (FOLD)
   for (int kt = 0; kt < KT; ++kt) {
     const bool odd = kt & 1;
     const char* sa = odd ? sA1 : sA0;
@@ -306,7 +308,14 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
     char* nb = odd ? sB0 : sB1;
     const bool more = kt + 1 < KT;
     const long long kb = (long long)(kt + 1) * (BK * 2);
-    const long long ka = FOLD ? gather_koff(ag, kt + 1, BK) : kb;
+    if (FOLD) {
+      c0_n += BK;
+      if (c0_n == ag.C) {
+        c0_n = 0;
+        ++cell_n;
+      }
+    }
+    const long long ka = FOLD ? gather_koff(ag, cell_n, c0_n) : kb;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     bf16x8_t fa_[2][4], fb_[2][2];  // [buffer][block]
