@@ -239,7 +239,10 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
             int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
             const float* __restrict__ ln_colsum) {
   constexpr int BK = 64;
-  using aoff_t = typename std::conditional<FOLD, int32_t, uint32_t>::type;
+  // A offsets relative to the tile's first row are never negative (the tile's
+  // rows come in increasing ViT row order, gathered or not), so they stay
+  // unsigned 32-bit and the DMA takes a scalar base plus a 32-bit offset
+  using aoff_t = uint32_t;
   __shared__ __attribute__((aligned(1024))) char sA0[QB];
   __shared__ __attribute__((aligned(1024))) char sB0[QB];
   __shared__ __attribute__((aligned(1024))) char sA1[QB];
