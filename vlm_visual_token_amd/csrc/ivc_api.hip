@@ -153,6 +153,14 @@ struct ivc_connector {
   // (the learned query projected and folded once at create), [16, C] bf16 hi / lo
   void* qt0_hi;
   void* qt0_lo;
+  // folded pooling, layers l >= 1: the previous layer's output projection
+  // folded into this layer's query projection, Wqo = Wq_l Wo_{l-1} (fp32, as
+  // bf16 hi / lo parts) and bqo = Wq_l bo_{l-1} + bq_l; no per-tile q is formed
+  // between layers.  (cr_*: scratch of the products made at create.)
+  void *wqo_hi[IVC_MAX_POOL_LAYERS], *wqo_lo[IVC_MAX_POOL_LAYERS];
+  float* bqo[IVC_MAX_POOL_LAYERS];
+  void* cr_woT;
+  float* cr_wqo;
   void *wq[IVC_MAX_POOL_LAYERS], *wo[IVC_MAX_POOL_LAYERS];
   float *bq[IVC_MAX_POOL_LAYERS], *bo[IVC_MAX_POOL_LAYERS];
   void* wkv;   // [2 * layers * C, C]: Wk_0; Wv_0; Wk_1; Wv_1; ...
@@ -533,6 +541,15 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       h->wkT = dt == IVC_BF16 ? cv.take(Lp * C * C * e) : nullptr;
       h->qt0_hi = dt == IVC_BF16 ? cv.take(16 * C * 2) : nullptr;
       h->qt0_lo = dt == IVC_BF16 ? cv.take(16 * C * 2) : nullptr;
+      const bool qo = dt == IVC_BF16 && c.pool_mode == IVC_POOL_FOLDED &&
+                      fold_query_fused_supported((int)C, c.pool_heads) && Lp > 1;
+      for (size_t l = 0; l < Lp; ++l) {
+        h->wqo_hi[l] = qo && l > 0 ? cv.take(C * C * 2) : nullptr;
+        h->wqo_lo[l] = qo && l > 0 ? cv.take(C * C * 2) : nullptr;
+        h->bqo[l] = qo && l > 0 ? (float*)cv.take(C * 4) : nullptr;
+      }
+      h->cr_woT = qo ? cv.take(C * C * 2) : nullptr;
+      h->cr_wqo = qo ? (float*)cv.take(C * C * 4) : nullptr;
       for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
         h->g_w1[b] = cv.take(he * hh * e);
         h->g_b1[b] = (float*)cv.take(he * 4);
@@ -626,6 +643,22 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
         STEP(launch_zero_heads(h->qt0_hi, h->qt0_lo, 1, H, (int)C, s) == hipSuccess
                  ? IVC_OK
                  : fail(IVC_ERR_HIP, "query fold launch failed"));
+    }
+    for (size_t l = 1; l < Lp; ++l) {
+      if (h->wqo_hi[l] == nullptr) continue;
+      // Wqo = Wq_l Wo_{l-1}: A = Wq_l, W rows = columns of Wo_{l-1}; fp32 FMA
+      GemmArgs g = mk_gemm(h->wq[l], (long long)C, DT_BF16, h->cr_woT, DT_BF16, nullptr,
+                           h->cr_wqo, DT_F32, (int)C, (int)C, (int)C, ACT_NONE);
+      // bqo = Wq_l bo_{l-1} + bq_l
+      GemmArgs gb = mk_gemm(h->bo[l - 1], (long long)C, DT_F32, h->wq[l], DT_BF16, h->bq[l],
+                            h->bqo[l], DT_F32, 1, (int)C, (int)C, ACT_NONE);
+      const bool ok =
+          launch_transpose_bf16(h->wo[l - 1], h->cr_woT, (int)C, (int)C, s) == hipSuccess &&
+          launch_gemm_simt(g, s) == hipSuccess &&
+          launch_split_bf16(h->cr_wqo, h->wqo_hi[l], h->wqo_lo[l], (long long)C * C, s) ==
+              hipSuccess &&
+          launch_gemm_simt(gb, s) == hipSuccess;
+      STEP(ok ? IVC_OK : fail(IVC_ERR_HIP, "query-output fold launch failed"));
     }
   }
 #undef STEP
@@ -906,11 +939,17 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     // the first layer's folded query is the same for every tile: made once at create
     const bool qt_shared = fq_fused && l == 0 && h->qt0_hi != nullptr;
     if (fq_fused) {
-      if (!qt_shared)
+      if (!qt_shared) {
+        // l >= 1: from the previous layer's value-fold output o through the
+        // folded output + query projections (or through q when not folded)
+        const bool qo = h->wqo_hi[l] != nullptr;
         LAUNCH("pool_query_fold", s,
-               launch_fold_query_fused(w.q, C, h->wq[l], h->bq[l],
+               launch_fold_query_fused(qo ? w.o : w.q, C, qo ? h->wqo_hi[l] : h->wq[l],
+                                       qo ? h->bqo[l] : h->bq[l],
                                        (const char*)h->wkT + (size_t)l * C * C * h->esz, w.qt_hi,
-                                       w.qt_lo, T, C, H, qscale, s));
+                                       w.qt_lo, T, C, H, qscale, s,
+                                       qo ? h->wqo_lo[l] : nullptr));
+      }
       if (l == 0 && H < 16)  // heads H .. 15 of the per-tile buffers, read by the later layers
         LAUNCH("pool_fold_pad", s, launch_zero_heads(w.qt_hi, w.qt_lo, T, H, C, s));
     } else {
@@ -1001,10 +1040,14 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       pa.O = w.o;
       LAUNCH("pool_attn", s, launch_pool_attn(pa, s));
     }
-    float* qn = (l == L - 1 && pooled) ? pooled : w.q;
-    LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
-                                 mk_gemm(w.o, C, DT_F32, h->wo[l], dt, h->bo[l], qn, DT_F32, T,
-                                         C, C, ACT_NONE), s, &w.sc));
+    // the output projection, unless the next layer's query fold reads o itself
+    // through the folded weights (only the last layer's q, the pooled vector, is formed)
+    if (!(fq_fused && l + 1 < L && h->wqo_hi[l + 1] != nullptr)) {
+      float* qn = (l == L - 1 && pooled) ? pooled : w.q;
+      LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
+                                   mk_gemm(w.o, C, DT_F32, h->wo[l], dt, h->bo[l], qn, DT_F32, T,
+                                           C, C, ACT_NONE), s, &w.sc));
+    }
   }
   const float* pooled_v = pooled ? pooled : w.q;
 

@@ -89,17 +89,20 @@ struct ARow {
 
 // Main loop of one wave: MB x NB blocks of 16 x 16, K steps w, w + NWV, ...
 // (each 32 wide), up to PD of them loaded at once.  arow / wrow: this lane's
-// operand rows, already offset by 8 * (lane / 16) elements.
-template <int MB, int NB, int NWV, int PD, int NS>
-IVC_DEV void f32a_mainloop(const ARow<NS> (&arow)[MB], const bf16_t* const (&wrow)[NB], int w,
-                           int nks, f32x4_t (&acc)[MB][NB]) {
+// operand rows, already offset by 8 * (lane / 16) elements.  WS: the weights
+// are fp32 values held as bf16 high (wrow) + low (wlo) parts, and each step
+// adds a_hi.w_hi, a_lo.w_hi, a_hi.w_lo (a_lo.w_lo is below 2^-16 of them).
+template <int MB, int NB, int NWV, int PD, int NS, bool WS = false>
+IVC_DEV void f32a_mainloop(const ARow<NS> (&arow)[MB], const bf16_t* const (&wrow)[NB],
+                           const bf16_t* const (&wlo)[NB], int w, int nks,
+                           f32x4_t (&acc)[MB][NB]) {
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = w; s0 < nks; s0 += NWV * PD) {
     typename ARow<NS>::Raw xa[PD][MB];
-    u32x4 xw[PD][NB];
+    u32x4 xw[PD][NB], xl[WS ? PD : 1][NB];
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
       const int k0 = 32 * min(s0 + NWV * i, nks - 1);
@@ -107,6 +110,11 @@ IVC_DEV void f32a_mainloop(const ARow<NS> (&arow)[MB], const bf16_t* const (&wro
       for (int mb = 0; mb < MB; ++mb) arow[mb].load(k0, xa[i][mb]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) xw[i][nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + k0);
+      if (WS) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          xl[WS ? i : 0][nb] = *reinterpret_cast<const u32x4*>(wlo[nb] + k0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // all loads of the group go out first
     // no branch between the loads and their use (it would let the compiler
@@ -131,6 +139,10 @@ IVC_DEV void f32a_mainloop(const ARow<NS> (&arow)[MB], const bf16_t* const (&wro
           const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, xw[i][nb]);
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mb], bw, acc[mb][nb], 0, 0, 0);
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mb], bw, acc[mb][nb], 0, 0, 0);
+          if (WS) {
+            const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, xl[WS ? i : 0][nb]);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mb], bl, acc[mb][nb], 0, 0, 0);
+          }
         }
     }
   }
@@ -158,7 +170,7 @@ IVC_DEV void f32a_tile(const ARow<NS> (&arow)[MB], const bf16_t* __restrict__ W,
     wrow[nb] = W + (long long)min(n0 + 16 * nb + lo16, N - 1) * ldw + 8 * hi4;
 
   f32x4_t acc[MB][NB];
-  f32a_mainloop<MB, NB, NWV, PD, NS>(arow, wrow, w, K / 32, acc);
+  f32a_mainloop<MB, NB, NWV, PD, NS>(arow, wrow, wrow, w, K / 32, acc);
 
   // partial tiles -> LDS; output layout: lane holds column 16nb + lo16, rows 16mb + 4hi4 + v
 #pragma unroll
@@ -351,10 +363,12 @@ hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float sc
 // summed through LDS, then the 16 x C block of q~_h with K = D = C / H,
 // wave w taking columns [w C/8, (w+1) C/8); the bf16 halves go through a
 // wave-private LDS slab so each row leaves with 16-byte stores.
-template <int D>
+// WS: Wq given as bf16 high (Wq) + low (Wq_lo) parts of fp32 weights.
+template <int D, bool WS>
 __global__ void __launch_bounds__(512)
 k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __restrict__ Wq,
-                   const float* __restrict__ bq, const bf16_t* __restrict__ WkT,
+                   const bf16_t* __restrict__ Wq_lo, const float* __restrict__ bq,
+                   const bf16_t* __restrict__ WkT,
                    bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
                    float scale) {
   constexpr int NB = D / 16, LDR = D + 4, KS = D / 32;
@@ -388,11 +402,15 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
     ARow<1> arow[1];
     arow[0].p[0] = q + (long long)min(m0 + lo16, T - 1) * ldq + 8 * hi4;
     const bf16_t* wrow[NB];
+    const bf16_t* wlo[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
       wrow[nb] = Wq + (long long)(h * D + 16 * nb + lo16) * C + 8 * hi4;
+      wlo[nb] = WS ? Wq_lo + (long long)(h * D + 16 * nb + lo16) * C + 8 * hi4 : wrow[nb];
+    }
     f32x4_t acc[1][NB];
-    f32a_mainloop<1, NB, 8, 4, 1>(arow, wrow, w, C / 32, acc);
+    // (split weights at d = 128 load half as many K steps at once, to stay in registers)
+    f32a_mainloop<1, NB, 8, (WS && D >= 128) ? 2 : 4, 1, WS>(arow, wrow, wlo, w, C / 32, acc);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -571,21 +589,45 @@ bool fold_query_fused_supported(int C, int H) {
 
 hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, const float* bq,
                                    const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
-                                   float scale, hipStream_t s) {
+                                   float scale, hipStream_t s, const void* Wq_lo) {
   if (T <= 0) return hipSuccess;
   if (!fold_query_fused_supported(C, H) || !q || !Wq || !bq || !WkT || !qt_hi || !qt_lo ||
       (uintptr_t)q % 16 || (uintptr_t)Wq % 16 || (uintptr_t)WkT % 16 || (uintptr_t)qt_hi % 16 ||
-      (uintptr_t)qt_lo % 16 || ldq < 0 || ldq % 4)
+      (uintptr_t)qt_lo % 16 || ldq < 0 || ldq % 4 || (uintptr_t)Wq_lo % 16)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((T + 15) / 16), (unsigned)H);
   const int d = C / H;
-#define IVC_FQF(DV)                                                                                \
-  hipLaunchKernelGGL(k_fold_query_fused<DV>, grid, dim3(512), 0, s, q, ldq, (const bf16_t*)Wq, bq, \
-                     (const bf16_t*)WkT, (bf16_t*)qt_hi, (bf16_t*)qt_lo, T, C, scale)
-  if (d == 32) IVC_FQF(32);
-  else if (d == 64) IVC_FQF(64);
-  else IVC_FQF(128);
+#define IVC_FQF(DV, WSV)                                                                           \
+  hipLaunchKernelGGL((k_fold_query_fused<DV, WSV>), grid, dim3(512), 0, s, q, ldq,                 \
+                     (const bf16_t*)Wq, (const bf16_t*)Wq_lo, bq, (const bf16_t*)WkT,             \
+                     (bf16_t*)qt_hi, (bf16_t*)qt_lo, T, C, scale)
+  if (Wq_lo != nullptr) {
+    if (d == 32) IVC_FQF(32, true);
+    else if (d == 64) IVC_FQF(64, true);
+    else IVC_FQF(128, true);
+  } else {
+    if (d == 32) IVC_FQF(32, false);
+    else if (d == 64) IVC_FQF(64, false);
+    else IVC_FQF(128, false);
+  }
 #undef IVC_FQF
+  return hipGetLastError();
+}
+
+// fp32 values as bf16 high and low parts: hi = bf16(x), lo = bf16(x - hi)
+__global__ void k_split_bf16(const float* __restrict__ x, bf16_t* __restrict__ hi,
+                             bf16_t* __restrict__ lo, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    const bf16_t h = f32_to_bf16(x[i]);
+    hi[i] = h;
+    lo[i] = f32_to_bf16(x[i] - bf16_to_f32(h));
+  }
+}
+
+hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_split_bf16, dim3(256), dim3(256), 0, s, x, (bf16_t*)hi, (bf16_t*)lo, n);
   return hipGetLastError();
 }
 

@@ -264,9 +264,12 @@ hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* g
 // (the same values as a query projection followed by the key fold).  q: rows
 // of stride ldq (0: one row shared by every tile).
 bool fold_query_fused_supported(int C, int H);
+// Wq_lo: if set, Wq and Wq_lo are the bf16 high and low parts of fp32 weights.
 hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, const float* bq,
                                    const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
-                                   float scale, hipStream_t s);
+                                   float scale, hipStream_t s, const void* Wq_lo = nullptr);
+// hi = bf16(x), lo = bf16(x - hi) for n fp32 values
+hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long long n, hipStream_t s);
 // qt_hi / qt_lo [T, 16, C]: heads H .. 15 set to zero
 hipError_t launch_zero_heads(void* qt_hi, void* qt_lo, int T, int H, int C, hipStream_t s);
 // The value fold reading the token pass's partials directly (no merge launch):
