@@ -312,6 +312,20 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
   // l_run holds this lane's share (its 4 tokens per chunk) of head lo16's sum.
   int cur_t = -1;
   bf16x8_t qh[KS], ql[KS];
+  // q~ of the next tile, loaded just before the DMA of its first chunk, so the
+  // wait for that chunk covers it and a tile change does not drain the ring
+  // (one tile ahead; a short tile whose prefetch is overwritten loads its own)
+  bf16x8_t qn_h[KS], qn_l[KS];
+  int pf_t = -1;
+  auto prefetch_q = [&](int t) {
+    const size_t qrow = (qt_shared ? 0 : (size_t)t * FH * C) + (size_t)lo16 * C + cw0 + 8 * hi4;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      qn_h[k] = *reinterpret_cast<const bf16x8_t*>(qt_hi + qrow + 32 * k);
+      qn_l[k] = *reinterpret_cast<const bf16x8_t*>(qt_lo + qrow + 32 * k);
+    }
+    pf_t = t;
+  };
   f32x4_t acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -337,9 +351,15 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
   else pi.start(c_beg, NC, c_end, valid, N);
   ci = pi;
   int issued = 0, consumed = 0;
-  if (!pi.done(NC, c_end)) { dma(pi, st0); pi.next(NC, c_end, valid, N); ++issued; }
-  if (!pi.done(NC, c_end)) { dma(pi, st1); pi.next(NC, c_end, valid, N); ++issued; }
-  if (!pi.done(NC, c_end)) { dma(pi, st2); pi.next(NC, c_end, valid, N); ++issued; }
+  auto dma_next = [&](char* stage) {
+    if (pf_t < 0 || (!qt_shared && pi.t != pf_t)) prefetch_q(pi.t);
+    dma(pi, stage);
+    pi.next(NC, c_end, valid, N);
+    ++issued;
+  };
+  if (!pi.done(NC, c_end)) dma_next(st0);
+  if (!pi.done(NC, c_end)) dma_next(st1);
+  if (!pi.done(NC, c_end)) dma_next(st2);
 
   auto step = [&](const char* stage, char* next_stage) {
     // this chunk's DMA is done once at most (issued - consumed - 1) chunks remain in flight
@@ -356,15 +376,23 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
     if (ci.t != cur_t) {
       if (cur_t >= 0) flush(cur_t);
       cur_t = ci.t;
-      // q~ rows of this tile (or the one block every tile shares)
-      const size_t qrow = (qt_shared ? 0 : (size_t)ci.t * FH * C) + (size_t)lo16 * C + cw0 + 8 * hi4;
+      if (qt_shared || pf_t == ci.t) {
+        // prefetched before this chunk's DMA, which the wait above covered
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        qh[k] = *reinterpret_cast<const bf16x8_t*>(qt_hi + qrow + 32 * k);
-        ql[k] = *reinterpret_cast<const bf16x8_t*>(qt_lo + qrow + 32 * k);
+        for (int k = 0; k < KS; ++k) {
+          qh[k] = qn_h[k];
+          ql[k] = qn_l[k];
+        }
+      } else {
+        // q~ rows of this tile, loaded now
+        const size_t qrow = (size_t)ci.t * FH * C + (size_t)lo16 * C + cw0 + 8 * hi4;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          qh[k] = *reinterpret_cast<const bf16x8_t*>(qt_hi + qrow + 32 * k);
+          ql[k] = *reinterpret_cast<const bf16x8_t*>(qt_lo + qrow + 32 * k);
+        }
+        IVC_WAIT_VM(0);
       }
-      // q~ is used at once; waiting here keeps the wait off the common path
-      IVC_WAIT_VM(0);
       m_run = -INFINITY;
       l_run = 0.f;
     }
@@ -402,7 +430,7 @@ k_pool_folded(const bf16_t* __restrict__ X, int rows, int has_cls, const int* __
     for (int ww = 1; ww < NW; ++ww) s4 += *reinterpret_cast<const f32x4_t*>(&sP[ww][lo16][4 * hi4]);
     // the next DMA goes out after this step's LDS reads: the compiler makes an
     // LDS read that follows an LDS DMA wait for it
-    if (!pi.done(NC, c_end)) { dma(pi, next_stage); pi.next(NC, c_end, valid, N); ++issued; }
+    if (!pi.done(NC, c_end)) dma_next(next_stage);
     const int n0 = 16 * ci.j;
     float cmax = -INFINITY;
 #pragma unroll
