@@ -167,6 +167,13 @@ struct ivc_connector {
   float* bkv;  // [2 * layers * C]
   void* wkT;   // bf16 only: [layers][C, C], wkT[l][c][j] = Wk_l[j][c] (query fold)
   void *g_w1[IVC_GATE_BLOCKS], *g_w2[IVC_GATE_BLOCKS], *g_cw;
+  // Row strides (elements) of the router matrices above: wq, wo, wkv, wkT and
+  // wqo rows (C wide) at lr, gate W1 rows (gate_hidden wide) at lg1, gate W2
+  // rows at lg2.  With bf16 weights each row is padded by 16 bytes: the
+  // router products read 16 rows of one K step per load instruction, and at a
+  // power-of-two stride those reads collide (measured: 16-byte padding makes
+  // a 208 x 1024 x 1024 product ~25% faster; 128 bytes of padding does not).
+  long long lr, lg1, lg2;
   float *g_b1[IVC_GATE_BLOCKS], *g_b2[IVC_GATE_BLOCKS], *g_lw[IVC_GATE_BLOCKS],
       *g_lb[IVC_GATE_BLOCKS], *g_cb;
 };
@@ -209,6 +216,13 @@ ivc_status widen(const void* src, int dtype, float* dst, long long n, hipStream_
 
 ivc_status copy_mat(const void* src, void* dst, size_t bytes, hipStream_t s) {
   HIP_OK(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
+  return IVC_OK;
+}
+
+// dense [rows, cols] matrix of e-byte elements into rows of stride ld
+ivc_status copy_rows(const void* src, void* dst, size_t rows, size_t cols, size_t ld, size_t e,
+                     hipStream_t s) {
+  HIP_OK(hipMemcpy2DAsync(dst, ld * e, src, cols * e, cols * e, rows, hipMemcpyDeviceToDevice, s));
   return IVC_OK;
 }
 
@@ -491,6 +505,9 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
   ivc_connector* h = new ivc_connector();
   h->cfg = c;
   h->esz = (int)e;
+  h->lr = (long long)C + (dt == IVC_BF16 ? 8 : 0);
+  h->lg1 = (long long)hh + (dt == IVC_BF16 ? 8 : 0);
+  h->lg2 = (long long)he + (dt == IVC_BF16 ? 8 : 0);
   {
     // the token pass of folded pooling splits its work over the compute units
     int dev = 0, n = 0;
@@ -531,29 +548,29 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       h->query = cv.take(C * e);
       h->query_f = (float*)cv.take(C * 4);
       for (size_t l = 0; l < Lp; ++l) {
-        h->wq[l] = cv.take(C * C * e);
+        h->wq[l] = cv.take(C * h->lr * e);
         h->bq[l] = (float*)cv.take(C * 4);
-        h->wo[l] = cv.take(C * C * e);
+        h->wo[l] = cv.take(C * h->lr * e);
         h->bo[l] = (float*)cv.take(C * 4);
       }
-      h->wkv = cv.take(2 * Lp * C * C * e);
+      h->wkv = cv.take(2 * Lp * C * h->lr * e);
       h->bkv = (float*)cv.take(2 * Lp * C * 4);
-      h->wkT = dt == IVC_BF16 ? cv.take(Lp * C * C * e) : nullptr;
+      h->wkT = dt == IVC_BF16 ? cv.take(Lp * C * h->lr * e) : nullptr;
       h->qt0_hi = dt == IVC_BF16 ? cv.take(16 * C * 2) : nullptr;
       h->qt0_lo = dt == IVC_BF16 ? cv.take(16 * C * 2) : nullptr;
       const bool qo = dt == IVC_BF16 && c.pool_mode == IVC_POOL_FOLDED &&
                       fold_query_fused_supported((int)C, c.pool_heads) && Lp > 1;
       for (size_t l = 0; l < Lp; ++l) {
-        h->wqo_hi[l] = qo && l > 0 ? cv.take(C * C * 2) : nullptr;
-        h->wqo_lo[l] = qo && l > 0 ? cv.take(C * C * 2) : nullptr;
+        h->wqo_hi[l] = qo && l > 0 ? cv.take(C * h->lr * 2) : nullptr;
+        h->wqo_lo[l] = qo && l > 0 ? cv.take(C * h->lr * 2) : nullptr;
         h->bqo[l] = qo && l > 0 ? (float*)cv.take(C * 4) : nullptr;
       }
       h->cr_woT = qo ? cv.take(C * C * 2) : nullptr;
       h->cr_wqo = qo ? (float*)cv.take(C * C * 4) : nullptr;
       for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
-        h->g_w1[b] = cv.take(he * hh * e);
+        h->g_w1[b] = cv.take(he * h->lg1 * e);
         h->g_b1[b] = (float*)cv.take(he * 4);
-        h->g_w2[b] = cv.take(hh * he * e);
+        h->g_w2[b] = cv.take(hh * h->lg2 * e);
         h->g_b2[b] = (float*)cv.take(hh * 4);
         h->g_lw[b] = (float*)cv.take(hh * 4);
         h->g_lb[b] = (float*)cv.take(hh * 4);
@@ -605,14 +622,16 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
     STEP(copy_mat(w->pool_query, h->query, C * e, s));
     STEP(widen(w->pool_query, dt, h->query_f, C, s));
     for (size_t l = 0; l < Lp; ++l) {
-      STEP(copy_mat(w->pool_wq[l], h->wq[l], C * C * e, s));
+      STEP(copy_rows(w->pool_wq[l], h->wq[l], C, C, h->lr, e, s));
       STEP(widen(w->pool_bq[l], dt, h->bq[l], C, s));
-      STEP(copy_mat(w->pool_wo[l], h->wo[l], C * C * e, s));
+      STEP(copy_rows(w->pool_wo[l], h->wo[l], C, C, h->lr, e, s));
       STEP(widen(w->pool_bo[l], dt, h->bo[l], C, s));
-      STEP(copy_mat(w->pool_wk[l], (char*)h->wkv + (2 * l) * C * C * e, C * C * e, s));
-      STEP(copy_mat(w->pool_wv[l], (char*)h->wkv + (2 * l + 1) * C * C * e, C * C * e, s));
+      STEP(copy_rows(w->pool_wk[l], (char*)h->wkv + (2 * l) * C * h->lr * e, C, C, h->lr, e, s));
+      STEP(copy_rows(w->pool_wv[l], (char*)h->wkv + (2 * l + 1) * C * h->lr * e, C, C, h->lr, e,
+                     s));
       if (h->wkT != nullptr)
-        STEP(launch_transpose_bf16(w->pool_wk[l], (char*)h->wkT + l * C * C * e, (int)C, (int)C, s)
+        STEP(launch_transpose_bf16(w->pool_wk[l], (long long)C, (char*)h->wkT + l * C * h->lr * e,
+                                   h->lr, (int)C, (int)C, s)
                      == hipSuccess
                  ? IVC_OK
                  : fail(IVC_ERR_HIP, "weight transpose launch failed"));
@@ -620,9 +639,9 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       STEP(widen(w->pool_bv[l], dt, h->bkv + (2 * l + 1) * C, C, s));
     }
     for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
-      STEP(copy_mat(w->gate_w1[b], h->g_w1[b], he * hh * e, s));
+      STEP(copy_rows(w->gate_w1[b], h->g_w1[b], he, hh, h->lg1, e, s));
       STEP(widen(w->gate_b1[b], dt, h->g_b1[b], he, s));
-      STEP(copy_mat(w->gate_w2[b], h->g_w2[b], hh * he * e, s));
+      STEP(copy_rows(w->gate_w2[b], h->g_w2[b], hh, he, h->lg2, e, s));
       STEP(widen(w->gate_b2[b], dt, h->g_b2[b], hh, s));
       STEP(widen(w->gate_ln_w[b], dt, h->g_lw[b], hh, s));
       STEP(widen(w->gate_ln_b[b], dt, h->g_lb[b], hh, s));
@@ -635,8 +654,8 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
       // launch of a route call, for one tile (every tile's would be equal)
       const int H = c.pool_heads;
       const float qscale = (1.0f / sqrtf((float)((int)C / H))) * 1.4426950408889634f;
-      STEP(launch_fold_query_fused(h->query_f, 0, h->wq[0], h->bq[0], h->wkT, h->qt0_hi,
-                                   h->qt0_lo, 1, (int)C, H, qscale, s) == hipSuccess
+      STEP(launch_fold_query_fused(h->query_f, 0, h->wq[0], h->lr, h->bq[0], h->wkT, h->lr,
+                                   h->qt0_hi, h->qt0_lo, 1, (int)C, H, qscale, s) == hipSuccess
                ? IVC_OK
                : fail(IVC_ERR_HIP, "query fold launch failed"));
       if (H < 16)
@@ -647,16 +666,18 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
     for (size_t l = 1; l < Lp; ++l) {
       if (h->wqo_hi[l] == nullptr) continue;
       // Wqo = Wq_l Wo_{l-1}: A = Wq_l, W rows = columns of Wo_{l-1}; fp32 FMA
-      GemmArgs g = mk_gemm(h->wq[l], (long long)C, DT_BF16, h->cr_woT, DT_BF16, nullptr,
-                           h->cr_wqo, DT_F32, (int)C, (int)C, (int)C, ACT_NONE);
+      GemmArgs g = mk_gemm(h->wq[l], h->lr, DT_BF16, h->cr_woT, DT_BF16, nullptr, h->cr_wqo,
+                           DT_F32, (int)C, (int)C, (int)C, ACT_NONE);
       // bqo = Wq_l bo_{l-1} + bq_l
       GemmArgs gb = mk_gemm(h->bo[l - 1], (long long)C, DT_F32, h->wq[l], DT_BF16, h->bq[l],
                             h->bqo[l], DT_F32, 1, (int)C, (int)C, ACT_NONE);
+      gb.ldw = h->lr;
       const bool ok =
-          launch_transpose_bf16(h->wo[l - 1], h->cr_woT, (int)C, (int)C, s) == hipSuccess &&
-          launch_gemm_simt(g, s) == hipSuccess &&
-          launch_split_bf16(h->cr_wqo, h->wqo_hi[l], h->wqo_lo[l], (long long)C * C, s) ==
+          launch_transpose_bf16(h->wo[l - 1], h->lr, h->cr_woT, (long long)C, (int)C, (int)C, s) ==
               hipSuccess &&
+          launch_gemm_simt(g, s) == hipSuccess &&
+          launch_split_bf16(h->cr_wqo, h->wqo_hi[l], h->wqo_lo[l], (long long)C, (int)C, h->lr,
+                            s) == hipSuccess &&
           launch_gemm_simt(gb, s) == hipSuccess;
       STEP(ok ? IVC_OK : fail(IVC_ERR_HIP, "query-output fold launch failed"));
     }
@@ -911,9 +932,18 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
   const int hh = c.gate_hidden, he = hh * c.gate_expansion;
 
   const bool folded = c.pool_mode == IVC_POOL_FOLDED;
+  // router product with fp32 activations and one of the connector's router
+  // matrices (rows at stride ldw)
+  auto rgemm = [&](const float* A, long long lda, const void* W, long long ldw, const float* bias,
+                   float* Cout, int M, int Nn, int K, int act) {
+    GemmArgs g = mk_gemm(A, lda, DT_F32, W, dt, bias, Cout, DT_F32, M, Nn, K, act);
+    g.ldw = ldw;
+    return g;
+  };
   if (!folded) {
     // K and V of every layer from the raw tokens (CLS skipped by the row remap)
     GemmArgs kv = mk_gemm(vit, C, dt, h->wkv, dt, h->bkv, w.kv, dt, T * N, 2 * L * C, C, ACT_NONE);
+    kv.ldw = h->lr;
     kv.a_rpg = N;
     kv.a_gstride = rows;
     kv.a_goff = c.has_cls;
@@ -930,8 +960,8 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
   int fG = 0, fQ = 0, fseg = 0;
   if (folded) folded_geometry(T, N, C, h->ncu, &fG, &fQ, &fseg);
   for (int l = 0; l < L; ++l) {
-    const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * C * h->esz;
-    const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * C * h->esz;
+    const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * h->lr * h->esz;
+    const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * h->lr * h->esz;
     const float* bv = h->bkv + (size_t)(2 * l + 1) * C;
     // q~_h = Wk_h^T q_h * log2(e) / sqrt(d) (scores in log2 units), per head
     // a product [T, d] x [d, C] with the transposed key weights
@@ -944,27 +974,28 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
         // folded output + query projections (or through q when not folded)
         const bool qo = h->wqo_hi[l] != nullptr;
         LAUNCH("pool_query_fold", s,
-               launch_fold_query_fused(qo ? w.o : w.q, C, qo ? h->wqo_hi[l] : h->wq[l],
+               launch_fold_query_fused(qo ? w.o : w.q, C, qo ? h->wqo_hi[l] : h->wq[l], h->lr,
                                        qo ? h->bqo[l] : h->bq[l],
-                                       (const char*)h->wkT + (size_t)l * C * C * h->esz, w.qt_hi,
-                                       w.qt_lo, T, C, H, qscale, s,
+                                       (const char*)h->wkT + (size_t)l * C * h->lr * h->esz,
+                                       h->lr, w.qt_hi, w.qt_lo, T, C, H, qscale, s,
                                        qo ? h->wqo_lo[l] : nullptr));
       }
       if (l == 0 && H < 16)  // heads H .. 15 of the per-tile buffers, read by the later layers
         LAUNCH("pool_fold_pad", s, launch_zero_heads(w.qt_hi, w.qt_lo, T, H, C, s));
     } else {
       LAUNCH("pool_q_proj", s, gemm("pool_q_proj",
-                                   mk_gemm(w.q, C, DT_F32, h->wq[l], dt, h->bq[l], w.qp, DT_F32,
-                                           T, C, C, ACT_NONE), s, &w.sc));
+                                   rgemm(w.q, C, h->wq[l], h->lr, h->bq[l], w.qp, T, C, C,
+                                         ACT_NONE), s, &w.sc));
     }
     if (folded) {
       if (fq_fused) {
         // q~ already written by the fused launch
       } else if (h->wkT != nullptr) {
         const int d = C / H;
-        GemmArgs fq = mk_gemm(w.qp, C, DT_F32, (const char*)h->wkT + (size_t)l * C * C * h->esz,
-                              DT_BF16, nullptr, w.qt_hi, DT_BF16, T, C, d, ACT_NONE);
-        fq.ldw = C;
+        const void* wkT_l = (const char*)h->wkT + (size_t)l * C * h->lr * h->esz;
+        GemmArgs fq = mk_gemm(w.qp, C, DT_F32, wkT_l, DT_BF16, nullptr, w.qt_hi, DT_BF16, T, C, d,
+                              ACT_NONE);
+        fq.ldw = h->lr;
         fq.ldc = 16ll * C;
         fq.batch = H;
         fq.a_bs = d;
@@ -1007,16 +1038,17 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       LAUNCH("pool_folded", s, launch_pool_folded(fa, s));
       if (merged_value) {
         LAUNCH("pool_fold_value", s,
-               launch_fold_value_merged(w.part, valid_tokens, N, fQ, fseg, wv, bv, w.o, T, C, H,
-                                        s));
+               launch_fold_value_merged(w.part, valid_tokens, N, fQ, fseg, wv, h->lr, bv, w.o, T,
+                                        C, H, s));
       } else {
         const int d = C / H;
         GemmArgs fv = mk_gemm(w.xbar, (long long)H * C, DT_F32, wv, dt, bv, w.o, DT_F32, T, d, C,
                               ACT_NONE);
         fv.ldc = C;
+        fv.ldw = h->lr;
         fv.batch = H;
         fv.a_bs = C;
-        fv.w_bs = (long long)d * C;
+        fv.w_bs = (long long)d * h->lr;
         fv.c_bs = d;
         fv.bias_bs = d;
         LAUNCH("pool_fold_value", s, gemm("pool_fold_value", fv, s, &w.sc));
@@ -1045,8 +1077,8 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     if (!(fq_fused && l + 1 < L && h->wqo_hi[l + 1] != nullptr)) {
       float* qn = (l == L - 1 && pooled) ? pooled : w.q;
       LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
-                                   mk_gemm(w.o, C, DT_F32, h->wo[l], dt, h->bo[l], qn, DT_F32, T,
-                                           C, C, ACT_NONE), s, &w.sc));
+                                   rgemm(w.o, C, h->wo[l], h->lr, h->bo[l], qn, T, C, C, ACT_NONE),
+                                   s, &w.sc));
     }
   }
   const float* pooled_v = pooled ? pooled : w.q;
@@ -1061,18 +1093,18 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
       if (b == 0) {
         LAUNCH("gate_fc1", s, gemm("gate_fc1",
-                                  mk_gemm(xb, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1,
-                                          DT_F32, T, he, hh, ACT_GELU), s, &w.sc));
+                                  rgemm(xb, hh, h->g_w1[b], h->lg1, h->g_b1[b], w.y1, T, he, hh,
+                                        ACT_GELU), s, &w.sc));
       } else {
         float* xn = (b & 1) ? w.x : w.x2;
         LAUNCH("gate_ln_fc1", s,
                launch_f32a_ln_rows(xb, w.y2, h->g_lw[b - 1], h->g_lb[b - 1], c.ln_eps, xn,
-                                   h->g_w1[b], h->g_b1[b], w.y1, T, he, hh, ACT_GELU, s));
+                                   h->g_w1[b], h->lg1, h->g_b1[b], w.y1, T, he, hh, ACT_GELU, s));
         xb = xn;
       }
       LAUNCH("gate_fc2", s, gemm("gate_fc2",
-                                mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2,
-                                        DT_F32, T, hh, he, ACT_NONE), s, &w.sc));
+                                rgemm(w.y1, he, h->g_w2[b], h->lg2, h->g_b2[b], w.y2, T, hh, he,
+                                      ACT_NONE), s, &w.sc));
     }
     const int b = IVC_GATE_BLOCKS - 1;
     LAUNCH("gate_res_ln_head", s,
@@ -1082,11 +1114,11 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     HIP_OK(hipMemcpyAsync(w.x, pooled_v, (size_t)T * hh * 4, hipMemcpyDeviceToDevice, s));
     for (int b = 0; b < IVC_GATE_BLOCKS; ++b) {
       LAUNCH("gate_fc1", s, gemm("gate_fc1",
-                                mk_gemm(w.x, hh, DT_F32, h->g_w1[b], dt, h->g_b1[b], w.y1,
-                                        DT_F32, T, he, hh, ACT_GELU), s, &w.sc));
+                                rgemm(w.x, hh, h->g_w1[b], h->lg1, h->g_b1[b], w.y1, T, he, hh,
+                                      ACT_GELU), s, &w.sc));
       LAUNCH("gate_fc2", s, gemm("gate_fc2",
-                                mk_gemm(w.y1, he, DT_F32, h->g_w2[b], dt, h->g_b2[b], w.y2,
-                                        DT_F32, T, hh, he, ACT_NONE), s, &w.sc));
+                                rgemm(w.y1, he, h->g_w2[b], h->lg2, h->g_b2[b], w.y2, T, hh, he,
+                                      ACT_NONE), s, &w.sc));
       if (b + 1 < IVC_GATE_BLOCKS)
         LAUNCH("gate_res_ln", s,
                launch_residual_ln(w.x, w.y2, h->g_lw[b], h->g_lb[b], T, hh, c.ln_eps, s));

@@ -240,7 +240,7 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
 template <int MAXS>
 __global__ void __launch_bounds__(512)
 k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ valid, int Ntok,
-                    int Q, int segmax, const bf16_t* __restrict__ Wv,
+                    int Q, int segmax, const bf16_t* __restrict__ Wv, long long ldw,
                     const float* __restrict__ bv, float* __restrict__ o, int T, int C, int H) {
   constexpr int FH = 16;
   const int lane = threadIdx.x & 63;
@@ -278,7 +278,7 @@ k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ vali
   arow[0].inv = 1.0f / L;
   // all K steps of a wave in one round of loads while the registers allow it
   constexpr int PD = MAXS <= 3 ? 4 : 2;
-  f32a_tile<1, 4, 8, PD, ACT_NONE, 0, MAXS>(arow, Wv + (long long)h * d * C, C, bv + h * d,
+  f32a_tile<1, 4, 8, PD, ACT_NONE, 0, MAXS>(arow, Wv + (long long)h * d * ldw, ldw, bv + h * d,
                                             o + h * d, nullptr, C, T, d, C, 1.f, m0, n0);
 }
 
@@ -290,18 +290,18 @@ int fold_value_merged_max_parts(int T, int N, int Q) {
 }
 
 hipError_t launch_fold_value_merged(const float* part, const int* valid, int N, int Q, int segmax,
-                                    const void* Wv, const float* bv, float* o, int T, int C, int H,
-                                    hipStream_t s) {
+                                    const void* Wv, long long ldw, const float* bv, float* o, int T,
+                                    int C, int H, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int maxs = fold_value_merged_max_parts(T, N, Q);
   if (maxs < 1 || maxs > 4 || H < 1 || C % H || (C / H) % 16 || C % 32 || (uintptr_t)part % 16 ||
-      (uintptr_t)Wv % 16 || ((size_t)C * 2) % 16)
+      (uintptr_t)Wv % 16 || ldw < C || ldw % 8)
     return hipErrorInvalidValue;
   const int d = C / H;
   const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((T + 15) / 16), (unsigned)H);
 #define IVC_FVM(S)                                                                                 \
   hipLaunchKernelGGL(k_fold_value_merged<S>, grid, dim3(512), 0, s, part, valid, N, Q, segmax,     \
-                     (const bf16_t*)Wv, bv, o, T, C, H)
+                     (const bf16_t*)Wv, ldw, bv, o, T, C, H)
   if (maxs <= 2) IVC_FVM(2);
   else if (maxs == 3) IVC_FVM(3);
   else IVC_FVM(4);
@@ -367,8 +367,8 @@ hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float sc
 template <int D, bool WS>
 __global__ void __launch_bounds__(512)
 k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __restrict__ Wq,
-                   const bf16_t* __restrict__ Wq_lo, const float* __restrict__ bq,
-                   const bf16_t* __restrict__ WkT,
+                   const bf16_t* __restrict__ Wq_lo, long long ldwq, const float* __restrict__ bq,
+                   const bf16_t* __restrict__ WkT, long long ldk,
                    bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
                    float scale) {
   constexpr int NB = D / 16, LDR = D + 4, KS = D / 32;
@@ -392,7 +392,7 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
       const int n = c0 + 16 * min(g + j, nbw - 1) + lo16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        xw[j][ks] = *reinterpret_cast<const u32x4*>(WkT + (long long)n * C + h * D + 32 * ks +
+        xw[j][ks] = *reinterpret_cast<const u32x4*>(WkT + (long long)n * ldk + h * D + 32 * ks +
                                                     8 * hi4);
     }
   };
@@ -405,8 +405,8 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
     const bf16_t* wlo[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      wrow[nb] = Wq + (long long)(h * D + 16 * nb + lo16) * C + 8 * hi4;
-      wlo[nb] = WS ? Wq_lo + (long long)(h * D + 16 * nb + lo16) * C + 8 * hi4 : wrow[nb];
+      wrow[nb] = Wq + (long long)(h * D + 16 * nb + lo16) * ldwq + 8 * hi4;
+      wlo[nb] = WS ? Wq_lo + (long long)(h * D + 16 * nb + lo16) * ldwq + 8 * hi4 : wrow[nb];
     }
     f32x4_t acc[1][NB];
     // (split weights at d = 128 load half as many K steps at once, to stay in registers)
@@ -489,7 +489,7 @@ template <int ACT>
 __global__ void __launch_bounds__(512)
 k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
                const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
-               float* __restrict__ x_out, const bf16_t* __restrict__ W,
+               float* __restrict__ x_out, const bf16_t* __restrict__ W, long long ldw,
                const float* __restrict__ bias, float* __restrict__ Cm, int M, int N, int K) {
   __shared__ __attribute__((aligned(16))) float xs[16 * 1024];  // [16][K], K <= 1024
   const int lane = threadIdx.x & 63;
@@ -557,27 +557,28 @@ k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
   __syncthreads();
   ARow<1> arow[1];
   arow[0].p[0] = xs + lo16 * K + 8 * hi4;
-  f32a_tile<1, 4, 8, 4, ACT, 0, 1>(arow, W, K, bias, Cm, nullptr, N, M, N, K, 1.f, m0, n0);
+  f32a_tile<1, 4, 8, 4, ACT, 0, 1>(arow, W, ldw, bias, Cm, nullptr, N, M, N, K, 1.f, m0, n0);
 }
 
 bool f32a_ln_rows_supported(int K) { return K % 256 == 0 && K >= 256 && K <= 1024; }
 
 hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* gamma,
                                const float* beta, float eps, float* x_out, const void* W,
-                               const float* bias, float* Cm, int M, int N, int K, int act,
-                               hipStream_t s) {
+                               long long ldw, const float* bias, float* Cm, int M, int N, int K,
+                               int act, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (!f32a_ln_rows_supported(K) || x_in == x_out || N <= 0 || (uintptr_t)x_in % 16 ||
+  if (!f32a_ln_rows_supported(K) || x_in == x_out || N <= 0 || ldw < K || ldw % 8 ||
+      (uintptr_t)x_in % 16 ||
       (uintptr_t)y % 16 || (uintptr_t)x_out % 16 || (uintptr_t)gamma % 16 ||
       (uintptr_t)beta % 16 || (uintptr_t)W % 16 || (act != ACT_GELU && act != ACT_NONE))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16));
   if (act == ACT_GELU)
     hipLaunchKernelGGL(k_f32a_ln_rows<ACT_GELU>, grid, dim3(512), 0, s, x_in, y, gamma, beta, eps,
-                       x_out, (const bf16_t*)W, bias, Cm, M, N, K);
+                       x_out, (const bf16_t*)W, ldw, bias, Cm, M, N, K);
   else
     hipLaunchKernelGGL(k_f32a_ln_rows<ACT_NONE>, grid, dim3(512), 0, s, x_in, y, gamma, beta, eps,
-                       x_out, (const bf16_t*)W, bias, Cm, M, N, K);
+                       x_out, (const bf16_t*)W, ldw, bias, Cm, M, N, K);
   return hipGetLastError();
 }
 
@@ -587,19 +588,21 @@ bool fold_query_fused_supported(int C, int H) {
   return (d == 32 || d == 64 || d == 128) && C % 128 == 0 && C <= 1024;
 }
 
-hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, const float* bq,
-                                   const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
-                                   float scale, hipStream_t s, const void* Wq_lo) {
+hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, long long ldwq,
+                                   const float* bq, const void* WkT, long long ldk, void* qt_hi,
+                                   void* qt_lo, int T, int C, int H, float scale, hipStream_t s,
+                                   const void* Wq_lo) {
   if (T <= 0) return hipSuccess;
   if (!fold_query_fused_supported(C, H) || !q || !Wq || !bq || !WkT || !qt_hi || !qt_lo ||
       (uintptr_t)q % 16 || (uintptr_t)Wq % 16 || (uintptr_t)WkT % 16 || (uintptr_t)qt_hi % 16 ||
-      (uintptr_t)qt_lo % 16 || ldq < 0 || ldq % 4 || (uintptr_t)Wq_lo % 16)
+      (uintptr_t)qt_lo % 16 || ldq < 0 || ldq % 4 || (uintptr_t)Wq_lo % 16 || ldwq < C ||
+      ldwq % 8 || ldk < C || ldk % 8)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((T + 15) / 16), (unsigned)H);
   const int d = C / H;
 #define IVC_FQF(DV, WSV)                                                                           \
   hipLaunchKernelGGL((k_fold_query_fused<DV, WSV>), grid, dim3(512), 0, s, q, ldq,                 \
-                     (const bf16_t*)Wq, (const bf16_t*)Wq_lo, bq, (const bf16_t*)WkT,             \
+                     (const bf16_t*)Wq, (const bf16_t*)Wq_lo, ldwq, bq, (const bf16_t*)WkT, ldk,  \
                      (bf16_t*)qt_hi, (bf16_t*)qt_lo, T, C, scale)
   if (Wq_lo != nullptr) {
     if (d == 32) IVC_FQF(32, true);
@@ -614,45 +617,55 @@ hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq
   return hipGetLastError();
 }
 
-// fp32 values as bf16 high and low parts: hi = bf16(x), lo = bf16(x - hi)
+// fp32 values as bf16 high and low parts: hi = bf16(x), lo = bf16(x - hi);
+// x is a dense [rows, cols] matrix, hi and lo have row stride ld
 __global__ void k_split_bf16(const float* __restrict__ x, bf16_t* __restrict__ hi,
-                             bf16_t* __restrict__ lo, long long n) {
+                             bf16_t* __restrict__ lo, long long rows, int cols, long long ld) {
+  const long long n = rows * cols;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (long long)gridDim.x * blockDim.x) {
+    const long long r = i / cols, o = r * ld + (i - r * cols);
     const bf16_t h = f32_to_bf16(x[i]);
-    hi[i] = h;
-    lo[i] = f32_to_bf16(x[i] - bf16_to_f32(h));
+    hi[o] = h;
+    lo[o] = f32_to_bf16(x[i] - bf16_to_f32(h));
   }
 }
 
-hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long long n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_split_bf16, dim3(256), dim3(256), 0, s, x, (bf16_t*)hi, (bf16_t*)lo, n);
+hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long long rows, int cols,
+                             long long ld, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (ld < cols) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_split_bf16, dim3(256), dim3(256), 0, s, x, (bf16_t*)hi, (bf16_t*)lo, rows,
+                     cols, ld);
   return hipGetLastError();
 }
 
-// dst[c][r] = src[r][c] for a [R, Cc] bf16 matrix (weights, once at creation)
+// dst[c][r] = src[r][c] for a [R, Cc] bf16 matrix (weights, once at creation);
+// row strides lds (src) and ldd (dst)
 __global__ void __launch_bounds__(256)
-k_transpose_bf16(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int R, int Cc) {
+k_transpose_bf16(const bf16_t* __restrict__ src, long long lds, bf16_t* __restrict__ dst,
+                 long long ldd, int R, int Cc) {
   __shared__ bf16_t t[32][33];
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int i = ty; i < 32; i += 8) {
     const int r = r0 + i, c = c0 + tx;
-    t[i][tx] = (r < R && c < Cc) ? src[(long long)r * Cc + c] : (bf16_t)0;
+    t[i][tx] = (r < R && c < Cc) ? src[(long long)r * lds + c] : (bf16_t)0;
   }
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < Cc && r < R) dst[(long long)c * R + r] = t[tx][i];
+    if (c < Cc && r < R) dst[(long long)c * ldd + r] = t[tx][i];
   }
 }
 
-hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int Cc, hipStream_t s) {
+hipError_t launch_transpose_bf16(const void* src, long long lds, void* dst, long long ldd, int R,
+                                 int Cc, hipStream_t s) {
   if (R <= 0 || Cc <= 0) return hipSuccess;
+  if (lds < Cc || ldd < R) return hipErrorInvalidValue;
   dim3 grid((unsigned)((Cc + 31) / 32), (unsigned)((R + 31) / 32));
-  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, (const bf16_t*)src, (bf16_t*)dst, R,
-                     Cc);
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, (const bf16_t*)src, lds,
+                     (bf16_t*)dst, ldd, R, Cc);
   return hipGetLastError();
 }
 

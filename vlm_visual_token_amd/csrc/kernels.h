@@ -122,7 +122,9 @@ hipError_t launch_ln_fold_weights(const void* W, int N, int K, const float* gamm
                                   const float* beta, const float* b, void* Wg, float* colsum,
                                   float* bfold, hipStream_t s);
 // dst[c][r] = src[r][c], bf16 [R, Cc]
-hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int Cc, hipStream_t s);
+// dst[c][r] = src[r][c], [R, Cc] bf16; row strides lds (src) and ldd (dst)
+hipError_t launch_transpose_bf16(const void* src, long long lds, void* dst, long long ldd, int R,
+                                 int Cc, hipStream_t s);
 // split-K factor and workspace the SIMT kernel wants for a product
 int simt_ksplit(int M, int N, int K, int batch);
 size_t simt_part_elems(int M, int N, int batch, int ksplit);
@@ -258,27 +260,32 @@ hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt
 bool f32a_ln_rows_supported(int K);
 hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* gamma,
                                const float* beta, float eps, float* x_out, const void* W,
-                               const float* bias, float* Cm, int M, int N, int K, int act,
-                               hipStream_t s);
+                               long long ldw, const float* bias, float* Cm, int M, int N, int K,
+                               int act, hipStream_t s);
 // qp = Wq q + bq, then q~_h = scale * Wk_h^T qp_h for every head, in one launch
 // (the same values as a query projection followed by the key fold).  q: rows
 // of stride ldq (0: one row shared by every tile).
 bool fold_query_fused_supported(int C, int H);
 // Wq_lo: if set, Wq and Wq_lo are the bf16 high and low parts of fp32 weights.
-hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, const float* bq,
-                                   const void* WkT, void* qt_hi, void* qt_lo, int T, int C, int H,
-                                   float scale, hipStream_t s, const void* Wq_lo = nullptr);
-// hi = bf16(x), lo = bf16(x - hi) for n fp32 values
-hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long long n, hipStream_t s);
+// (Wq, Wq_lo rows at stride ldwq, WkT rows at stride ldk)
+hipError_t launch_fold_query_fused(const float* q, long long ldq, const void* Wq, long long ldwq,
+                                   const float* bq, const void* WkT, long long ldk, void* qt_hi,
+                                   void* qt_lo, int T, int C, int H, float scale, hipStream_t s,
+                                   const void* Wq_lo = nullptr);
+// hi = bf16(x), lo = bf16(x - hi) for a dense [rows, cols] fp32 matrix; hi and
+// lo with row stride ld
+hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long long rows, int cols,
+                             long long ld, hipStream_t s);
 // qt_hi / qt_lo [T, 16, C]: heads H .. 15 set to zero
 hipError_t launch_zero_heads(void* qt_hi, void* qt_lo, int T, int H, int C, hipStream_t s);
 // The value fold reading the token pass's partials directly (no merge launch):
 // o[t, h*d + i] = bv[h*d + i] + sum_c Wv[h*d + i, c] * xbar[t, h, c], bf16 Wv.
 // Usable when a tile's chunks meet at most 4 workgroups (max_parts <= 4).
 int fold_value_merged_max_parts(int T, int N, int Q);
+// (Wv rows at stride ldw)
 hipError_t launch_fold_value_merged(const float* part, const int* valid, int N, int Q, int segmax,
-                                    const void* Wv, const float* bv, float* o, int T, int C, int H,
-                                    hipStream_t s);
+                                    const void* Wv, long long ldw, const float* bv, float* o, int T,
+                                    int C, int H, hipStream_t s);
 // o[t, h*d + i] = bv[h*d+i] + sum_c Wv[h*d + i, c] * xbar[t, h, c]
 hipError_t launch_fold_value(int dtype, const float* xbar, const void* Wv, const float* bv,
                              float* o, int T, int C, int H, hipStream_t s);
