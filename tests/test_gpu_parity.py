@@ -306,8 +306,9 @@ def _small_bf16_router(pool_mode, C=512, H=8):
     return cfg
 
 
-# (C, H): head widths 64, 32 and 128 of the fused query projection + key fold
-@pytest.mark.parametrize("C,H", [(512, 8), (512, 16), (1024, 8)])
+# (C, H): head widths 64, 32 and 128 of the fused query projection + key fold;
+# head width 256 takes the separate query projection and key-fold products
+@pytest.mark.parametrize("C,H", [(512, 8), (512, 16), (1024, 8), (1024, 4)])
 @pytest.mark.parametrize("padded", [False, True])
 def test_folded_pool_small_matches_oracle_and_kv(padded, C, H):
     cfg = _small_bf16_router(1, C, H)
