@@ -121,7 +121,6 @@ hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float sc
 hipError_t launch_ln_fold_weights(const void* W, int N, int K, const float* gamma,
                                   const float* beta, const float* b, void* Wg, float* colsum,
                                   float* bfold, hipStream_t s);
-// dst[c][r] = src[r][c], bf16 [R, Cc]
 // dst[c][r] = src[r][c], [R, Cc] bf16; row strides lds (src) and ldd (dst)
 hipError_t launch_transpose_bf16(const void* src, long long lds, void* dst, long long ldd, int R,
                                  int Cc, hipStream_t s);
@@ -258,6 +257,7 @@ hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt
 // LayerNorm in its prologue); fp32 rows of K (a multiple of 256, <= 1024),
 // bf16 W [N, K]; x_in and x_out distinct.
 bool f32a_ln_rows_supported(int K);
+// (W rows at stride ldw)
 hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* gamma,
                                const float* beta, float eps, float* x_out, const void* W,
                                long long ldw, const float* bias, float* Cm, int M, int N, int K,
