@@ -306,6 +306,25 @@ def _small_bf16_router(pool_mode, C=512, H=8):
     return cfg
 
 
+# Gating with a wider hidden layer (expansion 2: W1 [2h, h], W2 [h, 2h], each
+# stored with its own padded row stride), folded and K/V pooling
+@pytest.mark.parametrize("pool_mode", [1, 0])
+def test_router_gate_expansion(pool_mode):
+    cfg = dict(_small_bf16_router(pool_mode), gate_expansion=2)
+    w = synth.make_weights(cfg)
+    x = synth.make_vit(cfg)
+    say(f"router gate expansion 2, pool_mode {pool_mode}")
+    r = _connector(cfg, w, cfg["T"]).route(torch.from_numpy(x).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    assert int(r["status"].item()) == 0
+    e_gate, _, _, e_pooled = O.connector_route(x, cfg, w)
+    assert_close(to_np(r["pooled"]), e_pooled, "bf16", "pooled")
+    assert np.abs(r["gate"].cpu().numpy() - e_gate).max() <= GATE_TOL
+    thr, use = O.decide(r["gate"].cpu().numpy()[:, 0], cfg)
+    assert float(r["thr"].item()) == thr
+    assert np.array_equal(r["use64"].cpu().numpy(), use)
+
+
 # (C, H): head widths 64, 32 and 128 of the fused query projection + key fold;
 # head width 256 takes the separate query projection and key-fold products
 @pytest.mark.parametrize("C,H", [(512, 8), (512, 16), (1024, 8), (1024, 4)])
