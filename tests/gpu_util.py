@@ -36,6 +36,10 @@ def workload(name, seed=0, **over):
     return cfg
 
 
+def host_gate_bias(cfg):
+    return gate_bias(cfg["name"]) if cfg["flash"] else None
+
+
 def host_weights(cfg, seed=0):
     return synth.make_weights(cfg, seed, gate_bias0=gate_bias(cfg["name"]) if cfg["flash"] else None)
 
@@ -75,10 +79,23 @@ def float_report(g, o):
 TOL = {"bf16": (1e-2, 5e-2), "f32": (1e-5, 1e-4)}
 
 
+def log_margin(what, **vals):
+    """Appends one JSON line (test, quantity, measured values) to the file named
+    by IVC_PARITY_LOG, if set: the record of how close each parity check sits
+    to its bar."""
+    path = os.environ.get("IVC_PARITY_LOG")
+    if not path:
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(test=test, what=what, **vals)) + "\n")
+
+
 def assert_close(g, o, dtype, what):
     rep = float_report(g, o)
     rel, mx = TOL[dtype]
     say(f"  {what}: rel_l2={rep['rel_l2']:.3e} max_abs/rms={rep['max_abs_over_rms']:.3e}")
+    log_margin(what, dtype=dtype, **rep)
     assert np.isfinite(np.asarray(g)).all(), what + " has non-finite values"
     assert rep["rel_l2"] <= rel, (what, rep)
     assert rep["max_abs_over_rms"] <= mx, (what, rep)

@@ -4,9 +4,11 @@ checks reject bad calls before touching the GPU."""
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
+from tests import abi_host_checks as H
 from vlm_visual_token_amd import ivc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -50,62 +52,36 @@ def test_struct_layout_matches_header(tmp_path):
     assert offs == exp
 
 
-def _cfg(**kw):
-    import synth
-    c = dict(synth.config("tiny_flash_f32"))
-    c.update(kw)
-    return c
-
-
-@pytest.mark.parametrize("bad,status", [
-    (dict(P=6), 1),
-    (dict(gate_hidden=32), 1),
-    (dict(pool_heads=3), 1),
-    (dict(C=62), 3),
-    (dict(pool_layers=9), 1),
-    (dict(ps_version=3), 1),
-    (dict(ln_fold=2), 1),
-    (dict(ln_fold=1), 2),  # the tiny workload is fp32: the fold needs bf16
-])
+@pytest.mark.parametrize("bad,status", H.BAD_CONFIGS)
 def test_create_rejects_bad_config_on_host(bad, status):
-    c = ivc.make_config(_cfg(**bad))
-    w = ivc.ivc_weights()
-    with pytest.raises(ivc.IvcError) as e:
-        ivc.ivc_connector_create(c, w, 0)
-    assert e.value.status == status
+    H.check_bad_config(bad, status)
 
 
 def test_create_rejects_bad_shuffle64_order_on_host():
-    c = ivc.make_config(_cfg())
-    c.shuffle64_order = 2
-    with pytest.raises(ivc.IvcError) as e:
-        ivc.ivc_connector_create(c, ivc.ivc_weights(), 0)
-    assert e.value.status == 1
+    H.check_bad_shuffle64_order()
 
 
 def test_create_rejects_missing_weights_on_host():
-    c = ivc.make_config(_cfg())
-    with pytest.raises(ivc.IvcError) as e:
-        ivc.ivc_connector_create(c, ivc.ivc_weights(), 0)
-    assert e.value.status == 1
-    assert "missing" in ivc.ivc_last_error()
+    H.check_missing_weights()
 
 
 def test_entry_points_reject_bad_arguments_on_host():
-    with pytest.raises(ivc.IvcError):
-        ivc.ivc_tile_offsets(None, -1, None, None, 0)
-    with pytest.raises(ivc.IvcError):
-        ivc.ivc_pixel_shuffle(7, None, 1, 8, 64, 1, 2, None, 0)
-    with pytest.raises(ivc.IvcError):
-        ivc.ivc_pixel_shuffle(0, None, 1, 8, 64, 1, 3, None, 0)
-    with pytest.raises(ivc.IvcError):
-        ivc.ivc_pixel_shuffle(0, None, 1, 8, 64, 1, 2, None, 0, ps_version=3)
-    with pytest.raises(ivc.IvcError):
-        ivc.ivc_pixel_shuffle(0, None, 1, 8, 64, 1, 4, None, 0, shuffle64_order=2)
-    with pytest.raises(ivc.IvcError) as e:
-        ivc.ivc_pixel_shuffle(1, 18, 1, 8, 64, 1, 2, 34, 0)  # pointers not 16-byte aligned
-    assert e.value.status == 3
-    assert ivc.ivc_connector_workspace_bytes(None, 1, 1) == 0
-    with pytest.raises(ivc.IvcError):
-        ivc.ivc_connector_run(None, None, 1, None, None, None, 0, 0)
-    assert ivc.ivc_status_string(4) == "workspace too small"
+    H.check_entry_points()
+
+
+# The same host checks in a child process against the library built with
+# AddressSanitizer and UndefinedBehaviorSanitizer on its host code, and the
+# sanitized index-math self-test.  CPU only: no GPU code runs.
+@pytest.mark.slow
+def test_host_checks_under_address_and_ub_sanitizers():
+    from vlm_visual_token_amd import build
+    san = build.build_sanitized()
+    r = subprocess.run([san["selftest"]], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    env = dict(os.environ, IVC_LIBRARY=san["lib"], LD_PRELOAD=san["asan_runtime"],
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "abi_host_checks.py")],
+                       capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
+    assert "host checks ok" in r.stdout and san["lib"] in r.stdout

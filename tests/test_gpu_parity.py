@@ -13,13 +13,21 @@ import torch
 
 import synth
 from oracle import connector as O
-from tests.gpu_util import (TORCH_DT, assert_close, dev_vit, dev_weights, host_weights, say,
-                            to_np, workload)
+from tests.gpu_util import (GOLDEN, TORCH_DT, assert_close, dev_vit, dev_weights, host_gate_bias,
+                            host_weights, log_margin, say, to_np, workload)
 
 pytestmark = pytest.mark.gpu
 
 GATE_TOL = 2e-3
 BAND = 1e-3  # tiles whose gate[:,0] is this close to a threshold are not compared for decisions
+
+
+def assert_gates(gate, e_gate, what="gate"):
+    """Gate probabilities within GATE_TOL absolute of the oracle's."""
+    dg = float(np.abs(np.asarray(gate, np.float64) - np.asarray(e_gate, np.float64)).max())
+    say(f"  {what} max abs diff {dg:.3e}")
+    log_margin(what, max_abs=dg, tol=GATE_TOL)
+    assert dg <= GATE_TOL, (what, dg)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -134,7 +142,7 @@ def test_tiny_route_matches_oracle(padded):
     gate = r["gate"].cpu().numpy()
     e_gate, e_thr, e_use, e_pooled = O.connector_route(x, cfg, w, valid)
     assert_close(to_np(r["pooled"]), e_pooled, "f32", "pooled")
-    assert np.abs(gate - e_gate).max() <= GATE_TOL
+    assert_gates(gate, e_gate)
     # decisions on the GPU's own gates: bit-exact
     thr, use = O.decide(gate[:, 0], cfg)
     assert float(r["thr"].item()) == thr
@@ -266,9 +274,7 @@ def test_flash_workload_end_to_end():
     assert_close(to_np(o64[tiles]), e64, "bf16", "out64")
     e_gate, _, _, e_pooled = O.connector_route(x, cfg, w)
     assert_close(to_np(r["pooled"][tiles]), e_pooled, "bf16", "pooled")
-    dg = np.abs(gate[tiles] - e_gate).max()
-    say(f"  gate max abs diff {dg:.3e}")
-    assert dg <= GATE_TOL
+    assert_gates(gate[tiles], e_gate)
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 13, 100, 208, 999, 1024, 1025, 5000])
@@ -319,7 +325,7 @@ def test_router_gate_expansion(pool_mode):
     assert int(r["status"].item()) == 0
     e_gate, _, _, e_pooled = O.connector_route(x, cfg, w)
     assert_close(to_np(r["pooled"]), e_pooled, "bf16", "pooled")
-    assert np.abs(r["gate"].cpu().numpy() - e_gate).max() <= GATE_TOL
+    assert_gates(r["gate"].cpu().numpy(), e_gate)
     thr, use = O.decide(r["gate"].cpu().numpy()[:, 0], cfg)
     assert float(r["thr"].item()) == thr
     assert np.array_equal(r["use64"].cpu().numpy(), use)
@@ -348,7 +354,7 @@ def test_folded_pool_small_matches_oracle_and_kv(padded, C, H):
     e_gate, _, _, e_pooled = O.connector_route(x, cfg, w, valid)
     assert_close(to_np(rf["pooled"]), e_pooled, "bf16", "folded pooled")
     assert_close(to_np(rk["pooled"]), e_pooled, "bf16", "kv pooled")
-    assert np.abs(rf["gate"].cpu().numpy() - e_gate).max() <= GATE_TOL
+    assert_gates(rf["gate"].cpu().numpy(), e_gate, "gate (folded)")
     gate = rf["gate"].cpu().numpy()
     thr, use = O.decide(gate[:, 0], cfg)
     assert float(rf["thr"].item()) == thr
@@ -373,9 +379,65 @@ def test_folded_pool_flash_workload():
     x = synth.make_vit_tiles(cfg, tiles)
     e_gate, _, _, e_pooled = O.connector_route(x, cfg, w)
     assert_close(to_np(r["pooled"][tiles]), e_pooled, "bf16", "pooled")
-    dg = np.abs(gate[tiles] - e_gate).max()
-    say(f"  gate max abs diff {dg:.3e}")
-    assert dg <= GATE_TOL
+    assert_gates(gate[tiles], e_gate)
+
+
+# Every tile of the 2B-Flash workload against the oracle's gates, stored by
+# tests/golden/make_flash_gates.py (the oracle alone, all 208 tiles): gates
+# within 2e-3; the GPU's decisions equal to the oracle's own, independently
+# computed ones on every tile whose gate[:,0] is at least 1e-3 from both
+# thresholds on both sides ([4B-Flash] section 4, inference decision;
+# [2B-Flash] routing decision); and bit-exact on the GPU's own gates.
+def _flash_fixture():
+    import json
+    import os
+    with open(os.path.join(GOLDEN, "flash_gates.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("path", ["kv", "folded", "forward"])
+def test_flash_gates_all_tiles_vs_oracle(path):
+    fx = _flash_fixture()
+    cfg = workload("internvl35_2b_flash", pool_mode=0 if path == "kv" else 1,
+                   ln_fold=1 if path == "forward" else 0)
+    T = cfg["T"]
+    assert fx["T"] == T and fx["gate_bias0"] == host_gate_bias(cfg)
+    say(f"2B-Flash all-tile gates: path={path} T={T}")
+    w = host_weights(cfg)
+    con = _connector(cfg, w, T)
+    xd = dev_vit(cfg)
+    r = con.forward(xd) if path == "forward" else con.route(xd)
+    torch.cuda.synchronize()
+    gate = r["gate"].cpu().numpy()
+    use = r["use64"].cpu().numpy()
+    g_thr = float(r["thr"].item())
+    e_gate = np.asarray(fx["gate"], np.float64)
+    e_use = np.asarray(fx["use64"], np.uint8)
+    e_thr = float(fx["threshold"])
+    assert_gates(gate, e_gate, f"gate all {T} tiles ({path})")
+    # the threshold is an interpolation between order statistics, and order
+    # statistics of two sets move by at most the largest element change
+    dthr = abs(g_thr - e_thr)
+    log_margin(f"threshold ({path})", max_abs=dthr, tol=GATE_TOL)
+    assert dthr <= GATE_TOL
+    # bit-exact decisions on the GPU's own gates
+    thr, own = O.decide(gate[:, 0], cfg)
+    assert g_thr == thr
+    assert np.array_equal(use, own)
+    # independent decisions away from both thresholds (either side's values)
+    g0, e0 = gate[:, 0].astype(np.float64), e_gate[:, 0]
+    near = np.zeros(T, bool)
+    for v in (g0, e0):
+        for t in (g_thr, e_thr, cfg["abs_threshold"]):
+            near |= np.abs(v - t) < BAND
+    far = ~near
+    mism = int((use[far] != e_use[far]).sum())
+    say(f"  decisions compared on {int(far.sum())}/{T} tiles, {int(near.sum())} in the band, "
+        f"{mism} differ; routed gpu {int(use.sum())} oracle {int(e_use.sum())}")
+    log_margin(f"decisions ({path})", compared=int(far.sum()), band=int(near.sum()),
+               mismatches=mism)
+    assert far.sum() >= T - 8
+    assert mism == 0
 
 
 # Batch sizes that split a tile's tokens over many token-pass workgroups (T = 3:
@@ -403,7 +465,7 @@ def test_folded_pool_batch_sizes(T, padded):
     x = synth.make_vit_tiles(cfg, tiles)
     e_gate, _, _, e_pooled = O.connector_route(x, cfg, w, valid[tiles] if padded else None)
     assert_close(to_np(r["pooled"][tiles]), e_pooled, "bf16", "pooled")
-    assert np.abs(gate[tiles] - e_gate).max() <= GATE_TOL
+    assert_gates(gate[tiles], e_gate)
 
 
 # ---------------------------------------------------------------------------
@@ -691,7 +753,7 @@ def test_ln_fold_run_routed_small(pattern):
     _check_routed(con, cfg, xd, torch.from_numpy(use.astype(np.uint8)).cuda())
 
 
-@pytest.mark.parametrize("name", ["internvl35_4b_std", "internvl3_38b"])
+@pytest.mark.parametrize("name", ["internvl35_4b_std", "internvl3_14b_ragged", "internvl3_38b"])
 def test_ln_fold_standard_connector_sampled(name):
     # standard (non-Flash) connectors: the statistics pass for r = 2 only, C = 1024 and 3200
     cfg = workload(name, ln_fold=1)

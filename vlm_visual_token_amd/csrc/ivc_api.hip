@@ -1376,7 +1376,11 @@ extern "C" ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t 
 }
 
 extern "C" const char* ivc_status_string(ivc_status st) {
-  switch (st) {
+  // a C caller may pass any int: read it as one before naming it (loading an
+  // out-of-range enum value is undefined behaviour in C++)
+  int v;
+  memcpy(&v, &st, sizeof v);
+  switch (v) {
     case IVC_OK: return "ok";
     case IVC_ERR_INVALID_ARG: return "invalid argument";
     case IVC_ERR_UNSUPPORTED: return "unsupported shape";

@@ -19,6 +19,7 @@
 //                       out_ids, out_pos, keep_map and a source code per row
 //   4. k_compact_copy   one wave per output row, 16-byte copies of the row
 #include "common.h"
+#include "index_math.h"
 #include "kernels.h"
 
 namespace ivc {
@@ -127,32 +128,20 @@ k_compact_map(const int32_t* __restrict__ ids, long long L, int img, const uint8
   int total;
   int k = blk_off[blockIdx.x] + block_excl_scan(c, sh, &total);
   const long long Lp = *out_len;
-  const long long drop = S - S64;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const long long p = base + e;
     if (p >= L) break;
     const bool is_img = tok[e] == img;
     const int tile = k / S, loc = k - tile * S;
-    long long f;  // slots deleted before p
-    bool keep = true;
-    long long code = 0;
-    if (tile < T) {
-      const int u = use64[tile] != 0;
-      f = drop * routed_before[tile] + (u ? max(0, loc - S64) : 0);
-      if (is_img) {
-        keep = !u || loc < S64;
-        code = u ? ((2ll << 60) | ((long long)tile * S64 + loc))
-                 : ((1ll << 60) | ((long long)tile * S + loc));
-      } else {
-        code = p;
-      }
-    } else {
-      // k == T*S exactly (text after the last slot) or a malformed sequence
-      f = drop * routed_before[T];
-      if (is_img) keep = false;  // more slots than tiles: status already set
-      code = p;
-    }
+    // slots deleted before p; k == T*S exactly is text after the last slot,
+    // and a slot past T*S (malformed sequence: status set) is dropped
+    const long long f = compact_deleted_before(k, T, S, S64, routed_before, use64);
+    const bool keep = !is_img || compact_keeps_slot(k, T, S, S64, use64);
+    long long code = p;  // text: its own embedding row
+    if (is_img && tile < T)
+      code = use64[tile] != 0 ? ((2ll << 60) | ((long long)tile * S64 + loc))
+                              : ((1ll << 60) | ((long long)tile * S + loc));
     const long long j = p - f;
     keep_map[p] = keep ? (int32_t)j : -1;
     if (keep) {

@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "index_math.h"
 #include "kernels.h"
 
 namespace ivc {
@@ -76,33 +77,6 @@ IVC_DEV bool map_tile(int& M, int N, const RowMap& rm, int& m0, int& n0) {
 
 IVC_DEV long long phys_row(int gm, int a_rpg, long long a_gstride, int a_goff) {
   return a_rpg > 0 ? (long long)(gm / a_rpg) * a_gstride + a_goff + gm % a_rpg : (long long)gm;
-}
-
-// Gathered A: ViT row of cell 0 of logical row m's grid block.
-IVC_DEV long long gather_row0(const AGather& g, int m) {
-  const int Q = g.P / g.r, S = Q * Q;
-  const int rank = m / S, s = m - rank * S;
-  const int t = g.list != nullptr ? g.list[rank] : rank;
-  const int qa = s / Q, qb = s - qa * Q;
-  const int a = g.v1 ? qb : qa, b = g.v1 ? qa : qb;  // v1: token (a, b) sits at b*Q + a
-  return (long long)t * g.rows + g.has_cls + (long long)(g.r * a) * g.P + g.r * b;
-}
-
-// Gathered A: byte offset of channels [c0, c0 + BK) of cell q relative to
-// cell 0's row (r is 2 or 4, so the cell's grid offset is shifts and masks;
-// the main loop steps (q, c0) along K without dividing).
-IVC_DEV long long gather_koff(const AGather& g, int q, int c0) {
-  int dm, dk;  // grid offset of cell q inside the block
-  if (g.twice) {  // r = 4 as two r = 2 shuffles: q = 4*(2*m2 + k2) + (2*m + k)
-    const int w = q >> 2, qq = q & 3;
-    dm = 2 * (w >> 1) + (qq >> 1);
-    dk = 2 * (w & 1) + (qq & 1);
-  } else {
-    const int sh = g.r == 4 ? 2 : 1;
-    dm = q >> sh;
-    dk = q & (g.r - 1);
-  }
-  return ((long long)(dm * g.P + dk) * g.C + c0) * 2;
 }
 
 // Byte XOR applied to a column offset in row r of an epilogue slab: one
@@ -239,9 +213,10 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
             int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
             const float* __restrict__ ln_colsum) {
   constexpr int BK = 64;
-  // A offsets relative to the tile's first row are never negative (the tile's
-  // rows come in increasing ViT row order, gathered or not), so they stay
-  // unsigned 32-bit and the DMA takes a scalar base plus a 32-bit offset
+  // A offsets relative to the tile's base row are never negative (plain A:
+  // the tile's first row; gathered A: the first grid row of the first row's
+  // ViT tile, see gather_base), so they stay unsigned 32-bit and the DMA
+  // takes a scalar base plus a 32-bit offset
   using aoff_t = uint32_t;
   __shared__ __attribute__((aligned(1024))) char sA0[QB];
   __shared__ __attribute__((aligned(1024))) char sB0[QB];
@@ -255,7 +230,7 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
 
   // DMA j (0..3) of wave w fills rows (4w + j)*8 .. +7 of A and of W; lane:
   // row + lane/8, LDS piece lane%8 holding global piece (lane%8) ^ f(row)
-  const long long a_row0 = FOLD ? gather_row0(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
+  const long long a_row0 = FOLD ? gather_base(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
   gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
   gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
   aoff_t a_off[4];

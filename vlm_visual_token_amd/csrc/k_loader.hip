@@ -28,6 +28,7 @@
 // and each writes its 4 cells into the 16C row.  The ViT tensor is read
 // exactly once for both paths.
 #include "common.h"
+#include "index_math.h"
 #include "kernels.h"
 
 namespace ivc {
@@ -72,7 +73,7 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
   for (int q = 0; q < 4; ++q) {
     const int gi = 2 * a2 + (q >> 1), gj = 2 * b2i + (q & 1);
     const u32x4* src =
-        reinterpret_cast<const u32x4*>(X + ((size_t)t * rows + has_cls + gi * P + gj) * C);
+        reinterpret_cast<const u32x4*>(X + ((size_t)t * rows + ps_cell_row(P, has_cls, gi, gj)) * C);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int v = lane + 64 * i;
@@ -153,12 +154,12 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
 
   if (STATS) {
     if (want2 && lane == 0) {
-      const int tok2 = ps_v1 ? b2i * Q2 + a2 : a2 * Q2 + b2i;
+      const int tok2 = ps_token(Q2, a2, b2i, ps_v1);
       *reinterpret_cast<float2*>(st2 + 2 * ((size_t)t2 * S2 + tok2)) = make_float2(mean2, rstd2);
     }
     if (FLASH && want4 && threadIdx.x == 0) {
       const int Q4 = P >> 2, S4 = Q4 * Q4;
-      const int tok4 = ps_v1 ? b4i * Q4 + a4 : a4 * Q4 + b4i;
+      const int tok4 = ps_token(Q4, a4, b4i, ps_v1);
       *reinterpret_cast<float2*>(st4 + 2 * ((size_t)t4 * S4 + tok4)) = make_float2(mean4, rstd4);
     }
     return;
@@ -166,7 +167,7 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
 
   // ---- r = 2 row: channel block q holds cell q
   if (want2) {
-    const int tok2 = ps_v1 ? b2i * Q2 + a2 : a2 * Q2 + b2i;
+    const int tok2 = ps_token(Q2, a2, b2i, ps_v1);
     E* dst = out2 + ((size_t)t2 * S2 + tok2) * (size_t)(4 * C);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -193,12 +194,11 @@ k_shuffle_ln(const E* __restrict__ X, int T, int P, int C, int has_cls,
   //      (two r=2 shuffles).
   if (FLASH && want4) {
     const int Q4 = P >> 2, S4 = Q4 * Q4;
-    const int tok4 = ps_v1 ? b4i * Q4 + a4 : a4 * Q4 + b4i;
+    const int tok4 = ps_token(Q4, a4, b4i, ps_v1);
     E* dst = out4 + ((size_t)t4 * S4 + tok4) * (size_t)(16 * C);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int m4 = 2 * (w >> 1) + (q >> 1), k4 = 2 * (w & 1) + (q & 1);
-      const int base = (twice_r2 ? 4 * w + q : 4 * m4 + k4) * C;
+      const int base = ps64_channel_block(w, q, twice_r2) * C;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int v = lane + 64 * i;
@@ -278,7 +278,7 @@ k_ln_stats(const float2* __restrict__ tokst, int T, int P, int C, float eps, int
     const int a = s / Q2, b = s - a * Q2;  // token (a, b) of the direct order
     const float2 mo = block2_moments(tokst + (size_t)t * N, P, 2 * a, 2 * b, (float)C);
     const int t2 = use64 != nullptr ? rank[t] : t;
-    const int tok = ps_v1 ? b * Q2 + a : s;
+    const int tok = ps_token(Q2, a, b, ps_v1);
     *reinterpret_cast<float2*>(st2 + 2 * ((size_t)t2 * S2 + tok)) =
         make_float2(mo.x, 1.0f / sqrtf(mo.y / (float)(4 * C) + eps));
     return;
@@ -297,7 +297,7 @@ k_ln_stats(const float2* __restrict__ tokst, int T, int P, int C, float eps, int
   const float2 mo = moments_pair(moments_pair(b00, b01, 2.f * fc), moments_pair(b10, b11, 2.f * fc),
                                  4.f * fc);
   const int t4 = use64 != nullptr ? rank[t] : t;
-  const int tok = ps_v1 ? b * Q4 + a : s;
+  const int tok = ps_token(Q4, a, b, ps_v1);
   *reinterpret_cast<float2*>(st4 + 2 * ((size_t)t4 * S4 + tok)) =
       make_float2(mo.x, 1.0f / sqrtf(mo.y / (float)(16 * C) + eps));
 }

@@ -12,7 +12,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libivc.so")
+# IVC_LIBRARY may name another build of the same library (the host-sanitized
+# debug build the CPU tests load); the default is the in-tree libivc.so
+LIB_PATH = os.environ.get("IVC_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libivc.so")
 
 IVC_OK = 0
 IVC_F32, IVC_BF16 = 0, 1
