@@ -85,3 +85,17 @@ def test_host_checks_under_address_and_ub_sanitizers():
                        capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
     assert "host checks ok" in r.stdout and san["lib"] in r.stdout
+
+
+def test_trace_log_names_entry_calls():
+    script = os.path.join(ROOT, "tests", "abi_host_checks.py")
+    on = subprocess.run([sys.executable, script], capture_output=True, text=True, timeout=300,
+                        env=dict(os.environ, IVC_TRACE="1"))
+    assert on.returncode == 0, on.stderr[-2000:]
+    lines = [ln for ln in on.stderr.splitlines() if ln.startswith("[ivc] ")]
+    assert any(ln.startswith("[ivc] create dtype=0 C=64 P=6") for ln in lines)
+    assert any(ln.startswith("[ivc] pixel_shuffle dtype=7") for ln in lines)
+    assert any(ln.startswith("[ivc] tile_offsets B=-1") for ln in lines)
+    off = subprocess.run([sys.executable, script], capture_output=True, text=True, timeout=300,
+                         env=dict(os.environ, IVC_TRACE="0"))
+    assert off.returncode == 0 and "[ivc]" not in off.stderr

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -31,6 +32,24 @@ static ivc_status fail(ivc_status s, const char* fmt, ...) {
   return s;
 }
 
+// IVC_TRACE=1 (any value but "0"): one line on stderr per entry-point call
+// (its shape arguments) and per kernel launch (name, stream; products also
+// their M x N x K and kernel family).  Read once, at the first call.
+static bool trace_on() {
+  static const bool on = [] {
+    const char* e = getenv("IVC_TRACE");
+    return e != nullptr && *e != 0 && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+#define TRACE(...)                          \
+  do {                                      \
+    if (trace_on()) {                       \
+      fprintf(stderr, "[ivc] " __VA_ARGS__); \
+      fputc('\n', stderr);                  \
+    }                                       \
+  } while (0)
+
 #define HIP_OK(expr)                                                                        \
   do {                                                                                      \
     hipError_t e_ = (expr);                                                                 \
@@ -42,6 +61,7 @@ static ivc_status fail(ivc_status s, const char* fmt, ...) {
 // Launch wrapper: optional per-kernel timing, then the launch's status.
 #define LAUNCH(name, stream, expr)   \
   do {                               \
+    TRACE("  launch %s stream=%p", name, (void*)(stream)); \
     prof_begin(name, stream);        \
     hipError_t le_ = (expr);         \
     prof_end(stream);                \
@@ -289,8 +309,22 @@ struct SimtScratch {
 
 // GEMM dispatch: MFMA for bf16 operands with K % 64 == 0, SIMT otherwise
 // (split over K when the product is skinny and scratch is available).
-hipError_t gemm(const char*, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
+void trace_gemm(const char* name, const GemmArgs& g, const char* family) {
+  TRACE("    %s: %s M=%d N=%d K=%d batch=%d act=%d fold=%d rowmap=%d", name, family, g.M, g.N,
+        g.K, g.batch, g.act, g.fold, g.rm.m_dev != nullptr);
+}
+
+hipError_t gemm(const char* name, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
   if (g.batch <= 0) g.batch = 1;
+  if (trace_on()) {
+    const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+    const char* fam = (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) ? "f32a split-bf16 MFMA"
+                      : (g.batch == 1 && gemm_mfma_supported(g))
+                          ? (big_tiles >= 256 && gemm_dma_supported(g) ? "256x256 LDS-DMA MFMA"
+                                                                        : "128x128 MFMA")
+                          : "SIMT";
+    trace_gemm(name, g, fam);
+  }
   if (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) return launch_gemm_f32a(g, 0, nullptr, 1.f, s);
   if (g.batch == 1 && gemm_mfma_supported(g)) {
     // 256 x 256 LDS-DMA tiles when they fill the chip, else 128 x 128 tiles
@@ -464,6 +498,11 @@ size_t plan_compact_batch(int T, long long L, int B, void* base, CompactBatchWs*
 extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weights* w,
                                            void* stream, ivc_connector** out) {
   if (!cfg || !w || !out) return fail(IVC_ERR_INVALID_ARG, "null argument");
+  TRACE("create dtype=%d C=%d P=%d has_cls=%d D=%d mlp1_hidden=%d flash=%d mlp2_hidden=%d "
+        "pool=%dx%d heads gate=%dx%d pool_mode=%d ps_version=%d shuffle64_order=%d ln_fold=%d",
+        cfg->dtype, cfg->vit_width, cfg->grid, cfg->has_cls, cfg->llm_width, cfg->mlp1_hidden,
+        cfg->flash, cfg->mlp2_hidden, cfg->pool_layers, cfg->pool_heads, cfg->gate_hidden,
+        cfg->gate_expansion, cfg->pool_mode, cfg->ps_version, cfg->shuffle64_order, cfg->ln_fold);
   *out = nullptr;
   ivc_status st = check_cfg(*cfg);
   if (st != IVC_OK) return st;
@@ -734,6 +773,8 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
                            void* out256, void* out64, void* ws, size_t ws_bytes, void* stream,
                            bool tokst_ready = false, bool lists_ready = false) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  TRACE("run%s T=%d vit=%p ws=%zu tokst_ready=%d lists_ready=%d", use64 ? "_routed" : "", T, vit,
+        ws_bytes, (int)tokst_ready, (int)lists_ready);
   const ivc_config& c = h->cfg;
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
   if (T == 0) return IVC_OK;
@@ -857,6 +898,7 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
                  M2, H1, rmh256);
   if (fold) {
     if (!gemm_dma_supported(g)) return fail(IVC_ERR_UNSUPPORTED, "ln_fold: mlp1 product shape");
+    trace_gemm("mlp1_gemm1", g, "256x256 LDS-DMA MFMA, gathered A");
     LAUNCH("mlp1_gemm1", s1, launch_gemm_dma(g, s1));
   } else {
     LAUNCH("mlp1_gemm1", s1, gemm("mlp1_gemm1", g, s1, &w.sc));
@@ -871,7 +913,8 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
                    M4, H2, rmh64);
     if (fold) {
       if (!gemm_dma_supported(g)) return fail(IVC_ERR_UNSUPPORTED, "ln_fold: mlp2 product shape");
-      LAUNCH("mlp2_gemm1", s, launch_gemm_dma(g, s));
+      trace_gemm("mlp2_gemm1", g, "256x256 LDS-DMA MFMA, gathered A");
+    LAUNCH("mlp2_gemm1", s, launch_gemm_dma(g, s));
     } else {
       LAUNCH("mlp2_gemm1", s, gemm("mlp2_gemm1", g, s, &w.sc));
     }
@@ -913,6 +956,8 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
                              float* pooled, int32_t* dev_status, void* ws, size_t ws_bytes,
                              void* stream, float* tokst = nullptr, const RunWs* lists = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  TRACE("route T=%d vit=%p valid=%p pool_mode=%d ws=%zu token_moments=%d", T, vit,
+        (const void*)valid_tokens, h->cfg.pool_mode, ws_bytes, tokst != nullptr);
   const ivc_config& c = h->cfg;
   if (!c.flash) return fail(IVC_ERR_INVALID_ARG, "route needs a flash connector");
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
@@ -1153,6 +1198,7 @@ extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
                                             double* threshold, uint8_t* use64, float* pooled,
                                             int32_t* dev_status, void* out256, void* out64,
                                             void* ws, size_t ws_bytes, void* stream) {
+  TRACE("forward T=%d (route, then route-first run)", T);
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward needs a flash connector");
   if (T > 0 && (!out256 || !out64)) return fail(IVC_ERR_INVALID_ARG, "null out256/out64");
@@ -1191,6 +1237,7 @@ extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids
                                             int32_t* out_pos, int32_t* keep_map, void* out_embeds,
                                             int64_t* out_len, int32_t* dev_status, void* ws,
                                             size_t ws_bytes, void* stream) {
+  TRACE("compact L=%lld T=%d img_context=%d ws=%zu", (long long)L, T, img_context_id, ws_bytes);
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (L < 0 || T < 0) return fail(IVC_ERR_INVALID_ARG, "negative L or T");
@@ -1257,6 +1304,7 @@ extern "C" ivc_status ivc_connector_compact_batch(
     const void* out256, const void* out64, int32_t T, int32_t* out_ids, int32_t* out_pos,
     int32_t* keep_map, void* out_embeds, int32_t* out_cu_seqlens, int32_t* dev_status, void* ws,
     size_t ws_bytes, void* stream) {
+  TRACE("compact_batch B=%d L=%lld T=%d ws=%zu", B, (long long)L, T, ws_bytes);
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (L < 0 || T < 0 || B < 0) return fail(IVC_ERR_INVALID_ARG, "negative L, T or B");
@@ -1320,6 +1368,7 @@ extern "C" ivc_status ivc_connector_compact_batch(
 extern "C" ivc_status ivc_route_decide(const float* gate, int32_t T, double rel_quantile,
                                        double abs_threshold, double* threshold, uint8_t* use64,
                                        void* stream) {
+  TRACE("route_decide T=%d rel_quantile=%g abs_threshold=%g", T, rel_quantile, abs_threshold);
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
   if (!(rel_quantile >= 0.0 && rel_quantile <= 1.0))
     return fail(IVC_ERR_INVALID_ARG, "rel_quantile outside [0, 1]");
@@ -1333,6 +1382,7 @@ extern "C" ivc_status ivc_route_decide(const float* gate, int32_t T, double rel_
 
 extern "C" ivc_status ivc_tile_offsets(const int32_t* tiles_per_image, int32_t B, int32_t* offsets,
                                        int32_t* dev_status, void* stream) {
+  TRACE("tile_offsets B=%d", B);
   if (B < 0) return fail(IVC_ERR_INVALID_ARG, "B = %d", B);
   if (!offsets || (B > 0 && !tiles_per_image)) return fail(IVC_ERR_INVALID_ARG, "null pointer");
   hipStream_t s = (hipStream_t)stream;
@@ -1344,6 +1394,8 @@ extern "C" ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t 
                                         int32_t C, int32_t has_cls, int32_t r,
                                         int32_t ps_version, int32_t shuffle64_order, void* out,
                                         void* stream) {
+  TRACE("pixel_shuffle dtype=%d T=%d P=%d C=%d has_cls=%d r=%d ps_version=%d shuffle64_order=%d",
+        dtype, T, P, C, has_cls, r, ps_version, shuffle64_order);
   if (dtype != IVC_F32 && dtype != IVC_BF16) return fail(IVC_ERR_INVALID_ARG, "dtype");
   if (ps_version < 0 || ps_version > 2) return fail(IVC_ERR_INVALID_ARG, "ps_version %d", ps_version);
   if (shuffle64_order != IVC_SHUFFLE64_DIRECT && shuffle64_order != IVC_SHUFFLE64_TWICE_R2)
