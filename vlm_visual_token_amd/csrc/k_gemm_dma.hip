@@ -10,15 +10,16 @@
 // fragment reads (ds_read_b128, one row per lane) are free of bank conflicts
 // without padding.
 //
-// Main loop: K step 64, two stages of 64 KB (A and W, 256 rows of 128 bytes
-// each): full 128-byte rows per DMA request.  The next step's DMA
-// instructions go out over the first half of the step's MFMAs and the next
-// sub-step's fragment reads are interleaved with them.  (A four-stage ring
-// of K step 32 was measured slower on every shape here: its 64-byte row
-// requests cost more than the deeper prefetch gains.)
+// Main loop: K step 64, full 128-byte rows per DMA request; three LDS
+// stages of A (32 KB each, DMA two steps ahead) and two of W (one step
+// ahead), 160 KB.  The DMA instructions go out over the first half of the
+// step's MFMAs and the next sub-step's fragment reads are interleaved with
+// them.  (A four-stage ring of K step 32 was measured slower on every shape
+// here: its 64-byte row requests cost more than the deeper prefetch gains.)
 // The compiler must not make an LDS read wait for the DMAs in flight: each
-// stage is a separate __shared__ array (the compiler tracks LDS DMA targets
-// per array).
+// stage is a separate __shared__ array, and the loop is unrolled over the
+// stages' cycle so each step names its arrays directly (the compiler tracks
+// LDS DMA targets per array, and only when it can tell which one).
 //
 // Epilogue: the 256 x 256 bf16 tile goes through LDS (the four 32 KB stage
 // arrays hold 64 rows each) and out with 16-byte row-contiguous stores;
@@ -100,11 +101,11 @@ template <int ACT, bool FOLD, int NJ = 2, int NTH = DNT>
 IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* q2, char* q3,
                         int wm, int wn, int m0, int n0, int M, int N, const float* bias,
                         bf16_t* Cm, long long ldc, const RowMap& rm, const float* ln_rows,
-                        const float* ln_colsum) {
+                        const float* ln_colsum, float2* rowst /* FOLD: [256] in LDS */) {
   constexpr int WC = 32 * NJ;  // columns per wave
   const int tid = threadIdx.x, lane = tid & 63;
   const bool odd_lane = lane & 1;
-  __shared__ float2 rowst[FOLD ? DBM : 1];  // (rstd, -rstd * mean) per tile row
+  // rowst: (rstd, -rstd * mean) per tile row
   float ccol[NJ];
   if (FOLD) {
     if (tid < DBM) {
@@ -140,18 +141,16 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         char* slab = i < 2 ? slab_lo : slab_hi;
-        float2 rs[16];  // this lane's 16 rows of block row i, read together
-        if (FOLD) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            rs[v] = rowst[wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)];
-        }
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           float x0, x1;
           if (FOLD) {
-            x0 = fmaf(rs[v].x, acc[i][j][v], fmaf(rs[v].y, ccol[j], bj));
-            x1 = fmaf(rs[v + 1].x, acc[i][j][v + 1], fmaf(rs[v + 1].y, ccol[j], bj));
+            // the row pair's (rstd, -rstd * mean), read as needed (16 pairs read
+            // ahead would hold 32 more registers at the kernel's peak)
+            const float2* rp = rowst + wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            const float2 r0 = rp[0], r1 = rp[1];
+            x0 = fmaf(r0.x, acc[i][j][v], fmaf(r0.y, ccol[j], bj));
+            x1 = fmaf(r1.x, acc[i][j][v + 1], fmaf(r1.y, ccol[j], bj));
           } else {
             x0 = acc[i][j][v] + bj;
             x1 = acc[i][j][v + 1] + bj;
@@ -196,8 +195,8 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// The kernel: K step 64, two stages; sA*/sB* hold 256 rows of 128 bytes, and
-// 16-byte piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// The main loop: K step 64, two stages; sA*/sB* hold 256 rows of 128 bytes,
+// and 16-byte piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
 // 8 waves of 128 x 64 (4 x 2 MFMA blocks, 128 accumulators each), two per
 // SIMD, so while one wave of a SIMD waits to issue its share of the operand
 // DMA the other issues MFMAs (4 waves of 128 x 128 with all 256 AGPRs were
@@ -205,53 +204,94 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
 // issues 8 of the step's 64 DMA instructions over the first half of the
 // step's MFMAs.
 // ---------------------------------------------------------------------------
-template <int ACT, bool FOLD>
-__global__ void __launch_bounds__(DNT, 1)
-k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_gstride,
-            int a_goff, const bf16_t* __restrict__ W, long long ldw,
-            const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc, int M, int N,
-            int K, RowMap rm, AGather ag, const float* __restrict__ ln_rows,
-            const float* __restrict__ ln_colsum) {
-  constexpr int BK = 64;
-  // A offsets relative to the tile's base row are never negative (plain A:
-  // the tile's first row; gathered A: the first grid row of the first row's
-  // ViT tile, see gather_base), so they stay unsigned 32-bit and the DMA
-  // takes a scalar base plus a 32-bit offset
-  using aoff_t = uint32_t;
-  __shared__ __attribute__((aligned(1024))) char sA0[QB];
-  __shared__ __attribute__((aligned(1024))) char sB0[QB];
-  __shared__ __attribute__((aligned(1024))) char sA1[QB];
-  __shared__ __attribute__((aligned(1024))) char sB1[QB];
-  int m0, n0;
-  if (!map_tile(M, N, rm, m0, n0)) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
-  const int wm = w >> 2, wn = w & 3;  // rows wm*128 .., columns wn*64 ..
+constexpr int BK = 64;
 
+struct GemmOps {
+  const bf16_t* A;
+  long long lda;
+  int a_rpg;
+  long long a_gstride;
+  int a_goff;
+  const bf16_t* W;
+  long long ldw;
+  int M, N, K;
+  AGather ag;
+};
+
+// Per-wave DMA addressing of one output tile: A rows from a scalar base plus
+// unsigned 32-bit offsets.  The offsets are never negative: plain A is
+// addressed from the tile's first row, gathered A from the first grid row of
+// the first row's ViT tile (gather_base), which no later row of the tile
+// precedes.
+struct TileDma {
+  __amdgpu_buffer_rsrc_t a_rs, b_rs;  // buffers based at the tile's base rows
+  uint32_t a_off[4];
+  uint32_t b_off[4];
+};
+
+// Raw buffer over [base, base + 4 GiB): the DMA takes the tile's base from
+// scalar registers, a 32-bit offset per lane and the K step's offset as a
+// scalar, so no 64-bit address is formed or kept per lane.
+IVC_DEV __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff,
+                                           0x00020000);
+}
+
+template <bool FOLD>
+IVC_DEV TileDma tile_dma(const GemmOps& o, int m0, int n0, int w, int lane) {
+  TileDma d;
   // DMA j (0..3) of wave w fills rows (4w + j)*8 .. +7 of A and of W; lane:
   // row + lane/8, LDS piece lane%8 holding global piece (lane%8) ^ f(row)
-  const long long a_row0 = FOLD ? gather_base(ag, m0) : phys_row(m0, a_rpg, a_gstride, a_goff);
-  gchar_t* a_tile = (gchar_t*)(A + a_row0 * lda);
-  gchar_t* b_tile = (gchar_t*)(W + (long long)n0 * ldw);
-  aoff_t a_off[4];
-  uint32_t b_off[4];
+  const long long a_row0 =
+      FOLD ? gather_base(o.ag, m0) : phys_row(m0, o.a_rpg, o.a_gstride, o.a_goff);
+  d.a_rs = raw_buffer(o.A + a_row0 * o.lda);
+  d.b_rs = raw_buffer(o.W + (long long)n0 * o.ldw);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = (w * 4 + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r & 7) ^ ((r >> 3) & 1));
-    const int gm = min(m0 + r, M - 1);
-    const long long pr = FOLD ? gather_row0(ag, gm) : phys_row(gm, a_rpg, a_gstride, a_goff);
-    a_off[j] = (aoff_t)(((pr - a_row0) * lda + c * 8) * 2);
-    b_off[j] = (uint32_t)(((long long)(min(n0 + r, N - 1) - n0) * ldw + c * 8) * 2);
+    const int gm = min(m0 + r, o.M - 1);
+    const long long pr =
+        FOLD ? gather_row0(o.ag, gm) : phys_row(gm, o.a_rpg, o.a_gstride, o.a_goff);
+    d.a_off[j] = (uint32_t)(((pr - a_row0) * o.lda + c * 8) * 2);
+    d.b_off[j] = (uint32_t)(((long long)(min(n0 + r, o.N - 1) - n0) * o.ldw + c * 8) * 2);
   }
-  auto dma_one = [&](int q, long long ka, long long kb, char* sa, char* sb) {  // q = 0..7
-    const int j = q >> 1;
-    if ((q & 1) == 0)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a_tile + ka + a_off[j]),
-                                       (lds_void_t*)(sa + (w * 4 + j) * 1024), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b_tile + kb + b_off[j]),
-                                       (lds_void_t*)(sb + (w * 4 + j) * 1024), 16, 0, 0);
+  return d;
+}
+
+// LDS stages of the main loop: A and W tiles of one K step each (32 KB):
+// three of A (its DMAs run two steps ahead) and two of W (one step ahead),
+// 160 KB, the CU's whole LDS.  A is the operand whose lines an XCD's L2 sees
+// fewer times (a band of 8 tile rows by 4 tile columns runs on an XCD at
+// once: each A panel is read by 4 tiles, each W panel by 8), so it takes the
+// L2 misses and gets the deeper prefetch (measured: 5-11% faster than two
+// stages of each on the projector shapes; three of W instead: no better).
+// The epilogue's slabs are the first two stages of each; the folded
+// epilogue's row statistics go to the third A stage.
+struct Stages {
+  char *sa0, *sa1, *sa2;
+  char *sb0, *sb1;
+};
+
+// s_waitcnt immediates (vmcnt in bits 3:0, expcnt and lgkmcnt left at their
+// maxima): wait until at most n vector-memory operations are outstanding.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
+
+// Sums the tile's K steps into acc (overwritten).  Each wave issues 4 DMA
+// instructions of W (step s + 1) and then 4 of A (step s + 2) per step, 1 KB
+// each, over the first half of the step's MFMAs; DMAs complete in issue
+// order, so the wait at a step's top lets A's newest step stay in flight.
+template <bool FOLD>
+IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma& d, const Stages& st,
+                         int w, int wm, int wn, int lane) {
+  const int n = o.K / BK;
+  auto dma_a = [&](int j, uint32_t ka, char* sa) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a_rs, (lds_void_t*)(sa + (w * 4 + j) * 1024), 16,
+                                             d.a_off[j], ka, 0, 0);
+  };
+  auto dma_b = [&](int j, uint32_t kb, char* sb) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.b_rs, (lds_void_t*)(sb + (w * 4 + j) * 1024), 16,
+                                             d.b_off[j], kb, 0, 0);
   };
   // fragment (i, kk) of A at fa[kk] + i * 4096 (rows wm*128 + i*32 + lane%32),
   // of W at fb[kk] + j * 4096 (rows wn*64 + j*32 + lane%32)
@@ -265,37 +305,73 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
       fb[kk] = (uint32_t)((wn * 64 + rl) * 128) + p;
     }
   }
-
-  f32x16_t acc[4][2];
+  // byte offset of A's next K step to issue (FOLD: each step of 64 lies
+  // inside one C-wide cell; the cell's grid offset comes from gather_koff)
+  int cell_n = 0, c0_n = 0;
+  auto a_koff = [&]() -> uint32_t {
+    const uint32_t k = FOLD ? (uint32_t)gather_koff(o.ag, cell_n, c0_n) : (uint32_t)(c0_n * 2);
+    c0_n += BK;
+    if (FOLD && c0_n == o.ag.C) {
+      c0_n = 0;
+      ++cell_n;
+    }
+    return k;
+  };
+  constexpr int NA = 3, NB = 2;
+  // prologue: A and W of step 0, then A of step 1, in the order the steady
+  // state's steps leave their DMAs (W, then A) so that the compiler's count
+  // of DMAs in flight agrees at the loop's entry and back edge
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_a(j, 0, st.sa0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_b(j, 0, st.sb0);
+  (void)a_koff();
+  if (n > 1) {
+    const uint32_t ka = a_koff();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma_a(j, ka, st.sa1);
+  }
+  // cleared with moves the compiler cannot move out of an enclosing loop
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int KT = K / BK;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dma_one(q, FOLD ? gather_koff(ag, 0, 0) : 0, 0, sA0, sB0);
-  int cell_n = 0, c0_n = 0;  // (cell, channel) of the next K step (FOLD)
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool odd = kt & 1;
-    const char* sa = odd ? sA1 : sA0;
-    const char* sb = odd ? sB1 : sB0;
-    char* na = odd ? sA0 : sA1;
-    char* nb = odd ? sB0 : sB1;
-    const bool more = kt + 1 < KT;
-    const long long kb = (long long)(kt + 1) * (BK * 2);
-    if (FOLD) {
-      c0_n += BK;
-      if (c0_n == ag.C) {
-        c0_n = 0;
-        ++cell_n;
+      for (int v = 0; v < 16; ++v) {
+        float z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        acc[i][j][v] = z;
       }
-    }
-    const long long ka = FOLD ? gather_koff(ag, cell_n, c0_n) : kb;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // One step with its stages fixed at compile time: step s reads stage
+  // IA / IB and fills stage (IA + NA - 1) % NA / (IB + NB - 1) % NB.  Each
+  // copy names its LDS arrays directly, so the compiler can tell the reads
+  // from the DMA targets in flight (with stage pointers chosen at run time
+  // it waits for every DMA before the first read).
+  // FULL: both operands' next DMAs are issued (the steady state, no
+  // conditional issue, so the compiler's count of DMAs in flight is exact and
+  // it adds no wait of its own beside the step's)
+  auto step = [&](int s, auto ia_c, auto ib_c, auto full_c) {
+    constexpr int IA = decltype(ia_c)::value, IB = decltype(ib_c)::value;
+    constexpr bool FULL = decltype(full_c)::value;
+    constexpr int JA = (IA + NA - 1) % NA, JB = (IB + NB - 1) % NB;
+    const char* sa = IA == 0 ? st.sa0 : IA == 1 ? st.sa1 : st.sa2;
+    const char* sb = IB == 0 ? st.sb0 : st.sb1;
+    char* na = JA == 0 ? st.sa0 : JA == 1 ? st.sa1 : st.sa2;
+    char* nb = JB == 0 ? st.sb0 : st.sb1;
+    const bool more_a = FULL || s + NA - 1 < n, more_b = FULL || s + NB - 1 < n;
+    const uint32_t ka = more_a ? a_koff() : 0;
+    const uint32_t kb = (uint32_t)((s + NB - 1) * (BK * 2));
+    // operands of step s complete; A's step s + 1 may still be in flight
+    // (issued last, one step ago)
+    if (FULL || s + 1 < n)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // execution barrier only: every wave has waited for its own DMAs of step
+    // s, and its reads of the stage about to be refilled ended before the
+    // MFMAs that used them.  (__syncthreads adds a release that waits for
+    // every DMA in flight, the deeper stage's included.)
+    asm volatile("s_barrier" ::: "memory");
     bf16x8_t fa_[2][4], fb_[2][2];  // [buffer][block]
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa_[0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[0] + i * 4096);
@@ -309,8 +385,13 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          // 8 DMA instructions over the first 16 MFMAs of the step
-          if (more && kk < 2 && j == 0) dma_one(kk * 4 + i, ka, kb, na, nb);
+          // 8 DMA instructions over the first 16 MFMAs of the step: W's
+          // four, then A's (the last issued are the ones left in flight)
+          if (kk < 2 && j == 0) {
+            const int q = kk * 4 + i;
+            if (q < 4 && more_b) dma_b(q, kb, nb);
+            if (q >= 4 && more_a) dma_a(q - 4, ka, na);
+          }
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[cb][i], fb_[cb][j], acc[i][j],
                                                               0, 0, 0);
         }
@@ -321,11 +402,59 @@ k_gemm_dma8(const bf16_t* __restrict__ A, long long lda, int a_rpg, long long a_
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using F = std::false_type;
+  using T = std::true_type;
+  // steady state while a whole cycle of steps issues every DMA (the last
+  // step of the cycle issues step s + 5 + max(NA, NB) - 1), then the guarded tail
+  // A stages cycle by 3, W stages by 2: six step bodies per cycle
+  int s = 0;
+  for (; s + 8 <= n; s += 6) {
+    step(s, I0{}, I0{}, T{});
+    step(s + 1, I1{}, I1{}, T{});
+    step(s + 2, I2{}, I0{}, T{});
+    step(s + 3, I0{}, I1{}, T{});
+    step(s + 4, I1{}, I0{}, T{});
+    step(s + 5, I2{}, I1{}, T{});
+  }
+  for (; s < n; s += 6) {
+    step(s, I0{}, I0{}, F{});
+    if (s + 1 < n) step(s + 1, I1{}, I1{}, F{});
+    if (s + 2 < n) step(s + 2, I2{}, I0{}, F{});
+    if (s + 3 < n) step(s + 3, I0{}, I1{}, F{});
+    if (s + 4 < n) step(s + 4, I1{}, I0{}, F{});
+    if (s + 5 < n) step(s + 5, I2{}, I1{}, F{});
   }
   __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ---------------------------------------------------------------------------
+// One output tile per workgroup.
+// ---------------------------------------------------------------------------
+template <int ACT, bool FOLD>
+__global__ void __launch_bounds__(DNT, 1)
+k_gemm_dma8(GemmOps o, const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc,
+            RowMap rm, const float* __restrict__ ln_rows, const float* __restrict__ ln_colsum) {
+  __shared__ __attribute__((aligned(1024))) char sA0[QB];
+  __shared__ __attribute__((aligned(1024))) char sB0[QB];
+  __shared__ __attribute__((aligned(1024))) char sA1[QB];
+  __shared__ __attribute__((aligned(1024))) char sB1[QB];
+  __shared__ __attribute__((aligned(1024))) char sA2[QB];  // also the folded epilogue's row statistics
+  int m0, n0;
+  if (!map_tile(o.M, o.N, rm, m0, n0)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
+  const int wm = w >> 2, wn = w & 3;  // rows wm*128 .., columns wn*64 ..
+  const TileDma d = tile_dma<FOLD>(o, m0, n0, w, lane);
+  const Stages st{sA0, sA1, sA2, sB0, sB1};
+  f32x16_t acc[4][2];
+  tile_ksteps<FOLD>(acc, o, d, st, w, wm, wn, lane);
   __syncthreads();
-  store_tile<ACT, FOLD, 2, DNT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, M, N, bias, Cm, ldc,
-                                    rm, ln_rows, ln_colsum);
+  store_tile<ACT, FOLD, 2, DNT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, o.M, o.N, bias, Cm, ldc,
+                                rm, ln_rows, ln_colsum, reinterpret_cast<float2*>(sA2));
 }
 
 // One workgroup per output n: the folded weights of the first Linear after a
@@ -390,19 +519,19 @@ bool gemm_dma_supported(const GemmArgs& g) {
 
 hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
   if (!gemm_dma_supported(g)) return hipErrorInvalidValue;
+  if (g.fold && g.act != ACT_GELU) return hipErrorInvalidValue;  // folded: the GELU'd first Linears
+  GemmOps o{(const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw,
+            g.M, g.N, g.K, g.ag};
   const int tiles = ((g.M + DBM - 1) / DBM) * ((g.N + DBN - 1) / DBN);
-#define IVC_DMA_LAUNCH(KERN)                                                                  \
-  hipLaunchKernelGGL(KERN, dim3((unsigned)tiles), dim3(DNT), 0, s, (const bf16_t*)g.A,    \
-                     g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw, g.bias,\
-                     (bf16_t*)g.Cm, g.ldc, g.M, g.N, g.K, g.rm, g.ag, g.ln_rows, g.ln_colsum)
-  if (g.fold) {  // the folded products are the GELU'd first Linears
-    if (g.act != ACT_GELU) return hipErrorInvalidValue;
-    IVC_DMA_LAUNCH((k_gemm_dma8<ACT_GELU, true>));
-  } else if (g.act == ACT_GELU) {
-    IVC_DMA_LAUNCH((k_gemm_dma8<ACT_GELU, false>));
-  } else {
-    IVC_DMA_LAUNCH((k_gemm_dma8<ACT_NONE, false>));
-  }
+#define IVC_DMA_LAUNCH(ACTV, FOLDV)                                                            \
+  hipLaunchKernelGGL((k_gemm_dma8<ACTV, FOLDV>), dim3((unsigned)tiles), dim3(DNT), 0, s, o, g.bias, \
+                     (bf16_t*)g.Cm, g.ldc, g.rm, g.ln_rows, g.ln_colsum)
+  if (g.fold)
+    IVC_DMA_LAUNCH(ACT_GELU, true);
+  else if (g.act == ACT_GELU)
+    IVC_DMA_LAUNCH(ACT_GELU, false);
+  else
+    IVC_DMA_LAUNCH(ACT_NONE, false);
 #undef IVC_DMA_LAUNCH
   return hipGetLastError();
 }
