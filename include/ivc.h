@@ -259,6 +259,31 @@ ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids, const voi
                                  void* out_embeds, int64_t* out_len, int32_t* dev_status,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory and cannot supply a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): ivc_connector_compact with the same arguments,
+ * outputs and device status, minus ws / ws_bytes.  Its scratch (per-block
+ * IMG_CONTEXT counts and offsets, routed tiles before each tile, a source
+ * code per output row) lives in a fixed device array of this library,
+ * IVC_COMPACT_NOALLOC_SCRATCH_BYTES per device, held until the process
+ * ends; its device address is taken when a connector is created on the
+ * device.  It allocates nothing.  Limits: L <= IVC_COMPACT_NOALLOC_MAX_LEN
+ * and T <= IVC_COMPACT_NOALLOC_MAX_TILES (IVC_ERR_UNSUPPORTED beyond, nothing
+ * enqueued); IVC_ERR_HIP if the array's address could not be taken.  Every
+ * call on one device shares that device's array: calls that overlap on one
+ * device (different streams, or different host threads) race and must not be
+ * issued; calls ordered on one stream are fine (each call writes all the
+ * scratch it reads before reading it). */
+#define IVC_COMPACT_NOALLOC_MAX_LEN 262144
+#define IVC_COMPACT_NOALLOC_MAX_TILES 4096
+#define IVC_COMPACT_NOALLOC_SCRATCH_BYTES 2116096 /* the workspace of those maxima */
+ivc_status ivc_connector_compact_noalloc(ivc_connector* h, const int32_t* ids, const void* embeds,
+                                         int64_t L, int32_t img_context_id, const uint8_t* use64,
+                                         const void* out256, const void* out64, int32_t T,
+                                         int32_t* out_ids, int32_t* out_pos, int32_t* keep_map,
+                                         void* out_embeds, int64_t* out_len, int32_t* dev_status,
+                                         void* stream);
+
 /* Variable-length batch form of ivc_connector_compact: B prompts packed
  * back to back, as varlen attention takes them.  Sequence b is positions
  * cu_seqlens[b] .. cu_seqlens[b+1]-1 of ids/embeds, and its images own

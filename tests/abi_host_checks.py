@@ -72,6 +72,9 @@ def check_entry_points():
     expect_status(lambda: ivc.ivc_pixel_shuffle(1, 18, 1, 8, 64, 1, 2, 34, 0), 3)
     assert ivc.ivc_connector_workspace_bytes(None, 1, 1) == 0
     expect_status(lambda: ivc.ivc_connector_run(None, None, 1, None, None, None, 0, 0))
+    expect_status(lambda: ivc.ivc_connector_compact_noalloc(None, None, None, 1, 0, None, None,
+                                                            None, 1, None, None, None, None, None,
+                                                            None, 0), 1)
     assert ivc.ivc_status_string(4) == "workspace too small"
     for s in range(-1, 9):
         assert isinstance(ivc.ivc_status_string(s), str)

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -154,6 +155,7 @@ struct ivc_connector {
   ivc_config cfg;
   int esz;
   int ncu = 256;  // compute units of the device the connector was created on
+  int dev = 0;     // that device
   // second stream (default priority) on which the mlp1 chain runs beside the
   // mlp2 chain; forked from and joined back to the caller's stream by events
   hipStream_t aux = nullptr;
@@ -492,6 +494,8 @@ size_t plan_compact_batch(int T, long long L, int B, void* base, CompactBatchWs*
 
 }  // namespace
 
+static void noalloc_scratch_init(int dev);
+
 // ---------------------------------------------------------------------------
 // create / destroy
 // ---------------------------------------------------------------------------
@@ -553,6 +557,10 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
       h->ncu = n;
+    h->dev = dev;
+    // the device address of this device's copy of the no-allocation scratch
+    // (ivc_connector_compact_noalloc); a failure is reported by that call
+    noalloc_scratch_init(dev);
   }
   if (c.flash && dt == IVC_BF16) {
     if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
@@ -1230,14 +1238,12 @@ extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
 // ---------------------------------------------------------------------------
 // compact
 // ---------------------------------------------------------------------------
-extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids,
-                                            const void* embeds, int64_t L, int32_t img_context_id,
-                                            const uint8_t* use64, const void* out256,
-                                            const void* out64, int32_t T, int32_t* out_ids,
-                                            int32_t* out_pos, int32_t* keep_map, void* out_embeds,
-                                            int64_t* out_len, int32_t* dev_status, void* ws,
-                                            size_t ws_bytes, void* stream) {
-  TRACE("compact L=%lld T=%d img_context=%d ws=%zu", (long long)L, T, img_context_id, ws_bytes);
+static ivc_status compact_impl(ivc_connector* h, const int32_t* ids, const void* embeds,
+                               int64_t L, int32_t img_context_id, const uint8_t* use64,
+                               const void* out256, const void* out64, int32_t T, int32_t* out_ids,
+                               int32_t* out_pos, int32_t* keep_map, void* out_embeds,
+                               int64_t* out_len, int32_t* dev_status, void* ws, size_t ws_bytes,
+                               void* stream) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (L < 0 || T < 0) return fail(IVC_ERR_INVALID_ARG, "negative L or T");
@@ -1288,6 +1294,76 @@ extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids
   hipStream_t s = (hipStream_t)stream;
   LAUNCH("compact", s, launch_compact(a, s));
   return IVC_OK;
+}
+
+extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids,
+                                            const void* embeds, int64_t L, int32_t img_context_id,
+                                            const uint8_t* use64, const void* out256,
+                                            const void* out64, int32_t T, int32_t* out_ids,
+                                            int32_t* out_pos, int32_t* keep_map, void* out_embeds,
+                                            int64_t* out_len, int32_t* dev_status, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  TRACE("compact L=%lld T=%d img_context=%d ws=%zu", (long long)L, T, img_context_id, ws_bytes);
+  return compact_impl(h, ids, embeds, L, img_context_id, use64, out256, out64, T, out_ids, out_pos,
+                      keep_map, out_embeds, out_len, dev_status, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// compaction without allocation or workspace: the same kernels, their scratch
+// (per-block IMG_CONTEXT counts and offsets, routed tiles before each tile, a
+// source code per output row) in a fixed device array of this library
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[IVC_COMPACT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};       // device address of `scratch`, per device
+hipError_t g_scratch_err[kMaxDevices] = {};  // why it could not be taken
+}  // namespace
+
+// Once per device, with that device current: the device address of its copy
+// of `scratch`.  (In host code the array's name stands for a host-side
+// handle, not a device address; kernels must be given this pointer.)
+static void noalloc_scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] != nullptr) return;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    g_scratch_err[dev] = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return;
+  }
+  g_scratch_ptr[dev] = p;
+}
+
+extern "C" ivc_status ivc_connector_compact_noalloc(
+    ivc_connector* h, const int32_t* ids, const void* embeds, int64_t L, int32_t img_context_id,
+    const uint8_t* use64, const void* out256, const void* out64, int32_t T, int32_t* out_ids,
+    int32_t* out_pos, int32_t* keep_map, void* out_embeds, int64_t* out_len, int32_t* dev_status,
+    void* stream) {
+  TRACE("compact_noalloc L=%lld T=%d img_context=%d", (long long)L, T, img_context_id);
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  if (L > IVC_COMPACT_NOALLOC_MAX_LEN || T > IVC_COMPACT_NOALLOC_MAX_TILES)
+    return fail(IVC_ERR_UNSUPPORTED,
+                "compact_noalloc: L = %lld, T = %d beyond its fixed scratch (L <= %d, T <= %d)",
+                (long long)L, T, IVC_COMPACT_NOALLOC_MAX_LEN, IVC_COMPACT_NOALLOC_MAX_TILES);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (h->dev >= 0 && h->dev < kMaxDevices) ws = g_scratch_ptr[h->dev];
+  }
+  if (ws == nullptr)
+    return fail(IVC_ERR_HIP, "compact_noalloc: no scratch address for device %d (%s)", h->dev,
+                hipGetErrorString(h->dev >= 0 && h->dev < kMaxDevices ? g_scratch_err[h->dev]
+                                                                      : hipErrorInvalidDevice));
+  if (plan_compact(IVC_COMPACT_NOALLOC_MAX_TILES, IVC_COMPACT_NOALLOC_MAX_LEN, nullptr, nullptr) >
+      sizeof(scratch))
+    return fail(IVC_ERR_WORKSPACE, "compact_noalloc: scratch smaller than its stated maximum");
+  return compact_impl(h, ids, embeds, L, img_context_id, use64, out256, out64, T, out_ids, out_pos,
+                      keep_map, out_embeds, out_len, dev_status, ws, sizeof(scratch), stream);
 }
 
 extern "C" size_t ivc_connector_compact_batch_workspace_bytes(const ivc_connector* h,
