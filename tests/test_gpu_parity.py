@@ -480,7 +480,8 @@ def _check_routed(con, cfg, xd, use_d):
     torch.cuda.synchronize()
     keep256 = torch.from_numpy(use == 0).cuda()
     keep64 = torch.from_numpy(use != 0).cuda()
-    # chosen path: bit-identical to the full run (same K order per output element)
+    # chosen path: bit-identical to the full run (same K order per output
+    # element: a Flash connector's products keep one tile per workgroup)
     assert torch.equal(r256[keep256], f256[keep256])
     assert torch.equal(r64[keep64], f64[keep64])
     # other path: untouched

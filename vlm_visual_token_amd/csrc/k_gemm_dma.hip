@@ -59,6 +59,17 @@ namespace {
 constexpr int DBM = 256, DBN = 256, DNT = 512;  // tile rows, columns; threads
 constexpr int QB = 32768;  // bytes of one stage array (also one epilogue slab of 64 rows)
 
+// Output tile t of the band order: bands of 8 tile rows, each walked column
+// by column, so tiles with nearby indices share A and W panels.
+IVC_DEV void band_tile(int t, int tiles_m, int tiles_n, int& m0, int& n0) {
+  constexpr int GM = 8;
+  const int in_group = GM * tiles_n;
+  const int first_m = (t / in_group) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  m0 = (first_m + (t % in_group) % gsize) * DBM;
+  n0 = ((t % in_group) / gsize) * DBN;
+}
+
 // Tile of this workgroup; false if it has none (uniform, before any barrier).
 IVC_DEV bool map_tile(int& M, int N, const RowMap& rm, int& m0, int& n0) {
   if (rm.m_dev != nullptr) M = min(M, *rm.m_dev * rm.m_mult);
@@ -67,12 +78,7 @@ IVC_DEV bool map_tile(int& M, int N, const RowMap& rm, int& m0, int& n0) {
   if ((int)blockIdx.x >= nb) return false;
   int bid = blockIdx.x;
   if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);  // consecutive ids on one XCD
-  constexpr int GM = 8;
-  const int in_group = GM * tiles_n;
-  const int first_m = (bid / in_group) * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  m0 = (first_m + (bid % in_group) % gsize) * DBM;
-  n0 = ((bid % in_group) / gsize) * DBN;
+  band_tile(bid, tiles_m, tiles_n, m0, n0);
   return true;
 }
 
@@ -283,8 +289,8 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
 // order, so the wait at a step's top lets A's newest step stay in flight.
 template <bool FOLD>
 IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma& d, const Stages& st,
-                         int w, int wm, int wn, int lane) {
-  const int n = o.K / BK;
+                         int k0, int k1, int w, int wm, int wn, int lane) {
+  const int n = k1 - k0;  // K steps k0 .. k1 - 1 (the step counter s below runs from 0)
   auto dma_a = [&](int j, uint32_t ka, char* sa) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.a_rs, (lds_void_t*)(sa + (w * 4 + j) * 1024), 16,
                                              d.a_off[j], ka, 0, 0);
@@ -307,7 +313,12 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
   }
   // byte offset of A's next K step to issue (FOLD: each step of 64 lies
   // inside one C-wide cell; the cell's grid offset comes from gather_koff)
-  int cell_n = 0, c0_n = 0;
+  int cell_n = 0, c0_n = k0 * BK;  // (cell, channel) of K step k0 (plain A: c0_n is the K element)
+  if (FOLD) {
+    cell_n = c0_n / o.ag.C;
+    c0_n -= cell_n * o.ag.C;
+  }
+  const uint32_t kb0 = (uint32_t)(k0 * (BK * 2));  // W's byte offset of step k0
   auto a_koff = [&]() -> uint32_t {
     const uint32_t k = FOLD ? (uint32_t)gather_koff(o.ag, cell_n, c0_n) : (uint32_t)(c0_n * 2);
     c0_n += BK;
@@ -321,11 +332,13 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
   // prologue: A and W of step 0, then A of step 1, in the order the steady
   // state's steps leave their DMAs (W, then A) so that the compiler's count
   // of DMAs in flight agrees at the loop's entry and back edge
+  {
+    const uint32_t ka = a_koff();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma_a(j, 0, st.sa0);
+    for (int j = 0; j < 4; ++j) dma_a(j, ka, st.sa0);
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma_b(j, 0, st.sb0);
-  (void)a_koff();
+  for (int j = 0; j < 4; ++j) dma_b(j, kb0, st.sb0);
   if (n > 1) {
     const uint32_t ka = a_koff();
 #pragma unroll
@@ -360,7 +373,7 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
     char* nb = JB == 0 ? st.sb0 : st.sb1;
     const bool more_a = FULL || s + NA - 1 < n, more_b = FULL || s + NB - 1 < n;
     const uint32_t ka = more_a ? a_koff() : 0;
-    const uint32_t kb = (uint32_t)((s + NB - 1) * (BK * 2));
+    const uint32_t kb = kb0 + (uint32_t)((s + NB - 1) * (BK * 2));
     // operands of step s complete; A's step s + 1 may still be in flight
     // (issued last, one step ago)
     if (FULL || s + 1 < n)
@@ -432,26 +445,171 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
 }
 
 // ---------------------------------------------------------------------------
-// One output tile per workgroup.
+// Leftover tiles.  A product of NT tiles on G compute units runs
+// floor(NT / G) whole rounds plus a partial one in which most CUs can sit
+// idle (mlp2's first product on the 2B-Flash workload: 416 tiles on 256 CUs,
+// the second round 160 tiles; that round costs as much as a full one).  With
+// TailSplit scratch the whole rounds stay one tile per workgroup and each of
+// the r leftover tiles is cut along K into s pieces (gemm_tail_split: the
+// fewest rounds of pieces times piece length; 160 tiles: 3 pieces, two
+// rounds of a third).  Every piece stores its fp32 partial tile, then counts
+// itself in the tile's counter; the piece that counts last adds all s
+// partials in piece order (so the result does not depend on arrival order)
+// and runs the epilogue.  No workgroup waits on another.  Partials and
+// counters are device-coherent (sc1) accesses, so nothing is flushed; a
+// counter holds (launch ticket << 8) | pieces done, so stale values from
+// earlier launches need no clearing.
+// ---------------------------------------------------------------------------
+struct TailSplit {
+  float* part;                // [2 G][128 * 512] fp32 partial tiles (slot per piece)
+  unsigned long long* cnt;    // [G] per leftover tile
+  unsigned long long ticket;  // this launch's tag, nonzero, < 2^56
+  int G;                      // workgroups of a whole round (a multiple of 8)
+};
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int CPOL_SC1 = 16;  // device-coherent load / store
+
+// A scalar zero the compiler cannot see through: the 32 piece offsets of a
+// partial tile built on it are formed where used, not hoisted to the
+// kernel's entry as 32 live scalar registers.
+IVC_DEV int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  return z;
+}
+
+// Partial slot i: 16-byte piece q of thread tid at (q * 512 + tid) * 16, so
+// each store or load instruction covers 1 KB contiguous.
+IVC_DEV __amdgpu_buffer_rsrc_t part_slot(float* part, int i) {
+  return __builtin_amdgcn_make_buffer_rsrc(part + (size_t)i * (128 * DNT), (short)0,
+                                           128 * DNT * 4, 0x00020000);
+}
+
+// Counts one more finished piece of a leftover tile; returns how many had
+// finished before it.
+IVC_DEV int piece_arrive(unsigned long long* c, unsigned long long ticket) {
+  unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {  // at most s contenders: every failed exchange means another one succeeded
+    const bool ours = (cur >> 8) == ticket;
+    const unsigned long long nv = ours ? cur + 1 : ((ticket << 8) | 1ull);
+    if (__hip_atomic_compare_exchange_strong(c, &cur, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return ours ? (int)(cur & 0xff) : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The product: one output tile (or, for leftover tiles, one K piece of one)
+// per workgroup.
 // ---------------------------------------------------------------------------
 template <int ACT, bool FOLD>
 __global__ void __launch_bounds__(DNT, 1)
 k_gemm_dma8(GemmOps o, const float* __restrict__ bias, bf16_t* __restrict__ Cm, long long ldc,
-            RowMap rm, const float* __restrict__ ln_rows, const float* __restrict__ ln_colsum) {
+            RowMap rm, const float* __restrict__ ln_rows, const float* __restrict__ ln_colsum,
+            TailSplit ts) {
   __shared__ __attribute__((aligned(1024))) char sA0[QB];
   __shared__ __attribute__((aligned(1024))) char sB0[QB];
   __shared__ __attribute__((aligned(1024))) char sA1[QB];
   __shared__ __attribute__((aligned(1024))) char sB1[QB];
   __shared__ __attribute__((aligned(1024))) char sA2[QB];  // also the folded epilogue's row statistics
-  int m0, n0;
-  if (!map_tile(o.M, o.N, rm, m0, n0)) return;
-  const int lane = threadIdx.x & 63;
+  int m0, n0, k0 = 0, k1 = o.K / BK, tt = -1, s = 1, piece = 0;
+  {
+    int M = o.M;
+    if (ts.part != nullptr && rm.m_dev != nullptr) M = min(M, *rm.m_dev * rm.m_mult);
+    const int tiles_m = (M + DBM - 1) / DBM, tiles_n = (o.N + DBN - 1) / DBN;
+    const int NT = tiles_m * tiles_n, KT = k1;
+    const int q = ts.part != nullptr ? NT / ts.G : 0, r = NT - q * ts.G;
+    if (ts.part != nullptr && r > 0) s = gemm_tail_split(r, ts.G, KT);
+    if (s == 1) {  // nothing split: one tile per workgroup
+      if (!map_tile(o.M, o.N, rm, m0, n0)) return;
+    } else {
+      o.M = M;
+      const int full = q * ts.G, bid = blockIdx.x;
+      int t;
+      if (bid < full) {
+        t = (bid & 7) * (full >> 3) + (bid >> 3);  // consecutive tiles on one XCD
+      } else {
+        int p = bid - full;
+        const int np = r * s;
+        if (p >= np) return;
+        // pieces XCD-major too: an XCD runs the same K piece of neighbouring tiles
+        if ((np & 7) == 0) p = (p & 7) * (np >> 3) + (p >> 3);
+        tt = p % r;
+        piece = p / r;
+        t = full + tt;
+        k0 = KT * piece / s;
+        k1 = KT * (piece + 1) / s;
+      }
+      band_tile(t, tiles_m, tiles_n, m0, n0);
+    }
+  }
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0..7
   const int wm = w >> 2, wn = w & 3;  // rows wm*128 .., columns wn*64 ..
   const TileDma d = tile_dma<FOLD>(o, m0, n0, w, lane);
   const Stages st{sA0, sA1, sA2, sB0, sB1};
   f32x16_t acc[4][2];
-  tile_ksteps<FOLD>(acc, o, d, st, w, wm, wn, lane);
+  tile_ksteps<FOLD>(acc, o, d, st, k0, k1, w, wm, wn, lane);
+  if (tt >= 0) {
+    // a piece of a leftover tile: store the partial, count in
+    {
+      const __amdgpu_buffer_rsrc_t slot = part_slot(ts.part, tt * s + piece);
+      const int zs = opaque_zero();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4_t v = {acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                               acc[i][j][4 * v4 + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, slot, tid * 16,
+                                                   zs + ((i * 2 + j) * 4 + v4) * (DNT * 16),
+                                                   CPOL_SC1);
+          }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every wave's stores complete before the count
+    __syncthreads();
+    // the verdict goes through the third A stage (free now; the LDS is full)
+    int* last_piece = reinterpret_cast<int*>(sA2);
+    if (tid == 0) *last_piece = piece_arrive(ts.cnt + tt, ts.ticket) == s - 1;
+    __syncthreads();
+    if (!*last_piece) return;
+    // the last piece: all s partials, in piece order
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float z;
+          asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+          acc[i][j][v] = z;
+        }
+    for (int pc = 0; pc < s; ++pc) {
+      const __amdgpu_buffer_rsrc_t slot = part_slot(ts.part, tt * s + pc);
+      const int zs = opaque_zero();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f32x4_t pv[4];
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            pv[v4] = __builtin_amdgcn_raw_buffer_load_b128(
+                slot, tid * 16, zs + ((i * 2 + j) * 4 + v4) * (DNT * 16), CPOL_SC1);
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            acc[i][j][4 * v4] += pv[v4].x;
+            acc[i][j][4 * v4 + 1] += pv[v4].y;
+            acc[i][j][4 * v4 + 2] += pv[v4].z;
+            acc[i][j][4 * v4 + 3] += pv[v4].w;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  }
   __syncthreads();
   store_tile<ACT, FOLD, 2, DNT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, o.M, o.N, bias, Cm, ldc,
                                 rm, ln_rows, ln_colsum, reinterpret_cast<float2*>(sA2));
@@ -523,9 +681,23 @@ hipError_t launch_gemm_dma(const GemmArgs& g, hipStream_t s) {
   GemmOps o{(const bf16_t*)g.A, g.lda, g.a_rpg, g.a_gstride, g.a_goff, (const bf16_t*)g.W, g.ldw,
             g.M, g.N, g.K, g.ag};
   const int tiles = ((g.M + DBM - 1) / DBM) * ((g.N + DBN - 1) / DBN);
+  TailSplit ts{nullptr, nullptr, 0, 0};
+  int grid = tiles;
+  if (g.tail_part != nullptr) {
+    if (g.tail_grid <= 0 || g.tail_grid % 8 != 0 || g.tail_cnt == nullptr || g.tail_ticket == 0 ||
+        (g.tail_ticket >> 56) != 0)
+      return hipErrorInvalidValue;
+    ts = TailSplit{g.tail_part, g.tail_cnt, g.tail_ticket, g.tail_grid};
+    if (g.rm.m_dev == nullptr) {  // the tile count is known: exactly the workgroups needed
+      const int q = tiles / g.tail_grid, r = tiles - q * g.tail_grid;
+      grid = q * g.tail_grid + (r > 0 ? r * gemm_tail_split(r, g.tail_grid, g.K / BK) : 0);
+    } else {  // an upper bound: the pieces add at most 2 G - r workgroups
+      grid = tiles + 2 * g.tail_grid;
+    }
+  }
 #define IVC_DMA_LAUNCH(ACTV, FOLDV)                                                            \
-  hipLaunchKernelGGL((k_gemm_dma8<ACTV, FOLDV>), dim3((unsigned)tiles), dim3(DNT), 0, s, o, g.bias, \
-                     (bf16_t*)g.Cm, g.ldc, g.rm, g.ln_rows, g.ln_colsum)
+  hipLaunchKernelGGL((k_gemm_dma8<ACTV, FOLDV>), dim3((unsigned)grid), dim3(DNT), 0, s, o, g.bias, \
+                     (bf16_t*)g.Cm, g.ldc, g.rm, g.ln_rows, g.ln_colsum, ts)
   if (g.fold)
     IVC_DMA_LAUNCH(ACT_GELU, true);
   else if (g.act == ACT_GELU)

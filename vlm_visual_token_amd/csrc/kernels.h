@@ -99,7 +99,42 @@ struct GemmArgs {
   AGather ag;
   const float* ln_rows = nullptr;
   const float* ln_colsum = nullptr;
+  // leftover tiles cut along K (DMA kernels): tail_grid = workgroups of a
+  // whole round (a multiple of 8); tail_part / tail_cnt: scratch of
+  // gemm_tail_bytes(tail_grid) bytes (partials, then counters), not shared
+  // with a product running at the same time; tail_ticket: nonzero, < 2^56,
+  // different from every earlier launch's.  tail_part null: one tile per
+  // workgroup throughout.
+  float* tail_part = nullptr;
+  unsigned long long* tail_cnt = nullptr;
+  unsigned long long tail_ticket = 0;
+  int tail_grid = 0;
 };
+
+// K pieces for each of r leftover tiles (those past the last whole round of
+// G tiles) of a product with KT K steps: the fewest rounds of pieces times
+// the piece length, at most 4 pieces of at least 32 K steps each (a shorter
+// piece does not earn back its pipeline fill and its partial tile's store
+// and load: measured slower at 16-21 steps), at most two rounds of pieces
+// (r * s <= 2 G), and only for a gain of 5% or more.
+__host__ __device__ inline int gemm_tail_split(int r, int G, int KT) {
+  float best = 1.0f;
+  int bs = 1;
+  for (int s = 2; s <= 4; ++s) {
+    if (KT < 32 * s || r * s > 2 * G) break;
+    const float cost = (float)((r * s + G - 1) / G) / (float)s;
+    if (cost < best * 0.95f) {
+      best = cost;
+      bs = s;
+    }
+  }
+  return bs;
+}
+// Scratch of the leftover-tile pieces: 2 G partial tiles of 256 x 256 fp32,
+// then G counters.
+inline size_t gemm_tail_bytes(int G) {
+  return (size_t)2 * G * 256 * 256 * 4 + (size_t)G * 8;
+}
 // bf16 A and W, fp32 accumulation on MFMA, bf16 out.  Needs K % 64 == 0.
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t s);
 bool gemm_mfma_supported(const GemmArgs& g);
