@@ -351,10 +351,12 @@ ivc_status ivc_pixel_shuffle(int32_t dtype, const void* vit, int32_t T, int32_t 
                              int32_t shuffle64_order, void* out, void* stream);
 
 /* Per-kernel timing for measurement: when enabled, the library records a
- * hipEvent pair around each kernel it launches on the call's stream and
- * accumulates the elapsed time per kernel name after the events complete.
- * While enabled, run and run_routed keep both projector chains on the call's
- * stream (no fork), so each kernel is timed alone.
+ * hipEvent pair around each kernel it launches, on the stream it launches it
+ * on, and accumulates the elapsed time per kernel name after the events
+ * complete.  on = 1: run and run_routed keep both projector chains on the
+ * call's stream (no fork), so each kernel is timed alone; on = 2: the chains
+ * keep their two streams, as with timing off, so each span is that of the
+ * kernel beside whatever the other chain runs meanwhile; 0: off.
  * ivc_profile_read synchronises the recorded events, then returns up to
  * `cap` entries (name, total ms, launches).  Not thread-safe; off by default. */
 void ivc_profile_enable(int on);

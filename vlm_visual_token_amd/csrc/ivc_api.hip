@@ -80,6 +80,7 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 bool g_prof_on = false;
+bool g_prof_keep_fork = false;  // mode 2: the projector chains keep their two streams
 std::vector<ProfRec> g_prof_pending;
 std::vector<hipEvent_t> g_prof_free;
 std::vector<std::string> g_prof_names;
@@ -131,7 +132,10 @@ static void prof_collect() {
   g_prof_pending.clear();
 }
 
-extern "C" void ivc_profile_enable(int on) { g_prof_on = on != 0; }
+extern "C" void ivc_profile_enable(int on) {
+  g_prof_on = on != 0;
+  g_prof_keep_fork = on == 2;
+}
 extern "C" void ivc_profile_reset(void) {
   prof_collect();
   g_prof_names.clear();
@@ -906,7 +910,7 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   // share one SIMT scratch buffer.)
   // (While per-kernel timing is on, both chains stay on the caller's stream so
   // each kernel's events time it alone.)
-  const bool fork = c.flash && h->aux != nullptr && !g_prof_on;
+  const bool fork = c.flash && h->aux != nullptr && (!g_prof_on || g_prof_keep_fork);
   hipStream_t s1 = s;
   if (fork) {
     HIP_OK(hipEventRecord(h->ev_fork, s));
@@ -1129,7 +1133,8 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       // of a tile's partials happens in its operand load)
       const bool merged_value = dt == IVC_BF16 && fold_value_merged_max_parts(T, N, fQ) <= 4;
       fa.xbar = merged_value ? nullptr : w.xbar;
-      LAUNCH("pool_folded", s, launch_pool_folded(fa, s));
+      // the first layer's pass also writes per-token LayerNorm moments: timed apart
+      LAUNCH(fa.tokst ? "pool_folded_stats" : "pool_folded", s, launch_pool_folded(fa, s));
       if (merged_value) {
         LAUNCH("pool_fold_value", s,
                launch_fold_value_merged(w.part, valid_tokens, N, fQ, fseg, wv, h->lr, bv, w.o, T,

@@ -301,8 +301,10 @@ def ivc_pixel_shuffle(dtype, vit, T, P, C, has_cls, r, out, stream=None, ps_vers
                                     _stream(stream)), "ivc_pixel_shuffle")
 
 
-def ivc_profile_enable(on: bool) -> None:
-    load().ivc_profile_enable(1 if on else 0)
+def ivc_profile_enable(on) -> None:
+    """False/0: off; True/1: per-kernel events, projector chains on one stream;
+    2: per-kernel events, chains on their two streams."""
+    load().ivc_profile_enable(int(on))
 
 
 def ivc_profile_reset() -> None:
