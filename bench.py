@@ -104,6 +104,9 @@ def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
             "gate_ln_fc1": dict(flops=None, bytes=G * cfg["gate_hidden"] * e),
             "gate_fc1": dict(flops=None, bytes=G * cfg["gate_hidden"] * e),
             "gate_fc2": dict(flops=None, bytes=G * cfg["gate_hidden"] * e),
+            # the one-launch Gating: the pooling's last output projection and
+            # the eight block products stream their weights once
+            "gating": dict(flops=None, bytes=(C * C + 8 * G * cfg["gate_hidden"]) * e),
             "compact": dict(flops=None, bytes=2 * Lp * D * e + L_seq * 4 * 2 + Lp * 4 * 2),
         })
     return out
@@ -539,6 +542,7 @@ LAUNCH_FAMILY = {
     "gate_fc1": ("k_gemm",), "gate_ln_fc1": ("k_gemm_f32a", "k_f32a_ln_rows"),
     "gate_fc2": ("k_gemm",), "gate_res_ln": ("k_residual_ln", "k_f32a_ln_rows"),
     "gate_res_ln_head": ("k_residual_ln", "k_f32a_ln_rows"),
+    "gating": ("k_gating_fused",),
     "quantile_decide": ("k_quantile_decide",), "route_lists": ("k_route_lists",),
     "compact": ("k_compact_count", "k_set_i64"), "compact_batch": ("k_compact_count",),
 }

@@ -87,6 +87,8 @@ typedef enum { IVC_SHUFFLE64_DIRECT = 0, IVC_SHUFFLE64_TWICE_R2 = 1 } ivc_shuffl
 #define IVC_DEV_ERR_VALID_TOKENS 2 /* a valid_tokens[t] outside [1, P*P]        */
 #define IVC_DEV_ERR_TILE_COUNT 4   /* a tiles_per_image[i] < 0, or sum > INT32_MAX */
 #define IVC_DEV_ERR_SEQ_LAYOUT 8   /* batch: cu_seqlens / tile_offsets not an ordered partition */
+#define IVC_DEV_ERR_ROUTER_SYNC 16 /* route: a phase of the one-launch Gating waited past
+                                      its bound (a few seconds); gates undefined   */
 
 #define IVC_MAX_POOL_LAYERS 8
 #define IVC_GATE_BLOCKS 4

@@ -64,6 +64,23 @@ IVC_DEV u32x4 pack16(const float* f, bf16_t*) {
 }
 template <typename E> IVC_DEV u32x4 pack(const float* f) { return pack16(f, (E*)nullptr); }
 
+// ---- write-through stores ---------------------------------------------------
+// For data that workgroups of one launch hand to each other across XCDs:
+// relaxed device-scope atomic stores, which the memory system performs at
+// the device's coherence point (nothing left behind in one XCD's L2).
+IVC_DEV void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+IVC_DEV void st_coh4(float* p, float4 v) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+  __hip_atomic_store(q, (unsigned long long)__float_as_uint(v.x) |
+                            ((unsigned long long)__float_as_uint(v.y) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (unsigned long long)__float_as_uint(v.z) |
+                                ((unsigned long long)__float_as_uint(v.w) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- wavefront reductions (64 lanes) ---------------------------------------
 IVC_DEV float wave_sum(float v) {
 #pragma unroll

@@ -45,6 +45,13 @@ static bool trace_on() {
   }();
   return on;
 }
+// True when the variable is set to "0" (read at every call, so a process can
+// switch between forms for comparison).
+static bool env_off(const char* name) {
+  const char* e = getenv(name);
+  return e != nullptr && strcmp(e, "0") == 0;
+}
+
 #define TRACE(...)                          \
   do {                                      \
     if (trace_on()) {                       \
@@ -464,6 +471,9 @@ size_t plan_run(const ivc_connector* h, int T, void* base, RunWs* w) {
 struct RouteWs {
   void *kv, *qt_hi, *qt_lo;
   float *q, *qp, *o, *part, *xbar, *y1, *y2, *x, *x2;
+  // one-launch Gating: further per-phase row buffers and the phase counters
+  float *y1b[3], *y2b[3], *x3;
+  unsigned long long* sync;
   SimtScratch sc;
 };
 size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
@@ -492,6 +502,12 @@ size_t plan_route(const ivc_connector* h, int T, void* base, RouteWs* w) {
   r.y2 = (float*)cv.take((size_t)T * hh * 4);
   r.x = (float*)cv.take((size_t)T * hh * 4);
   r.x2 = (float*)cv.take((size_t)T * hh * 4);
+  for (int i = 0; i < 3; ++i) {
+    r.y1b[i] = (float*)cv.take((size_t)T * he * 4);
+    r.y2b[i] = (float*)cv.take((size_t)T * hh * 4);
+  }
+  r.x3 = (float*)cv.take((size_t)T * hh * 4);
+  r.sync = (unsigned long long*)cv.take(gating_fused_sync_words(T) * sizeof(unsigned long long));
   r.sc.need(T, (int)C, (int)C, 1);
   r.sc.need(T, (int)he, (int)hh, 1);
   r.sc.need(T, (int)hh, (int)he, 1);
@@ -1048,6 +1064,11 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     LAUNCH("pool_kv_gemm", s, gemm("pool_kv_gemm", kv, s));
   }
 
+  // The pooling's last output projection and the Gating network in one
+  // launch (IVC_GATING_FUSED=0 selects the launch-per-product form, which
+  // does the same arithmetic).
+  const bool gate1 = dt == IVC_BF16 && gating_fused_supported(T, (int)hh, (int)he) &&
+                     hh == C && !env_off("IVC_GATING_FUSED");
   // query projection and key fold in one launch where the shape allows it;
   // its first layer reads the learned query as a row of stride 0 for every tile
   const bool fq_fused = c.pool_mode == IVC_POOL_FOLDED && h->wkT != nullptr &&
@@ -1173,7 +1194,7 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     }
     // the output projection, unless the next layer's query fold reads o itself
     // through the folded weights (only the last layer's q, the pooled vector, is formed)
-    if (!(fq_fused && l + 1 < L && h->wqo_hi[l + 1] != nullptr)) {
+    if (!(fq_fused && l + 1 < L && h->wqo_hi[l + 1] != nullptr) && !(gate1 && l == L - 1)) {
       float* qn = (l == L - 1 && pooled) ? pooled : w.q;
       LAUNCH("pool_o_proj", s, gemm("pool_o_proj",
                                    rgemm(w.o, C, h->wo[l], h->lr, h->bo[l], qn, T, C, C, ACT_NONE),
@@ -1184,7 +1205,45 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
 
   // Gating: x = pooled; 4 x (x += LN(W2 GELU(W1 x + b1) + b2)); softmax(Wc x + bc)
   static_assert(IVC_GATE_BLOCKS >= 2, "the gating chain below alternates two row buffers");
-  if (dt == IVC_BF16 && f32a_ln_rows_supported(hh)) {
+  if (gate1) {
+    static_assert(IVC_GATE_BLOCKS == 4, "the one-launch Gating runs four blocks");
+    GatingFusedArgs ga;
+    ga.o = w.o;
+    ga.wo = (const uint16_t*)h->wo[L - 1];
+    ga.ldwo = h->lr;
+    ga.bo = h->bo[L - 1];
+    ga.xb[0] = const_cast<float*>(pooled_v);
+    ga.xb[1] = w.x;
+    ga.xb[2] = w.x2;
+    ga.xb[3] = w.x3;
+    ga.y1[0] = w.y1;
+    ga.y2[0] = w.y2;
+    for (int i = 0; i < 3; ++i) {
+      ga.y1[i + 1] = w.y1b[i];
+      ga.y2[i + 1] = w.y2b[i];
+    }
+    for (int b = 0; b < 4; ++b) {
+      ga.w1[b] = (const uint16_t*)h->g_w1[b];
+      ga.w2[b] = (const uint16_t*)h->g_w2[b];
+      ga.b1[b] = h->g_b1[b];
+      ga.b2[b] = h->g_b2[b];
+      ga.lw[b] = h->g_lw[b];
+      ga.lb[b] = h->g_lb[b];
+    }
+    ga.ldw1 = h->lg1;
+    ga.ldw2 = h->lg2;
+    ga.wc = (const uint16_t*)h->g_cw;
+    ga.bc = h->g_cb;
+    ga.gate = gate;
+    ga.T = T;
+    ga.h = (int)hh;
+    ga.he = (int)he;
+    ga.eps = c.ln_eps;
+    ga.sync = w.sync;
+    ga.tag = next_ticket() & 0xffffffffffffull;
+    ga.status = dev_status;
+    LAUNCH("gating", s, launch_gating_fused(ga, s));
+  } else if (dt == IVC_BF16 && f32a_ln_rows_supported(hh)) {
     // block b > 0 takes block b-1's residual LayerNorm into its first Linear's
     // prologue (rows alternate between two buffers; block 0 reads the pooled
     // rows in place); the last block's LayerNorm runs with the classifier head

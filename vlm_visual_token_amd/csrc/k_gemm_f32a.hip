@@ -17,6 +17,7 @@
 // round of load latency; then the eight partial tiles are added in a fixed
 // order through LDS: results do not depend on timing.
 #include "common.h"
+#include "gate_rows.h"
 #include "kernels.h"
 
 namespace ivc {
@@ -152,7 +153,17 @@ IVC_DEV void f32a_mainloop(const ARow<NS> (&arow)[MB], const bf16_t* const (&wro
 // steps loaded per wave at once: the main loop, then the NWV partial tiles
 // summed through LDS in wave order, bias, activation and the store.
 // OUT: 0 = fp32 C, 1 = C * scale as bf16 high part (Cm) and low part (C2).
-template <int MB, int NB, int NWV, int PD, int ACT, int OUT, int NS>
+// The partial-tile buffer of f32a_tile: one array per size, so the tile
+// functions of every instance in one kernel share it.
+template <int NF>
+IVC_DEV float* f32a_red_lds() {
+  __shared__ __attribute__((aligned(16))) float red[NF];
+  return red;
+}
+
+// CCOH: write-through stores of C (read by workgroups of the same launch on
+// other XCDs).
+template <int MB, int NB, int NWV, int PD, int ACT, int OUT, int NS, bool CCOH = false>
 IVC_DEV void f32a_tile(const ARow<NS> (&arow)[MB], const bf16_t* __restrict__ W, long long ldw,
                        const float* __restrict__ bias, void* __restrict__ Cm,
                        void* __restrict__ C2, long long ldc, int M, int N, int K, float scale,
@@ -160,7 +171,7 @@ IVC_DEV void f32a_tile(const ARow<NS> (&arow)[MB], const bf16_t* __restrict__ W,
   constexpr int BM = 16 * MB, BN = 16 * NB, LDR = BN + 4;
   constexpr int NTH = NWV * 64, RPP = NTH / BN;  // epilogue rows per pass
   static_assert(NTH % BN == 0 && BM % RPP == 0, "epilogue shape");
-  __shared__ __attribute__((aligned(16))) float red[NWV][BM][LDR];
+  float(*red)[BM][LDR] = reinterpret_cast<float(*)[BM][LDR]>(f32a_red_lds<NWV * BM * LDR>());
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo16 = lane & 15, hi4 = lane >> 4;
@@ -197,7 +208,10 @@ IVC_DEV void f32a_tile(const ARow<NS> (&arow)[MB], const bf16_t* __restrict__ W,
     if (ACT == ACT_GELU) v = gelu_erf(v);
     const long long o = (long long)m * ldc + n;
     if (OUT == 0) {
-      reinterpret_cast<float*>(Cm)[o] = v;
+      if (CCOH)
+        st_coh(reinterpret_cast<float*>(Cm) + o, v);
+      else
+        reinterpret_cast<float*>(Cm)[o] = v;
     } else {
       v *= scale;
       const bf16_t h = f32_to_bf16(v);
@@ -485,17 +499,20 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
 // wave-reduced), the workgroups of the first column block also write them to
 // x_out (x_in and x_out must differ: the others still read x_in), and the
 // product reads its activation rows from LDS.
-template <int ACT>
-__global__ void __launch_bounds__(512)
-k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
-               const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
-               float* __restrict__ x_out, const bf16_t* __restrict__ W, long long ldw,
-               const float* __restrict__ bias, float* __restrict__ Cm, int M, int N, int K) {
+// One (16-row, 64-column) tile; store_x: this tile writes its rows of x_out.
+// COH: write-through stores of x_out and C (read by workgroups of the same
+// launch on other XCDs).
+template <int ACT, bool COH = false>
+IVC_DEV void ln_rows_tile(const float* __restrict__ x_in, const float* __restrict__ y,
+                          const float* __restrict__ gamma, const float* __restrict__ beta,
+                          float eps, float* __restrict__ x_out, bool store_x,
+                          const bf16_t* __restrict__ W, long long ldw,
+                          const float* __restrict__ bias, float* __restrict__ Cm, int M, int N,
+                          int K, int m0, int n0) {
   __shared__ __attribute__((aligned(16))) float xs[16 * 1024];  // [16][K], K <= 1024
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo16 = lane & 15, hi4 = lane >> 4;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
   const int vpl = K / 256;  // float4 vectors per lane (K % 256 == 0, K <= 1024)
   // both rows' y, x, gamma and beta loaded up front (one round of latency)
   float4 v[2][4], xv[2][4], gv[4], bv[4];
@@ -549,15 +566,30 @@ k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
         o.z = x.z + (v[rr][i].z - mean) * rstd * g.z + b.z;
         o.w = x.w + (v[rr][i].w - mean) * rstd * g.w + b.w;
         reinterpret_cast<float4*>(xs + r * K)[j] = o;
-        if (blockIdx.x == 0 && m0 + r < M)
-          reinterpret_cast<float4*>(x_out + (long long)tr[rr] * K)[j] = o;
+        if (store_x && m0 + r < M) {
+          if (COH)
+            st_coh4(x_out + (long long)tr[rr] * K + 4 * j, o);
+          else
+            reinterpret_cast<float4*>(x_out + (long long)tr[rr] * K)[j] = o;
+        }
       }
     }
   }
   __syncthreads();
   ARow<1> arow[1];
   arow[0].p[0] = xs + lo16 * K + 8 * hi4;
-  f32a_tile<1, 4, 8, 4, ACT, 0, 1>(arow, W, ldw, bias, Cm, nullptr, N, M, N, K, 1.f, m0, n0);
+  f32a_tile<1, 4, 8, 4, ACT, 0, 1, COH>(arow, W, ldw, bias, Cm, nullptr, N, M, N, K, 1.f, m0,
+                                        n0);
+}
+
+template <int ACT>
+__global__ void __launch_bounds__(512)
+k_f32a_ln_rows(const float* __restrict__ x_in, const float* __restrict__ y,
+               const float* __restrict__ gamma, const float* __restrict__ beta, float eps,
+               float* __restrict__ x_out, const bf16_t* __restrict__ W, long long ldw,
+               const float* __restrict__ bias, float* __restrict__ Cm, int M, int N, int K) {
+  ln_rows_tile<ACT>(x_in, y, gamma, beta, eps, x_out, blockIdx.x == 0, W, ldw, bias, Cm, M, N,
+                    K, blockIdx.y * 16, blockIdx.x * 64);
 }
 
 bool f32a_ln_rows_supported(int K) { return K % 256 == 0 && K >= 256 && K <= 1024; }
@@ -686,6 +718,155 @@ hipError_t launch_zero_heads(void* qt_hi, void* qt_lo, int T, int H, int C, hipS
   if (T <= 0 || H >= 16) return hipSuccess;
   hipLaunchKernelGGL(k_zero_heads, dim3(8, (unsigned)T), dim3(256), 0, s, (bf16_t*)qt_hi,
                      (bf16_t*)qt_lo, H, C);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The Gating network (InternVL3_5-4B-Flash Gating and CrossAttentionPooling
+// page, section 3) and, before it, the pooling's last output projection, in
+// one launch.  Its phases are the launches of the per-block form, with the
+// same tile functions and so the same arithmetic:
+//   [out-projection]  x0 = o . Wo^T + bo                       (the pooled rows)
+//   block 0           y1_0 = GELU(x0 . W1^T + b1);  y2_0 = y1_0 . W2^T + b2
+//   block b = 1..3    x_b = x_{b-1} + LN(y2_{b-1}) (prologue);
+//                     y1_b = GELU(x_b . W1^T + b1);  y2_b = y1_b . W2^T + b2
+//   head              x = x_3 + LN(y2_3);  gate = softmax(Wc x + bc)
+// Consecutive ranges of workgroups run consecutive phases, one (16-row,
+// 64-column) tile or one head row each.  A tile needs only its own 16 rows of
+// the previous phase, so each phase keeps one device-scope counter per
+// 16-row block (each on a line and memory channel of its own, so the polls of
+// waiting workgroups do not queue behind one another); a workgroup waits
+// until its block's counter in the previous phase is full (rows of later
+// blocks can run ahead).
+// Coherence across the XCDs' L2 caches without cache-wide write-back or
+// invalidation: every phase writes a buffer of its own with write-through
+// stores and counts itself done once they are acknowledged; the readers'
+// plain loads cannot hit a stale line, since no XCD reads a block before it
+// is complete and the launch starts with invalidated caches.
+// Progress: workgroups are dispatched in index order on each XCD and every
+// wait is for lower-indexed workgroups, so the lowest unfinished workgroup
+// always runs.  A wait still gives up after a few seconds and reports
+// IVC_DEV_ERR_ROUTER_SYNC rather than hang.  The counters carry the launch's
+// tag in their high bits: values an earlier launch (or uninitialised
+// workspace) left there never count.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Adds one to a tagged counter: the first caller of a launch finds another
+// tag there and resets the count under this launch's tag (only one such
+// exchange succeeds).
+IVC_DEV void tagged_count(unsigned long long* c, unsigned long long tag) {
+  unsigned long long cur = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((cur >> 16) != tag) {
+    if (__hip_atomic_compare_exchange_strong(c, &cur, tag << 16, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      break;
+  }
+  __hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+IVC_DEV void phase_wait(const unsigned long long* c, unsigned long long want, int* status) {
+  for (int spin = 0;; ++spin) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) break;
+    if (spin >= (1 << 23)) {
+      if (status != nullptr) atomicOr(status, 16);  // IVC_DEV_ERR_ROUTER_SYNC
+      break;
+    }
+    __builtin_amdgcn_s_sleep(10);  // ~640 cycles between polls
+  }
+}
+
+// Counter of (phase p, row block r): one per 512 bytes, so polls and counts on
+// different counters go to different cache lines and memory channels.
+constexpr int kSyncStride = 64;
+
+}  // namespace
+
+__global__ void __launch_bounds__(512) k_gating_fused(GatingFusedArgs a) {
+  const int bid = blockIdx.x;
+  int p = 0;
+  while (p + 1 < a.nph && bid >= a.first[p + 1]) ++p;
+  const int lt = bid - a.first[p];
+  const int T = a.T, nt = a.h / 64, mt = (T + 15) / 16;
+  const int ph = p - (a.o != nullptr ? 1 : 0);  // -1: out-projection, 0..7: blocks, 8: head
+  const int rb = ph == 8 ? lt / 16 : lt / nt;  // 16-row block of this workgroup's work
+  if (p > 0) {
+    if (threadIdx.x == 0)
+      phase_wait(a.sync + ((size_t)(p - 1) * mt + rb) * kSyncStride,
+                 (a.tag << 16) | (unsigned long long)nt, a.status);
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int lo16 = lane & 15, hi4 = lane >> 4;
+  if (ph == 8) {
+    residual_ln_row<true, bf16_t>(lt, a.xb[3], a.y2[3], a.lw[3], a.lb[3], a.h, a.eps,
+                                  (const bf16_t*)a.wc, a.bc, a.gate);
+  } else {
+    const int N = ph < 0 ? a.h : ((ph & 1) ? a.h : a.he);
+    const int m0 = 16 * rb, n0 = 64 * (lt % nt);
+    const int blk = ph < 0 ? 0 : ph >> 1;
+    if (ph >= 2 && (ph & 1) == 0) {
+      // block blk's first Linear with block blk-1's residual LayerNorm in front
+      ln_rows_tile<ACT_GELU, true>(a.xb[blk - 1], a.y2[blk - 1], a.lw[blk - 1], a.lb[blk - 1],
+                                   a.eps, a.xb[blk], n0 == 0, (const bf16_t*)a.w1[blk], a.ldw1,
+                                   a.b1[blk], a.y1[blk], T, N, a.h, m0, n0);
+    } else {
+      const float* A;
+      const bf16_t* W;
+      long long lda, ldw;
+      const float* bias;
+      float* Cm;
+      if (ph < 0) {
+        A = a.o, lda = a.h, W = (const bf16_t*)a.wo, ldw = a.ldwo, bias = a.bo, Cm = a.xb[0];
+      } else if (ph == 0) {
+        A = a.xb[0], lda = a.h, W = (const bf16_t*)a.w1[0], ldw = a.ldw1, bias = a.b1[0];
+        Cm = a.y1[0];
+      } else {
+        A = a.y1[blk], lda = a.he, W = (const bf16_t*)a.w2[blk], ldw = a.ldw2, bias = a.b2[blk];
+        Cm = a.y2[blk];
+      }
+      const int K = ph > 0 ? a.he : a.h;
+      ARow<1> arow[1];
+      arow[0].p[0] = A + (long long)min(m0 + lo16, T - 1) * lda + 8 * hi4;
+      if (ph == 0)
+        f32a_tile<1, 4, 8, 4, ACT_GELU, 0, 1, true>(arow, W, ldw, bias, Cm, nullptr, N, T, N, K,
+                                                    1.f, m0, n0);
+      else
+        f32a_tile<1, 4, 8, 4, ACT_NONE, 0, 1, true>(arow, W, ldw, bias, Cm, nullptr, N, T, N, K,
+                                                    1.f, m0, n0);
+    }
+  }
+  if (p + 1 < a.nph) {
+    // every wave's write-through stores acknowledged before the count
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) tagged_count(a.sync + ((size_t)p * mt + rb) * kSyncStride, a.tag);
+  }
+}
+
+bool gating_fused_supported(int T, int h, int he) {
+  return T > 0 && h == he && h % 256 == 0 && h >= 256 && h <= 1024 &&
+         (long long)((T + 15) / 16) * (h / 64) * 9 + T <= 0x7fffffffll;
+}
+
+size_t gating_fused_sync_words(int T) { return (size_t)10 * ((T + 15) / 16) * kSyncStride; }
+
+hipError_t launch_gating_fused(GatingFusedArgs a, hipStream_t s) {
+  if (!gating_fused_supported(a.T, a.h, a.he) || a.xb[0] == nullptr || a.sync == nullptr ||
+      (uintptr_t)a.sync % 8 || (a.o != nullptr && a.wo == nullptr) || a.tag == 0 ||
+      a.tag >= (1ull << 48))
+    return hipErrorInvalidValue;
+  for (int i = 0; i < 4; ++i)
+    if (a.y1[i] == nullptr || a.y2[i] == nullptr || (i > 0 && a.xb[i] == nullptr))
+      return hipErrorInvalidValue;
+  const int tiles = ((a.T + 15) / 16) * (a.h / 64);
+  int n = 0, g = 0;
+  if (a.o != nullptr) a.first[n++] = g, g += tiles;
+  for (int i = 0; i < 8; ++i) a.first[n++] = g, g += tiles;
+  a.first[n++] = g, g += a.T;
+  a.first[n] = g;
+  a.nph = n;
+  hipLaunchKernelGGL(k_gating_fused, dim3((unsigned)g), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -291,6 +291,42 @@ hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt
 // too (a Gating block's first Linear with the previous block's residual
 // LayerNorm in its prologue); fp32 rows of K (a multiple of 256, <= 1024),
 // bf16 W [N, K]; x_in and x_out distinct.
+// The pooling's last output projection (optional: o == nullptr skips it and
+// xb[0] holds the pooled rows; else it writes them there) and the whole
+// Gating network in one launch.  Every product is an f32a tile and h == he.
+// Each phase writes buffers of its own: xb[1..3] (block inputs), y1[b],
+// y2[b] ([T, h] fp32 each).  sync: gating_fused_sync_words(T) device words
+// of workspace; tag: nonzero, below 2^48, different for every launch.
+struct GatingFusedArgs {
+  const float* o = nullptr;
+  const uint16_t* wo = nullptr;  // bf16
+  long long ldwo = 0;
+  const float* bo = nullptr;
+  float* xb[4] = {};
+  float* y1[4] = {};
+  float* y2[4] = {};
+  const uint16_t* w1[4] = {};  // bf16
+  const uint16_t* w2[4] = {};
+  long long ldw1 = 0, ldw2 = 0;
+  const float* b1[4] = {};
+  const float* b2[4] = {};
+  const float* lw[4] = {};
+  const float* lb[4] = {};
+  const uint16_t* wc = nullptr;  // bf16 [2, h]
+  const float* bc = nullptr;
+  float* gate = nullptr;
+  int T = 0, h = 0, he = 0;
+  float eps = 0.f;
+  unsigned long long* sync = nullptr;
+  unsigned long long tag = 0;
+  int* status = nullptr;
+  int first[12] = {};  // set by the launcher
+  int nph = 0;
+};
+bool gating_fused_supported(int T, int h, int he);
+size_t gating_fused_sync_words(int T);
+hipError_t launch_gating_fused(GatingFusedArgs a, hipStream_t s);
+
 bool f32a_ln_rows_supported(int K);
 // (W rows at stride ldw)
 hipError_t launch_f32a_ln_rows(const float* x_in, const float* y, const float* gamma,
