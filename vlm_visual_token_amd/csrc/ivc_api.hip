@@ -912,8 +912,10 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     // shuffled row's (mean, rstd) from its 4 or 16 cells
     float* tokst = (float*)((char*)ws + tokst_offset(h, T));
     if (!tokst_ready)
-      LAUNCH("token_stats", s, launch_token_stats(vit, T, c.has_cls + c.grid * c.grid, c.has_cls,
-                                                  c.grid * c.grid, C, tokst, s));
+      LAUNCH("token_stats", s,
+             launch_token_stats(vit, T, c.has_cls + c.grid * c.grid, c.has_cls, c.grid * c.grid,
+                                C, tokst, s,
+                                c.flash && (C == 512 || C == 1024)));  // as the token pass
     LAUNCH("ln_stats", s, launch_ln_stats(tokst, T, c.grid, C, c.ln_eps, sa.ps_v1, c.flash,
                                           sa.use64, sa.rank, sa.st2, sa.st4, s));
   } else {

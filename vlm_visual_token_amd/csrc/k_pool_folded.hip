@@ -568,23 +568,91 @@ k_token_stats(const bf16_t* __restrict__ X, int rows, int has_cls, int N,
     tokst[(size_t)t * N + 16 * j + lane] = moments_8(&sTS[lane * NW], (float)(C / 8));
 }
 
+// Connectors without the pooling (any width, e.g. C = 3200 or 1024), whose
+// moments need not match a token pass: one wave per token, two tokens per
+// wave, the lane holding 16-byte pieces lane, lane + 64, ... of the row; two
+// passes from registers (mean, then the sum of squared deviations), each
+// wave-reduced.
+template <int KP>
+__global__ void __launch_bounds__(512)
+k_token_stats_any(const bf16_t* __restrict__ X, int rows, int has_cls, int N, int C,
+                  long long ntok, float2* __restrict__ tokst) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int vpr = C / 8;  // 16-byte pieces per row
+  const long long tok0 = ((long long)blockIdx.x * 8 + w) * 2;
+  bf16x8_t a[2][KP];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const long long tok = min(tok0 + r, ntok - 1);
+    const long long t = tok / N, n = tok - t * N;
+    const bf16_t* src = X + ((size_t)t * rows + has_cls + n) * (size_t)C;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int v = lane + 64 * k;
+      a[r][k] = v < vpr ? __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(
+                                                         reinterpret_cast<const u32x4*>(src) + v))
+                        : bf16x8_t{};
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    float f[KP][8];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      unpack16(__builtin_bit_cast(u32x4, a[r][k]), f[k], (bf16_t*)nullptr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += f[k][e];  // pieces past the row are zero
+    }
+    const float mean = wave_sum(s) / (float)C;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      if (lane + 64 * k < vpr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = f[k][e] - mean;
+          q = fmaf(d, d, q);
+        }
+      }
+    }
+    q = wave_sum(q);
+    if (lane == 0 && tok0 + r < ntok) tokst[tok0 + r] = make_float2(mean, q);
+  }
+}
+
 bool token_stats_supported(int dtype, int C, int N) {
-  return dtype == DT_BF16 && (C == 512 || C == 1024) && N % 16 == 0 && N > 0;
+  return dtype == DT_BF16 && N % 16 == 0 && N > 0 && C % 8 == 0 && C >= 64 && C <= 8 * 64 * 8;
 }
 
 hipError_t launch_token_stats(const void* X, int T, int rows, int has_cls, int N, int C,
-                              float* tokst, hipStream_t s) {
+                              float* tokst, hipStream_t s, bool pool_order) {
   if (T <= 0) return hipSuccess;
   if (!token_stats_supported(DT_BF16, C, N) || (uintptr_t)X % 16 || (uintptr_t)tokst % 8)
     return hipErrorInvalidValue;
   const long long nb = (long long)T * (N / 16);
   if (nb > 0x7fffffffll) return hipErrorInvalidValue;
-  if (C == 1024)
+  if (pool_order && C != 512 && C != 1024) return hipErrorInvalidValue;
+  if (pool_order && C == 1024) {
     hipLaunchKernelGGL(k_token_stats<1024>, dim3((unsigned)nb), dim3(512), 0, s,
                        (const bf16_t*)X, rows, has_cls, N, (float2*)tokst);
-  else
+  } else if (pool_order) {
     hipLaunchKernelGGL(k_token_stats<512>, dim3((unsigned)nb), dim3(512), 0, s, (const bf16_t*)X,
                        rows, has_cls, N, (float2*)tokst);
+  } else {
+    // 16 tokens per workgroup, as above (nb workgroups)
+    const long long ntok = (long long)T * N;
+    const int kp = (C / 8 + 63) / 64;
+#define IVC_TSA(K)                                                                                 \
+  hipLaunchKernelGGL(k_token_stats_any<K>, dim3((unsigned)nb), dim3(512), 0, s, (const bf16_t*)X, \
+                     rows, has_cls, N, C, ntok, (float2*)tokst)
+    if (kp <= 2) IVC_TSA(2);
+    else if (kp <= 4) IVC_TSA(4);
+    else if (kp <= 7) IVC_TSA(7);
+    else IVC_TSA(8);
+#undef IVC_TSA
+  }
   return hipGetLastError();
 }
 

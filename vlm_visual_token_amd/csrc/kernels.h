@@ -278,11 +278,14 @@ struct FoldedArgs {
 void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax);
 bool pool_folded_supported(int dtype, int C, int H);
 // Each token's LayerNorm moments over its C channels, tokst[t * N + n] =
-// (mean, sum of squared deviations), with the same arithmetic as the token
-// pass's statistics; bf16, C of 512 or 1024, N a multiple of 16.
+// (mean, sum of squared deviations); bf16, C a multiple of 8 up to 4096, N a
+// multiple of 16.  pool_order (C of 512 or 1024 only): the same arithmetic
+// as the first token pass of the folded pooling, bit for bit (Flash
+// connectors, whose forward takes the moments from that pass); otherwise
+// two passes per token over its row.
 bool token_stats_supported(int dtype, int C, int N);
 hipError_t launch_token_stats(const void* X, int T, int rows, int has_cls, int N, int C,
-                              float* tokst, hipStream_t s);
+                              float* tokst, hipStream_t s, bool pool_order);
 hipError_t launch_pool_folded(const FoldedArgs& a, hipStream_t s);
 // qt[t, h, :] = scale * sum_i Q[t, h*d + i] * Wk[h*d + i, :] as bf16 high + low parts
 hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt_hi, void* qt_lo,
