@@ -201,14 +201,13 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// The main loop: K step 64, two stages; sA*/sB* hold 256 rows of 128 bytes,
-// and 16-byte piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
+// The main loop: K step 64; sA*/sB* hold 256 rows of 128 bytes, and 16-byte
+// piece c of row r sits at c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1).
 // 8 waves of 128 x 64 (4 x 2 MFMA blocks, 128 accumulators each), two per
-// SIMD, so while one wave of a SIMD waits to issue its share of the operand
-// DMA the other issues MFMAs (4 waves of 128 x 128 with all 256 AGPRs were
-// 3-8% slower: nothing could cover their DMA issue stalls).  Each wave
-// issues 8 of the step's 64 DMA instructions over the first half of the
-// step's MFMAs.
+// SIMD (4 waves of 128 x 128 with all 256 AGPRs were 3-8% slower: nothing
+// could cover their DMA issue stalls).  The two waves of a SIMD take turns:
+// one runs a half step's 16 MFMAs while the other reads its next half
+// step's fragments and issues its share of the operand DMA (tile_ksteps).
 // ---------------------------------------------------------------------------
 constexpr int BK = 64;
 
@@ -284,9 +283,9 @@ struct Stages {
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8); }
 
 // Sums the tile's K steps into acc (overwritten).  Each wave issues 4 DMA
-// instructions of W (step s + 1) and then 4 of A (step s + 2) per step, 1 KB
-// each, over the first half of the step's MFMAs; DMAs complete in issue
-// order, so the wait at a step's top lets A's newest step stay in flight.
+// instructions of W (step s + 1) and 4 of A (step s + 2) per step, 1 KB
+// each, in its load phases (below); DMAs complete in issue order, so a wait
+// can let A's newest step stay in flight.
 template <bool FOLD>
 IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma& d, const Stages& st,
                          int k0, int k1, int w, int wm, int wn, int lane) {
@@ -329,9 +328,7 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
     return k;
   };
   constexpr int NA = 3, NB = 2;
-  // prologue: A and W of step 0, then A of step 1, in the order the steady
-  // state's steps leave their DMAs (W, then A) so that the compiler's count
-  // of DMAs in flight agrees at the loop's entry and back edge
+  // prologue (every wave): A and W of step 0, A of step 1
   {
     const uint32_t ka = a_koff();
 #pragma unroll
@@ -344,7 +341,6 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
 #pragma unroll
     for (int j = 0; j < 4; ++j) dma_a(j, ka, st.sa1);
   }
-  // cleared with moves the compiler cannot move out of an enclosing loop
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -355,92 +351,114 @@ IVC_DEV void tile_ksteps(f32x16_t (&acc)[4][2], const GemmOps& o, const TileDma&
         asm volatile("v_mov_b32 %0, 0" : "=v"(z));
         acc[i][j][v] = z;
       }
-  // One step with its stages fixed at compile time: step s reads stage
-  // IA / IB and fills stage (IA + NA - 1) % NA / (IB + NB - 1) % NB.  Each
-  // copy names its LDS arrays directly, so the compiler can tell the reads
-  // from the DMA targets in flight (with stage pointers chosen at run time
-  // it waits for every DMA before the first read).
-  // FULL: both operands' next DMAs are issued (the steady state, no
-  // conditional issue, so the compiler's count of DMAs in flight is exact and
-  // it adds no wait of its own beside the step's)
-  auto step = [&](int s, auto ia_c, auto ib_c, auto full_c) {
+  // step 0's operands in LDS from every wave (A of step 1 may still fly)
+  if (n > 1)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  asm volatile("s_barrier" ::: "memory");
+  // Ping-pong: the two waves of a SIMD (w and w + 4) alternate between a load
+  // phase (the next half step's fragments from LDS, plus a share of the
+  // operand DMA) and a compute phase (that half step's 16 MFMAs), offset by
+  // one phase, with a workgroup barrier after every phase: while one wave of
+  // a SIMD runs its MFMAs the other issues its loads.  Half step h of step s
+  // reads K columns 32h .. 32h + 31 of step s's stages.
+  // DMA: W of step s + 1 in the load phase of half 0 (into the stage step
+  // s - 1 used, free: its last reader finished one barrier earlier), A of
+  // step s + 2 in the load phase of half 1; at the end of half 1's load phase
+  // a wave waits until only that A remains in flight, so step s + 1's
+  // operands are complete before any wave reads them.
+  bf16x8_t ra[2][4], rb[2][2];  // [kk within the half][block]
+  auto load = [&](int s, auto ia_c, auto ib_c, auto h_c, auto full_c) {
     constexpr int IA = decltype(ia_c)::value, IB = decltype(ib_c)::value;
+    constexpr int H = decltype(h_c)::value;
     constexpr bool FULL = decltype(full_c)::value;
-    constexpr int JA = (IA + NA - 1) % NA, JB = (IB + NB - 1) % NB;
     const char* sa = IA == 0 ? st.sa0 : IA == 1 ? st.sa1 : st.sa2;
     const char* sb = IB == 0 ? st.sb0 : st.sb1;
-    char* na = JA == 0 ? st.sa0 : JA == 1 ? st.sa1 : st.sa2;
-    char* nb = JB == 0 ? st.sb0 : st.sb1;
-    const bool more_a = FULL || s + NA - 1 < n, more_b = FULL || s + NB - 1 < n;
-    const uint32_t ka = more_a ? a_koff() : 0;
-    const uint32_t kb = kb0 + (uint32_t)((s + NB - 1) * (BK * 2));
-    // operands of step s complete; A's step s + 1 may still be in flight
-    // (issued last, one step ago)
-    if (FULL || s + 1 < n)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    // execution barrier only: every wave has waited for its own DMAs of step
-    // s, and its reads of the stage about to be refilled ended before the
-    // MFMAs that used them.  (__syncthreads adds a release that waits for
-    // every DMA in flight, the deeper stage's included.)
-    asm volatile("s_barrier" ::: "memory");
-    bf16x8_t fa_[2][4], fb_[2][2];  // [buffer][block]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa_[0][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[0] + i * 4096);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) fb_[0][j] = *reinterpret_cast<const bf16x8_t*>(sb + fb[0] + j * 4096);
     __builtin_amdgcn_sched_barrier(0);
+    if (H == 0) {
+      constexpr int JB = (IB + 1) % NB;
+      char* nb = JB == 0 ? st.sb0 : st.sb1;
+      if (FULL || s + 1 < n) {
+        const uint32_t kb = kb0 + (uint32_t)((s + 1) * (BK * 2));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int cb = kk & 1, nbuf = cb ^ 1;
+        for (int j = 0; j < 4; ++j) dma_b(j, kb, nb);
+      }
+    } else {
+      constexpr int JA = (IA + 2) % NA;
+      char* na = JA == 0 ? st.sa0 : JA == 1 ? st.sa1 : st.sa2;
+      if (FULL || s + 2 < n) {
+        const uint32_t ka = a_koff();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          // 8 DMA instructions over the first 16 MFMAs of the step: W's
-          // four, then A's (the last issued are the ones left in flight)
-          if (kk < 2 && j == 0) {
-            const int q = kk * 4 + i;
-            if (q < 4 && more_b) dma_b(q, kb, nb);
-            if (q >= 4 && more_a) dma_a(q - 4, ka, na);
-          }
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa_[cb][i], fb_[cb][j], acc[i][j],
-                                                              0, 0, 0);
-        }
-        if (kk < 3) {
-          fa_[nbuf][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[kk + 1] + i * 4096);
-          if (i < 2) fb_[nbuf][i] = *reinterpret_cast<const bf16x8_t*>(sb + fb[kk + 1] + i * 4096);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) dma_a(j, ka, na);
       }
     }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ra[q][i] = *reinterpret_cast<const bf16x8_t*>(sa + fa[2 * H + q] + i * 4096);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        rb[q][j] = *reinterpret_cast<const bf16x8_t*>(sb + fb[2 * H + q] + j * 4096);
+    }
+    if (H == 1) {
+      // step s + 1's operands complete (only A of step s + 2 may fly)
+      if (FULL || s + 2 < n)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(4) & ~(15 << 8));  // and this phase's LDS reads
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & ~(15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this phase's LDS reads (lgkmcnt 0)
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  auto compute = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[q][i], rb[q][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using F = std::false_type;
-  using T = std::true_type;
-  // steady state while a whole cycle of steps issues every DMA (the last
-  // step of the cycle issues step s + 5 + max(NA, NB) - 1), then the guarded tail
-  // A stages cycle by 3, W stages by 2: six step bodies per cycle
+  using TF = std::true_type;
+  using FF = std::false_type;
+  auto stepx = [&](int s, auto ia_c, auto ib_c, auto full_c) {
+    load(s, ia_c, ib_c, I0{}, full_c);
+    compute();
+    load(s, ia_c, ib_c, I1{}, full_c);
+    compute();
+  };
+  const bool late = w >= 4;  // the second wave of each SIMD runs one phase behind
+  if (late) asm volatile("s_barrier" ::: "memory");
   int s = 0;
+  // steady state while every step of the cycle issues both DMAs (the last
+  // issues A of step s + 7), then the guarded tail
   for (; s + 8 <= n; s += 6) {
-    step(s, I0{}, I0{}, T{});
-    step(s + 1, I1{}, I1{}, T{});
-    step(s + 2, I2{}, I0{}, T{});
-    step(s + 3, I0{}, I1{}, T{});
-    step(s + 4, I1{}, I0{}, T{});
-    step(s + 5, I2{}, I1{}, T{});
+    stepx(s, I0{}, I0{}, TF{});
+    stepx(s + 1, I1{}, I1{}, TF{});
+    stepx(s + 2, I2{}, I0{}, TF{});
+    stepx(s + 3, I0{}, I1{}, TF{});
+    stepx(s + 4, I1{}, I0{}, TF{});
+    stepx(s + 5, I2{}, I1{}, TF{});
   }
   for (; s < n; s += 6) {
-    step(s, I0{}, I0{}, F{});
-    if (s + 1 < n) step(s + 1, I1{}, I1{}, F{});
-    if (s + 2 < n) step(s + 2, I2{}, I0{}, F{});
-    if (s + 3 < n) step(s + 3, I0{}, I1{}, F{});
-    if (s + 4 < n) step(s + 4, I1{}, I0{}, F{});
-    if (s + 5 < n) step(s + 5, I2{}, I1{}, F{});
+    stepx(s, I0{}, I0{}, FF{});
+    if (s + 1 < n) stepx(s + 1, I1{}, I1{}, FF{});
+    if (s + 2 < n) stepx(s + 2, I2{}, I0{}, FF{});
+    if (s + 3 < n) stepx(s + 3, I0{}, I1{}, FF{});
+    if (s + 4 < n) stepx(s + 4, I1{}, I0{}, FF{});
+    if (s + 5 < n) stepx(s + 5, I2{}, I1{}, FF{});
   }
+  if (!late) asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
 }
 
