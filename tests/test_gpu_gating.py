@@ -86,3 +86,24 @@ def test_gating_one_launch_smaller_call_after_larger():
     _same(small, small_ref)
     big_ref = _route(con, xd, None, False)
     _same(big, big_ref)
+
+
+def test_gating_one_launch_large_batch():
+    """600 tiles (38 row blocks, the last one ragged; 6,072 workgroups over
+    ten phases): many more workgroups than fit on the chip at once."""
+    from vlm_visual_token_amd import Connector
+    from tests.gpu_util import dev_weights
+    cfg = workload("internvl35_2b_flash", pool_mode=1)
+    T = 600
+    cfg["tiles"], cfg["T"] = [T], T
+    say("one-launch gating: T=600")
+    w = host_weights(cfg)
+    con = Connector(cfg, dev_weights(cfg, w), max_tiles=T)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(600)
+    # values need not come from synth: both forms read the same device tensor
+    xd = torch.randn((T, cfg["rows"], cfg["C"]), generator=g, device="cuda").to(torch.bfloat16)
+    one = _route(con, xd, None, True)
+    per = _route(con, xd, None, False)
+    _same(one, per)
+
