@@ -738,7 +738,7 @@ def summarize_workload(wdir: str) -> dict:
             L["algorithmic_flops"] = a["flops"]
             if L.get("duration_us"):
                 L["tflops"] = a["flops"] / L["duration_us"] / 1e6
-    out["commands"] = [c.replace("{WL}", meta["workload"]) for c in meta.get("commands", [])]
+    out["commands"] = [c.replace("{WL}", meta["workload"]) for c in PROFILE_COMMANDS]
     return out
 
 
@@ -757,8 +757,9 @@ def write_counters_md(summary: dict, path: str) -> None:
              "FETCH_SIZE counts L2 misses, which the 256 MB memory-side cache may serve "
              "before HBM.")
     L.append("")
-    L.append("Commands (from the repository root, `cd /tmp && export TMPDIR=/tmp` first for "
-             "the profiler's own files; `$R` is the repository path):")
+    L.append("Commands (`$R` is the repository path, `$OUT` an output directory with "
+             "`$OUT/pmc/<workload>` created beforehand; `cd /tmp && export TMPDIR=/tmp` first "
+             "for the profiler's own files):")
     L.append("")
     L.append("```")
     L.extend(summary["commands"])
@@ -844,10 +845,10 @@ def committed_counters(workload: str, path: str | None = None) -> dict | None:
 
 
 BENCH_STATS_COMMANDS = [
-    "timeout -s KILL 300 rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/bstats -o p "
+    "timeout -s KILL 300 rocprofv3 --kernel-trace --stats -f csv -d $OUT/bstats -o p "
     "-- python3 $R/bench.py --no-cpu-baseline --mall-flush-steps 0 --compact-prompts 0 "
-    "--configs none > $R/gpurun_out/bstats/bench.json",
-    "python3 $R/bench.py --stats-summary $R/gpurun_out/bstats",
+    "--configs none > $OUT/bstats/bench.json",
+    "python3 $R/bench.py --stats-summary $OUT/bstats",
 ]
 
 
@@ -885,6 +886,9 @@ def bench_stats_summary(d: str) -> None:
              "kernel).  The run times the step as bench.py's default run does (warm-up, "
              "the timed steps, the kernels-alone event pass) and skips the CPU baseline, "
              "the cache-flush pass, the batched compaction and the other workloads.")
+    L.append("")
+    L.append("`$R` is the repository path, `$OUT` an output directory (`$OUT/bstats` created "
+             "beforehand).")
     L.append("")
     L.append("```")
     L.extend(BENCH_STATS_COMMANDS)
@@ -943,15 +947,15 @@ def calibrate_copy(torch):
 
 
 PROFILE_COMMANDS = [
-    "B=\"python3 $R/bench.py --profile-workload {WL} --profile-out $R/gpurun_out/pmc/{WL}\"",
-    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc/{WL}/fetch "
-    "-o p -- $B --steps 2 --warmup 1 2> $R/gpurun_out/pmc/{WL}/fetch.log",
+    "B=\"python3 $R/bench.py --profile-workload {WL} --profile-out $OUT/pmc/{WL}\"",
+    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/pmc/{WL}/fetch "
+    "-o p -- $B --steps 2 --warmup 1 2> $OUT/pmc/{WL}/fetch.log",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE SQ_INSTS_VALU_MFMA_MOPS_BF16 "
-    "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d $R/gpurun_out/pmc/{WL}/write -o p "
-    "-- $B --steps 2 --warmup 1 2> $R/gpurun_out/pmc/{WL}/write.log",
-    "timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/pmc/{WL}/trace "
-    "-o p -- $B --steps 20 --warmup 5 2> $R/gpurun_out/pmc/{WL}/trace.log",
-    "python3 $R/bench.py --counters-summary $R/gpurun_out/pmc",
+    "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d $OUT/pmc/{WL}/write -o p "
+    "-- $B --steps 2 --warmup 1 2> $OUT/pmc/{WL}/write.log",
+    "timeout -s KILL 180 rocprofv3 --kernel-trace --stats -f csv -d $OUT/pmc/{WL}/trace "
+    "-o p -- $B --steps 20 --warmup 5 2> $OUT/pmc/{WL}/trace.log",
+    "python3 $R/bench.py --counters-summary $OUT/pmc",
 ]
 
 

@@ -589,7 +589,7 @@ k_gemm_dma8(GemmOps o, const float* __restrict__ bias, bf16_t* __restrict__ Cm, 
     }
     __builtin_amdgcn_s_waitcnt(0);  // every wave's stores complete before the count
     __syncthreads();
-    // the verdict goes through the third A stage (free now; the LDS is full)
+    // the decision goes through the third A stage (free now; the LDS is full)
     int* last_piece = reinterpret_cast<int*>(sA2);
     if (tid == 0) *last_piece = piece_arrive(ts.cnt + tt, ts.ticket) == s - 1;
     __syncthreads();
