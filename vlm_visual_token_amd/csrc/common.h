@@ -81,6 +81,14 @@ IVC_DEV void st_coh4(float* p, float4 v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- XCD-aware workgroup order ------------------------------------------------
+// The dispatcher deals workgroups to the 8 XCDs in turn (linear id i runs on
+// XCD i % 8), each XCD with its own L2.  This renumbers the n workgroups of
+// a launch so that XCD k runs the consecutive range [k n/8, (k+1) n/8): work
+// items with nearby numbers, which share operands, then share one L2.  (n
+// not a multiple of 8: unchanged.)
+IVC_DEV int xcd_major(int i, int n) { return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3); }
+
 // ---- wavefront reductions (64 lanes) ---------------------------------------
 IVC_DEV float wave_sum(float v) {
 #pragma unroll

@@ -260,7 +260,10 @@ k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ vali
   const int lane = threadIdx.x & 63;
   const int lo16 = lane & 15, hi4 = lane >> 4;
   const int d = C / H;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 16, h = blockIdx.z;
+  // the 16-tile row blocks of one head in one XCD's range (they share Wv_h)
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int wg = xcd_major(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
+  const int n0 = (wg % nx) * 64, m0 = ((wg / nx) % ny) * 16, h = wg / (nx * ny);
   const int NC = (Ntok + 15) / 16;
   const int t = min(m0 + lo16, T - 1);
   int nv = valid != nullptr ? valid[t] : Ntok;
@@ -393,7 +396,10 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo16 = lane & 15, hi4 = lane >> 4;
-  const int m0 = blockIdx.x * 16, h = blockIdx.y;
+  // the 16-tile row blocks of one head in one XCD's range (they share the
+  // head's rows of Wq and columns of Wk)
+  const int wg = xcd_major(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int m0 = (wg % gridDim.x) * 16, h = wg / gridDim.x;
 
   const int CW = C / 8, nbw = CW / 16;  // columns and 16-column blocks of this wave (<= 8)
   const int c0 = w * CW;
