@@ -101,12 +101,14 @@ def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
             # the query and value folds and the gating products stream their weights
             "pool_query_fold": dict(flops=None, bytes=2 * C * C * e),
             "pool_fold_value": dict(flops=None, bytes=2 * C * C * e),
+            # a layer's value fold and the next layer's query fold in one launch
+            "pool_fold_value_query": dict(flops=None, bytes=4 * C * C * e),
             "gate_ln_fc1": dict(flops=None, bytes=G * cfg["gate_hidden"] * e),
             "gate_fc1": dict(flops=None, bytes=G * cfg["gate_hidden"] * e),
             "gate_fc2": dict(flops=None, bytes=G * cfg["gate_hidden"] * e),
-            # the one-launch Gating: the pooling's last output projection and
-            # the eight block products stream their weights once
-            "gating": dict(flops=None, bytes=(C * C + 8 * G * cfg["gate_hidden"]) * e),
+            # the one-launch Gating: the pooling's last value fold and output
+            # projection and the eight block products stream their weights once
+            "gating": dict(flops=None, bytes=(2 * C * C + 8 * G * cfg["gate_hidden"]) * e),
             "compact": dict(flops=None, bytes=2 * Lp * D * e + L_seq * 4 * 2 + Lp * 4 * 2),
         })
     return out
@@ -539,6 +541,7 @@ LAUNCH_FAMILY = {
     "pool_fold_query": ("k_gemm_f32a", "k_fold_query"), "pool_fold_pad": ("k_zero_heads",),
     "pool_folded": ("k_pool_folded",), "pool_folded_stats": ("k_pool_folded",),
     "pool_fold_value": ("k_fold_value", "k_gemm"), "pool_attn": ("k_pool_attn",),
+    "pool_fold_value_query": ("k_fold_value_query",),
     "gate_fc1": ("k_gemm",), "gate_ln_fc1": ("k_gemm_f32a", "k_f32a_ln_rows"),
     "gate_fc2": ("k_gemm",), "gate_res_ln": ("k_residual_ln", "k_f32a_ln_rows"),
     "gate_res_ln_head": ("k_residual_ln", "k_f32a_ln_rows"),

@@ -1080,6 +1080,12 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
   const float scale = 1.0f / sqrtf((float)(C / H));
   int fG = 0, fQ = 0, fseg = 0;
   if (folded) folded_geometry(T, N, C, h->ncu, &fG, &fQ, &fseg);
+  // A layer's value fold runs in one launch with the next layer's query fold,
+  // and the last layer's in the one-launch Gating (IVC_FOLD_MERGED=0 keeps
+  // them apart; the same arithmetic either way).
+  const bool vq_ok = folded && fq_fused && dt == IVC_BF16 && !env_off("IVC_FOLD_MERGED");
+  bool qt_made = false;      // this layer's q~ came with the previous layer's value fold
+  bool vf_in_gating = false;  // the last value fold runs as the Gating launch's first phase
   for (int l = 0; l < L; ++l) {
     const void* wk = (const char*)h->wkv + (size_t)(2 * l) * C * h->lr * h->esz;
     const void* wv = (const char*)h->wkv + (size_t)(2 * l + 1) * C * h->lr * h->esz;
@@ -1090,7 +1096,7 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
     // the first layer's folded query is the same for every tile: made once at create
     const bool qt_shared = fq_fused && l == 0 && h->qt0_hi != nullptr;
     if (fq_fused) {
-      if (!qt_shared) {
+      if (!qt_shared && !qt_made) {
         // l >= 1: from the previous layer's value-fold output o through the
         // folded output + query projections (or through q when not folded)
         const bool qo = h->wqo_hi[l] != nullptr;
@@ -1158,7 +1164,41 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
       fa.xbar = merged_value ? nullptr : w.xbar;
       // the first layer's pass also writes per-token LayerNorm moments: timed apart
       LAUNCH(fa.tokst ? "pool_folded_stats" : "pool_folded", s, launch_pool_folded(fa, s));
-      if (merged_value) {
+      const bool next_vq = merged_value && vq_ok && l + 1 < L && h->wqo_hi[l + 1] != nullptr &&
+                           h->wqo_lo[l + 1] != nullptr &&
+                           fold_value_query_supported(T, N, fQ, C, H);
+      qt_made = false;
+      if (next_vq) {
+        FoldVQArgs va;
+        va.part = w.part;
+        va.valid = valid_tokens;
+        va.N = N;
+        va.Q = fQ;
+        va.segmax = fseg;
+        va.Wv = (const uint16_t*)wv;
+        va.ldwv = h->lr;
+        va.bv = bv;
+        va.o = w.o;
+        va.Wq = (const uint16_t*)h->wqo_hi[l + 1];
+        va.Wq_lo = (const uint16_t*)h->wqo_lo[l + 1];
+        va.ldwq = h->lr;
+        va.bq = h->bqo[l + 1];
+        va.WkT = (const uint16_t*)((const char*)h->wkT + (size_t)(l + 1) * C * h->lr * h->esz);
+        va.ldk = h->lr;
+        va.qt_hi = (uint16_t*)w.qt_hi;
+        va.qt_lo = (uint16_t*)w.qt_lo;
+        va.scale = qscale;
+        va.T = T;
+        va.C = C;
+        va.H = H;
+        va.sync = w.sync;
+        va.tag = next_ticket() & 0xffffffffffffull;
+        va.status = dev_status;
+        LAUNCH("pool_fold_value_query", s, launch_fold_value_query(va, s));
+        qt_made = true;
+      } else if (merged_value && vq_ok && gate1 && l == L - 1) {
+        vf_in_gating = true;  // made by the Gating launch
+      } else if (merged_value) {
         LAUNCH("pool_fold_value", s,
                launch_fold_value_merged(w.part, valid_tokens, N, fQ, fseg, wv, h->lr, bv, w.o, T,
                                         C, H, s));
@@ -1210,6 +1250,18 @@ static ivc_status route_impl(ivc_connector* h, const void* vit, const int32_t* v
   if (gate1) {
     static_assert(IVC_GATE_BLOCKS == 4, "the one-launch Gating runs four blocks");
     GatingFusedArgs ga;
+    if (vf_in_gating) {
+      ga.vf_part = w.part;
+      ga.vf_valid = valid_tokens;
+      ga.vf_N = N;
+      ga.vf_Q = fQ;
+      ga.vf_segmax = fseg;
+      ga.vf_H = H;
+      ga.vf_wv = (const uint16_t*)((const char*)h->wkv + (size_t)(2 * (L - 1) + 1) * C * h->lr *
+                                                             h->esz);
+      ga.vf_ldw = h->lr;
+      ga.vf_bv = h->bkv + (size_t)(2 * (L - 1) + 1) * C;
+    }
     ga.o = w.o;
     ga.wo = (const uint16_t*)h->wo[L - 1];
     ga.ldwo = h->lr;

@@ -251,19 +251,17 @@ k_gemm_f32a(const float* __restrict__ A, long long lda, long long a_bs,
 // over the partials s of tile t (workgroups g0 .. g1 of the token pass, in
 // order), M their largest running max: the same arithmetic as the merge
 // kernel of the token pass.  grid (ceil(d / 64), ceil(T / 16), H).
-template <int MAXS>
-__global__ void __launch_bounds__(512)
-k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ valid, int Ntok,
-                    int Q, int segmax, const bf16_t* __restrict__ Wv, long long ldw,
-                    const float* __restrict__ bv, float* __restrict__ o, int T, int C, int H) {
+// One (16-tile, 64-column) tile of head h's value fold.  COH: write-through
+// stores of o (read by workgroups of the same launch on other XCDs).
+template <int MAXS, bool COH>
+IVC_DEV void fold_value_tile(const float* __restrict__ part, const int* __restrict__ valid,
+                             int Ntok, int Q, int segmax, const bf16_t* __restrict__ Wv,
+                             long long ldw, const float* __restrict__ bv, float* __restrict__ o,
+                             int T, int C, int H, int n0, int m0, int h) {
   constexpr int FH = 16;
   const int lane = threadIdx.x & 63;
   const int lo16 = lane & 15, hi4 = lane >> 4;
   const int d = C / H;
-  // the 16-tile row blocks of one head in one XCD's range (they share Wv_h)
-  const int nx = gridDim.x, ny = gridDim.y;
-  const int wg = xcd_major(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
-  const int n0 = (wg % nx) * 64, m0 = ((wg / nx) % ny) * 16, h = wg / (nx * ny);
   const int NC = (Ntok + 15) / 16;
   const int t = min(m0 + lo16, T - 1);
   int nv = valid != nullptr ? valid[t] : Ntok;
@@ -295,8 +293,21 @@ k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ vali
   arow[0].inv = 1.0f / L;
   // all K steps of a wave in one round of loads while the registers allow it
   constexpr int PD = MAXS <= 3 ? 4 : 2;
-  f32a_tile<1, 4, 8, PD, ACT_NONE, 0, MAXS>(arow, Wv + (long long)h * d * ldw, ldw, bv + h * d,
-                                            o + h * d, nullptr, C, T, d, C, 1.f, m0, n0);
+  f32a_tile<1, 4, 8, PD, ACT_NONE, 0, MAXS, COH>(arow, Wv + (long long)h * d * ldw, ldw,
+                                                 bv + h * d, o + h * d, nullptr, C, T, d, C, 1.f,
+                                                 m0, n0);
+}
+
+template <int MAXS>
+__global__ void __launch_bounds__(512)
+k_fold_value_merged(const float* __restrict__ part, const int* __restrict__ valid, int Ntok,
+                    int Q, int segmax, const bf16_t* __restrict__ Wv, long long ldw,
+                    const float* __restrict__ bv, float* __restrict__ o, int T, int C, int H) {
+  // the 16-tile row blocks of one head in one XCD's range (they share Wv_h)
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int wg = xcd_major(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
+  fold_value_tile<MAXS, false>(part, valid, Ntok, Q, segmax, Wv, ldw, bv, o, T, C, H,
+                               (wg % nx) * 64, ((wg / nx) % ny) * 16, wg / (nx * ny));
 }
 
 int fold_value_merged_max_parts(int T, int N, int Q) {
@@ -381,13 +392,14 @@ hipError_t launch_gemm_f32a(const GemmArgs& g, int out_split, void* C2, float sc
 // wave w taking columns [w C/8, (w+1) C/8); the bf16 halves go through a
 // wave-private LDS slab so each row leaves with 16-byte stores.
 // WS: Wq given as bf16 high (Wq) + low (Wq_lo) parts of fp32 weights.
+// The (16-tile, head h) block of the fused query fold.
 template <int D, bool WS>
-__global__ void __launch_bounds__(512)
-k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __restrict__ Wq,
-                   const bf16_t* __restrict__ Wq_lo, long long ldwq, const float* __restrict__ bq,
-                   const bf16_t* __restrict__ WkT, long long ldk,
-                   bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
-                   float scale) {
+IVC_DEV void fold_query_tile(const float* __restrict__ q, long long ldq,
+                             const bf16_t* __restrict__ Wq, const bf16_t* __restrict__ Wq_lo,
+                             long long ldwq, const float* __restrict__ bq,
+                             const bf16_t* __restrict__ WkT, long long ldk,
+                             bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
+                             float scale, int m0, int h) {
   constexpr int NB = D / 16, LDR = D + 4, KS = D / 32;
   constexpr int SR = 128 + 8;  // slab row (bf16): up to 128 columns per wave, 16 bytes of pad
   __shared__ __attribute__((aligned(16))) float red[8][16][LDR];
@@ -396,10 +408,6 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo16 = lane & 15, hi4 = lane >> 4;
-  // the 16-tile row blocks of one head in one XCD's range (they share the
-  // head's rows of Wq and columns of Wk)
-  const int wg = xcd_major(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
-  const int m0 = (wg % gridDim.x) * 16, h = wg / gridDim.x;
 
   const int CW = C / 8, nbw = CW / 16;  // columns and 16-column blocks of this wave (<= 8)
   const int c0 = w * CW;
@@ -494,6 +502,20 @@ k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __r
     *reinterpret_cast<u32x4*>(qt_hi + o) = *reinterpret_cast<const u32x4*>(&sh[r][8 * p]);
     *reinterpret_cast<u32x4*>(qt_lo + o) = *reinterpret_cast<const u32x4*>(&sl[r][8 * p]);
   }
+}
+
+template <int D, bool WS>
+__global__ void __launch_bounds__(512)
+k_fold_query_fused(const float* __restrict__ q, long long ldq, const bf16_t* __restrict__ Wq,
+                   const bf16_t* __restrict__ Wq_lo, long long ldwq, const float* __restrict__ bq,
+                   const bf16_t* __restrict__ WkT, long long ldk,
+                   bf16_t* __restrict__ qt_hi, bf16_t* __restrict__ qt_lo, int T, int C,
+                   float scale) {
+  // the 16-tile row blocks of one head in one XCD's range (they share the
+  // head's rows of Wq and columns of Wk)
+  const int wg = xcd_major(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  fold_query_tile<D, WS>(q, ldq, Wq, Wq_lo, ldwq, bq, WkT, ldk, qt_hi, qt_lo, T, C, scale,
+                         (wg % gridDim.x) * 16, wg / gridDim.x);
 }
 
 // A Gating block's first Linear with the previous block's residual LayerNorm
@@ -788,23 +810,39 @@ constexpr int kSyncStride = 64;
 
 }  // namespace
 
+// VF: 0, or the value fold's partials per tile (2..4) when the launch starts
+// with the pooling's last value fold.
+template <int VF>
 __global__ void __launch_bounds__(512) k_gating_fused(GatingFusedArgs a) {
   const int bid = blockIdx.x;
   int p = 0;
   while (p + 1 < a.nph && bid >= a.first[p + 1]) ++p;
   const int lt = bid - a.first[p];
   const int T = a.T, nt = a.h / 64, mt = (T + 15) / 16;
-  const int ph = p - (a.o != nullptr ? 1 : 0);  // -1: out-projection, 0..7: blocks, 8: head
-  const int rb = ph == 8 ? lt / 16 : lt / nt;  // 16-row block of this workgroup's work
+  // -2: value fold, -1: out-projection, 0..7: blocks, 8: head
+  const int ph = p - (VF > 0 ? 1 : 0) - (a.o != nullptr ? 1 : 0);
+  // value fold: (64-column block, row block, head), XCD-major like its own launch
+  const int vnx = VF > 0 ? (a.h / a.vf_H + 63) / 64 : 1;
+  const int vwg = ph == -2 ? xcd_major(lt, vnx * mt * a.vf_H) : 0;
+  // 16-row block of this workgroup's work
+  const int rb = ph == -2 ? (vwg / vnx) % mt : ph == 8 ? lt / 16 : lt / nt;
   if (p > 0) {
+    // the previous phase's workgroups per row block
+    const int prev = (VF > 0 && p == 1) ? vnx * a.vf_H : nt;
     if (threadIdx.x == 0)
       phase_wait(a.sync + ((size_t)(p - 1) * mt + rb) * kSyncStride,
-                 (a.tag << 16) | (unsigned long long)nt, a.status);
+                 (a.tag << 16) | (unsigned long long)prev, a.status);
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
   const int lo16 = lane & 15, hi4 = lane >> 4;
-  if (ph == 8) {
+  if (ph == -2) {
+    if constexpr (VF > 0)
+      fold_value_tile<VF, true>(a.vf_part, a.vf_valid, a.vf_N, a.vf_Q, a.vf_segmax,
+                                (const bf16_t*)a.vf_wv, a.vf_ldw, a.vf_bv,
+                                const_cast<float*>(a.o), T, a.h, a.vf_H, 64 * (vwg % vnx),
+                                16 * rb, vwg / (vnx * mt));
+  } else if (ph == 8) {
     residual_ln_row<true, bf16_t>(lt, a.xb[3], a.y2[3], a.lw[3], a.lb[3], a.h, a.eps,
                                   (const bf16_t*)a.wc, a.bc, a.gate);
   } else {
@@ -855,7 +893,8 @@ bool gating_fused_supported(int T, int h, int he) {
          (long long)((T + 15) / 16) * (h / 64) * 9 + T <= 0x7fffffffll;
 }
 
-size_t gating_fused_sync_words(int T) { return (size_t)10 * ((T + 15) / 16) * kSyncStride; }
+// counters of up to 11 phases (value fold, out-projection, 8 block products, head)
+size_t gating_fused_sync_words(int T) { return (size_t)11 * ((T + 15) / 16) * kSyncStride; }
 
 hipError_t launch_gating_fused(GatingFusedArgs a, hipStream_t s) {
   if (!gating_fused_supported(a.T, a.h, a.he) || a.xb[0] == nullptr || a.sync == nullptr ||
@@ -865,14 +904,105 @@ hipError_t launch_gating_fused(GatingFusedArgs a, hipStream_t s) {
   for (int i = 0; i < 4; ++i)
     if (a.y1[i] == nullptr || a.y2[i] == nullptr || (i > 0 && a.xb[i] == nullptr))
       return hipErrorInvalidValue;
-  const int tiles = ((a.T + 15) / 16) * (a.h / 64);
+  const int mt = (a.T + 15) / 16, tiles = mt * (a.h / 64);
+  int vf = 0;
+  if (a.vf_part != nullptr) {
+    vf = fold_value_merged_max_parts(a.T, a.vf_N, a.vf_Q);
+    if (a.o == nullptr || a.vf_wv == nullptr || a.vf_bv == nullptr || a.vf_H < 1 ||
+        a.h % a.vf_H || (a.h / a.vf_H) % 16 || vf < 1 || vf > 4 || (uintptr_t)a.vf_part % 16 ||
+        (uintptr_t)a.vf_wv % 16 || a.vf_ldw < a.h || a.vf_ldw % 8 ||
+        (long long)mt * ((a.h / a.vf_H + 63) / 64) * a.vf_H > 0x7fffffffll - 10ll * tiles - a.T)
+      return hipErrorInvalidValue;
+    if (vf < 2) vf = 2;
+  }
   int n = 0, g = 0;
+  if (vf > 0) a.first[n++] = g, g += mt * ((a.h / a.vf_H + 63) / 64) * a.vf_H;
   if (a.o != nullptr) a.first[n++] = g, g += tiles;
   for (int i = 0; i < 8; ++i) a.first[n++] = g, g += tiles;
   a.first[n++] = g, g += a.T;
   a.first[n] = g;
   a.nph = n;
-  hipLaunchKernelGGL(k_gating_fused, dim3((unsigned)g), dim3(512), 0, s, a);
+  if (vf == 0)
+    hipLaunchKernelGGL(k_gating_fused<0>, dim3((unsigned)g), dim3(512), 0, s, a);
+  else if (vf == 2)
+    hipLaunchKernelGGL(k_gating_fused<2>, dim3((unsigned)g), dim3(512), 0, s, a);
+  else if (vf == 3)
+    hipLaunchKernelGGL(k_gating_fused<3>, dim3((unsigned)g), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_gating_fused<4>, dim3((unsigned)g), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- one layer's value fold and the next layer's query fold ------------------
+// Workgroups [0, nA): value-fold tiles (64-column block, 16-tile row block,
+// head), numbered as in k_fold_value_merged; [nA, nA + nB): query-fold blocks
+// (row block, head), numbered as in k_fold_query_fused.  A query-fold
+// workgroup waits for the counter of its row block, which every value-fold
+// workgroup of that row block increments after its write-through stores of o
+// are acknowledged; all of them come earlier in the launch order.
+template <int MAXS, int D>
+__global__ void __launch_bounds__(512) k_fold_value_query(FoldVQArgs a) {
+  const int T = a.T, C = a.C, H = a.H, d = C / H;
+  const int mt = (T + 15) / 16, nx = (d + 63) / 64;
+  const int nA = nx * mt * H;
+  const int bid = blockIdx.x;
+  if (bid < nA) {
+    const int wg = xcd_major(bid, nA);
+    const int rb = (wg / nx) % mt;
+    fold_value_tile<MAXS, true>(a.part, a.valid, a.N, a.Q, a.segmax, (const bf16_t*)a.Wv, a.ldwv,
+                                a.bv, a.o, T, C, H, 64 * (wg % nx), 16 * rb, wg / (nx * mt));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) tagged_count(a.sync + (size_t)rb * kSyncStride, a.tag);
+  } else {
+    const int wg = xcd_major(bid - nA, mt * H);
+    const int rb = wg % mt;
+    if (threadIdx.x == 0)
+      phase_wait(a.sync + (size_t)rb * kSyncStride, (a.tag << 16) | (unsigned long long)(nx * H),
+                 a.status);
+    __syncthreads();
+    fold_query_tile<D, true>(a.o, C, (const bf16_t*)a.Wq, (const bf16_t*)a.Wq_lo, a.ldwq, a.bq,
+                             (const bf16_t*)a.WkT, a.ldk, (bf16_t*)a.qt_hi, (bf16_t*)a.qt_lo, T,
+                             C, a.scale, 16 * rb, wg / mt);
+  }
+}
+
+bool fold_value_query_supported(int T, int N, int Q, int C, int H) {
+  if (T <= 0 || H < 1 || H > 16 || C % H) return false;
+  const int d = C / H, m = fold_value_merged_max_parts(T, N, Q);
+  const long long mt = (T + 15) / 16;
+  // the query fold's LDS next to the value fold's: head widths up to 64
+  return (d == 32 || d == 64) && C % 128 == 0 && C <= 1024 && m >= 1 && m <= 4 &&
+         mt * ((d + 63) / 64) * H + mt * H <= 0x7fffffffll;
+}
+
+size_t fold_value_query_sync_words(int T) { return (size_t)((T + 15) / 16) * kSyncStride; }
+
+hipError_t launch_fold_value_query(const FoldVQArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (!fold_value_query_supported(a.T, a.N, a.Q, a.C, a.H) || !a.part || !a.Wv || !a.bv ||
+      !a.o || !a.Wq || !a.Wq_lo || !a.bq || !a.WkT || !a.qt_hi || !a.qt_lo || !a.sync ||
+      (uintptr_t)a.sync % 8 || a.tag == 0 || a.tag >= (1ull << 48) || (uintptr_t)a.part % 16 ||
+      (uintptr_t)a.Wv % 16 || a.ldwv < a.C || a.ldwv % 8 || (uintptr_t)a.o % 16 ||
+      (uintptr_t)a.Wq % 16 || (uintptr_t)a.Wq_lo % 16 || (uintptr_t)a.WkT % 16 ||
+      (uintptr_t)a.qt_hi % 16 || (uintptr_t)a.qt_lo % 16 || a.ldwq < a.C || a.ldwq % 8 ||
+      a.ldk < a.C || a.ldk % 8)
+    return hipErrorInvalidValue;
+  const int d = a.C / a.H, mt = (a.T + 15) / 16;
+  const unsigned g = (unsigned)(mt * ((d + 63) / 64) * a.H + mt * a.H);
+  int maxs = fold_value_merged_max_parts(a.T, a.N, a.Q);
+  if (maxs < 2) maxs = 2;
+#define IVC_FVQ(S, DV) hipLaunchKernelGGL((k_fold_value_query<S, DV>), dim3(g), dim3(512), 0, s, a)
+  if (d == 32) {
+    if (maxs == 2) IVC_FVQ(2, 32);
+    else if (maxs == 3) IVC_FVQ(3, 32);
+    else IVC_FVQ(4, 32);
+  } else {
+    if (maxs == 2) IVC_FVQ(2, 64);
+    else if (maxs == 3) IVC_FVQ(3, 64);
+    else IVC_FVQ(4, 64);
+  }
+#undef IVC_FVQ
   return hipGetLastError();
 }
 

@@ -300,7 +300,17 @@ hipError_t launch_fold_query(int dtype, const float* Q, const void* Wk, void* qt
 // Each phase writes buffers of its own: xb[1..3] (block inputs), y1[b],
 // y2[b] ([T, h] fp32 each).  sync: gating_fused_sync_words(T) device words
 // of workspace; tag: nonzero, below 2^48, different for every launch.
+// Optionally (vf_part set, o set) a leading phase makes o itself: the
+// pooling's last value fold from the token pass's partials, as
+// launch_fold_value_merged computes it (vf_* are that launcher's arguments,
+// with C = h).
 struct GatingFusedArgs {
+  const float* vf_part = nullptr;
+  const int* vf_valid = nullptr;
+  int vf_N = 0, vf_Q = 0, vf_segmax = 0, vf_H = 0;
+  const uint16_t* vf_wv = nullptr;  // bf16
+  long long vf_ldw = 0;
+  const float* vf_bv = nullptr;
   const float* o = nullptr;
   const uint16_t* wo = nullptr;  // bf16
   long long ldwo = 0;
@@ -363,6 +373,38 @@ hipError_t launch_fold_value_merged(const float* part, const int* valid, int N, 
 // o[t, h*d + i] = bv[h*d+i] + sum_c Wv[h*d + i, c] * xbar[t, h, c]
 hipError_t launch_fold_value(int dtype, const float* xbar, const void* Wv, const float* bv,
                              float* o, int T, int C, int H, hipStream_t s);
+// One layer's value fold (launch_fold_value_merged's arguments) and the next
+// layer's fused query fold reading its output o (launch_fold_query_fused's,
+// with q = o, ldq = C) in one launch: the query-fold workgroups of a 16-tile
+// row block start once that block's value-fold workgroups have counted
+// themselves in sync (fold_value_query_sync_words(T) device words of
+// workspace; tag: nonzero, below 2^48, different for every launch).  Same
+// values as the two launches.
+struct FoldVQArgs {
+  const float* part = nullptr;
+  const int* valid = nullptr;
+  int N = 0, Q = 0, segmax = 0;
+  const uint16_t* Wv = nullptr;  // bf16
+  long long ldwv = 0;
+  const float* bv = nullptr;
+  float* o = nullptr;
+  const uint16_t* Wq = nullptr;  // bf16 high part (and Wq_lo the low part) of fp32 weights
+  const uint16_t* Wq_lo = nullptr;
+  long long ldwq = 0;
+  const float* bq = nullptr;
+  const uint16_t* WkT = nullptr;
+  long long ldk = 0;
+  uint16_t* qt_hi = nullptr;
+  uint16_t* qt_lo = nullptr;
+  float scale = 0.f;
+  int T = 0, C = 0, H = 0;
+  unsigned long long* sync = nullptr;
+  unsigned long long tag = 0;
+  int* status = nullptr;
+};
+bool fold_value_query_supported(int T, int N, int Q, int C, int H);
+size_t fold_value_query_sync_words(int T);
+hipError_t launch_fold_value_query(const FoldVQArgs& a, hipStream_t s);
 
 // ---- per-kernel timing (ivc_profile_*) -----------------------------------------
 void prof_begin(const char* name, hipStream_t s);
