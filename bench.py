@@ -110,6 +110,11 @@ def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
             # projection and the eight block products stream their weights once
             "gating": dict(flops=None, bytes=(2 * C * C + 8 * G * cfg["gate_hidden"]) * e),
             "compact": dict(flops=None, bytes=2 * Lp * D * e + L_seq * 4 * 2 + Lp * 4 * 2),
+            # its halves when forward_compact runs it: the index work (ids read;
+            # ids, positions and keep map written; a source code per output row)
+            # and the row copy
+            "compact_index": dict(flops=None, bytes=L_seq * 4 * 4 + Lp * 8),
+            "compact_copy": dict(flops=None, bytes=2 * Lp * D * e + Lp * 8),
         })
     return out
 
@@ -289,24 +294,31 @@ class FlashStep:
         self.ivc.ivc_tile_offsets(self.tiles_d, len(cfg["tiles"]), self.off_d, self.st_d,
                                   self.stream)
         if self.args.run_mode == "routed":
-            # route + route-first run in one call (the LayerNorm statistics
-            # pass runs beside the router)
+            # route + route-first run + compaction in one call: the compaction's
+            # index work runs beside the projector chains, its row copy after them
             if self.rbuf is None:
                 self.rbuf = dict(
                     gate=torch.empty((T, 2), dtype=torch.float32, device="cuda"),
                     thr=torch.empty(1, dtype=torch.float64, device="cuda"),
                     use64=torch.empty(T, dtype=torch.uint8, device="cuda"), pooled=None,
                     status=torch.zeros(1, dtype=torch.int32, device="cuda"),
-                    out256=self.o256, out64=self.o64)
-            self.rbuf = self.con.forward(self.x, with_pooled=False, stream=self.stream,
-                                         out=self.rbuf)
+                    out256=self.o256, out64=self.o64,
+                    ids=torch.empty(self.L, dtype=torch.int32, device="cuda"),
+                    pos=torch.empty(self.L, dtype=torch.int32, device="cuda"),
+                    keep_map=torch.empty(self.L, dtype=torch.int32, device="cuda"),
+                    embeds=torch.empty((self.L, cfg["D"]), dtype=torch.bfloat16, device="cuda"),
+                    len=torch.zeros(1, dtype=torch.int64, device="cuda"))
+            self.rbuf = self.con.forward_compact(self.x, self.ids_d, self.emb_d,
+                                                 self.synth.IMG_CONTEXT, with_pooled=False,
+                                                 stream=self.stream, out=self.rbuf)
+            self.cbuf = self.rbuf
         else:
             self.rbuf = self.con.route(self.x, with_pooled=False, stream=self.stream,
                                        out=self.rbuf)
             self.con.run(self.x, self.o256, self.o64, stream=self.stream)
-        self.cbuf = self.con.compact(self.ids_d, self.emb_d, self.rbuf["use64"], self.o256,
-                                     self.o64, self.synth.IMG_CONTEXT, stream=self.stream,
-                                     out=self.cbuf)
+            self.cbuf = self.con.compact(self.ids_d, self.emb_d, self.rbuf["use64"], self.o256,
+                                         self.o64, self.synth.IMG_CONTEXT, stream=self.stream,
+                                         out=self.cbuf)
 
     def algorithmic(self):
         use64 = self.rbuf["use64"].cpu().numpy()
@@ -530,6 +542,8 @@ def std_config_result(name, args, torch, synth, ivc, Connector) -> dict:
 AUX_KERNELS = {"k_pool_folded_merge", "k_pool_merge", "k_splitk_reduce", "k_compact_plan",
                "k_compact_map", "k_compact_copy", "k_cbatch_bounds", "k_cbatch_plan",
                "k_cbatch_map"}
+# kernels after which the row copy belongs to the same compaction launch
+COPY_AFTER = {"k_compact_map", "k_cbatch_map", "k_cbatch_plan"}
 # the kernel family each launch name may start with (a check of the alignment)
 LAUNCH_FAMILY = {
     "tile_offsets": ("k_tile_offsets",), "token_stats": ("k_token_stats",),
@@ -548,6 +562,7 @@ LAUNCH_FAMILY = {
     "gating": ("k_gating_fused",),
     "quantile_decide": ("k_quantile_decide",), "route_lists": ("k_route_lists",),
     "compact": ("k_compact_count", "k_set_i64"), "compact_batch": ("k_compact_count",),
+    "compact_index": ("k_compact_count", "k_set_i64"), "compact_copy": ("k_compact_copy",),
 }
 
 
@@ -621,7 +636,17 @@ def label_dispatches(disp: dict, launches: list[str]) -> dict:
     dispatch is a kernel outside AUX_KERNELS.  Dispatches of the connector's
     set-up (before the first traced launch) are the surplus at the front."""
     ids = sorted(k for k, d in disp.items() if "ivc::" in d["symbol"])
-    heads = [i for i in ids if kernel_base(disp[i]["symbol"]) not in AUX_KERNELS]
+
+    def is_head(n: int) -> bool:
+        base = kernel_base(disp[ids[n]]["symbol"])
+        if base not in AUX_KERNELS:
+            return True
+        # the row copy is a launch of its own unless the index kernels of its
+        # compaction come right before it
+        return (base == "k_compact_copy" and n > 0
+                and kernel_base(disp[ids[n - 1]]["symbol"]) not in COPY_AFTER)
+
+    heads = [ids[n] for n in range(len(ids)) if is_head(n)]
     skip = len(heads) - len(launches)
     if skip < 0:
         raise ValueError(f"{len(launches)} traced launches but only {len(heads)} dispatches")
@@ -634,10 +659,11 @@ def label_dispatches(disp: dict, launches: list[str]) -> dict:
         head_label[i] = name
     labels, cur = {}, None
     first = heads[skip] if skip < len(heads) else None
+    head_set = set(heads)
     for i in ids:
         if i in head_label:
             cur = head_label[i]
-        elif first is None or i < first or kernel_base(disp[i]["symbol"]) not in AUX_KERNELS:
+        elif first is None or i < first or i in head_set:
             continue
         labels[i] = cur
     return labels

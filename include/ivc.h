@@ -261,6 +261,30 @@ ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids, const voi
                                  void* out_embeds, int64_t* out_len, int32_t* dev_status,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* ivc_connector_forward followed by ivc_connector_compact of its use64,
+ * out256 and out64 ([4B-Flash] sections 2-5; [2B-Flash] dual pipeline and
+ * routing decision; [14B] token injection), with the same outputs bit for
+ * bit.  The compaction's index work (ids, positions, keep map, L') needs only
+ * the decision, so it runs beside the projector products, on a stream of the
+ * connector's own that `stream` then waits for (no host synchronisation); the
+ * embedding rows are copied once the products are done.  Arguments as in those two calls,
+ * one dev_status for both; one workspace of
+ * ivc_connector_forward_compact_workspace_bytes(h, max_tiles, max_seq_len)
+ * bytes holds the forward's and the compaction's scratch side by side
+ * (IVC_ERR_WORKSPACE if smaller; the compaction's arguments are checked
+ * before anything is enqueued).  Requires flash = 1. */
+size_t ivc_connector_forward_compact_workspace_bytes(const ivc_connector* h, int32_t max_tiles,
+                                                     int64_t max_seq_len);
+ivc_status ivc_connector_forward_compact(ivc_connector* h, const void* vit,
+                                         const int32_t* valid_tokens, int32_t T, float* gate,
+                                         double* threshold, uint8_t* use64, float* pooled,
+                                         int32_t* dev_status, void* out256, void* out64,
+                                         const int32_t* ids, const void* embeds, int64_t L,
+                                         int32_t img_context_id, int32_t* out_ids,
+                                         int32_t* out_pos, int32_t* keep_map, void* out_embeds,
+                                         int64_t* out_len, void* ws, size_t ws_bytes,
+                                         void* stream);
+
 /* For callers that cannot allocate device memory and cannot supply a
  * workspace (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): ivc_connector_compact with the same arguments,

@@ -107,6 +107,29 @@ def test_label_dispatches_assigns_aux_kernels_to_their_launch(tmp_path):
         bench.label_dispatches(disp, _LAUNCHES * 3)
 
 
+def test_label_dispatches_split_compaction():
+    # forward_compact: the index kernels right after the decision, the row copy
+    # after the products, as a launch of its own
+    disp = {i + 1: {"symbol": sym, "counters": {}} for i, sym in enumerate([
+        "void ivc::k_widen(void const*, int, float*, long long)",
+        "void ivc::k_quantile_decide(float const*)",
+        "void ivc::k_compact_count(int const*)",
+        "void ivc::k_compact_plan(int const*)",
+        "void ivc::k_compact_map(int const*)",
+        "void ivc::k_gemm_dma8<1, true>(ivc::GemmOps)",
+        "void ivc::k_compact_copy<4>(long long const*)",
+        "void ivc::k_compact_count(int const*)",
+        "void ivc::k_compact_plan(int const*)",
+        "void ivc::k_compact_map(int const*)",
+        "void ivc::k_compact_copy<4>(long long const*)",
+    ])}
+    launches = ["quantile_decide", "compact_index", "mlp1_gemm1", "compact_copy", "compact"]
+    labels = bench.label_dispatches(disp, launches)
+    assert [labels.get(i) for i in sorted(disp)] == [
+        None, "quantile_decide", "compact_index", "compact_index", "compact_index", "mlp1_gemm1",
+        "compact_copy", "compact", "compact", "compact", "compact"]
+
+
 def test_counter_summary_round_trip(tmp_path):
     wdir = tmp_path / "internvl35_4b_std"
     # fetch reads half of a copy's bytes (scale 2), write reads them all (scale 1)

@@ -22,6 +22,9 @@ class Connector:
         self.h = ivc.ivc_connector_create(self.c_cfg, self.c_w, stream)
         self._weights = None
         self.ws_bytes = ivc.ivc_connector_workspace_bytes(self.h, max_tiles, max_seq_len)
+        if cfg.get("flash") and max_seq_len > 0:  # room for forward_compact too
+            self.ws_bytes = max(self.ws_bytes, ivc.ivc_connector_forward_compact_workspace_bytes(
+                self.h, max_tiles, max_seq_len))
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
         self.S = (cfg["P"] // 2) ** 2
         self.S64 = (cfg["P"] // 4) ** 2
@@ -92,6 +95,36 @@ class Connector:
         ivc.ivc_connector_forward(self.h, vit, valid, T, out["gate"], out["thr"], out["use64"],
                                   out["pooled"], out["status"], out["out256"], out["out64"],
                                   self.ws, self.ws_bytes, stream)
+        return out
+
+    def forward_compact(self, vit: torch.Tensor, ids, embeds, img_context_id: int, valid=None,
+                        with_pooled=True, stream=None, out=None):
+        """forward + compact of its outputs in one call (ivc_connector_forward_compact):
+        the forward's outputs and the compaction's (ids, pos, keep_map, embeds, len)."""
+        T = vit.shape[0]
+        L = ids.shape[0]
+        D = self.cfg["D"]
+        if out is None:
+            out = dict(
+                gate=torch.empty((T, 2), dtype=torch.float32, device=self.device),
+                thr=torch.empty(1, dtype=torch.float64, device=self.device),
+                use64=torch.empty(T, dtype=torch.uint8, device=self.device),
+                pooled=(torch.empty((T, self.cfg["C"]), dtype=torch.float32, device=self.device)
+                        if with_pooled else None),
+                status=torch.zeros(1, dtype=torch.int32, device=self.device),
+                out256=torch.empty((T, self.S, D), dtype=self.dtype, device=self.device),
+                out64=torch.empty((T, self.S64, D), dtype=self.dtype, device=self.device),
+                ids=torch.empty(L, dtype=torch.int32, device=self.device),
+                pos=torch.empty(L, dtype=torch.int32, device=self.device),
+                keep_map=torch.empty(L, dtype=torch.int32, device=self.device),
+                embeds=torch.empty((L, D), dtype=self.dtype, device=self.device),
+                len=torch.zeros(1, dtype=torch.int64, device=self.device),
+            )
+        ivc.ivc_connector_forward_compact(
+            self.h, vit, valid, T, out["gate"], out["thr"], out["use64"], out["pooled"],
+            out["status"], out["out256"], out["out64"], ids, embeds, L, img_context_id,
+            out["ids"], out["pos"], out["keep_map"], out["embeds"], out["len"], self.ws,
+            self.ws_bytes, stream)
         return out
 
     def compact(self, ids, embeds, use64, out256, out64, img_context_id: int, stream=None,

@@ -10,6 +10,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -173,6 +174,8 @@ struct ivc_connector {
   // mlp2 chain; forked from and joined back to the caller's stream by events
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipStream_t aux2 = nullptr;  // side work beside both projector chains
+  hipEvent_t ev_side = nullptr;
   char* blob = nullptr;
   // mlp1 / mlp2
   float *m1_ln_w, *m1_ln_b, *m1_b1, *m1_b2;
@@ -623,7 +626,9 @@ extern "C" ivc_status ivc_connector_create(const ivc_config* cfg, const ivc_weig
   if (c.flash && dt == IVC_BF16) {
     if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
+        hipStreamCreateWithFlags(&h->aux2, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_side, hipEventDisableTiming) != hipSuccess) {
       (void)hipGetLastError();
       ivc_connector_destroy(h);
       return fail(IVC_ERR_HIP, "stream/event creation failed");
@@ -804,6 +809,8 @@ extern "C" void ivc_connector_destroy(ivc_connector* h) {
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->aux) (void)hipStreamDestroy(h->aux);
+  if (h->ev_side) (void)hipEventDestroy(h->ev_side);
+  if (h->aux2) (void)hipStreamDestroy(h->aux2);
   delete h;
 }
 
@@ -835,9 +842,14 @@ extern "C" size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t 
 // ---------------------------------------------------------------------------
 // tokst_ready: the per-token moments are already in the workspace; lists_ready:
 // so are the per-path tile lists of use64 (both left by forward's route half)
+// side: work the caller adds at the point where the projector chains fork
+// (on a stream of its own beside both chains when they fork; joined with the
+// caller's stream at the end)
+using SideWork = std::function<ivc_status(hipStream_t)>;
 static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const uint8_t* use64,
                            void* out256, void* out64, void* ws, size_t ws_bytes, void* stream,
-                           bool tokst_ready = false, bool lists_ready = false) {
+                           bool tokst_ready = false, bool lists_ready = false,
+                           const SideWork* side = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   TRACE("run%s T=%d vit=%p ws=%zu tokst_ready=%d lists_ready=%d", use64 ? "_routed" : "", T, vit,
         ws_bytes, (int)tokst_ready, (int)lists_ready);
@@ -935,6 +947,28 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     HIP_OK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
     s1 = h->aux;
   }
+  // side work starts here too, on a third stream when the chains fork: its
+  // small workgroups take compute units as the products' tiles free them
+  const bool side_apart = side != nullptr && fork && h->aux2 != nullptr;
+  if (side != nullptr) {
+    hipStream_t ss = s;
+    if (side_apart) {
+      HIP_OK(hipStreamWaitEvent(h->aux2, h->ev_fork, 0));
+      ss = h->aux2;
+    }
+    const ivc_status st = (*side)(ss);
+    if (side_apart) {  // joined below, or here if the side work failed
+      HIP_OK(hipEventRecord(h->ev_side, ss));
+      if (st != IVC_OK) (void)hipStreamWaitEvent(s, h->ev_side, 0);
+    }
+    if (st != IVC_OK) {
+      if (fork) {  // nothing was enqueued on the mlp1 chain's stream yet
+        (void)hipEventRecord(h->ev_join, s1);
+        (void)hipStreamWaitEvent(s, h->ev_join, 0);
+      }
+      return st;
+    }
+  }
   const int M2 = (int)(T * S);
   // first product of a projector: the LayerNorm'd rows, or (ln_fold) the raw
   // ViT rows gathered in shuffle order with the LayerNorm applied in the epilogue
@@ -997,6 +1031,7 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3", g, s, &w.sc));
   }
   if (fork) HIP_OK(hipStreamWaitEvent(s, h->ev_join, 0));
+  if (side_apart) HIP_OK(hipStreamWaitEvent(s, h->ev_side, 0));
   return IVC_OK;
 }
 
@@ -1360,12 +1395,10 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
 // forward = route + route-first run in one call
 // ---------------------------------------------------------------------------
 
-extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
-                                            const int32_t* valid_tokens, int32_t T, float* gate,
-                                            double* threshold, uint8_t* use64, float* pooled,
-                                            int32_t* dev_status, void* out256, void* out64,
-                                            void* ws, size_t ws_bytes, void* stream) {
-  TRACE("forward T=%d (route, then route-first run)", T);
+static ivc_status forward_impl(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
+                               int32_t T, float* gate, double* threshold, uint8_t* use64,
+                               float* pooled, int32_t* dev_status, void* out256, void* out64,
+                               void* ws, size_t ws_bytes, void* stream, const SideWork* side) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward needs a flash connector");
   if (T > 0 && (!out256 || !out64)) return fail(IVC_ERR_INVALID_ARG, "null out256/out64");
@@ -1391,18 +1424,30 @@ extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
   ivc_status st = route_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status,
                              ws, ws_bytes, stream, tokst, lists ? &rl : nullptr);
   if (st != IVC_OK) return st;
-  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream, tokst != nullptr, lists);
+  return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream, tokst != nullptr, lists,
+                  side);
+}
+
+extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
+                                            const int32_t* valid_tokens, int32_t T, float* gate,
+                                            double* threshold, uint8_t* use64, float* pooled,
+                                            int32_t* dev_status, void* out256, void* out64,
+                                            void* ws, size_t ws_bytes, void* stream) {
+  TRACE("forward T=%d (route, then route-first run)", T);
+  return forward_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status, out256,
+                      out64, ws, ws_bytes, stream, nullptr);
 }
 
 // ---------------------------------------------------------------------------
 // compact
 // ---------------------------------------------------------------------------
-static ivc_status compact_impl(ivc_connector* h, const int32_t* ids, const void* embeds,
+// checks a compaction's arguments and lays out its workspace (nothing launched)
+static ivc_status compact_prep(ivc_connector* h, const int32_t* ids, const void* embeds,
                                int64_t L, int32_t img_context_id, const uint8_t* use64,
                                const void* out256, const void* out64, int32_t T, int32_t* out_ids,
                                int32_t* out_pos, int32_t* keep_map, void* out_embeds,
                                int64_t* out_len, int32_t* dev_status, void* ws, size_t ws_bytes,
-                               void* stream) {
+                               CompactArgs* out) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   const ivc_config& c = h->cfg;
   if (L < 0 || T < 0) return fail(IVC_ERR_INVALID_ARG, "negative L or T");
@@ -1450,6 +1495,21 @@ static ivc_status compact_impl(ivc_connector* h, const int32_t* ids, const void*
   a.blk_off = w.off;
   a.routed_before = w.rb;
   a.src = w.src;
+  *out = a;
+  return IVC_OK;
+}
+
+static ivc_status compact_impl(ivc_connector* h, const int32_t* ids, const void* embeds,
+                               int64_t L, int32_t img_context_id, const uint8_t* use64,
+                               const void* out256, const void* out64, int32_t T, int32_t* out_ids,
+                               int32_t* out_pos, int32_t* keep_map, void* out_embeds,
+                               int64_t* out_len, int32_t* dev_status, void* ws, size_t ws_bytes,
+                               void* stream) {
+  CompactArgs a{};
+  const ivc_status st = compact_prep(h, ids, embeds, L, img_context_id, use64, out256, out64, T,
+                                     out_ids, out_pos, keep_map, out_embeds, out_len, dev_status,
+                                     ws, ws_bytes, &a);
+  if (st != IVC_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   LAUNCH("compact", s, launch_compact(a, s));
   return IVC_OK;
@@ -1465,6 +1525,54 @@ extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids
   TRACE("compact L=%lld T=%d img_context=%d ws=%zu", (long long)L, T, img_context_id, ws_bytes);
   return compact_impl(h, ids, embeds, L, img_context_id, use64, out256, out64, T, out_ids, out_pos,
                       keep_map, out_embeds, out_len, dev_status, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// forward + compact in one call: the compaction's index half needs only the
+// decision, so it runs beside the projector chains on a stream of its own; the
+// row copy follows the join
+// ---------------------------------------------------------------------------
+static size_t forward_ws_bytes(const ivc_connector* h, int T) {
+  return (tokst_offset(h, T) + tokst_bytes(h, T) + 255) & ~(size_t)255;
+}
+
+extern "C" size_t ivc_connector_forward_compact_workspace_bytes(const ivc_connector* h,
+                                                                int32_t max_tiles,
+                                                                int64_t max_seq_len) {
+  if (!h || max_tiles < 0 || max_seq_len < 0) return 0;
+  return forward_ws_bytes(h, max_tiles) + plan_compact(max_tiles, max_seq_len, nullptr, nullptr);
+}
+
+extern "C" ivc_status ivc_connector_forward_compact(
+    ivc_connector* h, const void* vit, const int32_t* valid_tokens, int32_t T, float* gate,
+    double* threshold, uint8_t* use64, float* pooled, int32_t* dev_status, void* out256,
+    void* out64, const int32_t* ids, const void* embeds, int64_t L, int32_t img_context_id,
+    int32_t* out_ids, int32_t* out_pos, int32_t* keep_map, void* out_embeds, int64_t* out_len,
+    void* ws, size_t ws_bytes, void* stream) {
+  TRACE("forward_compact T=%d L=%lld img_context=%d ws=%zu", T, (long long)L, img_context_id,
+        ws_bytes);
+  if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
+  if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
+  if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward_compact needs a flash connector");
+  const size_t fw = forward_ws_bytes(h, T);
+  if (!ws || ws_bytes < fw) return fail(IVC_ERR_WORKSPACE, "forward_compact: workspace too small");
+  // the compaction's scratch sits after the forward's: the two run at once
+  CompactArgs a{};
+  ivc_status st = compact_prep(h, ids, embeds, L, img_context_id, use64, out256, out64, T, out_ids,
+                               out_pos, keep_map, out_embeds, out_len, dev_status,
+                               (char*)ws + fw, ws_bytes - fw, &a);
+  if (st != IVC_OK) return st;
+  const SideWork side = [&](hipStream_t s1) -> ivc_status {
+    LAUNCH("compact_index", s1, launch_compact_index(a, s1));
+    return IVC_OK;
+  };
+  st = forward_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status, out256,
+                    out64, ws, fw, stream, &side);
+  if (st != IVC_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) LAUNCH("compact_index", s, launch_compact_index(a, s));  // no run, no side chain
+  LAUNCH("compact_copy", s, launch_compact_copy(a, s));
+  return IVC_OK;
 }
 
 // ---------------------------------------------------------------------------

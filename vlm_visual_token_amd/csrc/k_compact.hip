@@ -421,7 +421,9 @@ hipError_t launch_compact_batch(const CompactBatchArgs& ba, hipStream_t s) {
   return launch_copy(a, ba.total, s);
 }
 
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+// The index half: ids, positions, keep map, L' and each output row's source
+// (needs use64 and ids only, not the projector outputs).
+hipError_t launch_compact_index(const CompactArgs& a, hipStream_t s) {
   const long long nblk = compact_blocks(a.L);
   if (a.L == 0) {
     // nothing to scan; out_len = 0 (a kernel, not a memset, so the call can be graph-captured)
@@ -436,7 +438,19 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
                      a.use64, a.T, a.S, a.S64, (const int32_t*)a.blk_off,
                      (const int32_t*)a.routed_before, (const long long*)a.out_len, a.out_ids,
                      a.out_pos, a.keep_map, a.src);
+  return hipGetLastError();
+}
+
+// The copy half: the embedding rows, from the index half's sources.
+hipError_t launch_compact_copy(const CompactArgs& a, hipStream_t s) {
+  if (a.L == 0) return hipSuccess;
   return launch_copy(a, (const long long*)a.out_len, s);
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  const hipError_t e = launch_compact_index(a, s);
+  if (e != hipSuccess) return e;
+  return launch_compact_copy(a, s);
 }
 
 // ---- ragged tile offsets -------------------------------------------------------

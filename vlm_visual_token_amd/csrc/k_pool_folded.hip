@@ -238,7 +238,8 @@ void folded_geometry(int T, int N, int C, int ncu, int* G, int* Q, int* segmax) 
   long long g = (long long)(ncu > 0 ? ncu : 256) * wpc;
   if (g > total) g = total;
   if (g < 1) g = 1;
-  const long long q = (total + g - 1) / g;
+  // no chunks (T = 0): no workgroups, and a quota of 1 keeps the layout defined
+  const long long q = total > 0 ? (total + g - 1) / g : 1;
   *Q = (int)q;
   *G = (int)((total + q - 1) / q);
   *segmax = (int)((q + NC - 1) / NC) + 1;

@@ -243,6 +243,10 @@ struct CompactBatchArgs {
   int32_t* layout_ok;        // [1]
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+// its two halves: the index work (reads ids and use64) and the row copy
+// (reads the index half's sources and out_len, and out256 / out64)
+hipError_t launch_compact_index(const CompactArgs& a, hipStream_t s);
+hipError_t launch_compact_copy(const CompactArgs& a, hipStream_t s);
 hipError_t launch_compact_batch(const CompactBatchArgs& a, hipStream_t s);
 
 // Per-path tile lists of a routing decision: rank[t] = index of t among the

@@ -90,6 +90,10 @@ def load() -> ctypes.CDLL:
         "ivc_connector_forward": (c_int32, [P, P, P, c_int32, P, P, P, P, P, P, P, P, c_size_t, P]),
         "ivc_connector_compact": (c_int32, [P, P, P, c_int64, c_int32, P, P, P, c_int32, P, P, P,
                                             P, P, P, P, c_size_t, P]),
+        "ivc_connector_forward_compact": (c_int32, [P, P, P, c_int32, P, P, P, P, P, P, P, P, P,
+                                                    c_int64, c_int32, P, P, P, P, P, P, c_size_t,
+                                                    P]),
+        "ivc_connector_forward_compact_workspace_bytes": (c_size_t, [P, c_int32, c_int64]),
         "ivc_connector_compact_noalloc": (c_int32, [P, P, P, c_int64, c_int32, P, P, P, c_int32, P,
                                                     P, P, P, P, P, P]),
         "ivc_connector_compact_batch": (c_int32, [P, P, P, c_int32, P, c_int64, c_int32, P, P, P,
@@ -118,6 +122,7 @@ def exported_symbols() -> list[str]:
         "ivc_connector_create", "ivc_connector_destroy", "ivc_connector_workspace_bytes",
         "ivc_connector_run", "ivc_connector_run_routed", "ivc_connector_route", "ivc_connector_forward",
         "ivc_connector_compact", "ivc_connector_compact_noalloc",
+        "ivc_connector_forward_compact", "ivc_connector_forward_compact_workspace_bytes",
         "ivc_connector_compact_batch", "ivc_connector_compact_batch_workspace_bytes", "ivc_route_decide",
         "ivc_tile_offsets",
         "ivc_pixel_shuffle", "ivc_profile_enable", "ivc_profile_reset", "ivc_profile_read",
@@ -256,6 +261,21 @@ def ivc_connector_compact(h, ids, embeds, L, img_context_id, use64, out256, out6
                                         _ptr(out_pos), _ptr(keep_map), _ptr(out_embeds),
                                         _ptr(out_len), _ptr(dev_status), _ptr(ws), ws_bytes,
                                         _stream(stream)), "ivc_connector_compact")
+
+
+def ivc_connector_forward_compact_workspace_bytes(h, max_tiles, max_seq_len) -> int:
+    return int(load().ivc_connector_forward_compact_workspace_bytes(h, max_tiles, max_seq_len))
+
+
+def ivc_connector_forward_compact(h, vit, valid_tokens, T, gate, threshold, use64, pooled,
+                                  dev_status, out256, out64, ids, embeds, L, img_context_id,
+                                  out_ids, out_pos, keep_map, out_embeds, out_len, ws, ws_bytes,
+                                  stream=None) -> None:
+    _check(load().ivc_connector_forward_compact(
+        h, _ptr(vit), _ptr(valid_tokens), T, _ptr(gate), _ptr(threshold), _ptr(use64),
+        _ptr(pooled), _ptr(dev_status), _ptr(out256), _ptr(out64), _ptr(ids), _ptr(embeds), L,
+        img_context_id, _ptr(out_ids), _ptr(out_pos), _ptr(keep_map), _ptr(out_embeds),
+        _ptr(out_len), _ptr(ws), ws_bytes, _stream(stream)), "ivc_connector_forward_compact")
 
 
 def ivc_connector_compact_noalloc(h, ids, embeds, L, img_context_id, use64, out256, out64, T,
