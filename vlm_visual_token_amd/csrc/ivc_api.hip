@@ -840,8 +840,24 @@ extern "C" size_t ivc_connector_workspace_bytes(const ivc_connector* h, int32_t 
 // ---------------------------------------------------------------------------
 // run
 // ---------------------------------------------------------------------------
+// The LayerNorm-folded products address a tile's gathered ViT rows with 32-bit
+// byte offsets (route-first tiles may gather from anywhere in the batch), so a
+// call keeps its ViT rows under this many bytes and larger batches run as
+// consecutive sub-batches.  IVC_FOLD_CHUNK_BYTES sets a smaller cap (tests).
+static long long fold_chunk_cap() {
+  const long long def = (1ll << 31) - (1ll << 24);
+  const char* e = getenv("IVC_FOLD_CHUNK_BYTES");
+  if (e != nullptr && *e != '\0') {
+    const long long v = atoll(e);
+    if (v > 0 && v < def) return v;
+  }
+  return def;
+}
+
 // tokst_ready: the per-token moments are already in the workspace; lists_ready:
-// so are the per-path tile lists of use64 (both left by forward's route half)
+// so are the per-path tile lists of use64 (both left by forward's route half);
+// tokst_in: the moments of these T tiles are here instead (a sub-batch of a
+// call whose moments were made for the whole batch)
 // side: work the caller adds at the point where the projector chains fork
 // (on a stream of its own beside both chains when they fork; joined with the
 // caller's stream at the end)
@@ -849,7 +865,7 @@ using SideWork = std::function<ivc_status(hipStream_t)>;
 static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const uint8_t* use64,
                            void* out256, void* out64, void* ws, size_t ws_bytes, void* stream,
                            bool tokst_ready = false, bool lists_ready = false,
-                           const SideWork* side = nullptr) {
+                           const SideWork* side = nullptr, const float* tokst_in = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   TRACE("run%s T=%d vit=%p ws=%zu tokst_ready=%d lists_ready=%d", use64 ? "_routed" : "", T, vit,
         ws_bytes, (int)tokst_ready, (int)lists_ready);
@@ -867,6 +883,33 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   const size_t need = tstats ? tokst_offset(h, T) + tokst_bytes(h, T) : plan_run(h, T, nullptr, nullptr);
   if (!ws || ws_bytes < need)
     return fail(IVC_ERR_WORKSPACE, "run needs %zu workspace bytes, got %zu", need, ws_bytes);
+  const bool fold = c.ln_fold != 0;
+  const long long rows_t = (long long)c.has_cls + (long long)c.grid * c.grid;
+  const long long tile_bytes = rows_t * c.vit_width * h->esz;
+  const long long cap = fold_chunk_cap();
+  if (fold && (long long)T * tile_bytes >= cap) {
+    // consecutive sub-batches under the cap, one after another on the stream
+    // (tiles are independent; each sub-batch builds its own path lists, in the
+    // workspace below where the whole batch's moments sit)
+    const int per = (int)((cap - 1) / tile_bytes);
+    if (per < 1) return fail(IVC_ERR_UNSUPPORTED, "ln_fold: one tile's ViT rows exceed the cap");
+    const float* tok = tokst_in != nullptr ? tokst_in
+                       : (tstats && tokst_ready) ? (const float*)((char*)ws + tokst_offset(h, T))
+                                                 : nullptr;
+    const long long S64 = (long long)(c.grid / 4) * (c.grid / 4);
+    const size_t row = (size_t)c.llm_width * h->esz;
+    for (int t0 = 0; t0 < T; t0 += per) {
+      const int n = T - t0 < per ? T - t0 : per;
+      const ivc_status st = run_impl(
+          h, (const char*)vit + (size_t)t0 * tile_bytes, n, use64 ? use64 + t0 : nullptr,
+          (char*)out256 + (size_t)t0 * S * row,
+          out64 ? (void*)((char*)out64 + (size_t)t0 * S64 * row) : nullptr, ws, ws_bytes, stream,
+          false, false, t0 == 0 ? side : nullptr,
+          tok ? tok + (size_t)t0 * c.grid * c.grid * 2 : nullptr);
+      if (st != IVC_OK) return st;
+    }
+    return IVC_OK;
+  }
   RunWs w;
   plan_run(h, T, ws, &w);
   hipStream_t s = (hipStream_t)stream;
@@ -892,9 +935,6 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     rm64.c_rpg = S4;
   }
 
-  const bool fold = c.ln_fold != 0;
-  if (fold && (long long)T * (c.has_cls + c.grid * c.grid) * C * 2 >= (1ll << 31) - (1ll << 24))
-    return fail(IVC_ERR_UNSUPPORTED, "ln_fold: %d tiles of ViT rows exceed 2 GiB", T);
   ShuffleArgs sa{};
   sa.dtype = dt;
   sa.X = vit;
@@ -922,8 +962,9 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   if (fold && tstats) {
     // per-token moments (unless the first token pass left them), then each
     // shuffled row's (mean, rstd) from its 4 or 16 cells
-    float* tokst = (float*)((char*)ws + tokst_offset(h, T));
-    if (!tokst_ready)
+    float* tokst = tokst_in != nullptr ? const_cast<float*>(tokst_in)
+                                       : (float*)((char*)ws + tokst_offset(h, T));
+    if (!tokst_ready && tokst_in == nullptr)
       LAUNCH("token_stats", s,
              launch_token_stats(vit, T, c.has_cls + c.grid * c.grid, c.has_cls, c.grid * c.grid,
                                 C, tokst, s,
