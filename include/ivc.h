@@ -160,10 +160,11 @@ typedef struct ivc_connector ivc_connector;
  * library-owned device memory (biases and LayerNorm parameters widened to
  * float32; the K/V projections of all pooling layers packed into one
  * [2 * layers * C, C] matrix), synchronises `stream`, and returns the handle
- * in *out.  A bf16 flash connector also owns a second stream (default
- * priority) and two events: run and run_routed fork the mlp1 chain onto that
- * stream after the loader and join it back into the caller's stream, so the
- * two projector chains share the chip.  The handle's weights are immutable
+ * in *out.  A bf16 flash connector also owns two more streams (default
+ * priority) and three events: run and run_routed fork the mlp1 chain onto the
+ * first after the loader and join it back into the caller's stream, so the
+ * two projector chains share the chip; forward_compact runs the compaction's
+ * index work on the second beside them.  The handle's weights are immutable
  * afterwards; calls may use several streams, but one handle must not be used
  * by two host threads at once (the fork/join events are shared).  Errors:
  * IVC_ERR_INVALID_ARG, IVC_ERR_UNSUPPORTED, IVC_ERR_MISALIGNED, IVC_ERR_OOM,
