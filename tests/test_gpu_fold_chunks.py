@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import synth
 from tests.gpu_util import dev_vit, dev_weights, host_weights, say, workload
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +90,27 @@ def test_run_sub_batches_standard_connector():
     mx = ((a - b).abs().max() / a.pow(2).mean().sqrt()).item()
     say(f"  rel-L2 {rel:.2e}, max-abs/rms {mx:.2e}")
     assert rel < 2e-3 and mx < 5e-2
+
+
+def test_forward_compact_sub_batches_bit_identical():
+    """forward_compact with the run half in sub-batches (the compaction's index
+    work beside the first one): the same outputs bit for bit."""
+    from vlm_visual_token_amd import Connector
+    cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
+    T = 24
+    cfg["tiles"], cfg["T"] = [T], T
+    ids, emb = synth.make_sequence(cfg)
+    say(f"forward_compact in sub-batches of 10 tiles (T={T}, L={len(ids)})")
+    con = Connector(cfg, dev_weights(cfg, host_weights(cfg)), max_tiles=T, max_seq_len=len(ids))
+    xd = dev_vit(cfg)
+    ids_d = torch.from_numpy(ids).cuda()
+    emb_d = torch.from_numpy(emb).to(torch.bfloat16).cuda()
+    img = synth.IMG_CONTEXT
+    whole = _clone(con.forward_compact(xd, ids_d, emb_d, img))
+    torch.cuda.synchronize()
+    parts = _with_cap(10 * _tile_bytes(cfg) + 1,
+                      lambda: _clone(con.forward_compact(xd, ids_d, emb_d, img)))
+    for k in ("gate", "thr", "use64", "status", "ids", "pos", "keep_map", "len"):
+        assert torch.equal(whole[k], parts[k]), k
+    n = int(whole["len"].item())
+    assert torch.equal(whole["embeds"][:n], parts["embeds"][:n])

@@ -74,6 +74,22 @@ def test_forward_compact_flash_workload(ln_fold):
     say(f"  routed {int(use.sum())}/{cfg['T']}, L' = {n}")
 
 
+def test_forward_compact_flash_padded():
+    """bf16 with a padding mask: the chains fork, and the moments come from the
+    statistics pass (the token pass does not read every token)."""
+    from vlm_visual_token_amd import Connector
+    cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
+    T = 24
+    cfg["tiles"], cfg["T"] = [T], T
+    ids, emb = synth.make_sequence(cfg)
+    say(f"forward_compact 2B-Flash padded: T={T} L={len(ids)}")
+    con = Connector(cfg, dev_weights(cfg, host_weights(cfg)), max_tiles=T, max_seq_len=len(ids))
+    vd = torch.from_numpy(synth.make_valid_tokens(cfg, seed=5)).cuda()
+    f, c, fc = _both(con, dev_vit(cfg), torch.from_numpy(ids).cuda(),
+                     torch.from_numpy(emb).to(torch.bfloat16).cuda(), vd)
+    _same(f, c, fc)
+
+
 @pytest.mark.parametrize("name,padded", [("tiny_flash_f32", False), ("tiny_flash_f32", True)])
 def test_forward_compact_tiny(name, padded):
     """fp32: the chains do not fork, the index work runs on the caller's stream."""
