@@ -453,49 +453,99 @@ def roofline_of(kern: dict, alg: dict, counters: dict | None) -> dict:
     return roof
 
 
-def compact_batch_stress(con, cfg, n_prompts, use64_one, torch, synth, ivc) -> dict:
+class CompactBatch:
     """Batched compaction at serving scale: n_prompts prompts of this
     workload's layout packed back to back (each with its own tiles, routed as
-    the timed batch was), one ivc_connector_compact_batch call per step.
-    Rows are copies, so the embedding and feature buffers are zero-filled."""
-    B = n_prompts
-    ids, _, cu, to = synth.make_batch_sequences(cfg, [cfg["tiles"]] * B, 0, with_embeds=False)
-    L, T, D, S, S64 = len(ids), int(to[-1]), cfg["D"], cfg["S"], cfg["S64"]
-    use = np.tile(use64_one, B).astype(np.uint8)
-    dev = "cuda"
-    ids_d = torch.from_numpy(ids).to(dev)
-    cu_d = torch.from_numpy(cu).to(dev)
-    to_d = torch.from_numpy(to).to(dev)
-    use_d = torch.from_numpy(use).to(dev)
-    emb = torch.zeros((L, D), dtype=torch.bfloat16, device=dev)
-    o256 = torch.zeros((T, S, D), dtype=torch.bfloat16, device=dev)
-    o64 = torch.zeros((T, S64, D), dtype=torch.bfloat16, device=dev)
-    n = ivc.ivc_connector_compact_batch_workspace_bytes(con.h, T, L, B)
-    ws = torch.empty(n, dtype=torch.uint8, device=dev)
-    out = None
-    stream = torch.cuda.current_stream()
+    use64_one routes one batch), one ivc_connector_compact_batch call per
+    step.  Rows are copies, so the embedding and feature buffers are
+    zero-filled."""
+
+    def __init__(self, con, cfg, n_prompts, use64_one, torch, synth, ivc):
+        self.con, self.synth, self.torch = con, synth, torch
+        B = n_prompts
+        ids, _, cu, to = synth.make_batch_sequences(cfg, [cfg["tiles"]] * B, 0,
+                                                    with_embeds=False)
+        L, T, D = len(ids), int(to[-1]), cfg["D"]
+        self.B, self.L, self.T, self.D, self.S, self.S64 = B, L, T, D, cfg["S"], cfg["S64"]
+        self.use = np.tile(use64_one, B).astype(np.uint8)
+        dev = "cuda"
+        self.ids_d = torch.from_numpy(ids).to(dev)
+        self.cu_d = torch.from_numpy(cu).to(dev)
+        self.to_d = torch.from_numpy(to).to(dev)
+        self.use_d = torch.from_numpy(self.use).to(dev)
+        self.emb = torch.zeros((L, D), dtype=torch.bfloat16, device=dev)
+        self.o256 = torch.zeros((T, cfg["S"], D), dtype=torch.bfloat16, device=dev)
+        self.o64 = torch.zeros((T, cfg["S64"], D), dtype=torch.bfloat16, device=dev)
+        n = ivc.ivc_connector_compact_batch_workspace_bytes(con.h, T, L, B)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.out = None
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        self.out = self.con.compact_batch(self.ids_d, self.cu_d, self.emb, self.to_d, self.use_d,
+                                          self.o256, self.o64, self.synth.IMG_CONTEXT,
+                                          stream=self.stream, out=self.out, ws=self.ws)
+
+    def out_len(self) -> int:
+        return int(self.out["cu"][-1].item())
+
+    def algorithmic(self) -> dict:
+        Lp = self.out_len()
+        return {"compact_batch": dict(flops=None, bytes=2 * Lp * self.D * 2 + self.L * 4 * 2
+                                      + Lp * 4 * 2)}
+
+    def close(self):
+        del self.emb, self.o256, self.o64, self.ws, self.out
+        self.torch.cuda.empty_cache()
+
+
+class CompactBatchWork(CompactBatch):
+    """The batched compaction of bench.py's figure on a connector of its own
+    (for the profiler): 64 prompts of the 2B-Flash layout, every other tile
+    routed (half the tiles, as the timed batch routes them)."""
+
+    def __init__(self, args, torch, synth, ivc, Connector, n_prompts=64):
+        cfg = dict(synth.config(WORKLOAD), pool_mode=args.pool_mode, ln_fold=args.ln_fold)
+        with open(os.path.join(ROOT, "tests", "golden", "gate_bias.json")) as f:
+            bias = json.load(f)["gate_bias0"][WORKLOAD]
+        self.own = Connector(cfg, weights_on_gpu(cfg, torch, synth, bias), max_tiles=cfg["T"])
+        use_one = (np.arange(cfg["T"]) % 2).astype(np.uint8)
+        super().__init__(self.own, cfg, n_prompts, use_one, torch, synth, ivc)
+
+    def close(self):
+        super().close()
+        self.own.close()
+
+
+def compact_batch_stress(con, cfg, n_prompts, use64_one, torch, synth, ivc) -> dict:
+    """The batched compaction timed: 2 warm-up calls, then 10 between events."""
+    work = CompactBatch(con, cfg, n_prompts, use64_one, torch, synth, ivc)
     for _ in range(2):
-        out = con.compact_batch(ids_d, cu_d, emb, to_d, use_d, o256, o64, synth.IMG_CONTEXT,
-                                stream=stream, out=out, ws=ws)
+        work.step()
     torch.cuda.synchronize()
     reps = 10
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    ev0.record(work.stream)
     for _ in range(reps):
-        con.compact_batch(ids_d, cu_d, emb, to_d, use_d, o256, o64, synth.IMG_CONTEXT,
-                          stream=stream, out=out, ws=ws)
-    ev1.record(stream)
+        work.step()
+    ev1.record(work.stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / reps
-    Lp = int(out["cu"][-1].item())
-    assert int(out["status"].item()) == 0 and Lp == L - (S - S64) * int(use.sum())
-    byts = 2 * Lp * D * 2 + L * 4 * 2 + Lp * 4 * 2
+    L, T, S, S64 = work.L, work.T, work.S, work.S64
+    Lp = work.out_len()
+    assert int(work.out["status"].item()) == 0 and Lp == L - (S - S64) * int(work.use.sum())
+    byts = work.algorithmic()["compact_batch"]["bytes"]
     gbs = byts / (ms / 1e3) / 1e9
-    res = {"prompts": B, "tiles": T, "L": L, "L_out": Lp, "ms": ms, "gbs": gbs,
+    res = {"prompts": work.B, "tiles": T, "L": L, "L_out": Lp, "ms": ms, "gbs": gbs,
            "frac_hbm": gbs / PEAK_HBM_GBS, "algorithmic_bytes": byts}
-    del emb, o256, o64, ws, out
-    torch.cuda.empty_cache()
+    # the counter reading of a call of the same shape (64 prompts of this
+    # layout, half the tiles routed: profile workload compact_batch)
+    cc = committed_counters("compact_batch")
+    if cc and "compact_batch" in cc and work.B == 64:
+        res["traffic_bytes"] = cc["compact_batch"]["traffic_bytes"]
+        res["rocprof_us"] = cc["compact_batch"]["duration_us"]
+    work.close()
     return res
 
 
@@ -995,6 +1045,8 @@ def profile_workload(args, torch, synth, ivc, Connector):
     wl = args.profile_workload
     if wl == WORKLOAD:
         work = FlashStep(args, torch, synth, ivc, Connector)
+    elif wl == "compact_batch":
+        work = CompactBatchWork(args, torch, synth, ivc, Connector)
     else:
         work = StdRun(wl, torch, synth, ivc, Connector)
     for _ in range(args.warmup):
