@@ -33,8 +33,14 @@ IVC_DEV uint32_t cvt_pk(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-// 8 fp32 values -> bf16 high parts and the bf16 rounding of what they leave
+// 8 fp32 values -> bf16 high parts and the bf16 rounding of what they leave.
+// No contraction: where the caller formed x as a product, a fused
+// multiply-subtract would take lo from the unrounded product, and whether the
+// compiler fuses depends on what it can prove about the caller's step mask
+// (known to be 1 in the first step of a load round), so the same tile would
+// split differently in kernels that load different numbers of K steps at once.
 IVC_DEV void split8(const float4& x0, const float4& x1, bf16x8_t& hi, bf16x8_t& lo) {
+#pragma clang fp contract(off)
   u32x4 h, l;
   h.x = cvt_pk(x0.x, x0.y);
   h.y = cvt_pk(x0.z, x0.w);
