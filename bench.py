@@ -52,13 +52,14 @@ CALIB_COPY_KIB = 524288  # one calibration copy: 512 MiB read and 512 MiB writte
 # algorithmic work per kernel launch
 # ---------------------------------------------------------------------------
 def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
-                route_first: bool = True) -> dict:
+                route_first: bool = True, placed: bool = False) -> dict:
     """{launch name: {"flops": F, "bytes": B}} per launch (None where a kernel
     has no stated figure).  Flops are 2 M N K of the products; bytes are the
     operands read once and the results written once, bf16 activations and
     weights, fp32 statistics (8 bytes per row: mean and rstd).  On the
     route-first Flash step each projector runs on its own tiles only
-    (``n64`` tiles take the 64-token path)."""
+    (``n64`` tiles take the 64-token path); ``placed``: each chain's last
+    product also writes its rows into the compacted sequence (forward_compact)."""
     T, C, D, N = cfg["T"], cfg["C"], cfg["D"], cfg["N"]
     S, S64 = cfg["S"], cfg["S64"]
     H1, H2 = cfg["mlp1_hidden"], cfg["mlp2_hidden"]
@@ -75,7 +76,8 @@ def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
                            bytes=n256 * N * C * e + H1 * 4 * C * e + n256 * S * H1 * e
                            + (n256 * S * 8 if cfg.get("ln_fold") else 0)),
         "mlp1_gemm2": dict(flops=2.0 * n256 * S * D * H1,
-                           bytes=n256 * S * H1 * e + D * H1 * e + n256 * S * D * e),
+                           bytes=n256 * S * H1 * e + D * H1 * e
+                           + (2 if placed else 1) * n256 * S * D * e),
         "token_stats": dict(flops=None, bytes=x_read + T * N * 8),
         "ln_stats": dict(flops=None, bytes=T * N * 8 + (n256 * S + n64 * S64) * 8),
         # with the LayerNorm fold the loader only writes each row's statistics
@@ -93,7 +95,8 @@ def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
             "mlp2_gemm2": dict(flops=2.0 * n64 * S64 * H2 * H2,
                                bytes=2 * n64 * S64 * H2 * e + H2 * H2 * e),
             "mlp2_gemm3": dict(flops=2.0 * n64 * S64 * D * H2,
-                               bytes=n64 * S64 * H2 * e + D * H2 * e + n64 * S64 * D * e),
+                               bytes=n64 * S64 * H2 * e + D * H2 * e
+                               + (2 if placed else 1) * n64 * S64 * D * e),
             # folded pooling: one pass over a tile's tokens per layer; the first
             # layer's pass also writes each token's LayerNorm moments
             "pool_folded_stats": dict(flops=None, bytes=x_read + T * N * 8),
@@ -115,6 +118,10 @@ def algorithmic(cfg: dict, n64: int | None = None, L_seq: int = 0, Lp: int = 0,
             # and the row copy
             "compact_index": dict(flops=None, bytes=L_seq * 4 * 4 + Lp * 8),
             "compact_copy": dict(flops=None, bytes=2 * Lp * D * e + Lp * 8),
+            # the text rows alone (every output row's source code read): the
+            # image rows are the last products' second store
+            "compact_copy_text": dict(flops=None, bytes=2 * max(Lp - n256 * S - n64 * S64, 0)
+                                      * D * e + Lp * 8),
         })
     return out
 
@@ -295,7 +302,8 @@ class FlashStep:
                                   self.stream)
         if self.args.run_mode == "routed":
             # route + route-first run + compaction in one call: the compaction's
-            # index work runs beside the projector chains, its row copy after them
+            # index work and text rows run beside the projector chains, whose
+            # last products write the image rows into the compacted sequence
             if self.rbuf is None:
                 self.rbuf = dict(
                     gate=torch.empty((T, 2), dtype=torch.float32, device="cuda"),
@@ -323,8 +331,9 @@ class FlashStep:
     def algorithmic(self):
         use64 = self.rbuf["use64"].cpu().numpy()
         Lp = int(self.cbuf["len"].item())
-        return algorithmic(self.cfg, int(use64.sum()), self.L, Lp,
-                           route_first=self.args.run_mode == "routed")
+        routed = self.args.run_mode == "routed"
+        return algorithmic(self.cfg, int(use64.sum()), self.L, Lp, route_first=routed,
+                           placed=routed)
 
     def close(self):
         self.con.close()
@@ -591,7 +600,7 @@ def std_config_result(name, args, torch, synth, ivc, Connector) -> dict:
 # the compaction copy): their dispatches belong to the launch before them
 AUX_KERNELS = {"k_pool_folded_merge", "k_pool_merge", "k_splitk_reduce", "k_compact_plan",
                "k_compact_map", "k_compact_copy", "k_cbatch_bounds", "k_cbatch_plan",
-               "k_cbatch_map"}
+               "k_cbatch_map", "k_fill_i32"}
 # kernels after which the row copy belongs to the same compaction launch
 COPY_AFTER = {"k_compact_map", "k_cbatch_map", "k_cbatch_plan"}
 # the kernel family each launch name may start with (a check of the alignment)
@@ -613,6 +622,7 @@ LAUNCH_FAMILY = {
     "quantile_decide": ("k_quantile_decide",), "route_lists": ("k_route_lists",),
     "compact": ("k_compact_count", "k_set_i64"), "compact_batch": ("k_compact_count",),
     "compact_index": ("k_compact_count", "k_set_i64"), "compact_copy": ("k_compact_copy",),
+    "compact_copy_text": ("k_compact_copy_text",),
 }
 
 

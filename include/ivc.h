@@ -265,11 +265,15 @@ ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids, const voi
 /* ivc_connector_forward followed by ivc_connector_compact of its use64,
  * out256 and out64 ([4B-Flash] sections 2-5; [2B-Flash] dual pipeline and
  * routing decision; [14B] token injection), with the same outputs bit for
- * bit.  The compaction's index work (ids, positions, keep map, L') needs only
- * the decision, so it runs beside the projector products, on a stream of the
- * connector's own that `stream` then waits for (no host synchronisation); the
- * embedding rows are copied once the products are done.  Arguments as in those two calls,
- * one dev_status for both; one workspace of
+ * bit.  The compaction's index work (ids, positions, keep map, L', and the
+ * compacted row of every image slot) needs only the decision, so it runs
+ * beside the projector products, with the copy of the text embedding rows,
+ * on a stream of the connector's own that `stream` then waits for (no host
+ * synchronisation).  Each projector's last product writes its rows into
+ * out_embeds as well as into out256 / out64 when it runs on the 256 x 256
+ * kernel (bf16, enough rows to fill the chip); rows it cannot place are
+ * copied once the products are done.  Arguments as in those two calls, one
+ * dev_status for both; one workspace of
  * ivc_connector_forward_compact_workspace_bytes(h, max_tiles, max_seq_len)
  * bytes holds the forward's and the compaction's scratch side by side
  * (IVC_ERR_WORKSPACE if smaller; the compaction's arguments are checked

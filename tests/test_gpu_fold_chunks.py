@@ -114,3 +114,35 @@ def test_forward_compact_sub_batches_bit_identical():
         assert torch.equal(whole[k], parts[k]), k
     n = int(whole["len"].item())
     assert torch.equal(whole["embeds"][:n], parts["embeds"][:n])
+
+
+def test_forward_compact_placed_rows_in_sub_batches():
+    """The 208-tile 2B-Flash batch in two sub-batches of 104: mlp1's last
+    product places its rows in the compacted sequence itself in both, mlp2's
+    (104 x 64 rows) runs on the smaller-tile kernel and leaves its rows to the
+    row copy after the join.  Everything bit for bit as in one call, where
+    both last products place their rows."""
+    from vlm_visual_token_amd import Connector
+    cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
+    T = cfg["T"]
+    ids, emb = synth.make_sequence(cfg)
+    say(f"forward_compact in sub-batches of 104 tiles (T={T}, L={len(ids)})")
+    con = Connector(cfg, dev_weights(cfg, host_weights(cfg)), max_tiles=T, max_seq_len=len(ids))
+    xd = dev_vit(cfg)
+    ids_d = torch.from_numpy(ids).cuda()
+    emb_d = torch.from_numpy(emb).to(torch.bfloat16).cuda()
+    img = synth.IMG_CONTEXT
+    whole = _clone(con.forward_compact(xd, ids_d, emb_d, img))
+    torch.cuda.synchronize()
+    parts = _with_cap(104 * _tile_bytes(cfg) + 1,
+                      lambda: _clone(con.forward_compact(xd, ids_d, emb_d, img)))
+    for k in ("gate", "thr", "use64", "status", "ids", "pos", "keep_map", "len"):
+        assert torch.equal(whole[k], parts[k]), k
+    n = int(whole["len"].item())
+    assert torch.equal(whole["embeds"][:n], parts["embeds"][:n])
+    use = whole["use64"].cpu().numpy().astype(bool)
+    assert 0 < use.sum() < T
+    for t in np.nonzero(~use)[0]:
+        assert torch.equal(whole["out256"][t], parts["out256"][t]), f"out256 tile {t}"
+    for t in np.nonzero(use)[0]:
+        assert torch.equal(whole["out64"][t], parts["out64"][t]), f"out64 tile {t}"

@@ -3,9 +3,11 @@ ivc_connector_compact on the same inputs: gates, threshold, decisions,
 pooled vectors, the chosen path's projector rows, and the compacted ids,
 positions, keep map, length and embedding rows, bit for bit.  Parity of
 forward and compact with the oracle is covered by their own tests.  Also
-the forked path (bf16, the index work on a stream of its own beside both
-projector chains) and the unforked one (fp32), a padding mask, T = 0, and a
-workspace that is too small (reported before anything is enqueued)."""
+the forked path (bf16, the index work and text rows on a stream of its own
+beside both projector chains; at 208 tiles both chains' last products write
+their rows into the compacted sequence themselves), the unforked one (fp32),
+a padding mask, T = 0, a sequence with the wrong slot count (nothing placed),
+and a workspace that is too small (reported before anything is enqueued)."""
 import numpy as np
 import pytest
 import torch
@@ -143,3 +145,43 @@ def test_forward_compact_no_tiles_and_small_workspace():
     torch.cuda.synchronize()
     for k, v in sentinel.items():  # nothing was enqueued (bytes: unwritten rows may hold NaN)
         assert torch.equal(out[k].view(torch.uint8), v.view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("change", ["one_short", "one_extra"])
+def test_forward_compact_wrong_slot_count_places_nothing(change):
+    """A sequence whose IMG_CONTEXT count is not 256 per tile compacts to
+    length 0 with status bit 1 ([4B-Flash] section 4 compaction; the single
+    prompt rule).  At 208 tiles the projectors' last products place their
+    rows themselves, so they must place none here: the embedding rows keep
+    what the caller left in them."""
+    from vlm_visual_token_amd import Connector
+    cfg = workload("internvl35_2b_flash", pool_mode=1, ln_fold=1)
+    T = cfg["T"]
+    ids, emb = synth.make_sequence(cfg)
+    img = synth.IMG_CONTEXT
+    at = np.nonzero(ids == img)[0]
+    if change == "one_short":
+        keep = np.ones(len(ids), dtype=bool)
+        keep[at[len(at) // 2]] = False
+        ids2, emb2 = ids[keep], emb[keep]
+    else:
+        ids2 = np.insert(ids, at[-1] + 1, img)
+        emb2 = np.insert(emb, at[-1] + 1, emb[at[-1]], axis=0)
+    say(f"forward_compact, {change}: T={T} L={len(ids2)} (slots {int((ids2 == img).sum())})")
+    con = Connector(cfg, dev_weights(cfg, host_weights(cfg)), max_tiles=T, max_seq_len=len(ids2))
+    xd = dev_vit(cfg)
+    ids_d = torch.from_numpy(ids2).cuda()
+    emb_d = torch.from_numpy(emb2).to(torch.bfloat16).cuda()
+    out = con.forward_compact(xd, ids_d, emb_d, img)
+    torch.cuda.synchronize()
+    out["embeds"].fill_(7.0)  # exact in bf16
+    out["status"].zero_()  # the library only ORs bits in
+    r = con.forward_compact(xd, ids_d, emb_d, img, out=out)
+    torch.cuda.synchronize()
+    assert int(r["len"].item()) == 0
+    assert int(r["status"].item()) & 1
+    assert torch.all(r["embeds"] == 7.0)
+    f = _clone(con.forward(xd))
+    torch.cuda.synchronize()
+    for k in ("gate", "thr", "use64"):
+        assert torch.equal(f[k], r[k]), k

@@ -333,6 +333,16 @@ void trace_gemm(const char* name, const GemmArgs& g, const char* family) {
         g.tail_part != nullptr);
 }
 
+// Whether gemm() runs the product on the 256 x 256 LDS-DMA kernel (the only
+// one that honours RowMap::d_map).
+bool gemm_takes_dma(GemmArgs g) {
+  if (g.batch <= 0) g.batch = 1;
+  if (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) return false;
+  if (g.batch != 1 || !gemm_mfma_supported(g)) return false;
+  const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  return big_tiles >= 256 && gemm_dma_supported(g);
+}
+
 hipError_t gemm(const char* name, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
   if (g.batch <= 0) g.batch = 1;
   if (trace_on()) {
@@ -862,10 +872,22 @@ static long long fold_chunk_cap() {
 // (on a stream of its own beside both chains when they fork; joined with the
 // caller's stream at the end)
 using SideWork = std::function<ivc_status(hipStream_t)>;
+// Projector rows placed straight into a compacted sequence (forward_compact):
+// the last product of each chain also writes every row to its compacted row,
+// slot_dst[tile * S + slot] (the compaction's index half, which runs beside
+// the chains, fills it; -1: nowhere).  Only the 256 x 256 DMA kernel can; a
+// chain whose product runs elsewhere leaves its rows to the row copy.
+struct DirectRows {
+  const int32_t* slot_dst = nullptr;  // this call's tiles
+  void* out = nullptr;                // the compacted embedding rows
+  bool side_ordered = false;          // the index half precedes what is enqueued next on the stream
+  bool all256 = true, all64 = true;   // every mlp1 / mlp2 last product placed its rows
+};
 static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const uint8_t* use64,
                            void* out256, void* out64, void* ws, size_t ws_bytes, void* stream,
                            bool tokst_ready = false, bool lists_ready = false,
-                           const SideWork* side = nullptr, const float* tokst_in = nullptr) {
+                           const SideWork* side = nullptr, const float* tokst_in = nullptr,
+                           DirectRows* dr = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   TRACE("run%s T=%d vit=%p ws=%zu tokst_ready=%d lists_ready=%d", use64 ? "_routed" : "", T, vit,
         ws_bytes, (int)tokst_ready, (int)lists_ready);
@@ -900,12 +922,22 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     const size_t row = (size_t)c.llm_width * h->esz;
     for (int t0 = 0; t0 < T; t0 += per) {
       const int n = T - t0 < per ? T - t0 : per;
+      DirectRows sub;
+      if (dr != nullptr) {
+        sub = *dr;
+        sub.slot_dst = dr->slot_dst + (size_t)t0 * S;
+      }
       const ivc_status st = run_impl(
           h, (const char*)vit + (size_t)t0 * tile_bytes, n, use64 ? use64 + t0 : nullptr,
           (char*)out256 + (size_t)t0 * S * row,
           out64 ? (void*)((char*)out64 + (size_t)t0 * S64 * row) : nullptr, ws, ws_bytes, stream,
           false, false, t0 == 0 ? side : nullptr,
-          tok ? tok + (size_t)t0 * c.grid * c.grid * 2 : nullptr);
+          tok ? tok + (size_t)t0 * c.grid * c.grid * 2 : nullptr, dr != nullptr ? &sub : nullptr);
+      if (dr != nullptr) {
+        dr->side_ordered = sub.side_ordered;
+        dr->all256 = dr->all256 && sub.all256;
+        dr->all64 = dr->all64 && sub.all64;
+      }
       if (st != IVC_OK) return st;
     }
     return IVC_OK;
@@ -1010,6 +1042,24 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
       return st;
     }
   }
+  // the last products may place their rows in the compacted sequence once the
+  // index half is ordered before them (on its own stream: an event wait)
+  const bool direct = dr != nullptr && use64 != nullptr &&
+                      (dr->side_ordered || (side != nullptr && (side_apart || !fork)));
+  auto place = [&](GemmArgs& g, hipStream_t st, bool& all) -> ivc_status {
+    GemmArgs t = g;
+    t.rm.d_map = direct ? dr->slot_dst : nullptr;
+    t.rm.d_stride = (int)S;
+    t.rm.d_out = direct ? dr->out : nullptr;
+    if (!direct || !gemm_takes_dma(t)) {
+      if (dr != nullptr) all = false;
+      return IVC_OK;
+    }
+    if (side_apart) HIP_OK(hipStreamWaitEvent(st, h->ev_side, 0));
+    g = t;
+    return IVC_OK;
+  };
+  bool unused = false;
   const int M2 = (int)(T * S);
   // first product of a projector: the LayerNorm'd rows, or (ln_fold) the raw
   // ViT rows gathered in shuffle order with the LayerNorm applied in the epilogue
@@ -1051,6 +1101,10 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
   g = mk_gemm(w.h1, H1, dt, h->m1_w2, dt, h->m1_b2, out256, dt, M2, D, H1, ACT_NONE);
   g.rm = rm256;
   with_tail(g, h, w.tail);
+  {
+    const ivc_status pst = place(g, s1, dr != nullptr ? dr->all256 : unused);
+    if (pst != IVC_OK) return pst;
+  }
   LAUNCH("mlp1_gemm2", s1, gemm("mlp1_gemm2", g, s1, &w.sc));
   if (fork) HIP_OK(hipEventRecord(h->ev_join, s1));
   if (c.flash) {
@@ -1069,10 +1123,16 @@ static ivc_status run_impl(ivc_connector* h, const void* vit, int32_t T, const u
     LAUNCH("mlp2_gemm2", s, gemm("mlp2_gemm2", g, s, &w.sc));
     g = mk_gemm(w.g2, H2, dt, h->m2_w3, dt, h->m2_b3, out64, dt, M4, D, H2, ACT_NONE);
     g.rm = rm64;
+    {
+      const ivc_status pst = place(g, s, dr != nullptr ? dr->all64 : unused);
+      if (pst != IVC_OK) return pst;
+    }
     LAUNCH("mlp2_gemm3", s, gemm("mlp2_gemm3", g, s, &w.sc));
   }
   if (fork) HIP_OK(hipStreamWaitEvent(s, h->ev_join, 0));
   if (side_apart) HIP_OK(hipStreamWaitEvent(s, h->ev_side, 0));
+  // whatever is enqueued on s next follows the side work
+  if (dr != nullptr && side != nullptr) dr->side_ordered = true;
   return IVC_OK;
 }
 
@@ -1439,7 +1499,8 @@ extern "C" ivc_status ivc_connector_route(ivc_connector* h, const void* vit,
 static ivc_status forward_impl(ivc_connector* h, const void* vit, const int32_t* valid_tokens,
                                int32_t T, float* gate, double* threshold, uint8_t* use64,
                                float* pooled, int32_t* dev_status, void* out256, void* out64,
-                               void* ws, size_t ws_bytes, void* stream, const SideWork* side) {
+                               void* ws, size_t ws_bytes, void* stream, const SideWork* side,
+                               DirectRows* dr = nullptr) {
   if (!h) return fail(IVC_ERR_INVALID_ARG, "null handle");
   if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward needs a flash connector");
   if (T > 0 && (!out256 || !out64)) return fail(IVC_ERR_INVALID_ARG, "null out256/out64");
@@ -1466,7 +1527,7 @@ static ivc_status forward_impl(ivc_connector* h, const void* vit, const int32_t*
                              ws, ws_bytes, stream, tokst, lists ? &rl : nullptr);
   if (st != IVC_OK) return st;
   return run_impl(h, vit, T, use64, out256, out64, ws, ws_bytes, stream, tokst != nullptr, lists,
-                  side);
+                  side, nullptr, dr);
 }
 
 extern "C" ivc_status ivc_connector_forward(ivc_connector* h, const void* vit,
@@ -1570,18 +1631,30 @@ extern "C" ivc_status ivc_connector_compact(ivc_connector* h, const int32_t* ids
 
 // ---------------------------------------------------------------------------
 // forward + compact in one call: the compaction's index half needs only the
-// decision, so it runs beside the projector chains on a stream of its own; the
-// row copy follows the join
+// decision, so it runs beside the projector chains on a stream of its own,
+// with the text rows' copy; the chains' last products write their rows into
+// the compacted sequence themselves (what they cannot place is copied after
+// the join)
 // ---------------------------------------------------------------------------
 static size_t forward_ws_bytes(const ivc_connector* h, int T) {
   return (tokst_offset(h, T) + tokst_bytes(h, T) + 255) & ~(size_t)255;
+}
+
+// the compaction's scratch, then the compacted row of every image slot
+static size_t compact_slots_offset(int T, long long L) {
+  return (plan_compact(T, L, nullptr, nullptr) + 255) & ~(size_t)255;
+}
+static size_t compact_slots_bytes(const ivc_connector* h, int T) {
+  const ivc_config& c = h->cfg;
+  return (size_t)T * (size_t)(c.grid / 2) * (size_t)(c.grid / 2) * 4;
 }
 
 extern "C" size_t ivc_connector_forward_compact_workspace_bytes(const ivc_connector* h,
                                                                 int32_t max_tiles,
                                                                 int64_t max_seq_len) {
   if (!h || max_tiles < 0 || max_seq_len < 0) return 0;
-  return forward_ws_bytes(h, max_tiles) + plan_compact(max_tiles, max_seq_len, nullptr, nullptr);
+  return forward_ws_bytes(h, max_tiles) + compact_slots_offset(max_tiles, max_seq_len) +
+         compact_slots_bytes(h, max_tiles);
 }
 
 extern "C" ivc_status ivc_connector_forward_compact(
@@ -1596,23 +1669,40 @@ extern "C" ivc_status ivc_connector_forward_compact(
   if (T < 0) return fail(IVC_ERR_INVALID_ARG, "T = %d", T);
   if (!h->cfg.flash) return fail(IVC_ERR_INVALID_ARG, "forward_compact needs a flash connector");
   const size_t fw = forward_ws_bytes(h, T);
-  if (!ws || ws_bytes < fw) return fail(IVC_ERR_WORKSPACE, "forward_compact: workspace too small");
+  if (L < 0) return fail(IVC_ERR_INVALID_ARG, "negative L");
+  const size_t need = fw + compact_slots_offset(T, L) + compact_slots_bytes(h, T);
+  if (!ws || ws_bytes < need)
+    return fail(IVC_ERR_WORKSPACE, "forward_compact needs %zu workspace bytes, got %zu", need,
+                ws_bytes);
   // the compaction's scratch sits after the forward's: the two run at once
   CompactArgs a{};
   ivc_status st = compact_prep(h, ids, embeds, L, img_context_id, use64, out256, out64, T, out_ids,
                                out_pos, keep_map, out_embeds, out_len, dev_status,
                                (char*)ws + fw, ws_bytes - fw, &a);
   if (st != IVC_OK) return st;
+  DirectRows dr;
+  if (T > 0) {
+    a.slot_dst = (int32_t*)((char*)ws + fw + compact_slots_offset(T, L));
+    dr.slot_dst = a.slot_dst;
+    dr.out = out_embeds;
+  }
   const SideWork side = [&](hipStream_t s1) -> ivc_status {
     LAUNCH("compact_index", s1, launch_compact_index(a, s1));
+    LAUNCH("compact_copy_text", s1, launch_compact_copy_text(a, s1));
     return IVC_OK;
   };
   st = forward_impl(h, vit, valid_tokens, T, gate, threshold, use64, pooled, dev_status, out256,
-                    out64, ws, fw, stream, &side);
+                    out64, ws, fw, stream, &side, T > 0 ? &dr : nullptr);
   if (st != IVC_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (T == 0) LAUNCH("compact_index", s, launch_compact_index(a, s));  // no run, no side chain
-  LAUNCH("compact_copy", s, launch_compact_copy(a, s));
+  if (T == 0) {  // no run, no side chain: only text rows
+    LAUNCH("compact_index", s, launch_compact_index(a, s));
+    LAUNCH("compact_copy_text", s, launch_compact_copy_text(a, s));
+    return IVC_OK;
+  }
+  // rows of the chains whose last product could not place them
+  const int kinds = (dr.all256 ? 0 : 2) | (dr.all64 ? 0 : 4);
+  if (kinds != 0) LAUNCH("compact_copy", s, launch_compact_copy_kinds(a, kinds, s));
   return IVC_OK;
 }
 

@@ -17,7 +17,10 @@
 //   2. k_compact_plan   (one workgroup) block offsets, routed_before, L', status
 //   3. k_compact_map    per-position keep flag and destination; writes
 //                       out_ids, out_pos, keep_map and a source code per row
+//                       (and, optionally, the compacted row of every image
+//                       slot, so a projector can write its rows there itself)
 //   4. k_compact_copy   one wave per output row, 16-byte copies of the row
+//                       (k_compact_copy_text: the text rows only)
 #include "common.h"
 #include "index_math.h"
 #include "kernels.h"
@@ -62,7 +65,7 @@ __global__ void __launch_bounds__(1024)
 k_compact_plan(const int32_t* __restrict__ cnt, long long nblk, const uint8_t* __restrict__ use64,
                int T, int S, int S64, long long L, int32_t* __restrict__ blk_off,
                int32_t* __restrict__ routed_before, long long* __restrict__ out_len,
-               int32_t* __restrict__ status) {
+               int32_t* __restrict__ status, int32_t* __restrict__ slot_dst) {
   __shared__ long long carry_s;
   __shared__ int wsum[16];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -109,6 +112,10 @@ k_compact_plan(const int32_t* __restrict__ cnt, long long nblk, const uint8_t* _
       *out_len = ok ? L - (long long)(S - S64) * n_routed : 0;
     }
   }
+  // slot destinations: with the right slot count the map kernel writes every
+  // entry; otherwise nothing is placed (slots the sequence lacks included)
+  if (out_len != nullptr && slot_dst != nullptr && n_img != (long long)T * S)
+    for (long long i = threadIdx.x; i < (long long)T * S; i += blockDim.x) slot_dst[i] = -1;
 }
 
 __global__ void __launch_bounds__(CT)
@@ -116,7 +123,8 @@ k_compact_map(const int32_t* __restrict__ ids, long long L, int img, const uint8
               int T, int S, int S64, const int32_t* __restrict__ blk_off,
               const int32_t* __restrict__ routed_before, const long long* __restrict__ out_len,
               int32_t* __restrict__ out_ids, int32_t* __restrict__ out_pos,
-              int32_t* __restrict__ keep_map, long long* __restrict__ src) {
+              int32_t* __restrict__ keep_map, long long* __restrict__ src,
+              int32_t* __restrict__ slot_dst) {
   const long long base = (long long)blockIdx.x * CB + threadIdx.x * 4;
   int tok[4], c = 0;
 #pragma unroll
@@ -148,23 +156,28 @@ k_compact_map(const int32_t* __restrict__ ids, long long L, int img, const uint8
       out_ids[j] = tok[e];
       src[j] = code;
     }
+    // L' = 0 (wrong slot count): nothing is placed
+    if (slot_dst != nullptr && is_img && tile < T) slot_dst[k] = keep && Lp > 0 ? (int32_t)j : -1;
     out_pos[p] = p < Lp ? (int32_t)p : -1;
     if (p >= Lp) out_ids[p] = -1;
     if (is_img) ++k;
   }
 }
 
-// One wave per output row, 16-byte vectors.
+// One wave per output row, 16-byte vectors; rows whose source kind (0 text,
+// 1 out256, 2 out64) is not in `kinds` are left alone.
 template <int VPL>
 __global__ void __launch_bounds__(256)
 k_compact_copy(const long long* __restrict__ src, const long long* __restrict__ out_len,
                const u32x4* __restrict__ embeds, const u32x4* __restrict__ o256,
-               const u32x4* __restrict__ o64, u32x4* __restrict__ out, int vpr, long long L) {
+               const u32x4* __restrict__ o64, u32x4* __restrict__ out, int vpr, long long L,
+               int kinds) {
   const long long j = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (j >= L || j >= *out_len) return;
   const long long code = src[j];
   const int kind = (int)(code >> 60);
+  if (((kinds >> kind) & 1) == 0) return;
   const long long idx = code & ((1ll << 60) - 1);
   const u32x4* s = (kind == 0 ? embeds : kind == 1 ? o256 : o64) + idx * vpr;
   u32x4* d = out + j * vpr;
@@ -181,7 +194,47 @@ k_compact_copy(const long long* __restrict__ src, const long long* __restrict__ 
   }
 }
 
+// The text rows only (a few percent of a compacted sequence): one wave per
+// 64 consecutive output rows reads their source codes at once and copies the
+// text rows among them one after another.
+template <int VPL>
+__global__ void __launch_bounds__(256)
+k_compact_copy_text(const long long* __restrict__ src, const long long* __restrict__ out_len,
+                    const u32x4* __restrict__ embeds, u32x4* __restrict__ out, int vpr,
+                    long long L) {
+  const long long j0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int lane = threadIdx.x & 63;
+  const long long n = min(L, *out_len);
+  if (j0 >= n) return;
+  const bool in = j0 + lane < n;
+  const long long code = in ? src[j0 + lane] : 0;
+  unsigned long long m = __ballot(in && (code >> 60) == 0);
+  while (m != 0ull) {
+    const int b = __builtin_ctzll(m);
+    m &= m - 1;
+    const long long idx = __shfl(code, b);
+    const u32x4* s = embeds + idx * vpr;
+    u32x4* d = out + (j0 + b) * vpr;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < vpr) v[i] = __builtin_nontemporal_load(s + c);
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < vpr) __builtin_nontemporal_store(v[i], d + c);
+    }
+  }
+}
+
 __global__ void k_set_i64(long long* p, long long v) { *p = v; }
+
+__global__ void __launch_bounds__(256) k_fill_i32(int32_t* p, long long n, int32_t v) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    p[i] = v;
+}
 
 // ---- batched, ragged compaction ---------------------------------------------
 // Per sequence the closed form above holds with the sequence's own counters:
@@ -377,7 +430,8 @@ k_cbatch_map(const int32_t* __restrict__ ids, long long L, int img,
   }
 }
 
-static hipError_t launch_copy(const CompactArgs& a, const long long* len, hipStream_t s) {
+static hipError_t launch_copy(const CompactArgs& a, const long long* len, hipStream_t s,
+                              int kinds = 7) {
   const int esz = a.dtype == DT_BF16 ? 2 : 4;
   const int vpr = (int)((long long)a.D * esz / 16);
   const int vpl = (vpr + 63) / 64;
@@ -385,7 +439,7 @@ static hipError_t launch_copy(const CompactArgs& a, const long long* len, hipStr
 #define IVC_COPY(n)                                                                              \
   hipLaunchKernelGGL(k_compact_copy<n>, grid, dim3(256), 0, s, (const long long*)a.src, len,    \
                      (const u32x4*)a.embeds, (const u32x4*)a.out256, (const u32x4*)a.out64,     \
-                     (u32x4*)a.out_embeds, vpr, a.L)
+                     (u32x4*)a.out_embeds, vpr, a.L, kinds)
   if (vpl <= 1) IVC_COPY(1);
   else if (vpl <= 2) IVC_COPY(2);
   else if (vpl <= 4) IVC_COPY(4);
@@ -405,7 +459,7 @@ hipError_t launch_compact_batch(const CompactBatchArgs& ba, hipStream_t s) {
   }
   hipLaunchKernelGGL(k_compact_plan, dim3(1), dim3(1024), 0, s, (const int32_t*)a.blk_cnt, nblk,
                      a.use64, a.T, a.S, a.S64, a.L, a.blk_off, a.routed_before,
-                     (long long*)nullptr, a.status);
+                     (long long*)nullptr, a.status, (int32_t*)nullptr);
   hipLaunchKernelGGL(k_cbatch_bounds, dim3((unsigned)((ba.B + 1 + 3) / 4)), dim3(256), 0, s, a.ids,
                      a.L, a.img_id, ba.cu, ba.B, (const int32_t*)a.blk_off, ba.seq_img);
   hipLaunchKernelGGL(k_cbatch_plan, dim3(1), dim3(1024), 0, s, ba.cu, ba.tile_off, ba.B, a.L, a.T,
@@ -428,16 +482,22 @@ hipError_t launch_compact_index(const CompactArgs& a, hipStream_t s) {
   if (a.L == 0) {
     // nothing to scan; out_len = 0 (a kernel, not a memset, so the call can be graph-captured)
     hipLaunchKernelGGL(k_set_i64, dim3(1), dim3(1), 0, s, a.out_len, 0ll);
+    if (a.slot_dst != nullptr && a.T > 0) {  // tiles but no slots: nothing is placed
+      const long long n = (long long)a.T * a.S;
+      hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024)),
+                         dim3(256), 0, s, a.slot_dst, n, -1);
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_compact_count, dim3((unsigned)nblk), dim3(CT), 0, s, a.ids, a.L, a.img_id,
                      a.blk_cnt);
   hipLaunchKernelGGL(k_compact_plan, dim3(1), dim3(1024), 0, s, (const int32_t*)a.blk_cnt, nblk,
-                     a.use64, a.T, a.S, a.S64, a.L, a.blk_off, a.routed_before, a.out_len, a.status);
+                     a.use64, a.T, a.S, a.S64, a.L, a.blk_off, a.routed_before, a.out_len, a.status,
+                     a.slot_dst);
   hipLaunchKernelGGL(k_compact_map, dim3((unsigned)nblk), dim3(CT), 0, s, a.ids, a.L, a.img_id,
                      a.use64, a.T, a.S, a.S64, (const int32_t*)a.blk_off,
                      (const int32_t*)a.routed_before, (const long long*)a.out_len, a.out_ids,
-                     a.out_pos, a.keep_map, a.src);
+                     a.out_pos, a.keep_map, a.src, a.slot_dst);
   return hipGetLastError();
 }
 
@@ -445,6 +505,31 @@ hipError_t launch_compact_index(const CompactArgs& a, hipStream_t s) {
 hipError_t launch_compact_copy(const CompactArgs& a, hipStream_t s) {
   if (a.L == 0) return hipSuccess;
   return launch_copy(a, (const long long*)a.out_len, s);
+}
+
+hipError_t launch_compact_copy_kinds(const CompactArgs& a, int kinds, hipStream_t s) {
+  if (a.L == 0 || (kinds & 7) == 0) return hipSuccess;
+  return launch_copy(a, (const long long*)a.out_len, s, kinds & 7);
+}
+
+hipError_t launch_compact_copy_text(const CompactArgs& a, hipStream_t s) {
+  if (a.L == 0) return hipSuccess;
+  const int esz = a.dtype == DT_BF16 ? 2 : 4;
+  const int vpr = (int)((long long)a.D * esz / 16);
+  const int vpl = (vpr + 63) / 64;
+  dim3 grid((unsigned)((a.L + 255) / 256));
+#define IVC_COPY_TEXT(n)                                                                      \
+  hipLaunchKernelGGL(k_compact_copy_text<n>, grid, dim3(256), 0, s, (const long long*)a.src, \
+                     (const long long*)a.out_len, (const u32x4*)a.embeds,                    \
+                     (u32x4*)a.out_embeds, vpr, a.L)
+  if (vpl <= 1) IVC_COPY_TEXT(1);
+  else if (vpl <= 2) IVC_COPY_TEXT(2);
+  else if (vpl <= 4) IVC_COPY_TEXT(4);
+  else if (vpl <= 8) IVC_COPY_TEXT(8);
+  else if (vpl <= 16) IVC_COPY_TEXT(16);
+  else return hipErrorInvalidValue;
+#undef IVC_COPY_TEXT
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {

@@ -190,11 +190,23 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
     const int row = m0 + r, col = n0 + 8 * c;
     if (row < M && col < N) {
       long long orow = row;
-      if (pow2)
-        orow = ((long long)rm.c_map[row >> sh] << sh) + (row & (rm.c_rpg - 1));
-      else if (rm.c_map != nullptr)
-        orow = (long long)rm.c_map[row / rm.c_rpg] * rm.c_rpg + row % rm.c_rpg;
+      int ot = 0, slot = 0;  // output tile and row within it (row map only)
+      if (pow2) {
+        ot = rm.c_map[row >> sh];
+        slot = row & (rm.c_rpg - 1);
+        orow = ((long long)ot << sh) + slot;
+      } else if (rm.c_map != nullptr) {
+        ot = rm.c_map[row / rm.c_rpg];
+        slot = row % rm.c_rpg;
+        orow = (long long)ot * rm.c_rpg + slot;
+      }
       *reinterpret_cast<u32x4*>(Cm + orow * ldc + col) = val;
+      if (rm.d_map != nullptr) {  // the same row in its place in the compacted sequence
+        const int dj = rm.d_map[(long long)ot * rm.d_stride + slot];
+        if (dj >= 0)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(rm.d_out) + (long long)dj * ldc + col) =
+              val;
+      }
     }
   }
 }
@@ -681,7 +693,9 @@ bool gemm_dma_supported(const GemmArgs& g) {
       g.a_dtype == DT_BF16 && g.w_dtype == DT_BF16 && g.c_dtype == DT_BF16 && g.K % 64 == 0 &&
       g.K > 0 && g.M > 0 && g.N > 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
       ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.W % 16) == 0 && g.N % 8 == 0 &&
-      g.ldc % 8 == 0 && ((uintptr_t)g.Cm % 16) == 0;
+      g.ldc % 8 == 0 && ((uintptr_t)g.Cm % 16) == 0 &&
+      (g.rm.d_map == nullptr || (g.rm.c_map != nullptr && g.rm.d_out != nullptr &&
+                                 ((uintptr_t)g.rm.d_out % 16) == 0 && g.rm.d_stride >= g.rm.c_rpg));
   if (!base || !g.fold) return base;
   // gathered A: C-wide cells hold whole K steps; K = r*r*C; lda = C; signed
   // 32-bit offsets inside the gathered tensor; row statistics and colsum given

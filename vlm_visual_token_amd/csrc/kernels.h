@@ -45,12 +45,19 @@ int shuffle_max_width(int dtype);
 // Optional device-side row count and output-row scatter of a GEMM: the grid
 // is sized for the host M (an upper bound); the product covers
 // min(M, *m_dev * m_mult) rows, and output row m is written to row
-// c_map[m / c_rpg] * c_rpg + m % c_rpg.
+// c_map[m / c_rpg] * c_rpg + m % c_rpg.  With d_map (needs c_map; the
+// 256 x 256 DMA product only) the row is written a second time, to row
+// d_map[c_map[m / c_rpg] * d_stride + m % c_rpg] of d_out (same row stride
+// as C), unless that entry is negative: a projector's rows placed straight
+// into the compacted sequence.
 struct RowMap {
   const int* m_dev = nullptr;
   int m_mult = 1;
   const int* c_map = nullptr;
   int c_rpg = 1;
+  const int32_t* d_map = nullptr;
+  int d_stride = 0;
+  void* d_out = nullptr;
 };
 
 // A operand gathered straight from the ViT rows: logical row m is shuffled
@@ -224,6 +231,9 @@ struct CompactArgs {
   int32_t* blk_off;        // [nblk + 1]
   int32_t* routed_before;  // [T + 1]
   long long* src;          // [L] source row code per output row
+  // optional: the compacted row of every image slot k = tile * S + loc, or
+  // -1 (a deleted slot, or no valid compaction), written by the index half
+  int32_t* slot_dst = nullptr;  // [T * S]
 };
 long long compact_blocks(long long L);
 
@@ -247,6 +257,12 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 // (reads the index half's sources and out_len, and out256 / out64)
 hipError_t launch_compact_index(const CompactArgs& a, hipStream_t s);
 hipError_t launch_compact_copy(const CompactArgs& a, hipStream_t s);
+// the rows of some sources only (kinds: bit 0 text embeddings, bit 1 rows of
+// out256, bit 2 rows of out64), one wave per output row
+hipError_t launch_compact_copy_kinds(const CompactArgs& a, int kinds, hipStream_t s);
+// the text embedding rows only, one wave per 64 output rows (a few percent of
+// a compacted sequence's rows are text)
+hipError_t launch_compact_copy_text(const CompactArgs& a, hipStream_t s);
 hipError_t launch_compact_batch(const CompactBatchArgs& a, hipStream_t s);
 
 // Per-path tile lists of a routing decision: rank[t] = index of t among the
