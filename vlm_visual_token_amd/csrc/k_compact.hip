@@ -194,37 +194,58 @@ k_compact_copy(const long long* __restrict__ src, const long long* __restrict__ 
   }
 }
 
-// The text rows only (a few percent of a compacted sequence): one wave per
-// 64 consecutive output rows reads their source codes at once and copies the
-// text rows among them one after another.
+// The text rows only (a few percent of a compacted sequence, in runs between
+// the images): one wave per 16 consecutive output rows reads their source
+// codes at once and copies the text rows among them, up to four at a time
+// (all of their loads, then all of their stores).
+constexpr int kTextRowsPerWave = 16;
 template <int VPL>
 __global__ void __launch_bounds__(256)
 k_compact_copy_text(const long long* __restrict__ src, const long long* __restrict__ out_len,
                     const u32x4* __restrict__ embeds, u32x4* __restrict__ out, int vpr,
                     long long L) {
-  const long long j0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const long long j0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * kTextRowsPerWave;
   const int lane = threadIdx.x & 63;
   const long long n = min(L, *out_len);
   if (j0 >= n) return;
-  const bool in = j0 + lane < n;
+  const bool in = lane < kTextRowsPerWave && j0 + lane < n;
   const long long code = in ? src[j0 + lane] : 0;
   unsigned long long m = __ballot(in && (code >> 60) == 0);
   while (m != 0ull) {
-    const int b = __builtin_ctzll(m);
-    m &= m - 1;
-    const long long idx = __shfl(code, b);
-    const u32x4* s = embeds + idx * vpr;
-    u32x4* d = out + (j0 + b) * vpr;
-    u32x4 v[VPL];
+    int b[4];
+    int k = 0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int c = lane + 64 * i;
-      if (c < vpr) v[i] = __builtin_nontemporal_load(s + c);
+    for (int q = 0; q < 4; ++q) {
+      b[q] = 0;
+      if (m != 0ull) {
+        b[q] = __builtin_ctzll(m);
+        m &= m - 1;
+        k = q + 1;
+      }
+    }
+    u32x4 v[4][VPL];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const long long idx = __shfl(code, b[q]);
+      if (q < k) {
+        const u32x4* s = embeds + idx * vpr;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int c = lane + 64 * i;
+          if (c < vpr) v[q][i] = __builtin_nontemporal_load(s + c);
+        }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int c = lane + 64 * i;
-      if (c < vpr) __builtin_nontemporal_store(v[i], d + c);
+    for (int q = 0; q < 4; ++q) {
+      if (q < k) {
+        u32x4* d = out + (j0 + b[q]) * vpr;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int c = lane + 64 * i;
+          if (c < vpr) __builtin_nontemporal_store(v[q][i], d + c);
+        }
+      }
     }
   }
 }
@@ -517,7 +538,8 @@ hipError_t launch_compact_copy_text(const CompactArgs& a, hipStream_t s) {
   const int esz = a.dtype == DT_BF16 ? 2 : 4;
   const int vpr = (int)((long long)a.D * esz / 16);
   const int vpl = (vpr + 63) / 64;
-  dim3 grid((unsigned)((a.L + 255) / 256));
+  const long long rows_per_wg = 4ll * kTextRowsPerWave;
+  dim3 grid((unsigned)((a.L + rows_per_wg - 1) / rows_per_wg));
 #define IVC_COPY_TEXT(n)                                                                      \
   hipLaunchKernelGGL(k_compact_copy_text<n>, grid, dim3(256), 0, s, (const long long*)a.src, \
                      (const long long*)a.out_len, (const u32x4*)a.embeds,                    \

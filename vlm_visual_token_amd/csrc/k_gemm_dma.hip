@@ -101,16 +101,30 @@ IVC_DEV int slab_swz(int r) { return ((r & 1) | ((r >> 1) & 2)) << 6; }
 // odd lane row R+1, columns c-1, c: one 4-byte LDS write per two values.
 // FOLD: value = rstd_row * acc - rstd_row * mean_row * colsum[col] + bias[col],
 // with the tile's 256 (mean, rstd) pairs staged in LDS first.
+// With a row map each tile row's output row (and, with d_map, its second
+// destination) is looked up once, into LDS at rmap, while the first phase
+// runs; the store loop then reads it from there.
 // NJ: 32-column blocks per wave (4: waves of 128 x 128, 4 per tile; 2: waves
 // of 128 x 64, 8 per tile); NTH: threads of the workgroup.
 template <int ACT, bool FOLD, int NJ = 2, int NTH = DNT>
 IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* q2, char* q3,
                         int wm, int wn, int m0, int n0, int M, int N, const float* bias,
                         bf16_t* Cm, long long ldc, const RowMap& rm, const float* ln_rows,
-                        const float* ln_colsum, float2* rowst /* FOLD: [256] in LDS */) {
+                        const float* ln_colsum, float2* rowst /* FOLD: [256] in LDS */,
+                        char* rmap /* row map: 256 * 12 bytes of LDS */) {
   constexpr int WC = 32 * NJ;  // columns per wave
   const int tid = threadIdx.x, lane = tid & 63;
   const bool odd_lane = lane & 1;
+  long long* orow_s = reinterpret_cast<long long*>(rmap);    // [256] output row
+  int* dj_s = reinterpret_cast<int*>(rmap + DBM * 8);         // [256] second destination
+  if (rm.c_map != nullptr) {
+    for (int r = tid; r < DBM; r += NTH) {
+      const int row = min(m0 + r, M - 1);
+      const int ot = rm.c_map[row / rm.c_rpg], slot = row % rm.c_rpg;
+      orow_s[r] = (long long)ot * rm.c_rpg + slot;
+      if (rm.d_map != nullptr) dj_s[r] = rm.d_map[(long long)ot * rm.d_stride + slot];
+    }
+  }
   // rowst: (rstd, -rstd * mean) per tile row
   float ccol[NJ];
   if (FOLD) {
@@ -176,9 +190,6 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
     }
   }
   __syncthreads();
-  // output row of tile row r (route-first products scatter groups of c_rpg rows)
-  const bool pow2 = rm.c_map != nullptr && (rm.c_rpg & (rm.c_rpg - 1)) == 0;
-  const int sh = pow2 ? __builtin_ctz((unsigned)rm.c_rpg) : 0;
   constexpr int RPI = NTH / 32;  // rows per iteration (32 threads x 16 bytes per row)
 #pragma unroll 4
   for (int it = 0; it < DBM / RPI; ++it) {
@@ -189,20 +200,11 @@ IVC_DEV void store_tile(const f32x16_t (&acc)[4][NJ], char* q0, char* q1, char* 
         *reinterpret_cast<const u32x4*>(slab + (r & 63) * 512 + ((c * 16) ^ slab_swz(r & 63)));
     const int row = m0 + r, col = n0 + 8 * c;
     if (row < M && col < N) {
-      long long orow = row;
-      int ot = 0, slot = 0;  // output tile and row within it (row map only)
-      if (pow2) {
-        ot = rm.c_map[row >> sh];
-        slot = row & (rm.c_rpg - 1);
-        orow = ((long long)ot << sh) + slot;
-      } else if (rm.c_map != nullptr) {
-        ot = rm.c_map[row / rm.c_rpg];
-        slot = row % rm.c_rpg;
-        orow = (long long)ot * rm.c_rpg + slot;
-      }
+      // output row of tile row r (route-first products scatter groups of c_rpg rows)
+      const long long orow = rm.c_map != nullptr ? orow_s[r] : (long long)row;
       *reinterpret_cast<u32x4*>(Cm + orow * ldc + col) = val;
       if (rm.d_map != nullptr) {  // the same row in its place in the compacted sequence
-        const int dj = rm.d_map[(long long)ot * rm.d_stride + slot];
+        const int dj = dj_s[r];
         if (dj >= 0)
           *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(rm.d_out) + (long long)dj * ldc + col) =
               val;
@@ -642,7 +644,8 @@ k_gemm_dma8(GemmOps o, const float* __restrict__ bias, bf16_t* __restrict__ Cm, 
   }
   __syncthreads();
   store_tile<ACT, FOLD, 2, DNT>(acc, sA0, sB0, sA1, sB1, wm, wn, m0, n0, o.M, o.N, bias, Cm, ldc,
-                                rm, ln_rows, ln_colsum, reinterpret_cast<float2*>(sA2));
+                                rm, ln_rows, ln_colsum, reinterpret_cast<float2*>(sA2),
+                                sA2 + 4096);
 }
 
 // One workgroup per output n: the folded weights of the first Linear after a
