@@ -346,21 +346,18 @@ bool gemm_takes_dma(GemmArgs g) {
 hipError_t gemm(const char* name, GemmArgs g, hipStream_t s, const SimtScratch* sc = nullptr) {
   if (g.batch <= 0) g.batch = 1;
   if (trace_on()) {
-    const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    const char* fam = (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) ? "f32a split-bf16 MFMA"
-                      : (g.batch == 1 && gemm_mfma_supported(g))
-                          ? (big_tiles >= 256 && gemm_dma_supported(g) ? "256x256 LDS-DMA MFMA"
-                                                                        : "128x128 MFMA")
-                          : "SIMT";
+    const char* fam = gemm_takes_dma(g)                                   ? "256x256 LDS-DMA MFMA"
+                      : (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) ? "f32a split-bf16 MFMA"
+                      : (g.batch == 1 && gemm_mfma_supported(g))        ? "128x128 MFMA"
+                                                                        : "SIMT";
     trace_gemm(name, g, fam);
   }
+  // 256 x 256 LDS-DMA tiles when they fill the chip (the only kernel that
+  // places rows a second time), else 128 x 128 tiles, split-bf16 or SIMT
+  if (gemm_takes_dma(g)) return launch_gemm_dma(g, s);
+  if (g.rm.d_map != nullptr) return hipErrorInvalidValue;
   if (g.c_dtype == DT_F32 && gemm_f32a_supported(g)) return launch_gemm_f32a(g, 0, nullptr, 1.f, s);
-  if (g.batch == 1 && gemm_mfma_supported(g)) {
-    // 256 x 256 LDS-DMA tiles when they fill the chip, else 128 x 128 tiles
-    const long long big_tiles = (long long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-    if (big_tiles >= 256 && gemm_dma_supported(g)) return launch_gemm_dma(g, s);
-    return launch_gemm_mfma(g, s);
-  }
+  if (g.batch == 1 && gemm_mfma_supported(g)) return launch_gemm_mfma(g, s);
   g.ksplit = 1;
   if (sc != nullptr && sc->part != nullptr) {
     const int ks = simt_ksplit(g.M, g.N, g.K, g.batch);
