@@ -195,10 +195,10 @@ k_compact_copy(const long long* __restrict__ src, const long long* __restrict__ 
 }
 
 // The text rows only (a few percent of a compacted sequence, in runs between
-// the images): one wave per 16 consecutive output rows reads their source
-// codes at once and copies the text rows among them, up to four at a time
-// (all of their loads, then all of their stores).
-constexpr int kTextRowsPerWave = 16;
+// the images): one wave per 4 consecutive output rows reads their source
+// codes and copies the text rows among them together (all of their loads,
+// then all of their stores).
+constexpr int kTextRowsPerWave = 4;
 template <int VPL>
 __global__ void __launch_bounds__(256)
 k_compact_copy_text(const long long* __restrict__ src, const long long* __restrict__ out_len,
