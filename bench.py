@@ -43,6 +43,7 @@ METRIC = "connector tiles/s (+visual tokens/s) at 1 GPU; % of MFMA / HBM peak"
 WORKLOAD = "internvl35_2b_flash"
 STD_CONFIGS = {"4b": "internvl35_4b_std", "14b": "internvl3_14b_ragged", "38b": "internvl3_38b"}
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_CLOCK_GHZ = 2.4  # the clock the MFMA peak is quoted at
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "vlm_visual_token_amd", "csrc")
 CALIB_COPY_KIB = 524288  # one calibration copy: 512 MiB read and 512 MiB written
@@ -435,6 +436,8 @@ def annotate(kern: dict, alg: dict, counters: dict | None):
                 v["mfma_flops_counted"] = c["mfma_flops"]
             if c.get("mfma_util") is not None:
                 v["mfma_busy"] = c["mfma_util"]
+            if c.get("clock_ghz") is not None:
+                v["clock_ghz"] = c["clock_ghz"]
             if c.get("duration_us") is not None:
                 v["rocprof_us"] = c["duration_us"]
 
@@ -452,6 +455,11 @@ def roofline_of(kern: dict, alg: dict, counters: dict | None) -> dict:
                 "traffic": c.get("traffic_bytes"),
                 "algorithmic_flops_per_launch": a["flops"],
                 "mfma_flops_counted": c.get("mfma_flops")}
+        if c.get("clock_ghz"):
+            # the clock the kernel ran at (counter pass) and the fraction of the
+            # peak at that clock (the published peak assumes 2.4 GHz)
+            roof["clock_ghz"] = c["clock_ghz"]
+            roof["frac_at_clock"] = ach / (PEAK_BF16_TFLOPS * c["clock_ghz"] / PEAK_CLOCK_GHZ)
     else:
         ach = (a.get("bytes") or 0.0) / sec / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
@@ -800,6 +808,12 @@ def summarize_workload(wdir: str) -> dict:
             ent["mfma_util"] = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / 8 * 1024)
         if "duration_ns" in v:
             ent["duration_us"] = v["duration_ns"] / 1e3
+            if v.get("GRBM_GUI_ACTIVE") and v["duration_ns"] >= 50e3:
+                # shader clock over the dispatch: GRBM_GUI_ACTIVE (summed over the
+                # 8 XCDs) of the counter pass over the kernel-trace duration (for
+                # launches of 50 us or more: the counter also covers the dispatch's
+                # own start and end, which dominate shorter ones)
+                ent["clock_ghz"] = v["GRBM_GUI_ACTIVE"] / 8 / v["duration_ns"]
         out["kernels"].append(ent)
     alg, ev = meta["launches"], meta.get("events", {})
     for ent in out["kernels"]:
@@ -812,6 +826,8 @@ def summarize_workload(wdir: str) -> dict:
         if ent.get("mfma_util") is not None and ent.get("duration_us", 0) >= \
                 L.get("_util_us", -1.0):
             L["mfma_util"], L["_util_us"] = ent["mfma_util"], ent.get("duration_us", 0)
+            if ent.get("clock_ghz") is not None:
+                L["clock_ghz"] = ent["clock_ghz"]
     for lab, L in out["launches"].items():
         L.pop("_util_us", None)
         a = alg.get(lab, {})
@@ -838,7 +854,9 @@ def write_counters_md(summary: dict, path: str) -> None:
              "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same counters "
              "read for a 512 MiB device-to-device copy.  MFMA work: "
              "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops; MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES "
-             "over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs.  Durations: the kernel-trace pass "
+             "over (GRBM_GUI_ACTIVE / 8 XCDs) x 1024 SIMDs; GHz: GRBM_GUI_ACTIVE / 8 over the "
+             "kernel-trace duration (the shader clock the launch ran at; peaks assume 2.4).  "
+             "Durations: the kernel-trace pass "
              "(`us`) and HIP events around each launch in the same run (`us ev`); both passes "
              "run the two projector chains one after the other, so each kernel has the chip "
              "to itself.  Launch names come from the library's own trace (IVC_TRACE=1), "
@@ -863,7 +881,7 @@ def write_counters_md(summary: dict, path: str) -> None:
     def f(x, sc=1.0, nd=1):
         return "" if x is None else f"{x * sc:.{nd}f}"
     hdr = ["launch", "kernels", "us", "us ev", "traffic MB", "alg. MB", "traffic/alg",
-           "GB/s (alg)", "MFMA GFLOP", "alg. GFLOP", "TFLOP/s", "MFMA busy"]
+           "GB/s (alg)", "MFMA GFLOP", "alg. GFLOP", "TFLOP/s", "MFMA busy", "GHz"]
     L.append("| " + " | ".join(hdr) + " |")
     L.append("|" + "---|" * len(hdr))
     order = sorted(summary["launches"].items(), key=lambda kv: -(kv[1].get("duration_us") or 0))
@@ -875,7 +893,7 @@ def write_counters_md(summary: dict, path: str) -> None:
             f(x.get("algorithmic_bytes"), 1e-6), f(x.get("traffic_over_algorithmic"), 1, 2),
             f(x.get("gbs"), 1, 0), f(x.get("mfma_flops"), 1e-9),
             f(x.get("algorithmic_flops"), 1e-9), f(x.get("tflops"), 1, 0),
-            "" if not util else f"{100 * util:.0f}%"]) + " |")
+            "" if not util else f"{100 * util:.0f}%", f(x.get("clock_ghz"), 1, 2)]) + " |")
     L.append("")
     L.append("Per kernel:")
     L.append("")
@@ -910,7 +928,8 @@ def counters_summary(d: str) -> None:
 
 
 def committed_counters(workload: str, path: str | None = None) -> dict | None:
-    """{launch name: {"traffic_bytes", "mfma_flops", "mfma_util", "duration_us"}}
+    """{launch name: {"traffic_bytes", "mfma_flops", "mfma_util", "duration_us",
+    "clock_ghz"}}
     from the committed summary profiles/counters_<workload>.md, for the
     launches whose kernels' sources are unchanged since the counters were
     taken; None when there is no summary."""
@@ -929,7 +948,7 @@ def committed_counters(workload: str, path: str | None = None) -> dict | None:
                     for k, (_, sha) in x["sources"].items())
         if fresh:
             out[lab] = {k: x.get(k) for k in ("traffic_bytes", "mfma_flops", "mfma_util",
-                                             "duration_us")}
+                                             "duration_us", "clock_ghz")}
     return out
 
 
