@@ -80,6 +80,19 @@ def _write_pass(d, counters):
                 w.writerow([i + 1, wg * 100, sym, wg, cn, fn(i, sym)])
 
 
+def _write_trace(d, dur_ns):
+    """A kernel-trace pass of the same dispatches, dispatch i lasting dur_ns(i, sym)."""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "p_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Grid_Size_X", "Kernel_Name", "Workgroup_Size_X",
+                    "Start_Timestamp", "End_Timestamp"])
+        t = 1000
+        for i, (sym, wg) in enumerate(_DISPATCHES):
+            w.writerow([i + 1, wg * 100, sym, wg, t, t + dur_ns(i, sym)])
+            t += dur_ns(i, sym) + 500
+
+
 def _write_log(path):
     with open(path, "w") as f:
         f.write("[ivc] create dtype=1 C=1024\n")
@@ -140,7 +153,9 @@ def test_counter_summary_round_trip(tmp_path):
         "SQ_INSTS_VALU_MFMA_MOPS_BF16": lambda i, s: 1000.0 if "gemm" in s else 0.0,
         "SQ_VALU_MFMA_BUSY_CYCLES": lambda i, s: 8192.0 * 512 if "gemm" in s else 0.0,
         "GRBM_GUI_ACTIVE": lambda i, s: 8 * 8192.0})
-    for p in ("fetch", "write"):
+    # the GEMMs last 100 us in the trace pass, everything else 10 us
+    _write_trace(str(wdir / "trace"), lambda i, s: 100000 if "gemm" in s else 10000)
+    for p in ("fetch", "write", "trace"):
         _write_log(str(wdir / (p + ".log")))
     cfg = synth.config("internvl35_4b_std")
     with open(wdir / "algorithmic.json", "w") as f:
@@ -155,6 +170,11 @@ def test_counter_summary_round_trip(tmp_path):
     assert g1["traffic_bytes"] == pytest.approx((700 * 2 + 10) * 1024)
     assert g1["mfma_flops"] == 512000.0
     assert g1["mfma_util"] == pytest.approx(0.5)
+    # 8192 active cycles per XCD over 100 us: 0.08192 GHz; launches shorter
+    # than 50 us carry no clock
+    assert g1["duration_us"] == pytest.approx(100.0)
+    assert g1["clock_ghz"] == pytest.approx(8192 / 100e3)
+    assert "clock_ghz" not in k[("ln_stats", "k_ln_stats")]
     assert g1["workgroups"] == 100
     assert s["commands"][0].startswith(
         'B="python3 $R/bench.py --profile-workload internvl35_4b_std --profile-out')
@@ -168,6 +188,7 @@ def test_counter_summary_round_trip(tmp_path):
     bench.write_counters_md(s, str(md))
     c = bench.committed_counters("internvl35_4b_std", str(md))
     assert c["mlp1_gemm1"]["traffic_bytes"] == pytest.approx(g1["traffic_bytes"])
+    assert c["mlp1_gemm1"]["clock_ghz"] == pytest.approx(g1["clock_ghz"])
     assert c["compact"]["traffic_bytes"] == pytest.approx(L["compact"]["traffic_bytes"])
     # a launch whose kernel source hash no longer matches drops out
     md.write_text(md.read_text().replace(g1["source_sha256"], "0" * 64))
@@ -181,3 +202,19 @@ def test_gpus_above_one_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_roofline_at_the_measured_clock():
+    kern = {"mlp2_gemm1": {"ms_per_step": 0.7, "ms_avg": 0.7},
+            "pool_folded": {"ms_per_step": 0.3, "ms_avg": 0.1}}
+    alg = {"mlp2_gemm1": {"flops": 875e9, "bytes": 4e8}}
+    r = bench.roofline_of(kern, alg, {"mlp2_gemm1": {"clock_ghz": 1.8, "traffic_bytes": 1e9}})
+    assert r["kernel"] == "mlp2_gemm1" and r["bound"] == "mfma"
+    assert r["achieved"] == pytest.approx(1250.0)
+    assert r["frac"] == pytest.approx(0.5)
+    # the peak scaled to 1.8 of the 2.4 GHz it is quoted at: 1875 TFLOP/s
+    assert r["frac_at_clock"] == pytest.approx(1250.0 / 1875.0)
+    assert r["traffic"] == 1e9
+    # no counter summary: no clock figures
+    r2 = bench.roofline_of(kern, alg, None)
+    assert "clock_ghz" not in r2 and "frac_at_clock" not in r2
