@@ -112,29 +112,32 @@ IVC_DEV float2 moments_pair(float2 a, float2 b, float half_n) {
   return make_float2((a.x + b.x) * 0.5f, fmaf(d * d, half_n, a.y + b.y));
 }
 
-// erf by the approximation of Abramowitz & Stegun, Handbook of Mathematical
-// Functions, formula 7.1.28 (absolute error <= 3e-7; about 2e-6 when
-// evaluated in fp32, far below the bf16 rounding of the GELU outputs):
-//   erf(x) = 1 - 1 / (1 + a1 x + a2 x^2 + ... + a6 x^6)^16,  x >= 0,
-// odd extension.  One reciprocal and no exponential (7.1.26 needs both), the
-// 16th power by four squarings; large |x| overflows the power to inf, which
-// gives the limit 1.  Branch-free (a library erf branches per range, which
-// costs the GEMM epilogues dearly when the lanes of a wave fall in different
-// ranges).
-IVC_DEV float erf_as(float x) {
+// GELU, 0.5 x (1 + erf(x / sqrt 2)), with erf by the approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.28
+// (absolute error <= 3e-7):
+//   erf(u) = sign(u) (1 - r),  r = 1 / P(|u|)^16,
+//   P(v) = 1 + a1 v + a2 v^2 + ... + a6 v^6.
+// Then GELU(x) = max(x, 0) - 0.5 |x| r with u = x / sqrt 2, and P(|x| / sqrt 2)
+// is a polynomial in |x| whose coefficient k is a_k 2^(-k/2).  One reciprocal,
+// no exponential (7.1.26 needs both), the 16th power by four squarings;
+// large |x| overflows the power to inf, giving r = 0 (the |x| that r
+// multiplies is capped at 1e30, so GELU(+inf) = +inf; NaN stays NaN, and
+// GELU(-inf) is NaN, as 0.5 x (1 + erf) gives).  Absolute error <= 1e-6 in
+// fp32, far below the bf16 rounding of the outputs.  Branch-free: a library
+// erf branches per range, which costs the GEMM epilogues dearly when the
+// lanes of a wave fall in different ranges.
+IVC_DEV float gelu_erf(float x) {
   const float ax = fabsf(x);
-  float p = fmaf(0.0000430638f, ax, 0.0002765672f);
-  p = fmaf(p, ax, 0.0001520143f);
-  p = fmaf(p, ax, 0.0092705272f);
-  p = fmaf(p, ax, 0.0422820123f);
-  p = fmaf(p, ax, 0.0705230784f);
+  float p = fmaf(5.3829750000e-06f, ax, 4.8890635643e-05f);
+  p = fmaf(p, ax, 3.8003575000e-05f);
+  p = fmaf(p, ax, 3.2776263241e-03f);
+  p = fmaf(p, ax, 2.1141006150e-02f);
+  p = fmaf(p, ax, 4.9867346967e-02f);
   p = fmaf(p, ax, 1.0f);
   p = p * p;
   p = p * p;
   p = p * p;
   p = p * p;
-  return copysignf(1.0f - __builtin_amdgcn_rcpf(p), x);
+  // max(x, 0) as x - min(x, 0): a NaN x passes through (fmaxf would drop it)
+  return fmaf(-0.5f * fminf(ax, 1e30f), __builtin_amdgcn_rcpf(p), x - fminf(x, 0.0f));
 }
-
-// GELU, 0.5 x (1 + erf(x / sqrt 2)).
-IVC_DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
